@@ -1,0 +1,93 @@
+"""Dense chunked prefill attention, written out from its definition (fp64, CPU).
+
+Test infrastructure only (see the package docstring).
+
+What is computed (one chunk, one call):
+
+* A chunk of ``C`` query rows attends over ``T`` keys: the token-major K/V
+  history plus the chunk's own keys ("ANE Prefill Research", section "How the
+  ANE prefill path works": the chunk's rows, the K/V history and an additive
+  mask go in, the attention output comes out).
+* The score of row i against key t is ``scale * (q_i . k_t) + mask[i][t]``: an
+  additive float mask applied before the softmax ("The Four Principles for
+  Optimizing Transformers on the ANE", Principle 3, masking paragraph).  One
+  mask ``[C][T]`` serves every head; that page's ``qk_mask`` has no head axis.
+* A mask entry at or below -30000 marks a key as omitted: its softmax weight is
+  exactly zero, just as a key that was never gathered contributes nothing
+  ("ANE Prefill Research", "What worked", item 2 on folding the sparse
+  indexer's selection into the mask).  Entries above -30000 are ordinary
+  additive biases.  A row whose keys are all omitted outputs zeros.
+* Softmax over keys, then the weighted sum of values ("Flash attention on ANE:
+  fast long-context prefill", section "Flash attention: the core insight",
+  which restates FlashAttention; the tiled GPU kernel must agree with this
+  untiled definition).
+* Grouped-query attention: query head h reads KV head ``h // (Hq // Hkv)``.
+
+Unlike the GPU path, this materialises the masked score matrix (per head, in
+slabs of rows), which is exactly what the pages warn a real implementation must
+not do ("Flash attention on ANE", section "The problem with naive attention on
+ANE").
+"""
+from __future__ import annotations
+
+import numpy as np
+
+DROP_AT = -30000.0  # an entry <= this omits the key
+
+
+def _f64(x) -> np.ndarray:
+    return np.asarray(x, dtype=np.float64)
+
+
+def attention_weights(q_rows, k, mask_rows, scale) -> np.ndarray:
+    """Softmax weights of one head: ``q_rows [R][d]``, ``k [T][d]``,
+    ``mask_rows [R][T]`` -> ``[R][T]`` float64.
+
+    Omitted keys get weight exactly 0.0; an all-omitted row is all zeros.
+    """
+    q = _f64(q_rows)
+    kk = _f64(k)
+    m = _f64(mask_rows)
+    s = float(scale) * (q @ kk.T) + m
+    dropped = m <= DROP_AT
+    s[dropped] = -np.inf
+    row_max = s.max(axis=1, keepdims=True)
+    live = np.isfinite(row_max[:, 0])
+    w = np.zeros_like(s)
+    if live.any():
+        e = np.exp(s[live] - row_max[live])
+        w[live] = e / e.sum(axis=1, keepdims=True)
+    return w
+
+
+def dense_ref(Q, K, V, mask, scale, rows=None, heads=None, slab: int = 256) -> np.ndarray:
+    """Oracle for one chunk of dense prefill attention.
+
+    Q     [C][Hq][d]   query rows of the chunk
+    K, V  [T][Hkv][d]  token-major history plus the chunk's keys
+    mask  [C][T]       additive mask shared by all heads (fp16 values)
+    scale float        softmax scale (the fp32 value the library receives)
+    rows  optional sequence of chunk rows to evaluate (default: all)
+    heads optional sequence of query heads to evaluate (default: all)
+
+    Returns O [len(rows)][len(heads)][d] in float64.
+    """
+    C, Hq, d = Q.shape
+    T, Hkv, _ = K.shape
+    if Hq % Hkv:
+        raise ValueError("query heads must be a multiple of KV heads")
+    if mask.shape[0] != C or mask.shape[1] < T:
+        raise ValueError("mask must be [C][>=T]")
+    group = Hq // Hkv
+    rows = np.arange(C) if rows is None else np.asarray(rows)
+    heads = np.arange(Hq) if heads is None else np.asarray(heads)
+    out = np.zeros((len(rows), len(heads), d), dtype=np.float64)
+    for hi, h in enumerate(heads):
+        g = h // group
+        kg = _f64(K[:, g, :])
+        vg = _f64(V[:, g, :])
+        for s0 in range(0, len(rows), slab):
+            r = rows[s0:s0 + slab]
+            w = attention_weights(Q[r, h, :], kg, mask[r, :T], scale)
+            out[s0:s0 + slab, hi, :] = w @ vg
+    return out
