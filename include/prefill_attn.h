@@ -1,0 +1,173 @@
+/*
+ * prefill_attn.h -- C ABI of the MI355X (gfx950) long-context prefill attention library.
+ *
+ * Four operations make up the path:
+ *   prefill_attn_dense        chunked prefill attention under an arbitrary additive mask
+ *   build_pooled_index        mean-pooled key/value blocks
+ *   select_blocks             alpha-threshold block selection plus the local diagonal
+ *   prefill_attn_blocksparse  exact attention on selected blocks + pooled correction
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - bf16 and fp16 values travel as raw 16-bit patterns (uint16_t).
+ * - Every tensor pointer is a DEVICE pointer owned by the caller. The library
+ *   never allocates, frees, or keeps a pointer after the call returns; scratch
+ *   memory comes from the caller through `workspace`.
+ * - Tensors are dense and row-major in the order written; "token-major" means
+ *   [token][head][head_dim]. Pointers must be 16-byte aligned.
+ * - Query head h reads KV head h / (n_q / n_kv)  (grouped-query attention with
+ *   contiguous groups). n_q must be a multiple of n_kv.
+ * - head_dim d must be 64 or 128; `block` must be a power of two in [16, 256].
+ * - `stream` is a hipStream_t (NULL = the null stream). A call validates its
+ *   arguments on the host first; on any error it returns a negative status and
+ *   enqueues nothing. On success it enqueues its kernels on `stream` and returns
+ *   0 without synchronising. No call falls back to another implementation.
+ * - Batch size is 1; loop over sequences for a batch.
+ *
+ * Sources (page title, section):
+ *   "ANE Prefill Research" -- How the ANE prefill path works (what crosses the
+ *     boundary: the chunk's rows, a token-major K/V history and an additive
+ *     mask go in; the attention output comes out; the mask is arbitrary, not
+ *     causal by contract); What worked, item 2 (a selection folded into the
+ *     mask as -30000 contributes exactly nothing).
+ *   "Flash attention on ANE: fast long-context prefill" -- Flash attention:
+ *     the core insight (tiles and an online softmax instead of the N x N matrix).
+ *   "Wiring CoreML to on-device LLMs: KV-cache, ANE, and the token budget for
+ *     iPhone 16" -- The KV-cache growth formula (a static, caller-allocated
+ *     cache addressed by position).
+ *   "Porting FlashPrefill V2 to Apple silicon for faster prefill" -- Part I
+ *     (pooled index, threshold selection plus diagonal, exact peaks and a
+ *     pooled correction for the rest).
+ */
+#ifndef PREFILL_ATTN_H
+#define PREFILL_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+  PA_OK = 0,
+  PA_EINVAL = -1,        /* a bad argument: null/misaligned pointer, inconsistent sizes, bad scalar */
+  PA_EUNSUPPORTED = -2,  /* valid but outside what the kernels implement (d, block, sizes) */
+  PA_EHIP = -3,          /* the HIP runtime reported an error while enqueueing */
+  PA_EWORKSPACE = -4     /* workspace missing or smaller than the size helper returned */
+};
+
+/* Human-readable text for a status; for PA_EHIP it includes the runtime's message
+ * of the most recent failure on the calling thread. Never NULL. */
+const char* pa_status_string(int status);
+
+/*
+ * prefill_attn_dense -- one chunk of prefill attention over its K/V history.
+ * ("ANE Prefill Research", How the ANE prefill path works; "Flash attention on
+ * ANE", Flash attention: the core insight; "The Four Principles for Optimizing
+ * Transformers on the ANE", Principle 3, additive pre-softmax masks.)
+ *
+ *   Q        bf16 [C][n_q][d]      the chunk's query rows
+ *   K, V     bf16 [T][n_kv][d]     token-major keys/values: history plus the chunk's own
+ *   mask     fp16 [C][mask_ld]     additive mask, columns 0..T-1 used, shared by all heads;
+ *                                  an entry <= -30000 (or -inf) omits the key (weight exactly 0)
+ *   scale    softmax scale, finite and > 0
+ *   O        fp32 [C][n_q][d]      output; a row whose keys are all omitted gets zeros
+ *
+ *   O[i][h] = sum_t w_t V[t][g(h)],  w = softmax_t(scale * Q[i][h].K[t][g(h)] + mask[i][t])
+ *
+ * Requires C >= 1, T >= 1, mask_ld >= T. The mask alone decides visibility; the
+ * library assumes nothing about causality. `workspace` must hold at least
+ * prefill_attn_dense_workspace(C, T, n_q, n_kv, d) bytes (tile flags and, when
+ * the key range is split across workgroups, partial results); it is scratch,
+ * needs no initialisation and may be reused after the stream reaches the call's end.
+ * Errors: PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP.
+ */
+int prefill_attn_dense(const uint16_t* Q, int C, int n_q,
+                       const uint16_t* K, const uint16_t* V, int T, int n_kv, int d,
+                       const uint16_t* mask, int64_t mask_ld,
+                       float scale, float* O,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes prefill_attn_dense needs for these sizes (0 for invalid sizes). */
+size_t prefill_attn_dense_workspace(int C, int T, int n_q, int n_kv, int d);
+
+/*
+ * build_pooled_index -- mean of each block of `block` consecutive keys (and values).
+ * ("Porting FlashPrefill V2 to Apple silicon", Compress keys before the heavy work.)
+ *
+ *   K, V            bf16 [T][n_kv][d]
+ *   K_pool, V_pool  fp32 [n_kv][ceil(T/block)][d]
+ *
+ * Each mean is summed in fp64 in increasing key order, divided once by the
+ * block's key count (the last block may be partial) and rounded once to fp32,
+ * so the result is reproducible bit for bit.
+ * Errors: PA_EINVAL, PA_EUNSUPPORTED, PA_EHIP.
+ */
+int build_pooled_index(const uint16_t* K, const uint16_t* V, int T, int n_kv, int d, int block,
+                       float* K_pool, float* V_pool, void* stream);
+
+/*
+ * select_blocks -- which key blocks each query block attends to exactly.
+ * ("Porting FlashPrefill V2 to Apple silicon", A cheap map of where the
+ * attention lives; The algorithm starts here; figure "Where the kept blocks are".)
+ *
+ *   Q        bf16 [C][n_q][d]   chunk rows at absolute positions q_start .. q_start+C-1
+ *   K_pool   fp32 [n_kv][ceil(T/block)][d] from build_pooled_index; T == q_start + C
+ *   sel_idx  int32 [n_kv][n_qblk][ceil(T/block)]
+ *   sel_cnt  int32 [n_kv][n_qblk],  n_qblk = (q_start+C-1)/block - q_start/block + 1
+ *
+ * For row i at position p, query block j = p / block, and each fully visible
+ * block b < j: r_ib = Q[i].K_pool[b] (fp64, summed over d in increasing order),
+ * M_i = max_b r_ib. Row i votes for b iff r_ib - M_i > ln(alpha)/scale (strict;
+ * alpha = 0 keeps every block). The selection of (KV head g, query block j) is
+ * the union of the votes of this call's rows in block j over g's query heads,
+ * plus j itself. sel_idx lists it in ascending order (so j comes last) and is
+ * zero past sel_cnt.
+ * Requires alpha finite and >= 0, scale finite and > 0,
+ * ceil(T/block) <= 8192.
+ * Errors: PA_EINVAL, PA_EUNSUPPORTED, PA_EHIP.
+ */
+int select_blocks(const uint16_t* Q, int C, int q_start, int n_q, int n_kv, int d,
+                  const float* K_pool, int T, int block, float alpha, float scale,
+                  int32_t* sel_idx, int32_t* sel_cnt, void* stream);
+
+/*
+ * prefill_attn_blocksparse -- causal block-sparse prefill attention.
+ * ("Porting FlashPrefill V2 to Apple silicon", Compute the peaks, summarize the rest.)
+ *
+ *   Q, K, V, K_pool, V_pool, sel_idx, sel_cnt as above; T == q_start + C.
+ *   O   fp32 [C][n_q][d]
+ *
+ * Row i (position p, block j) of head h (KV head g) takes exact attention over
+ * every key of each selected block b < j and over keys j*block..p of its own
+ * block, and, for every unselected block b < j, the pooled pair
+ * (K_pool[g][b], V_pool[g][b]) with weight block * exp(scale*Q.K_pool - m):
+ * a skipped block stands for its `block` keys. All terms share one softmax.
+ * The selection arrays must come from select_blocks for the same chunk.
+ * Errors: PA_EINVAL, PA_EUNSUPPORTED, PA_EHIP.
+ */
+int prefill_attn_blocksparse(const uint16_t* Q, int C, int q_start, int n_q,
+                             const uint16_t* K, const uint16_t* V, int T, int n_kv, int d,
+                             const float* K_pool, const float* V_pool, int block,
+                             const int32_t* sel_idx, const int32_t* sel_cnt,
+                             float scale, float* O, void* stream);
+
+/*
+ * Kernel timing (instrumentation for benchmarks; off by default).
+ * When enabled, each launch of the named kernels is bracketed by HIP events
+ * recorded on the launch stream. pa_timing_read synchronises those events and
+ * returns the summed milliseconds and launch count for `kernel`, one of
+ * "attn_dense", "attn_blocksparse", "mask_classify", "attn_combine", "pool", "select".
+ * pa_timing_reset clears the totals. Returns PA_OK or PA_EINVAL/PA_EHIP.
+ */
+int pa_timing_enable(int on);
+int pa_timing_reset(void);
+int pa_timing_read(const char* kernel, double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PREFILL_ATTN_H */

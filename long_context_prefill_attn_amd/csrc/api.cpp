@@ -1,0 +1,239 @@
+// C ABI of the prefill attention library: argument validation, launch planning,
+// status codes and optional kernel timing. Every entry point validates on the
+// host before touching the GPU; on an error nothing is enqueued. There is no
+// fallback path: a request the kernels cannot serve is refused with a status.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/prefill_attn.h"
+#include "common.h"
+
+namespace {
+
+thread_local std::string g_last_hip_error;
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return PA_OK;
+  g_last_hip_error = hipGetErrorString(e);
+  return PA_EHIP;
+}
+
+bool aligned16(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool pow2_block(int b) { return b >= 16 && b <= 256 && (b & (b - 1)) == 0; }
+bool good_scale(float s) { return std::isfinite(s) && s > 0.f; }
+
+// ---------------------------------------------------------------- timing
+struct TimedKernel {
+  const char* name;
+  double total_ms = 0.0;
+  int64_t launches = 0;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pending;
+};
+
+std::mutex g_timing_mu;
+bool g_timing_on = false;
+TimedKernel g_timed[] = {{"attn_dense"}, {"attn_blocksparse"}, {"mask_classify"},
+                         {"attn_combine"}, {"pool"}, {"select"}};
+std::vector<hipEvent_t> g_event_pool;
+
+hipEvent_t take_event() {
+  if (!g_event_pool.empty()) {
+    hipEvent_t e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+TimedKernel* find_timed(const char* name) {
+  for (auto& t : g_timed)
+    if (std::strcmp(t.name, name) == 0) return &t;
+  return nullptr;
+}
+
+// Runs `launch` on `stream`, bracketed by events when timing is on.
+template <class F>
+hipError_t timed(const char* name, hipStream_t stream, F&& launch) {
+  hipEvent_t a = nullptr, b = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    if (g_timing_on) {
+      a = take_event();
+      b = take_event();
+    }
+  }
+  if (a && b) {
+    hipError_t e = hipEventRecord(a, stream);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t err = launch();
+  if (a && b) {
+    if (err == hipSuccess) err = hipEventRecord(b, stream);
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    if (err == hipSuccess) find_timed(name)->pending.emplace_back(a, b);
+    else { g_event_pool.push_back(a); g_event_pool.push_back(b); }
+  }
+  return err;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(int status) {
+  switch (status) {
+    case PA_OK: return "ok";
+    case PA_EINVAL: return "invalid argument";
+    case PA_EUNSUPPORTED: return "unsupported size or parameter";
+    case PA_EWORKSPACE: return "workspace missing or too small";
+    case PA_EHIP: {
+      thread_local std::string msg;
+      msg = "HIP runtime error: " + g_last_hip_error;
+      return msg.c_str();
+    }
+    default: return "unknown status";
+  }
+}
+
+size_t prefill_attn_dense_workspace(int C, int T, int n_q, int n_kv, int d) {
+  if (C < 1 || T < 1 || n_q < 1 || n_kv < 1 || n_q % n_kv || (d != 64 && d != 128)) return 0;
+  return pa::plan_dense(C, T, n_q, n_kv, d).total_bytes;
+}
+
+int prefill_attn_dense(const uint16_t* Q, int C, int n_q, const uint16_t* K, const uint16_t* V,
+                       int T, int n_kv, int d, const uint16_t* mask, int64_t mask_ld, float scale,
+                       float* O, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(mask) || !aligned16(O))
+    return PA_EINVAL;
+  if (C < 1 || T < 1 || n_q < 1 || n_kv < 1 || n_q % n_kv != 0) return PA_EINVAL;
+  if (mask_ld < T || !good_scale(scale)) return PA_EINVAL;
+  if (d != 64 && d != 128) return PA_EUNSUPPORTED;
+  const pa::DensePlan plan = pa::plan_dense(C, T, n_q, n_kv, d);
+  if ((long long)plan.n_qt * n_q * plan.splits >= (1LL << 31)) return PA_EUNSUPPORTED;
+  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
+      workspace_bytes < plan.total_bytes)
+    return PA_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* flags = static_cast<uint8_t*>(workspace);
+  float* part_o = plan.splits > 1 ? reinterpret_cast<float*>(flags + plan.flags_bytes) : nullptr;
+  float* part_ml =
+      plan.splits > 1 ? reinterpret_cast<float*>(flags + plan.flags_bytes + plan.part_o_bytes) : nullptr;
+  hipError_t e = timed("mask_classify", s, [&] {
+    return pa::launch_mask_classify(mask, mask_ld, C, T, flags, s);
+  });
+  if (e != hipSuccess) return hip_status(e);
+  e = timed("attn_dense", s, [&] {
+    return pa::launch_attn_dense(Q, C, n_q, K, V, T, n_kv, d, mask, mask_ld, scale, O, plan, flags,
+                                 part_o, part_ml, s);
+  });
+  if (e != hipSuccess) return hip_status(e);
+  if (plan.splits > 1) {
+    e = timed("attn_combine", s, [&] {
+      return pa::launch_attn_combine(C, n_q, d, plan.splits, part_o, part_ml, O, s);
+    });
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return PA_OK;
+}
+
+int build_pooled_index(const uint16_t* K, const uint16_t* V, int T, int n_kv, int d, int block,
+                       float* K_pool, float* V_pool, void* stream) {
+  if (!aligned16(K) || !aligned16(V) || !aligned16(K_pool) || !aligned16(V_pool)) return PA_EINVAL;
+  if (T < 1 || n_kv < 1) return PA_EINVAL;
+  if ((d != 64 && d != 128) || !pow2_block(block)) return PA_EUNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(timed("pool", s, [&] {
+    return pa::launch_pool(K, V, T, n_kv, d, block, K_pool, V_pool, s);
+  }));
+}
+
+int select_blocks(const uint16_t* Q, int C, int q_start, int n_q, int n_kv, int d,
+                  const float* K_pool, int T, int block, float alpha, float scale,
+                  int32_t* sel_idx, int32_t* sel_cnt, void* stream) {
+  if (!aligned16(Q) || !aligned16(K_pool) || !aligned16(sel_idx) || !aligned16(sel_cnt))
+    return PA_EINVAL;
+  if (C < 1 || q_start < 0 || n_q < 1 || n_kv < 1 || n_q % n_kv != 0) return PA_EINVAL;
+  if ((long long)q_start + C != T) return PA_EINVAL;
+  if (!std::isfinite(alpha) || alpha < 0.f || !good_scale(scale)) return PA_EINVAL;
+  if ((d != 64 && d != 128) || !pow2_block(block)) return PA_EUNSUPPORTED;
+  const int nb = (T + block - 1) / block;
+  if (nb > 8192) return PA_EUNSUPPORTED;
+  // theta = ln(alpha)/scale in fp64; alpha = 0 keeps every block
+  const double theta = alpha == 0.f ? -HUGE_VAL : std::log((double)alpha) / (double)scale;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(timed("select", s, [&] {
+    return pa::launch_select(Q, C, q_start, n_q, n_kv, d, K_pool, T, block, theta, sel_idx, sel_cnt, s);
+  }));
+}
+
+int prefill_attn_blocksparse(const uint16_t* Q, int C, int q_start, int n_q, const uint16_t* K,
+                             const uint16_t* V, int T, int n_kv, int d, const float* K_pool,
+                             const float* V_pool, int block, const int32_t* sel_idx,
+                             const int32_t* sel_cnt, float scale, float* O, void* stream) {
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(K_pool) || !aligned16(V_pool) ||
+      !aligned16(sel_idx) || !aligned16(sel_cnt) || !aligned16(O))
+    return PA_EINVAL;
+  if (C < 1 || q_start < 0 || n_q < 1 || n_kv < 1 || n_q % n_kv != 0) return PA_EINVAL;
+  if ((long long)q_start + C != T || !good_scale(scale)) return PA_EINVAL;
+  if (d != 64 && d != 128) return PA_EUNSUPPORTED;
+  if (block != 128) return PA_EUNSUPPORTED;  // the attention kernel tiles query blocks of 128
+  const int nb = (T + block - 1) / block;
+  if (nb > 8192) return PA_EUNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(timed("attn_blocksparse", s, [&] {
+    return pa::launch_attn_blocksparse(Q, C, q_start, n_q, K, V, T, n_kv, d, K_pool, V_pool, block,
+                                       sel_idx, sel_cnt, scale, O, s);
+  }));
+}
+
+int pa_timing_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  g_timing_on = on != 0;
+  return PA_OK;
+}
+
+int pa_timing_reset(void) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  for (auto& t : g_timed) {
+    for (auto& pr : t.pending) {
+      hipEventSynchronize(pr.second);
+      g_event_pool.push_back(pr.first);
+      g_event_pool.push_back(pr.second);
+    }
+    t.pending.clear();
+    t.total_ms = 0.0;
+    t.launches = 0;
+  }
+  return PA_OK;
+}
+
+int pa_timing_read(const char* kernel, double* total_ms, int64_t* launches) {
+  if (kernel == nullptr || total_ms == nullptr || launches == nullptr) return PA_EINVAL;
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  TimedKernel* t = find_timed(kernel);
+  if (t == nullptr) return PA_EINVAL;
+  for (auto& pr : t->pending) {
+    hipError_t e = hipEventSynchronize(pr.second);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, pr.first, pr.second);
+    if (e != hipSuccess) return hip_status(e);
+    t->total_ms += ms;
+    t->launches += 1;
+    g_event_pool.push_back(pr.first);
+    g_event_pool.push_back(pr.second);
+  }
+  t->pending.clear();
+  *total_ms = t->total_ms;
+  *launches = t->launches;
+  return PA_OK;
+}
+
+}  // extern "C"

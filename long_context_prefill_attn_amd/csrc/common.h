@@ -1,0 +1,88 @@
+// Shared device helpers and host-side launch declarations for the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// tile classification of the additive mask (one flag per 128 x 128 tile)
+enum : uint8_t { TILE_ZERO = 0, TILE_DROPPED = 1, TILE_MIXED = 2 };
+constexpr int FLAG_TILE = 128;
+
+// fp16 bit pattern of -30000; an entry is "dropped" when its value is <= -30000
+constexpr uint16_t F16_DROP_MAG = 0x7753;
+
+__device__ __forceinline__ bool f16_dropped(uint16_t h) {
+  const uint16_t mag = h & 0x7FFF;
+  return (h & 0x8000) && mag >= F16_DROP_MAG && mag <= 0x7C00;  // excludes NaN
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// Swap values between lane l and lane l^32 of a wave64 and return the partner's value.
+__device__ __forceinline__ float partner32(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  // r[0]: lanes 0..31 keep their own value, lanes 32..63 receive lanes 0..31;
+  // r[1]: lanes 0..31 receive lanes 32..63, lanes 32..63 keep their own value.
+  const bool low = (__lane_id() < 32);
+  return __uint_as_float(low ? r[1] : r[0]);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 f = {lo, hi};
+  bf16x2 b = __builtin_convertvector(f, bf16x2);  // v_cvt_pk_bf16_f32, round to nearest even
+  return __builtin_bit_cast(uint32_t, b);
+}
+
+}  // namespace pa
+
+// ---------------------------------------------------------------------------
+// host-side launchers (defined next to their kernels); all enqueue on `stream`
+// ---------------------------------------------------------------------------
+namespace pa {
+
+struct KernelTimer;  // opaque; see api.cpp
+
+hipError_t launch_pool(const uint16_t* K, const uint16_t* V, int T, int n_kv, int d, int block,
+                       float* K_pool, float* V_pool, hipStream_t stream);
+
+hipError_t launch_select(const uint16_t* Q, int C, int q_start, int n_q, int n_kv, int d,
+                         const float* K_pool, int T, int block, double theta,
+                         int32_t* sel_idx, int32_t* sel_cnt, hipStream_t stream);
+
+hipError_t launch_mask_classify(const uint16_t* mask, int64_t mask_ld, int C, int T,
+                                uint8_t* flags, hipStream_t stream);
+
+struct DensePlan {
+  int n_qt;      // query tiles of 128 rows
+  int n_ktile;   // flag tiles of 128 keys
+  int splits;    // key-range splits per (query tile, head)
+  size_t flags_bytes, part_o_bytes, part_ml_bytes, total_bytes;
+};
+DensePlan plan_dense(int C, int T, int n_q, int n_kv, int d);
+
+hipError_t launch_attn_dense(const uint16_t* Q, int C, int n_q, const uint16_t* K, const uint16_t* V,
+                             int T, int n_kv, int d, const uint16_t* mask, int64_t mask_ld,
+                             float scale, float* O, const DensePlan& plan, const uint8_t* flags,
+                             float* part_o, float* part_ml, hipStream_t stream);
+
+hipError_t launch_attn_combine(int C, int n_q, int d, int splits, const float* part_o,
+                               const float* part_ml, float* O, hipStream_t stream);
+
+hipError_t launch_attn_blocksparse(const uint16_t* Q, int C, int q_start, int n_q,
+                                   const uint16_t* K, const uint16_t* V, int T, int n_kv, int d,
+                                   const float* K_pool, const float* V_pool, int block,
+                                   const int32_t* sel_idx, const int32_t* sel_cnt,
+                                   float scale, float* O, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,115 @@
+// Mask-tile classification and split-key combination for dense prefill attention.
+#include "common.h"
+
+namespace pa {
+
+// ---------------------------------------------------------------------------
+// mask_classify: one workgroup per 128 x 128 tile of the fp16 mask.
+// ZERO     every entry is +-0      -> the attention kernel never reads the tile
+// DROPPED  every entry <= -30000   -> the attention kernel skips the tile
+// MIXED    anything else           -> the attention kernel reads the tile
+// A dropped entry omits its key ("ANE Prefill Research", What worked, item 2),
+// so a fully dropped tile contributes nothing and needs no arithmetic at all.
+// Each thread reads 8 x 16 bytes (rows tid/16 + 16i, columns (tid%16)*8 ..):
+// 16 lanes cover one 256-byte tile row, so a wave reads 4 rows per instruction.
+// grid = (ceil(T/128), ceil(C/128)), block = 256.
+// ---------------------------------------------------------------------------
+template <bool VEC>
+__global__ void __launch_bounds__(256) mask_classify_kernel(const uint16_t* __restrict__ mask,
+                                                            int64_t ld, int C, int T,
+                                                            uint8_t* __restrict__ flags) {
+  const int kt = blockIdx.x, qt = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int c0 = kt * FLAG_TILE + (tid % 16) * 8;
+  bool all_zero = true, all_drop = true;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = qt * FLAG_TILE + tid / 16 + 16 * i;
+    if (r >= C) break;
+    const uint16_t* p = mask + (size_t)r * ld + c0;
+    if (VEC && c0 + 8 <= T) {
+      const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint16_t lo = v[w] & 0xFFFF, hi = v[w] >> 16;
+        all_zero &= ((lo & 0x7FFF) == 0) && ((hi & 0x7FFF) == 0);
+        all_drop &= f16_dropped(lo) && f16_dropped(hi);
+      }
+    } else {
+      for (int e = 0; e < 8; ++e) {
+        if (c0 + e >= T) break;
+        const uint16_t h = p[e];
+        all_zero &= (h & 0x7FFF) == 0;
+        all_drop &= f16_dropped(h);
+      }
+    }
+  }
+  const int z = __syncthreads_and(all_zero);
+  const int dr = __syncthreads_and(all_drop);
+  if (tid == 0)
+    flags[(size_t)qt * gridDim.x + kt] = dr ? TILE_DROPPED : (z ? TILE_ZERO : TILE_MIXED);
+}
+
+hipError_t launch_mask_classify(const uint16_t* mask, int64_t mask_ld, int C, int T,
+                                uint8_t* flags, hipStream_t stream) {
+  dim3 grid((T + FLAG_TILE - 1) / FLAG_TILE, (C + FLAG_TILE - 1) / FLAG_TILE);
+  const bool vec = (mask_ld % 8) == 0 && (reinterpret_cast<uintptr_t>(mask) % 16) == 0;
+  if (vec)
+    hipLaunchKernelGGL(mask_classify_kernel<true>, grid, dim3(256), 0, stream, mask, mask_ld, C, T,
+                       flags);
+  else
+    hipLaunchKernelGGL(mask_classify_kernel<false>, grid, dim3(256), 0, stream, mask, mask_ld, C, T,
+                       flags);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// attn_combine: merge the partial (m, l, O) of the key-range splits of each
+// (row, head). m is in log2 units and is the reference each split used for its
+// weights: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, M = max m_s over
+// splits with l_s > 0. A row with no visible key in any split outputs zeros.
+// part_o [splits][rows*heads][d], part_ml [splits][rows*heads][2].
+// One thread per 4 output columns; block = 256.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) attn_combine_kernel(int rows, int d, int splits,
+                                                           const float* __restrict__ part_o,
+                                                           const float* __restrict__ part_ml,
+                                                           float* __restrict__ O) {
+  const int per_row = d / 4;
+  const int gid = blockIdx.x * 256 + threadIdx.x;
+  const int row = gid / per_row;
+  if (row >= rows) return;
+  const int c = (gid % per_row) * 4;
+  float M = -__builtin_inff();
+  for (int s = 0; s < splits; ++s) {
+    const float* ml = part_ml + ((size_t)s * rows + row) * 2;
+    if (ml[1] > 0.f) M = fmaxf(M, ml[0]);
+  }
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float L = 0.f;
+  if (M != -__builtin_inff()) {
+    for (int s = 0; s < splits; ++s) {
+      const float* ml = part_ml + ((size_t)s * rows + row) * 2;
+      if (!(ml[1] > 0.f)) continue;
+      const float w = exp2f(ml[0] - M);
+      L += w * ml[1];
+      const float4 o = *reinterpret_cast<const float4*>(part_o + ((size_t)s * rows + row) * d + c);
+      acc.x += w * o.x; acc.y += w * o.y; acc.z += w * o.z; acc.w += w * o.w;
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  *reinterpret_cast<float4*>(O + (size_t)row * d + c) =
+      make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+}
+
+hipError_t launch_attn_combine(int C, int n_q, int d, int splits, const float* part_o,
+                               const float* part_ml, float* O, hipStream_t stream) {
+  const int rows = C * n_q;
+  const long threads = (long)rows * (d / 4);
+  const int blocks = (int)((threads + 255) / 256);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(blocks), dim3(256), 0, stream, rows, d, splits,
+                     part_o, part_ml, O);
+  return hipGetLastError();
+}
+
+}  // namespace pa

@@ -1,0 +1,117 @@
+"""The C ABI library loads, exports every declared entry point, and refuses bad
+arguments on the host with the documented status codes (no GPU needed: every
+case here is rejected before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_prefill_attn_amd import _lib
+
+HDR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "prefill_attn.h")
+FAKE = 0x100000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HDR).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(?:int|size_t|const char\*)\s+(\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.lib()
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    lib = _lib.lib()
+    for code in (0, -1, -2, -3, -4, 7):
+        assert lib.pa_status_string(code)
+
+
+def dense(**kw):
+    a = dict(Q=FAKE, C=64, n_q=4, K=FAKE, V=FAKE, T=256, n_kv=2, d=128, mask=FAKE, ld=256,
+             scale=0.125, O=FAKE, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return _lib.lib().prefill_attn_dense(a["Q"], a["C"], a["n_q"], a["K"], a["V"], a["T"], a["n_kv"],
+                                         a["d"], a["mask"], a["ld"], a["scale"], a["O"], a["ws"],
+                                         a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=None), _lib.PA_EINVAL),
+    (dict(K=FAKE + 2), _lib.PA_EINVAL),           # misaligned
+    (dict(C=0), _lib.PA_EINVAL),
+    (dict(T=0), _lib.PA_EINVAL),
+    (dict(n_q=3), _lib.PA_EINVAL),                # not a multiple of n_kv
+    (dict(ld=255), _lib.PA_EINVAL),               # mask_ld < T
+    (dict(scale=float("nan")), _lib.PA_EINVAL),
+    (dict(scale=-1.0), _lib.PA_EINVAL),
+    (dict(scale=float("inf")), _lib.PA_EINVAL),
+    (dict(d=96), _lib.PA_EUNSUPPORTED),
+    (dict(), _lib.PA_EWORKSPACE),                 # no workspace
+    (dict(ws=FAKE + 16, ws_bytes=1 << 30), _lib.PA_EWORKSPACE),  # workspace not 256-aligned
+    (dict(ws=FAKE, ws_bytes=1), _lib.PA_EWORKSPACE),
+])
+def test_dense_rejects(kw, code):
+    assert dense(**kw) == code
+
+
+def test_dense_workspace_size():
+    lib = _lib.lib()
+    assert lib.prefill_attn_dense_workspace(64, 256, 4, 2, 128) >= 256
+    assert lib.prefill_attn_dense_workspace(0, 256, 4, 2, 128) == 0
+    assert lib.prefill_attn_dense_workspace(64, 256, 4, 2, 96) == 0
+
+
+def sel(**kw):
+    a = dict(Q=FAKE, C=256, q_start=0, n_q=4, n_kv=2, d=128, Kp=FAKE, T=256, block=128, alpha=0.1,
+             scale=0.125, idx=FAKE, cnt=FAKE, stream=None)
+    a.update(kw)
+    return _lib.lib().select_blocks(a["Q"], a["C"], a["q_start"], a["n_q"], a["n_kv"], a["d"], a["Kp"],
+                                    a["T"], a["block"], a["alpha"], a["scale"], a["idx"], a["cnt"],
+                                    a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Q=None), _lib.PA_EINVAL),
+    (dict(T=300), _lib.PA_EINVAL),                # T != q_start + C
+    (dict(alpha=float("nan")), _lib.PA_EINVAL),
+    (dict(alpha=-0.1), _lib.PA_EINVAL),
+    (dict(alpha=float("inf")), _lib.PA_EINVAL),
+    (dict(scale=0.0), _lib.PA_EINVAL),
+    (dict(block=100), _lib.PA_EUNSUPPORTED),
+    (dict(block=512), _lib.PA_EUNSUPPORTED),
+    (dict(d=80), _lib.PA_EUNSUPPORTED),
+    (dict(C=16 * 8192 + 16, T=16 * 8192 + 16, block=16), _lib.PA_EUNSUPPORTED),  # > 8192 blocks
+])
+def test_select_rejects(kw, code):
+    assert sel(**kw) == code
+
+
+def test_pool_and_blocksparse_reject():
+    lib = _lib.lib()
+    assert lib.build_pooled_index(None, FAKE, 10, 1, 128, 128, FAKE, FAKE, None) == _lib.PA_EINVAL
+    assert lib.build_pooled_index(FAKE, FAKE, 0, 1, 128, 128, FAKE, FAKE, None) == _lib.PA_EINVAL
+    assert lib.build_pooled_index(FAKE, FAKE, 10, 1, 128, 48, FAKE, FAKE, None) == _lib.PA_EUNSUPPORTED
+    bs = lambda **kw: lib.prefill_attn_blocksparse(
+        kw.get("Q", FAKE), 256, 0, 4, FAKE, FAKE, kw.get("T", 256), 2, kw.get("d", 128), FAKE, FAKE,
+        kw.get("block", 128), FAKE, FAKE, kw.get("scale", 0.1), FAKE, None)
+    assert bs(Q=None) == _lib.PA_EINVAL
+    assert bs(T=255) == _lib.PA_EINVAL
+    assert bs(scale=float("nan")) == _lib.PA_EINVAL
+    assert bs(block=64) == _lib.PA_EUNSUPPORTED
+    assert bs(d=256) == _lib.PA_EUNSUPPORTED
+
+
+def test_timing_api_host_side():
+    lib = _lib.lib()
+    ms, n = ctypes.c_double(), ctypes.c_int64()
+    assert lib.pa_timing_read(b"nope", ctypes.byref(ms), ctypes.byref(n)) == _lib.PA_EINVAL
+    assert lib.pa_timing_reset() == 0
+    assert lib.pa_timing_read(b"attn_dense", ctypes.byref(ms), ctypes.byref(n)) == 0
+    assert n.value == 0

@@ -1,0 +1,244 @@
+"""GPU parity: the HIP path, called through the C ABI, against the fp64 CPU oracle.
+
+Bars: pooled index and selection bit-exact; attention elementwise
+|gpu - oracle| <= 2e-3 + 1e-2 |oracle|. Inputs are the seeded workloads (or
+small seeded cases for edge shapes); no oracle input or expected value comes
+from the GPU.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import blocksparse_ref, dense_ref, pooled_index_ref, select_ref, selection_sets
+from workloads import CONFIGS, bf16_bits, causal_mask, make_workload
+from _util import assert_close, dev_bf16, dev_f16, f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def lp():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import long_context_prefill_attn_amd as m
+    m.lib()
+    return m
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+# ---------------------------------------------------------------- runners
+def gpu_dense(lp, q, k, v, mask, scale, ld=None):
+    C, T = q.shape[0], k.shape[0]
+    if ld is not None and ld != mask.shape[1]:
+        padded = np.full((C, ld), np.float16(7.0), dtype=np.float16)   # junk past T must be ignored
+        padded[:, :T] = mask[:, :T]
+        mask = padded
+    O = lp.prefill_attn_dense(dev_bf16(q), dev_bf16(k), dev_bf16(v), dev_f16(mask), scale)
+    torch.cuda.synchronize()
+    return O.cpu().numpy()
+
+
+def rand_bits(rng, *shape, s=1.0):
+    return bf16_bits(rng.standard_normal(shape).astype(np.float32) * s)
+
+
+# ---------------------------------------------------------------- pooled index
+@pytest.mark.parametrize("T,n_kv,d,block", [(4333, 4, 128, 128), (1000, 3, 64, 16), (777, 2, 128, 256),
+                                            (64, 1, 64, 64), (1, 2, 128, 128)])
+def test_pool_bit_exact(lp, T, n_kv, d, block):
+    rng = np.random.default_rng(T + d + block)
+    k, v = rand_bits(rng, T, n_kv, d), rand_bits(rng, T, n_kv, d, s=3.0)
+    say("pool", T, n_kv, d, block)
+    kp, vp = lp.build_pooled_index(dev_bf16(k), dev_bf16(v), block)
+    torch.cuda.synchronize()
+    rk, rv = pooled_index_ref(f64(k), f64(v), block)
+    assert np.array_equal(kp.cpu().numpy().view(np.uint32), rk.view(np.uint32))
+    assert np.array_equal(vp.cpu().numpy().view(np.uint32), rv.view(np.uint32))
+
+
+# ---------------------------------------------------------------- selection
+@pytest.mark.parametrize("C,q_start,n_q,n_kv,d,block,alpha", [
+    (512, 0, 4, 2, 128, 128, 0.1),
+    (300, 37, 4, 1, 128, 64, 0.2),       # chunk starting mid-block
+    (256, 256, 8, 2, 64, 32, 0.1),
+    (200, 1000, 2, 2, 128, 128, 0.0),    # alpha 0 keeps everything
+    (200, 1000, 2, 2, 128, 128, 1.0),    # alpha 1 keeps only the diagonal
+    (1, 5000, 4, 4, 128, 16, 0.3),       # a single row over 313 blocks
+])
+def test_select_bit_exact(lp, C, q_start, n_q, n_kv, d, block, alpha):
+    rng = np.random.default_rng(C + q_start)
+    T = q_start + C
+    q = rand_bits(rng, C, n_q, d, s=2.0)
+    k = rand_bits(rng, T, n_kv, d, s=2.0)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    say("select", C, q_start, n_q, n_kv, d, block, alpha)
+    kp, _ = lp.build_pooled_index(dev_bf16(k), dev_bf16(k), block)
+    idx, cnt = lp.select_blocks(dev_bf16(q), kp, q_start, block, alpha, scale)
+    torch.cuda.synchronize()
+    rkp, _ = pooled_index_ref(f64(k), f64(k), block)
+    ridx, rcnt = select_ref(f64(q), rkp, q_start, block, alpha, scale)
+    assert np.array_equal(cnt.cpu().numpy(), rcnt)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+
+
+# ---------------------------------------------------------------- dense: configs
+@pytest.mark.parametrize("name", ["tiny", "gqa4k", "fold2k5"])
+def test_dense_configs(lp, name):
+    w = make_workload(name)
+    for idx in range(len(w.spec.chunks)):
+        q_start, C, T, q, k, v, mask = w.chunk(idx)
+        say("dense", name, "chunk", idx, "C", C, "T", T)
+        got = gpu_dense(lp, q, k, v, mask, w.spec.scale)
+        want = dense_ref(f64(q), f64(k), f64(v), mask, w.spec.scale)
+        assert_close(got, want, f"{name} chunk {idx}")
+
+
+def test_dense_128k_sampled_rows(lp):
+    """Full 128K workload (32 chunks of 4,096, 32/8 heads): chunks 0, 7 and 31 as
+    the bench launches them, checked on sampled rows."""
+    w = make_workload("dense128k")
+    rows = np.concatenate([np.arange(0, 4096, 97), [4095]])
+    for idx in (0, 7, 31):
+        q_start, C, T, q, k, v, mask = w.chunk(idx)
+        say("dense128k chunk", idx, "T", T)
+        got = gpu_dense(lp, q, k, v, mask, w.spec.scale)
+        want = dense_ref(f64(q[rows]), f64(k), f64(v), mask[rows], w.spec.scale)
+        assert_close(got[rows], want, f"dense128k chunk {idx}")
+
+
+# ---------------------------------------------------------------- dense: edge cases
+def _edge(seed, C, T, n_q, n_kv, d, kind):
+    rng = np.random.default_rng(seed)
+    q = rand_bits(rng, C, n_q, d)
+    k = rand_bits(rng, T, n_kv, d)
+    v = rand_bits(rng, T, n_kv, d)
+    P0 = T - C
+    if kind == "causal":
+        mask = causal_mask(P0, C, T)
+    elif kind == "random":
+        m = rng.normal(0.0, 1.0, (C, T))
+        m[rng.random((C, T)) < 0.3] = -30000.0
+        m[rng.random((C, T)) < 0.05] = -np.inf
+        m[rng.random((C, T)) < 0.05] = -1.0e4          # finite, follows the formula
+        m[0, :] = -30000.0                               # an all-dropped row -> zeros
+        mask = m.astype(np.float16)
+    elif kind == "band":
+        # keys in [T/4, T/2) are dropped for every row: whole tiles to skip
+        mask = causal_mask(P0, C, T)
+        mask[:, T // 4: T // 2] = np.float16(-30000.0)
+    else:
+        raise ValueError(kind)
+    return q, k, v, mask
+
+
+@pytest.mark.parametrize("C,T,n_q,n_kv,d,kind,ld", [
+    (1, 1, 1, 1, 128, "causal", None),
+    (1, 301, 4, 2, 128, "causal", None),
+    (200, 5000, 2, 1, 128, "causal", None),     # few workgroups -> split key range + combine
+    (129, 700, 8, 8, 64, "random", None),
+    (333, 1500, 4, 1, 128, "random", 1513),     # padded, unaligned mask rows
+    (256, 4096, 4, 2, 128, "band", 4104),
+    (100, 100, 6, 2, 64, "causal", None),
+    (37, 4100, 4, 4, 128, "random", None),      # split path with a random mask
+])
+def test_dense_edge_cases(lp, C, T, n_q, n_kv, d, kind, ld):
+    q, k, v, mask = _edge(C * 7 + T, C, T, n_q, n_kv, d, kind)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    say("dense edge", C, T, n_q, n_kv, d, kind, ld)
+    got = gpu_dense(lp, q, k, v, mask, scale, ld=ld)
+    want = dense_ref(f64(q), f64(k), f64(v), mask, scale)
+    assert_close(got, want, f"edge {C},{T},{kind}")
+    if kind == "random":
+        assert np.all(got[0] == 0.0)
+
+
+def test_dense_is_deterministic(lp):
+    w = make_workload("gqa4k")
+    q_start, C, T, q, k, v, mask = w.chunk(1)
+    say("determinism gqa4k tail")
+    a = gpu_dense(lp, q, k, v, mask, w.spec.scale)
+    b = gpu_dense(lp, q, k, v, mask, w.spec.scale)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+# ---------------------------------------------------------------- block-sparse
+def _blocksparse_gpu(lp, q, k, v, q_start, block, alpha, scale):
+    Qd, Kd, Vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    kp, vp = lp.build_pooled_index(Kd, Vd, block)
+    idx, cnt = lp.select_blocks(Qd, kp, q_start, block, alpha, scale)
+    O = lp.prefill_attn_blocksparse(Qd, Kd, Vd, kp, vp, idx, cnt, q_start, block, scale)
+    torch.cuda.synchronize()
+    return kp.cpu().numpy(), vp.cpu().numpy(), idx.cpu().numpy(), cnt.cpu().numpy(), O.cpu().numpy()
+
+
+@pytest.mark.parametrize("seed,N,q_start,n_q,n_kv,d,alpha,s", [
+    (0, 1024, 0, 4, 2, 128, 0.1, 1.0),
+    (1, 1000, 300, 4, 1, 128, 0.2, 1.0),     # chunk starts mid-block, ragged end
+    (2, 700, 0, 2, 2, 64, 0.05, 1.0),
+    (3, 2048, 1024, 8, 2, 128, 0.5, 0.5),    # small |q|: pooled rows carry real weight
+])
+def test_blocksparse_small(lp, seed, N, q_start, n_q, n_kv, d, alpha, s):
+    rng = np.random.default_rng(seed)
+    q = rand_bits(rng, N - q_start, n_q, d, s=s)
+    k = rand_bits(rng, N, n_kv, d, s=s)
+    v = rand_bits(rng, N, n_kv, d)
+    B = 128
+    scale = float(np.float32(1 / math.sqrt(d)))
+    say("blocksparse small", seed, N, q_start, n_q, n_kv, d, alpha)
+    kp, vp, idx, cnt, got = _blocksparse_gpu(lp, q, k, v, q_start, B, alpha, scale)
+    rkp, rvp = pooled_index_ref(f64(k), f64(v), B)
+    assert np.array_equal(kp.view(np.uint32), rkp.view(np.uint32))
+    assert np.array_equal(vp.view(np.uint32), rvp.view(np.uint32))
+    ridx, rcnt = select_ref(f64(q), rkp, q_start, B, alpha, scale)
+    assert np.array_equal(cnt, rcnt) and np.array_equal(idx, ridx)
+    want = blocksparse_ref(f64(q), f64(k), f64(v), rkp, rvp, ridx, rcnt, q_start, B, scale)
+    assert_close(got, want, f"blocksparse seed {seed}")
+
+
+def test_blocksparse_alpha_zero_equals_dense(lp):
+    rng = np.random.default_rng(9)
+    N, n_q, n_kv, d = 1536, 4, 2, 128
+    q, k, v = rand_bits(rng, N, n_q, d), rand_bits(rng, N, n_kv, d), rand_bits(rng, N, n_kv, d)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    say("blocksparse alpha 0")
+    *_, cnt, got = _blocksparse_gpu(lp, q, k, v, 0, 128, 0.0, scale)
+    assert np.all(cnt == np.arange(1, N // 128 + 1)[None, :])
+    want = dense_ref(f64(q), f64(k), f64(v), causal_mask(0, N), scale)
+    assert_close(got, want, "alpha 0")
+
+
+def test_blocksparse_32k_sampled(lp):
+    """Full planted 32K workload as the bench runs it: pooled index bit-exact in
+    full, selection bit-exact on sampled query blocks of every KV head, and the
+    output on sampled rows of every head."""
+    w = make_workload("sparse32k")
+    s = w.spec
+    B = s.block
+    say("blocksparse 32K")
+    kp, vp, idx, cnt, got = _blocksparse_gpu(lp, w.Q, w.K, w.V, 0, B, s.alpha, s.scale)
+    Q64, K64, V64 = f64(w.Q), f64(w.K), f64(w.V)
+    rkp, rvp = pooled_index_ref(K64, V64, B)
+    assert np.array_equal(kp.view(np.uint32), rkp.view(np.uint32))
+    assert np.array_equal(vp.view(np.uint32), rvp.view(np.uint32))
+    qblocks = [0, 1, 17, 20, 64, 127, 200, 255]
+    sets = selection_sets(Q64, rkp, 0, B, s.alpha, s.scale, qblocks=qblocks)
+    nb = s.N // B
+    ridx = np.zeros((s.n_kv, nb, nb), dtype=np.int32)
+    rcnt = np.zeros((s.n_kv, nb), dtype=np.int32)
+    for (g, j), kept in sets.items():
+        ridx[g, j, :len(kept)] = kept
+        rcnt[g, j] = len(kept)
+        assert np.array_equal(idx[g, j], ridx[g, j]), (g, j)
+        assert cnt[g, j] == rcnt[g, j], (g, j)
+    visible = sum(j + 1 for j in range(nb)) * s.n_kv
+    say("sparsity", 1.0 - cnt.sum() / visible)
+    rows = np.array([j * B + o for j in qblocks for o in (0, 63, 127)])
+    want = blocksparse_ref(Q64, K64, V64, rkp, rvp, ridx, rcnt, 0, B, s.scale, rows=rows)
+    assert_close(got[rows], want, "sparse32k")
