@@ -1,0 +1,259 @@
+#!/usr/bin/env python3
+"""Prefill-attention benchmark on one MI355X.
+
+Default workload "prefill32k" (Qwen3-4B attention shapes: 32 query heads,
+8 KV heads, head_dim 128, 32,768 tokens, planted synthetic Q/K/V). One step is
+the whole hot path over that prompt, done both ways on the same tensors:
+
+  dense        8 chunks of 4,096 rows, each over its accumulated history, under
+               an fp16 causal mask (mask-tile classification, tiled attention,
+               split-key combine when needed);
+  blocksparse  pooled index (block 128), alpha 0.1 selection plus diagonal,
+               exact attention on kept blocks with the pooled correction.
+
+value = dense-equivalent FLOPs of the step (2 x 4*d*Hq*N(N+1)/2) / step time.
+Inputs are resident in HBM before timing starts. Also printed: per-part
+TFLOP/s, tokens/s and % of the bf16 dense MFMA peak, the roofline of the
+dominant kernel (HIP events around each of its launches, on its stream), and
+the fp64 CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0
+METRIC = "prefill attention TFLOP/s (dense-equiv) + tokens/s at 32K; % bf16 MFMA peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill32k", choices=["prefill32k", "dense128k"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU oracle sample")
+    return ap.parse_args()
+
+
+def source_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "long_context_prefill_attn_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(f"{kernel}:{workload}")
+    if not rec or rec.get("source_sha") != source_hash("attention.hip", "common.h"):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i["num_threads"] for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the path is built and timed on a single MI355X "
+              "(multi-GPU sharding is described in DESIGN.md, not built). Run with --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import long_context_prefill_attn_amd as lp
+    from workloads import causal_mask, dense_equiv_pairs, make_workload
+    from workloads.gen import chunk_list
+
+    assert torch.cuda.is_available(), "bench.py needs the GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+
+    def up_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    if args.workload == "prefill32k":
+        w = make_workload("sparse32k")
+        chunks = chunk_list(w.N, 4096)
+        do_sparse = True
+    else:
+        w = make_workload("dense128k")
+        chunks = w.spec.chunks
+        do_sparse = False
+    s = w.spec
+    N, Hq, Hkv, d, B = w.N, s.n_q, s.n_kv, s.d, s.block
+    scale = s.scale
+
+    Q, K, V = up_bf16(w.Q), up_bf16(w.K), up_bf16(w.V)
+    masks = [torch.from_numpy(causal_mask(q0, C)).to(dev) for q0, C in chunks]
+    O_dense = torch.empty((N, Hq, d), dtype=torch.float32, device=dev)
+    ws_bytes = max(lp.prefill_attn_dense_workspace(C, q0 + C, Hq, Hkv, d) for q0, C in chunks)
+    ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    nb = -(-N // B)
+    kp = torch.empty((Hkv, nb, d), dtype=torch.float32, device=dev)
+    vp = torch.empty_like(kp)
+    sel_idx = torch.empty((Hkv, nb, nb), dtype=torch.int32, device=dev)
+    sel_cnt = torch.empty((Hkv, nb), dtype=torch.int32, device=dev)
+    O_sparse = torch.empty((N, Hq, d), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    pairs = sum(dense_equiv_pairs(q0, C) for q0, C in chunks)
+    flops_dense = 4.0 * d * Hq * pairs
+    flops_sparse = 4.0 * d * Hq * dense_equiv_pairs(0, N) if do_sparse else 0.0
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def run_dense():
+        for (q0, C), m in zip(chunks, masks):
+            T = q0 + C
+            lp.prefill_attn_dense(Q[q0:T], K[:T], V[:T], m, scale, O=O_dense[q0:T], workspace=ws)
+
+    def run_sparse():
+        lp.build_pooled_index(K, V, B, K_pool=kp, V_pool=vp)
+        lp.select_blocks(Q, kp, 0, B, s.alpha, scale, sel_idx=sel_idx, sel_cnt=sel_cnt)
+        lp.prefill_attn_blocksparse(Q, K, V, kp, vp, sel_idx, sel_cnt, 0, B, scale, O=O_sparse)
+
+    for _ in range(args.warmup):
+        run_dense()
+        if do_sparse:
+            run_sparse()
+    torch.cuda.synchronize()
+
+    lp.timing.reset()
+    lp.timing.enable(True)
+    part_ev = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        e0, e1, e2 = ev(), ev(), ev()
+        e0.record()
+        run_dense()
+        e1.record()
+        if do_sparse:
+            run_sparse()
+        e2.record()
+        part_ev.append((e0, e1, e2))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    lp.timing.enable(False)
+
+    ms_step = wall * 1e3 / args.steps
+    dense_ms = float(np.median([a.elapsed_time(b) for a, b, _ in part_ev]))
+    sparse_ms = float(np.median([b.elapsed_time(c) for _, b, c in part_ev])) if do_sparse else 0.0
+    kern = {}
+    for name in ("attn_dense", "mask_classify", "attn_combine", "attn_blocksparse", "pool", "select"):
+        tot, n = lp.timing.read(name)
+        if n:
+            kern[name] = {"avg_ms": tot / n, "launches_per_step": n // args.steps, "ms_per_step": tot / args.steps}
+
+    assert torch.isfinite(O_dense).all().item(), "non-finite dense output"
+    if do_sparse:
+        assert torch.isfinite(O_sparse).all().item(), "non-finite block-sparse output"
+        visible = nb * (nb + 1) // 2 * Hkv
+        kept = int(sel_cnt.sum().item())
+        sparsity = 1.0 - kept / visible
+    tflops = (flops_dense + flops_sparse) / (ms_step * 1e-3) / 1e12
+
+    # roofline of the dominant kernel: dense attention, algorithmic FLOPs per launch
+    dom = "attn_dense"
+    per_launch_flops = flops_dense / len(chunks)
+    achieved = per_launch_flops / (kern[dom]["avg_ms"] * 1e-3) / 1e12
+    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": measured_traffic(dom, args.workload),
+                "algorithmic_flops_per_launch": per_launch_flops}
+
+    parts = {"dense": {"ms": round(dense_ms, 3),
+                       "tflops": round(flops_dense / (dense_ms * 1e-3) / 1e12, 2),
+                       "pct_peak": round(100 * flops_dense / (dense_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                       "tokens_per_s": round(N / (dense_ms * 1e-3))}}
+    if do_sparse:
+        parts["blocksparse"] = {"ms": round(sparse_ms, 3),
+                                "tflops_dense_equiv": round(flops_sparse / (sparse_ms * 1e-3) / 1e12, 2),
+                                "pct_peak_dense_equiv": round(100 * flops_sparse / (sparse_ms * 1e-3) / 1e12
+                                                              / PEAK_BF16_TFLOPS, 2),
+                                "tokens_per_s": round(N / (sparse_ms * 1e-3)),
+                                "skipped_block_fraction": round(sparsity, 4),
+                                "speedup_vs_dense": round(dense_ms / sparse_ms, 3)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, chunks, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC, "value": round(tflops, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; planted block structure)" if do_sparse else "synthetic (seeded N(0,1))",
+        "config": {"workload": args.workload, "tokens": N, "n_q": Hq, "n_kv": Hkv, "head_dim": d,
+                   "chunk": 4096, "block": B if do_sparse else None,
+                   "alpha": s.alpha if do_sparse else None,
+                   "step": "dense chunked + block-sparse prefill of the same prompt" if do_sparse
+                   else "dense chunked prefill", "parallelism": "none (1 GPU)"},
+        "tokens_per_s": round((2 if do_sparse else 1) * N / (ms_step * 1e-3)),
+        "pct_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "parts": parts, "kernels": kern, "roofline": roofline, "cpu_baseline": cpu,
+        "device": {"name": props.name, "cus": props.multi_processor_count},
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, chunks, budget_s):
+    """The fp64 oracle on a bounded sample: the last 4,096-row chunk of the dense
+    pass (all 32K keys), as many query heads as fit in the time budget."""
+    from oracle import dense_ref
+    from workloads import bf16_to_f32, causal_mask
+    s = w.spec
+    q0, C = chunks[-1]
+    T = q0 + C
+    q = bf16_to_f32(w.Q[q0:T]).astype(np.float64)
+    k = bf16_to_f32(w.K[:T]).astype(np.float64)
+    v = bf16_to_f32(w.V[:T]).astype(np.float64)
+    mask = causal_mask(q0, C)
+    heads = 0
+    flops = 0.0
+    t0 = time.perf_counter()
+    for h in range(s.n_q):
+        dense_ref(q, k, v, mask, s.scale, heads=[h])
+        heads += 1
+        flops += 4.0 * s.d * (C * q0 + C * (C + 1) / 2)
+        if time.perf_counter() - t0 > budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(flops / el / 1e12, 5), "unit": "TFLOP/s", "cores": cpu_threads(),
+            "kind": "oracle",
+            "sample": f"dense oracle (fp64 numpy) on chunk {len(chunks) - 1} ({C} rows over {T} keys), "
+                      f"{heads} of {s.n_q} query heads, {el:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()
