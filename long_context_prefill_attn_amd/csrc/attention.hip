@@ -38,83 +38,80 @@ constexpr int NT = 256;         // threads per workgroup (4 waves)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float SLACK = 8.0f;   // lazy-rescale threshold in log2 units
 
+#define LDS_AS __attribute__((address_space(3)))
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
 enum { MODE_PLAIN = 0, MODE_GMASK = 1, MODE_CAUSAL = 2, MODE_POOLED = 3 };
 
+// LDS tiles are row-major [64 keys][D] bf16 with no padding; the 16-byte chunk c
+// of row r sits at chunk position c ^ swz(r). The swizzle spreads the 8 rows a
+// K-operand read touches, and the 4 rows a transposed V read touches, over
+// distinct bank groups.
 template <int D>
 struct Geo {
-  static constexpr int KP = D + 8;               // K row pitch in halves (16-byte pad)
-  static constexpr int VP = BN + 4;              // V^T row pitch in halves (8-byte pad)
-  static constexpr int KH = BN * KP;             // halves of one K tile
-  static constexpr int VH = D * VP;              // halves of one V^T tile
-  static constexpr int STAGE = KH + VH;
-  static constexpr size_t LDS_BYTES = 2 * STAGE * sizeof(uint16_t);
-  static constexpr int KCH = BN * D / 8 / NT;    // 16-byte K chunks per thread
-  static constexpr int VUNITS = 2 * D;           // (4 keys x 8 dims) V units per tile
+  static constexpr int CPR = D / 8;              // 16-byte chunks per row
+  static constexpr int TILE = BN * D;            // halves of one K or V tile
+  static constexpr int STAGE = 2 * TILE;         // K tile then V tile
+  static constexpr size_t LDS_BYTES = 2 * STAGE * sizeof(uint16_t);  // two stages
+  static constexpr int RPI = 64 / CPR;           // rows written by one wave-wide 16-byte load
+  static constexpr int NI = BN / RPI / 4;        // such loads per wave per tile
+  static constexpr int KCH = BN * D / 8 / NT;    // 16-byte chunks per thread per tile
 };
 
-// ---------------------------------------------------------------------------
-// global -> register -> LDS staging of a 64-key K/V tile of KV head g
-// ---------------------------------------------------------------------------
-template <int D>
-struct KVRegs {
-  u32x4 k[Geo<D>::KCH];
-  u32x4 v[4];
-};
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
 
+// Issue the direct HBM -> LDS loads of a 64-key tile of K or V (KV head g).
+// Lane l of a wave-wide load lands at byte 16*l of the 1 KB it writes, so each
+// lane fetches the global chunk that belongs at that swizzled position. Rows
+// past T re-read row T-1 (finite data; their scores are masked to -inf).
 template <int D>
-__device__ __forceinline__ void load_kv(const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-                                        int T, int n_kv, int g, int kbase, KVRegs<D>& r) {
-  const int tid = threadIdx.x;
-  constexpr int CPR = D / 8;  // 16-byte chunks per key row
+__device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ src, int T, int n_kv, int g,
+                                           int kbase, uint16_t* tile) {
+  constexpr int CPR = Geo<D>::CPR, RPI = Geo<D>::RPI, NI = Geo<D>::NI;
+  const int lane = __lane_id(), wave = threadIdx.x >> 6;
+  const int r_in = lane / CPR, pc = lane % CPR;
 #pragma unroll
-  for (int i = 0; i < Geo<D>::KCH; ++i) {
-    const int c = tid + NT * i;
-    const int t = kbase + c / CPR;
-    r.k[i] = (t < T) ? *reinterpret_cast<const u32x4*>(K + ((size_t)t * n_kv + g) * D + (c % CPR) * 8)
-                     : u32x4{0, 0, 0, 0};
-  }
-  if (tid < Geo<D>::VUNITS) {
-    const int kg = tid % 16, col = tid / 16;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int t = kbase + 4 * kg + q;
-      r.v[q] = (t < T) ? *reinterpret_cast<const u32x4*>(V + ((size_t)t * n_kv + g) * D + col * 8)
-                       : u32x4{0, 0, 0, 0};
-    }
+  for (int i = 0; i < NI; ++i) {
+    const int row0 = (wave * NI + i) * RPI;
+    const int row = row0 + r_in;
+    const int c = pc ^ swz(row);
+    const int t = min(kbase + row, T - 1);
+    const uint16_t* gp = src + ((size_t)t * n_kv + g) * D + c * 8;
+    __builtin_amdgcn_global_load_lds(gp, (LDS_AS void*)(tile + row0 * D), 16, 0, 0);
   }
 }
 
+__device__ __forceinline__ void wait_tile_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Per-lane LDS offsets (in halves) of the MFMA operands inside a tile.
 template <int D>
-__device__ __forceinline__ void store_kv(uint16_t* ks, uint16_t* vts, const KVRegs<D>& r) {
-  const int tid = threadIdx.x;
-  constexpr int CPR = D / 8;
+struct LaneOffs {
+  int k[D / 16];   // K slice rows n, dims 16*st + 8*h .. +7
+  int v[D / 32];   // transposed V read: see attn_step
+};
+
+template <int D>
+__device__ __forceinline__ LaneOffs<D> lane_offsets() {
+  LaneOffs<D> o;
+  const int lane = __lane_id();
+  const int n = lane & 31, h = lane >> 5;
 #pragma unroll
-  for (int i = 0; i < Geo<D>::KCH; ++i) {
-    const int c = tid + NT * i;
-    *reinterpret_cast<u32x4*>(ks + (c / CPR) * Geo<D>::KP + (c % CPR) * 8) = r.k[i];
-  }
-  if (tid < Geo<D>::VUNITS) {
-    const int kg = tid % 16, col = tid / 16;
-    // transpose 4 keys x 8 dims -> 8 dims x 4 keys
+  for (int st = 0; st < D / 16; ++st) o.k[st] = n * D + (((2 * st + h) ^ swz(n)) * 8);
+  const int blk = lane >> 4, s = lane & 15, r = s >> 2, q = s & 3;
+  const int vrow = 4 * (blk >> 1) + r;   // row inside each 8-row group
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t a0 = r.v[0][w], a1 = r.v[1][w], a2 = r.v[2][w], a3 = r.v[3][w];
-      const u32x2 even = {(a0 & 0xFFFFu) | (a1 << 16), (a2 & 0xFFFFu) | (a3 << 16)};
-      const u32x2 odd = {(a0 >> 16) | (a1 & 0xFFFF0000u), (a2 >> 16) | (a3 & 0xFFFF0000u)};
-      const int d0 = col * 8 + 2 * w;
-      *reinterpret_cast<u32x2*>(vts + d0 * Geo<D>::VP + 4 * kg) = even;
-      *reinterpret_cast<u32x2*>(vts + (d0 + 1) * Geo<D>::VP + 4 * kg) = odd;
-    }
+  for (int nb = 0; nb < D / 32; ++nb) {
+    const int chunk = nb * 4 + (blk & 1) * 2 + (q >> 1);
+    o.v[nb] = vrow * D + ((chunk ^ swz(vrow)) * 8) + (q & 1) * 4;
   }
+  return o;
 }
 
-// ---------------------------------------------------------------------------
-// one 64-key step for the wave's 32 query rows
-// ---------------------------------------------------------------------------
 struct StepCtx {
   float scale_log2;
   int kvalid;                        // keys of the step inside [0, T)
   const uint16_t* __restrict__ mrow; // MODE_GMASK: mask row of this lane's query (may be null)
+  bool mask_vec;                     // MODE_GMASK: 8-byte aligned mask rows
   int key0;                          // absolute key (or pooled block) index of the step's first key
   int qpos;                          // MODE_CAUSAL: absolute position of this lane's query
   const uint32_t* selbits;           // MODE_POOLED: selected-block bitmap (LDS)
@@ -123,58 +120,75 @@ struct StepCtx {
 };
 
 template <int D>
-__device__ __forceinline__ f32x16 qk_slice(const uint16_t* __restrict__ kp, const bf16x8 (&qf)[D / 16]) {
-  f32x16 s = {};
+__device__ __forceinline__ f32x16 qk_slice(const uint16_t* __restrict__ kt, const LaneOffs<D>& lo,
+                                           const bf16x8 (&qf)[D / 16], f32x16 s) {
 #pragma unroll
   for (int st = 0; st < D / 16; ++st) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(kp + 16 * st);
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + lo.k[st]);
     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s, 0, 0, 0);
   }
   return s;
 }
 
-template <int D, int MODE>
-__device__ __forceinline__ void attn_step(const uint16_t* __restrict__ ks, const uint16_t* __restrict__ vts,
-                                          const uint16_t* __restrict__ ks2,
-                                          const uint16_t* __restrict__ vts2,
+// One 64-key step for the wave's 32 query rows.
+//   S^T slice kb (keys kb*32 .. +31): element i of a lane holds key kb*32 + 8*(i/4) + 4*h + i%4.
+//   P^T feeds the PV MFMA directly: slot 8h+i' of MFMA c holds key 16c + 8*(i'/4) + 4h + i'%4.
+//   The matching V^T operand comes from two ds_read_b64_tr_b16 reads per MFMA: in each
+//   16-lane block, lane 4r+q supplies the address of V[row base + r][d0 + 4q .. +3] and
+//   receives V[row base + 0..3][d0 + lane%16].
+template <int D, int MODE, bool TAIL>
+__device__ __forceinline__ void attn_step(const uint16_t* __restrict__ kt, const uint16_t* __restrict__ vt,
+                                          const uint16_t* __restrict__ kt2,
+                                          const uint16_t* __restrict__ vt2, const LaneOffs<D>& lo,
                                           const bf16x8 (&qf)[D / 16], f32x16 (&o)[D / 32], float& m,
                                           float& l, const StepCtx& cx) {
   const int lane = __lane_id();
-  const int n = lane & 31, h = lane >> 5;
-  constexpr int KP = Geo<D>::KP, VP = Geo<D>::VP;
+  const int h = lane >> 5;
 
   f32x16 s[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-    const int off = (kb * 32 + n) * KP + 8 * h;
-    s[kb] = qk_slice<D>(ks + off, qf);
-    if (MODE == MODE_POOLED) {
-      const f32x16 s2 = qk_slice<D>(ks2 + off, qf);
-      s[kb] += s2;
-    }
+    s[kb] = qk_slice<D>(kt + kb * 32 * D, lo, qf, f32x16{});
+    if (MODE == MODE_POOLED) s[kb] = qk_slice<D>(kt2 + kb * 32 * D, lo, qf, s[kb]);
   }
 
-  // scale, mask, row max. Element i of slice kb holds key kb*32 + 8*(i/4) + 4*h + i%4.
   float x[2][16];
   float mx = -__builtin_inff();
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
+    uint16_t mv[16];
+    if (MODE == MODE_GMASK) {
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int kk = kb * 32 + 8 * i4 + 4 * h;
+        if (!TAIL && cx.mask_vec) {
+          u32x2 w = {0, 0};
+          if (cx.mrow != nullptr) w = *reinterpret_cast<const u32x2*>(cx.mrow + cx.key0 + kk);
+          mv[4 * i4 + 0] = w[0] & 0xFFFF; mv[4 * i4 + 1] = w[0] >> 16;
+          mv[4 * i4 + 2] = w[1] & 0xFFFF; mv[4 * i4 + 3] = w[1] >> 16;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            mv[4 * i4 + e] = (cx.mrow != nullptr && kk + e < cx.kvalid) ? cx.mrow[cx.key0 + kk + e] : 0;
+        }
+      }
+    }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int kk = kb * 32 + 8 * (i >> 2) + 4 * h + (i & 3);
       float v = s[kb][i] * cx.scale_log2;
       if (MODE == MODE_GMASK) {
-        uint16_t mv = 0;
-        if (cx.mrow != nullptr && kk < cx.kvalid) mv = cx.mrow[cx.key0 + kk];
-        v = f16_dropped(mv) ? -__builtin_inff() : __builtin_fmaf((float)__builtin_bit_cast(_Float16, mv), LOG2E, v);
+        v = f16_dropped(mv[i]) ? -__builtin_inff()
+                               : __builtin_fmaf((float)__builtin_bit_cast(_Float16, mv[i]), LOG2E, v);
       } else if (MODE == MODE_CAUSAL) {
         if (cx.key0 + kk > cx.qpos) v = -__builtin_inff();
       } else if (MODE == MODE_POOLED) {
         const int b = cx.key0 + kk;
-        const bool live = b < cx.jlimit && !((cx.selbits[b >> 5] >> (b & 31)) & 1u);
+        bool live = false;
+        if (b < cx.jlimit) live = !((cx.selbits[b >> 5] >> (b & 31)) & 1u);
         v = live ? v + cx.pool_bias : -__builtin_inff();
       }
-      if (kk >= cx.kvalid) v = -__builtin_inff();
+      if (TAIL && kk >= cx.kvalid) v = -__builtin_inff();
       x[kb][i] = v;
       mx = fmaxf(mx, v);
     }
@@ -190,7 +204,6 @@ __device__ __forceinline__ void attn_step(const uint16_t* __restrict__ ks, const
   }
   const float mu = (m == -__builtin_inff()) ? 0.f : m;
 
-  // P = 2^(x - m), packed to bf16 in MFMA B-operand order
   u32x4 P[2][2];
   float psum = 0.f;
 #pragma unroll
@@ -208,27 +221,25 @@ __device__ __forceinline__ void attn_step(const uint16_t* __restrict__ ks, const
   }
   l += psum;
 
-  // O^T += V^T P^T. Slot 8h+i' of MFMA c holds key 16c + 8*(i'/4) + 4h + i'%4.
 #pragma unroll
   for (int nb = 0; nb < D / 32; ++nb) {
-    const int voff = (nb * 32 + n) * VP + 4 * h;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const int ko = voff + kb * 32 + 16 * c;
+        const int off = lo.v[nb] + (kb * 32 + 16 * c) * D;
         const bf16x8 b = __builtin_bit_cast(bf16x8, P[kb][c]);
         {
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vts + ko);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vts + ko + 8);
-          const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
-          o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), b, o[nb], 0, 0, 0);
+          const v4i16 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt + off));
+          const v4i16 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt + off + 8 * D));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, o[nb], 0, 0, 0);
         }
         if (MODE == MODE_POOLED) {
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vts2 + ko);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vts2 + ko + 8);
-          const u32x4 av = {lo[0], lo[1], hi[0], hi[1]};
-          o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av), b, o[nb], 0, 0, 0);
+          const v4i16 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt2 + off));
+          const v4i16 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt2 + off + 8 * D));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, o[nb], 0, 0, 0);
         }
       }
     }
@@ -280,7 +291,7 @@ attn_dense_kernel(const uint16_t* __restrict__ Q, int C, int n_q, const uint16_t
                   const uint16_t* __restrict__ V, int T, int n_kv, const uint16_t* __restrict__ mask,
                   int64_t mask_ld, float scale_log2, float* __restrict__ O,
                   const uint8_t* __restrict__ flags, int n_qt, int n_ktile, int splits,
-                  float* __restrict__ part_o, float* __restrict__ part_ml) {
+                  float* __restrict__ part_o, float* __restrict__ part_ml, int mask_vec) {
   extern __shared__ uint16_t lds[];
   __shared__ int s_lo, s_hi;
   const int tid = threadIdx.x;
@@ -322,6 +333,7 @@ attn_dense_kernel(const uint16_t* __restrict__ Q, int C, int n_q, const uint16_t
   StepCtx cx;
   cx.scale_log2 = scale_log2;
   cx.mrow = qvalid ? mask + (size_t)qrow * mask_ld : nullptr;
+  cx.mask_vec = mask_vec != 0;
   cx.qpos = 0; cx.selbits = nullptr; cx.jlimit = 0; cx.pool_bias = 0.f;
 
   auto next_live = [&](int s) {
@@ -329,30 +341,34 @@ attn_dense_kernel(const uint16_t* __restrict__ Q, int C, int n_q, const uint16_t
     return s;
   };
 
-  KVRegs<D> regs;
+  const LaneOffs<D> lo = lane_offsets<D>();
   int s = next_live(a);
   if (s < b) {
-    load_kv<D>(K, V, T, n_kv, g, s * BN, regs);
-    store_kv<D>(lds, lds + Geo<D>::KH, regs);
+    issue_tile<D>(K, T, n_kv, g, s * BN, lds);
+    issue_tile<D>(V, T, n_kv, g, s * BN, lds + Geo<D>::TILE);
   }
-  __syncthreads();
   int cur = 0;
   while (s < b) {
     const int nx = next_live(s + 1);
-    if (nx < b) load_kv<D>(K, V, T, n_kv, g, nx * BN, regs);
-    const uint16_t* ks = lds + cur * Geo<D>::STAGE;
-    const uint16_t* vts = ks + Geo<D>::KH;
+    wait_tile_loads();
+    __syncthreads();   // tile `cur` is in LDS for every wave; buffer cur^1 is free
+    if (nx < b) {
+      uint16_t* nxt = lds + (cur ^ 1) * Geo<D>::STAGE;
+      issue_tile<D>(K, T, n_kv, g, nx * BN, nxt);
+      issue_tile<D>(V, T, n_kv, g, nx * BN, nxt + Geo<D>::TILE);
+    }
+    const uint16_t* kt = lds + cur * Geo<D>::STAGE;
+    const uint16_t* vt = kt + Geo<D>::TILE;
     cx.key0 = s * BN;
     cx.kvalid = min(BN, T - s * BN);
-    if (frow[s / (FLAG_TILE / BN)] == TILE_MIXED)
-      attn_step<D, MODE_GMASK>(ks, vts, nullptr, nullptr, qf, o, m, l, cx);
-    else
-      attn_step<D, MODE_PLAIN>(ks, vts, nullptr, nullptr, qf, o, m, l, cx);
-    if (nx < b) {
-      uint16_t* kn = lds + (cur ^ 1) * Geo<D>::STAGE;
-      store_kv<D>(kn, kn + Geo<D>::KH, regs);
+    const bool mixed = frow[s / (FLAG_TILE / BN)] == TILE_MIXED;
+    if (cx.kvalid < BN) {
+      if (mixed) attn_step<D, MODE_GMASK, true>(kt, vt, nullptr, nullptr, lo, qf, o, m, l, cx);
+      else attn_step<D, MODE_PLAIN, true>(kt, vt, nullptr, nullptr, lo, qf, o, m, l, cx);
+    } else {
+      if (mixed) attn_step<D, MODE_GMASK, false>(kt, vt, nullptr, nullptr, lo, qf, o, m, l, cx);
+      else attn_step<D, MODE_PLAIN, false>(kt, vt, nullptr, nullptr, lo, qf, o, m, l, cx);
     }
-    __syncthreads();
     cur ^= 1;
     s = nx;
   }
@@ -389,49 +405,36 @@ __device__ __forceinline__ void split_hi_lo(float f, uint16_t& hi, uint16_t& lo)
 }
 
 template <int D>
-__device__ __forceinline__ void stage_pooled(const float* __restrict__ Kp, const float* __restrict__ Vp,
-                                             int nb, int g, int pbase, int jlimit, uint16_t* khi,
-                                             uint16_t* klo, uint16_t* vhi, uint16_t* vlo) {
+__device__ __forceinline__ void stage_pooled_one(const float* __restrict__ src, int pbase, int jlimit,
+                                                 uint16_t* hi_tile, uint16_t* lo_tile) {
   const int tid = threadIdx.x;
-  constexpr int CPR = D / 8;
-  const float* kg = Kp + (size_t)g * nb * D;
-  const float* vg = Vp + (size_t)g * nb * D;
+  constexpr int CPR = Geo<D>::CPR;
 #pragma unroll
   for (int i = 0; i < Geo<D>::KCH; ++i) {
     const int c = tid + NT * i;
-    const int key = c / CPR, col = (c % CPR) * 8;
-    const int bb = pbase + key;
-    uint16_t hv[8], lv[8];
+    const int row = c / CPR, lc = c % CPR;
+    const int bb = pbase + row;
+    float f[8];
+    if (bb < jlimit) {
+      const float4 x0 = *reinterpret_cast<const float4*>(src + (size_t)bb * D + lc * 8);
+      const float4 x1 = *reinterpret_cast<const float4*>(src + (size_t)bb * D + lc * 8 + 4);
+      f[0] = x0.x; f[1] = x0.y; f[2] = x0.z; f[3] = x0.w; f[4] = x1.x; f[5] = x1.y; f[6] = x1.z; f[7] = x1.w;
+    } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float f = (bb < jlimit) ? kg[(size_t)bb * D + col + e] : 0.f;
-      split_hi_lo<D>(f, hv[e], lv[e]);
+      for (int e = 0; e < 8; ++e) f[e] = 0.f;
     }
     u32x4 H, L;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      H[w] = hv[2 * w] | ((uint32_t)hv[2 * w + 1] << 16);
-      L[w] = lv[2 * w] | ((uint32_t)lv[2 * w + 1] << 16);
+      uint16_t h0, l0, h1, l1;
+      split_hi_lo<D>(f[2 * w], h0, l0);
+      split_hi_lo<D>(f[2 * w + 1], h1, l1);
+      H[w] = h0 | ((uint32_t)h1 << 16);
+      L[w] = l0 | ((uint32_t)l1 << 16);
     }
-    *reinterpret_cast<u32x4*>(khi + key * Geo<D>::KP + col) = H;
-    *reinterpret_cast<u32x4*>(klo + key * Geo<D>::KP + col) = L;
-  }
-  if (tid < Geo<D>::VUNITS) {
-    const int kg4 = tid % 16, col = (tid / 16) * 8;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      uint16_t hv[4], lv[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int bb = pbase + 4 * kg4 + q;
-        const float f = (bb < jlimit) ? vg[(size_t)bb * D + col + e] : 0.f;
-        split_hi_lo<D>(f, hv[q], lv[q]);
-      }
-      const u32x2 H = {hv[0] | ((uint32_t)hv[1] << 16), hv[2] | ((uint32_t)hv[3] << 16)};
-      const u32x2 L = {lv[0] | ((uint32_t)lv[1] << 16), lv[2] | ((uint32_t)lv[3] << 16)};
-      *reinterpret_cast<u32x2*>(vhi + (col + e) * Geo<D>::VP + 4 * kg4) = H;
-      *reinterpret_cast<u32x2*>(vlo + (col + e) * Geo<D>::VP + 4 * kg4) = L;
-    }
+    const int off = row * D + ((lc ^ swz(row)) * 8);
+    *reinterpret_cast<u32x4*>(hi_tile + off) = H;
+    *reinterpret_cast<u32x4*>(lo_tile + off) = L;
   }
 }
 
@@ -484,44 +487,52 @@ attn_blocksparse_kernel(const uint16_t* __restrict__ Q, int C, int q_start, int 
   cx.pool_bias = __builtin_log2f((float)BLK);
 
   // exact steps: two 64-key steps per selected block
+  const LaneOffs<D> lo = lane_offsets<D>();
   const int n_ex = 2 * cnt;
-  KVRegs<D> regs;
   if (n_ex > 0) {
-    load_kv<D>(K, V, T, n_kv, g, sl[0] * BLK, regs);
-    store_kv<D>(lds, lds + Geo<D>::KH, regs);
+    issue_tile<D>(K, T, n_kv, g, sl[0] * BLK, lds);
+    issue_tile<D>(V, T, n_kv, g, sl[0] * BLK, lds + Geo<D>::TILE);
   }
-  __syncthreads();
   int cur = 0;
   for (int e = 0; e < n_ex; ++e) {
     const int kbase = sl[e >> 1] * BLK + (e & 1) * BN;
-    if (e + 1 < n_ex) load_kv<D>(K, V, T, n_kv, g, sl[(e + 1) >> 1] * BLK + ((e + 1) & 1) * BN, regs);
-    const uint16_t* ks = lds + cur * Geo<D>::STAGE;
-    const uint16_t* vts = ks + Geo<D>::KH;
+    wait_tile_loads();
+    __syncthreads();
+    if (e + 1 < n_ex) {
+      const int nbase = sl[(e + 1) >> 1] * BLK + ((e + 1) & 1) * BN;
+      uint16_t* nxt = lds + (cur ^ 1) * Geo<D>::STAGE;
+      issue_tile<D>(K, T, n_kv, g, nbase, nxt);
+      issue_tile<D>(V, T, n_kv, g, nbase, nxt + Geo<D>::TILE);
+    }
+    const uint16_t* kt = lds + cur * Geo<D>::STAGE;
+    const uint16_t* vt = kt + Geo<D>::TILE;
     cx.key0 = kbase;
     cx.kvalid = min(BN, T - kbase);
-    if (kbase >= j * BLK)
-      attn_step<D, MODE_CAUSAL>(ks, vts, nullptr, nullptr, qf, o, m, l, cx);
-    else
-      attn_step<D, MODE_PLAIN>(ks, vts, nullptr, nullptr, qf, o, m, l, cx);
-    if (e + 1 < n_ex) {
-      uint16_t* kn = lds + (cur ^ 1) * Geo<D>::STAGE;
-      store_kv<D>(kn, kn + Geo<D>::KH, regs);
+    if (kbase >= j * BLK) {
+      // the diagonal block: causal by position; its keys may end before 64 (ragged T)
+      attn_step<D, MODE_CAUSAL, true>(kt, vt, nullptr, nullptr, lo, qf, o, m, l, cx);
+    } else {
+      attn_step<D, MODE_PLAIN, false>(kt, vt, nullptr, nullptr, lo, qf, o, m, l, cx);
     }
-    __syncthreads();
     cur ^= 1;
   }
+  wait_tile_loads();
+  __syncthreads();
 
   // pooled rows of the unselected visible blocks b < j, 64 per step
   uint16_t* khi = lds;
-  uint16_t* vhi = lds + Geo<D>::KH;
+  uint16_t* vhi = lds + Geo<D>::TILE;
   uint16_t* klo = lds + Geo<D>::STAGE;
-  uint16_t* vlo = klo + Geo<D>::KH;
+  uint16_t* vlo = klo + Geo<D>::TILE;
+  const float* kpg = Kp + (size_t)g * nb * D;
+  const float* vpg = Vp + (size_t)g * nb * D;
   for (int pbase = 0; pbase < j; pbase += BN) {
-    stage_pooled<D>(Kp, Vp, nb, g, pbase, j, khi, klo, vhi, vlo);
+    stage_pooled_one<D>(kpg, pbase, j, khi, klo);
+    stage_pooled_one<D>(vpg, pbase, j, vhi, vlo);
     __syncthreads();
     cx.key0 = pbase;
     cx.kvalid = min(BN, j - pbase);
-    attn_step<D, MODE_POOLED>(khi, vhi, klo, vlo, qf, o, m, l, cx);
+    attn_step<D, MODE_POOLED, true>(khi, vhi, klo, vlo, lo, qf, o, m, l, cx);
     __syncthreads();
   }
 
@@ -575,19 +586,20 @@ static hipError_t dense_impl(const uint16_t* Q, int C, int n_q, const uint16_t* 
                              float* part_ml, hipStream_t stream) {
   const float sl2 = scale * LOG2E;
   const int grid = p.n_qt * n_q * p.splits;
+  const int mask_vec = (mask_ld % 4 == 0) && (reinterpret_cast<uintptr_t>(mask) % 8 == 0);
   const size_t lds = Geo<D>::LDS_BYTES;
   if (p.splits > 1) {
     hipFuncSetAttribute((const void*)attn_dense_kernel<D, true>,
                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     hipLaunchKernelGGL((attn_dense_kernel<D, true>), dim3(grid), dim3(NT), lds, stream, Q, C, n_q, K, V,
                        T, n_kv, mask, mask_ld, sl2, O, flags, p.n_qt, p.n_ktile, p.splits, part_o,
-                       part_ml);
+                       part_ml, mask_vec);
   } else {
     hipFuncSetAttribute((const void*)attn_dense_kernel<D, false>,
                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     hipLaunchKernelGGL((attn_dense_kernel<D, false>), dim3(grid), dim3(NT), lds, stream, Q, C, n_q, K,
                        V, T, n_kv, mask, mask_ld, sl2, O, flags, p.n_qt, p.n_ktile, 1, part_o,
-                       part_ml);
+                       part_ml, mask_vec);
   }
   return hipGetLastError();
 }
