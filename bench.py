@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--workload", default="prefill32k", choices=["prefill32k", "dense128k"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU oracle sample")
+    ap.add_argument("--parts", default="dense,blocksparse",
+                    help="subset of the step to run (for profiler runs); the default runs the whole step")
     return ap.parse_args()
 
 
@@ -104,7 +106,7 @@ def main():
     if args.workload == "prefill32k":
         w = make_workload("sparse32k")
         chunks = chunk_list(w.N, 4096)
-        do_sparse = True
+        do_sparse = "blocksparse" in args.parts.split(",")
     else:
         w = make_workload("dense128k")
         chunks = w.spec.chunks
@@ -126,13 +128,16 @@ def main():
     O_sparse = torch.empty((N, Hq, d), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
+    run_dense_part = "dense" in args.parts.split(",")
     pairs = sum(dense_equiv_pairs(q0, C) for q0, C in chunks)
-    flops_dense = 4.0 * d * Hq * pairs
+    flops_dense = 4.0 * d * Hq * pairs if run_dense_part else 0.0
     flops_sparse = 4.0 * d * Hq * dense_equiv_pairs(0, N) if do_sparse else 0.0
 
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
     def run_dense():
+        if not run_dense_part:
+            return
         for (q0, C), m in zip(chunks, masks):
             T = q0 + C
             lp.prefill_attn_dense(Q[q0:T], K[:T], V[:T], m, scale, O=O_dense[q0:T], workspace=ws)
@@ -184,18 +189,20 @@ def main():
     tflops = (flops_dense + flops_sparse) / (ms_step * 1e-3) / 1e12
 
     # roofline of the dominant kernel: dense attention, algorithmic FLOPs per launch
-    dom = "attn_dense"
-    per_launch_flops = flops_dense / len(chunks)
+    dom = "attn_dense" if run_dense_part else "attn_blocksparse"
+    per_launch_flops = flops_dense / len(chunks) if run_dense_part else flops_sparse
     achieved = per_launch_flops / (kern[dom]["avg_ms"] * 1e-3) / 1e12
     roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": measured_traffic(dom, args.workload),
                 "algorithmic_flops_per_launch": per_launch_flops}
 
-    parts = {"dense": {"ms": round(dense_ms, 3),
-                       "tflops": round(flops_dense / (dense_ms * 1e-3) / 1e12, 2),
-                       "pct_peak": round(100 * flops_dense / (dense_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
-                       "tokens_per_s": round(N / (dense_ms * 1e-3))}}
+    parts = {}
+    if run_dense_part:
+        parts["dense"] = {"ms": round(dense_ms, 3),
+                          "tflops": round(flops_dense / (dense_ms * 1e-3) / 1e12, 2),
+                          "pct_peak": round(100 * flops_dense / (dense_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
+                          "tokens_per_s": round(N / (dense_ms * 1e-3))}
     if do_sparse:
         parts["blocksparse"] = {"ms": round(sparse_ms, 3),
                                 "tflops_dense_equiv": round(flops_sparse / (sparse_ms * 1e-3) / 1e12, 2),
@@ -203,7 +210,7 @@ def main():
                                                               / PEAK_BF16_TFLOPS, 2),
                                 "tokens_per_s": round(N / (sparse_ms * 1e-3)),
                                 "skipped_block_fraction": round(sparsity, 4),
-                                "speedup_vs_dense": round(dense_ms / sparse_ms, 3)}
+                                "speedup_vs_dense": round(dense_ms / sparse_ms, 3) if run_dense_part else None}
 
     cpu = None
     if not args.no_cpu_baseline:

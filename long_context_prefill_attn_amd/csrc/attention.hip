@@ -60,26 +60,56 @@ struct Geo {
 
 __device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
 
-// Issue the direct HBM -> LDS loads of a 64-key tile of K or V (KV head g).
-// Lane l of a wave-wide load lands at byte 16*l of the 1 KB it writes, so each
-// lane fetches the global chunk that belongs at that swizzled position. Rows
-// past T re-read row T-1 (finite data; their scores are masked to -inf).
-template <int D>
-__device__ __forceinline__ void issue_tile(const uint16_t* __restrict__ src, int T, int n_kv, int g,
-                                           int kbase, uint16_t* tile) {
-  constexpr int CPR = Geo<D>::CPR, RPI = Geo<D>::RPI, NI = Geo<D>::NI;
-  const int lane = __lane_id(), wave = threadIdx.x >> 6;
-  const int r_in = lane / CPR, pc = lane % CPR;
-#pragma unroll
-  for (int i = 0; i < NI; ++i) {
-    const int row0 = (wave * NI + i) * RPI;
-    const int row = row0 + r_in;
-    const int c = pc ^ swz(row);
-    const int t = min(kbase + row, T - 1);
-    const uint16_t* gp = src + ((size_t)t * n_kv + g) * D + c * 8;
-    __builtin_amdgcn_global_load_lds(gp, (LDS_AS void*)(tile + row0 * D), 16, 0, 0);
-  }
+// Direct HBM -> LDS loads of 64-key tiles of K or V for KV head g, through a
+// buffer resource whose range ends at row T: rows past T read as zeros (their
+// scores are masked). Lane l of a wave-wide 16-byte load lands at byte 16*l of
+// the 1 KB it writes, so each lane fetches the global chunk that belongs at
+// that swizzled position; the per-lane byte offsets are fixed for the whole
+// kernel and only the scalar row offset changes per tile.
+// One wave-wide 16-byte-per-lane buffer load into LDS. (Kept outside the
+// templates: hipcc's host pass drops kernel stubs when the buffer-resource type
+// appears inside templated device code.)
+__device__ __forceinline__ void buffer_load_lds16(const void* base, uint32_t range, LDS_AS void* dst,
+                                                  uint32_t voff, uint32_t soff) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, range, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
 }
+
+template <int D>
+struct TileLoader {
+  const uint16_t* kptr;   // K + g*D
+  const uint16_t* vptr;   // V + g*D
+  uint32_t range;          // bytes readable from kptr / vptr (rows 0..T-1)
+  uint32_t voff[Geo<D>::NI];   // per-lane byte offsets inside a tile
+  uint32_t row_bytes;           // bytes between consecutive tokens (n_kv * D * 2)
+
+  __device__ __forceinline__ void init(const uint16_t* K, const uint16_t* V, int T, int n_kv, int g) {
+    constexpr int CPR = Geo<D>::CPR, RPI = Geo<D>::RPI, NI = Geo<D>::NI;
+    row_bytes = (uint32_t)n_kv * D * 2;
+    range = (uint32_t)T * row_bytes - (uint32_t)g * D * 2;
+    kptr = K + (size_t)g * D;
+    vptr = V + (size_t)g * D;
+    const int lane = __lane_id(), wave = threadIdx.x >> 6;
+    const int r_in = lane / CPR, pc = lane % CPR;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int row = (wave * NI + i) * RPI + r_in;
+      voff[i] = (uint32_t)row * row_bytes + (uint32_t)((pc ^ swz(row)) * 16);
+    }
+  }
+
+  __device__ __forceinline__ void issue(bool is_v, int kbase, uint16_t* tile) const {
+    constexpr int RPI = Geo<D>::RPI, NI = Geo<D>::NI;
+    const int wave = threadIdx.x >> 6;
+    // the tile's row offset goes into the per-lane offset, which the range check covers
+    const uint32_t toff = (uint32_t)kbase * row_bytes;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      LDS_AS void* dst = (LDS_AS void*)(tile + (wave * NI + i) * RPI * D);
+      buffer_load_lds16(is_v ? vptr : kptr, range, dst, voff[i] + toff, 0);
+    }
+  }
+};
 
 __device__ __forceinline__ void wait_tile_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -246,6 +276,182 @@ __device__ __forceinline__ void attn_step(const uint16_t* __restrict__ kt, const
   }
 }
 
+// ---------------------------------------------------------------------------
+// Software-pipelined loop over "plain" 64-key steps (every key visible, no mask
+// to read). Iteration i computes S = K Q^T of step i+1 on the MFMA pipe while
+// the softmax of step i runs on the VALU, then O += V P of step i. K runs one
+// tile ahead of V, so two K buffers and two V buffers (64 KB for d = 128) hold
+// everything in flight:
+//   top of iteration i: V[i] and K[i+1] resident; issue K[i+2] (into K[i]'s
+//   buffer) and V[i+1] (into V[i-1]'s buffer) -- both free after the barrier.
+// Steps are visited in any order the source yields; the online softmax does not
+// depend on the order.
+// ---------------------------------------------------------------------------
+template <int D>
+__device__ __forceinline__ void qk_tile(const uint16_t* __restrict__ kt, const LaneOffs<D>& lo,
+                                        const bf16x8 (&qf)[D / 16], f32x16 (&s)[2]) {
+  s[0] = qk_slice<D>(kt, lo, qf, f32x16{});
+  s[1] = qk_slice<D>(kt + 32 * D, lo, qf, f32x16{});
+}
+
+// Row max of a raw (unscaled) S tile pair, completed across the two half-waves.
+__device__ __forceinline__ float row_max(const f32x16 (&s)[2]) {
+  float mx = -__builtin_inff();
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = __builtin_fmaxf(mx, s[kb][i]);
+  return __builtin_fmaxf(mx, partner32(mx));
+}
+
+// Raise the running max (log2 units) when a tile's max exceeds it by more than
+// the slack; rare after the first tiles, so it is a real branch.
+template <int D>
+__device__ __forceinline__ void raise_max(float mx_raw, float scale_log2, f32x16 (&o)[D / 32], float& m,
+                                          float& l) {
+  const float m_new = __builtin_fmaxf(m, mx_raw * scale_log2);
+  if (__builtin_expect(__any(m_new > m + SLACK), 0)) {
+    const float alpha = (m_new == -__builtin_inff()) ? 1.f : exp2f(m - m_new);
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb) o[nb] *= alpha;
+    l *= alpha;
+    m = m_new;
+  }
+}
+
+// P = 2^(S*scale_log2 - m) packed to bf16 in PV-operand order; l += sum of the packed values
+__device__ __forceinline__ void exp_pack(const f32x16 (&s)[2], float m, float scale_log2, u32x4 (&P)[2][2],
+                                         float& l) {
+  const float nmu = (m == -__builtin_inff()) ? 0.f : -m;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * c + 2 * w], scale_log2, nmu));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * c + 2 * w + 1], scale_log2, nmu));
+        P[kb][c][w] = pack_bf16x2(p0, p1);
+        l += p0 + p1;
+      }
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void pv_tile(const uint16_t* __restrict__ vt, const LaneOffs<D>& lo,
+                                        const u32x4 (&P)[2][2], f32x16 (&o)[D / 32]) {
+#pragma unroll
+  for (int nb = 0; nb < D / 32; ++nb) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int off = lo.v[nb] + (kb * 32 + 16 * c) * D;
+        const v4i16 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt + off));
+        const v4i16 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt + off + 8 * D));
+        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, P[kb][c]), o[nb], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// Scheduling of one pipeline iteration: each QK^T MFMA of the next tile is paired
+// with its K fragment read and a share of the current tile's exp/pack VALU work;
+// each PV MFMA with its two transposed V reads and a share of the row-max work.
+template <int D>
+__device__ __forceinline__ void interleave_iteration() {
+  constexpr int NQK = 2 * (D / 16);   // QK^T MFMAs per step
+  constexpr int NPV = 4 * (D / 32);   // PV MFMAs per step
+#pragma unroll
+  for (int k = 0; k < NQK; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
+  }
+#pragma unroll
+  for (int k = 0; k < NPV; ++k) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+  }
+}
+
+// Src: int first(); int next(int st); int kbase(int st); a state < 0 ends the walk.
+template <int D, class Src>
+__device__ __forceinline__ void plain_steps(const TileLoader<D>& tl, uint16_t* lds, const Src& src,
+                                            const LaneOffs<D>& lo, const bf16x8 (&qf)[D / 16],
+                                            f32x16 (&o)[D / 32], float& m, float& l, float scale_log2) {
+  constexpr int TL = Geo<D>::TILE;
+  uint16_t* kb0 = lds;
+  uint16_t* vb0 = lds + 2 * TL;
+  const int st0 = src.first();
+  if (st0 < 0) return;
+  const int kfb = src.kbase(st0);   // a valid tile to (re)load once the walk has ended
+  tl.issue(false, kfb, kb0);
+  tl.issue(true, kfb, vb0);
+  wait_tile_loads();
+  __syncthreads();
+  int st1 = src.next(st0);
+  tl.issue(false, st1 >= 0 ? src.kbase(st1) : kfb, kb0 + TL);
+  int i = 0;
+  // One pipeline iteration (see above); returns false after the last step. The
+  // loads are issued unconditionally so that the iteration is one basic block
+  // the scheduler can interleave. Unrolled by two below so the S registers
+  // ping-pong instead of being copied.
+  auto iter = [&](const f32x16 (&sc)[2], float mxc, f32x16 (&sn)[2], float& mxn) -> bool {
+    raise_max<D>(mxc, scale_log2, o, m, l);
+    wait_tile_loads();
+    __syncthreads();
+    const int st2 = st1 >= 0 ? src.next(st1) : -1;
+    tl.issue(false, st2 >= 0 ? src.kbase(st2) : kfb, kb0 + (i & 1) * TL);
+    tl.issue(true, st1 >= 0 ? src.kbase(st1) : kfb, vb0 + ((i + 1) & 1) * TL);
+    qk_tile<D>(kb0 + ((i + 1) & 1) * TL, lo, qf, sn);
+    u32x4 P[2][2];
+    exp_pack(sc, m, scale_log2, P, l);
+    pv_tile<D>(vb0 + (i & 1) * TL, lo, P, o);
+    mxn = row_max(sn);
+    interleave_iteration<D>();
+    if (st1 < 0) return false;
+    st1 = st2;
+    ++i;
+    return true;
+  };
+  f32x16 sa[2], sb[2];
+  float mxa, mxb;
+  qk_tile<D>(kb0, lo, qf, sa);
+  mxa = row_max(sa);
+  while (iter(sa, mxa, sb, mxb) && iter(sb, mxb, sa, mxa)) {
+  }
+  wait_tile_loads();
+  __syncthreads();   // LDS free for whatever follows
+}
+
+// Plain-step sources (see plain_steps).
+// Dense: steps [a, b) whose 128-key flag tile is ZERO and whose 64 keys all lie below T.
+struct DenseSrc {
+  int a, b, T;
+  const uint8_t* frow;
+  __device__ bool plain(int st) const { return frow[st >> 1] == TILE_ZERO && (st + 1) * BN <= T; }
+  __device__ int scan(int st) const {
+    while (st < b && !plain(st)) ++st;
+    return st < b ? st : -1;
+  }
+  __device__ int first() const { return scan(a); }
+  __device__ int next(int st) const { return scan(st + 1); }
+  __device__ int kbase(int st) const { return st * BN; }
+};
+
+// Block-sparse: the two 64-key halves of each selected block below the diagonal.
+struct SparseSrc {
+  const int32_t* sl;
+  int n;
+  __device__ int first() const { return n > 0 ? 0 : -1; }
+  __device__ int next(int e) const { return e + 1 < n ? e + 1 : -1; }
+  __device__ int kbase(int e) const { return sl[e >> 1] * 128 + (e & 1) * BN; }
+};
+
 // load this wave's 32 query rows as the B operand: lane holds Q[row n][dims 16st+8h .. +7]
 template <int D>
 __device__ __forceinline__ void load_q(const uint16_t* __restrict__ Q, int n_q, int head, int qrow,
@@ -336,41 +542,28 @@ attn_dense_kernel(const uint16_t* __restrict__ Q, int C, int n_q, const uint16_t
   cx.mask_vec = mask_vec != 0;
   cx.qpos = 0; cx.selbits = nullptr; cx.jlimit = 0; cx.pool_bias = 0.f;
 
-  auto next_live = [&](int s) {
-    while (s < b && frow[s / (FLAG_TILE / BN)] == TILE_DROPPED) ++s;
-    return s;
-  };
-
   const LaneOffs<D> lo = lane_offsets<D>();
-  int s = next_live(a);
-  if (s < b) {
-    issue_tile<D>(K, T, n_kv, g, s * BN, lds);
-    issue_tile<D>(V, T, n_kv, g, s * BN, lds + Geo<D>::TILE);
-  }
-  int cur = 0;
-  while (s < b) {
-    const int nx = next_live(s + 1);
+
+  // 1) plain steps: tiles flagged ZERO whose 64 keys all lie below T
+  TileLoader<D> tl;
+  tl.init(K, V, T, n_kv, g);
+  plain_steps<D>(tl, lds, DenseSrc{a, b, T, frow}, lo, qf, o, m, l, scale_log2);
+
+  // 2) the remaining steps: mask tiles (MIXED) and a ragged last step
+  for (int st = a; st < b; ++st) {
+    const uint8_t f = frow[st >> 1];
+    if (f == TILE_DROPPED || (f == TILE_ZERO && (st + 1) * BN <= T)) continue;
+    tl.issue(false, st * BN, lds);
+    tl.issue(true, st * BN, lds + Geo<D>::TILE);
     wait_tile_loads();
-    __syncthreads();   // tile `cur` is in LDS for every wave; buffer cur^1 is free
-    if (nx < b) {
-      uint16_t* nxt = lds + (cur ^ 1) * Geo<D>::STAGE;
-      issue_tile<D>(K, T, n_kv, g, nx * BN, nxt);
-      issue_tile<D>(V, T, n_kv, g, nx * BN, nxt + Geo<D>::TILE);
-    }
-    const uint16_t* kt = lds + cur * Geo<D>::STAGE;
-    const uint16_t* vt = kt + Geo<D>::TILE;
-    cx.key0 = s * BN;
-    cx.kvalid = min(BN, T - s * BN);
-    const bool mixed = frow[s / (FLAG_TILE / BN)] == TILE_MIXED;
-    if (cx.kvalid < BN) {
-      if (mixed) attn_step<D, MODE_GMASK, true>(kt, vt, nullptr, nullptr, lo, qf, o, m, l, cx);
-      else attn_step<D, MODE_PLAIN, true>(kt, vt, nullptr, nullptr, lo, qf, o, m, l, cx);
-    } else {
-      if (mixed) attn_step<D, MODE_GMASK, false>(kt, vt, nullptr, nullptr, lo, qf, o, m, l, cx);
-      else attn_step<D, MODE_PLAIN, false>(kt, vt, nullptr, nullptr, lo, qf, o, m, l, cx);
-    }
-    cur ^= 1;
-    s = nx;
+    __syncthreads();
+    cx.key0 = st * BN;
+    cx.kvalid = min(BN, T - st * BN);
+    if (f == TILE_MIXED)
+      attn_step<D, MODE_GMASK, true>(lds, lds + Geo<D>::TILE, nullptr, nullptr, lo, qf, o, m, l, cx);
+    else
+      attn_step<D, MODE_PLAIN, true>(lds, lds + Geo<D>::TILE, nullptr, nullptr, lo, qf, o, m, l, cx);
+    __syncthreads();
   }
 
   const float lt = l + partner32(l);
@@ -486,38 +679,25 @@ attn_blocksparse_kernel(const uint16_t* __restrict__ Q, int C, int q_start, int 
   cx.jlimit = j;
   cx.pool_bias = __builtin_log2f((float)BLK);
 
-  // exact steps: two 64-key steps per selected block
+  // exact steps: two 64-key steps per selected block; every selected block but
+  // the last (the diagonal) lies fully below the query block
   const LaneOffs<D> lo = lane_offsets<D>();
-  const int n_ex = 2 * cnt;
-  if (n_ex > 0) {
-    issue_tile<D>(K, T, n_kv, g, sl[0] * BLK, lds);
-    issue_tile<D>(V, T, n_kv, g, sl[0] * BLK, lds + Geo<D>::TILE);
-  }
-  int cur = 0;
-  for (int e = 0; e < n_ex; ++e) {
-    const int kbase = sl[e >> 1] * BLK + (e & 1) * BN;
+  TileLoader<D> tl;
+  tl.init(K, V, T, n_kv, g);
+  plain_steps<D>(tl, lds, SparseSrc{sl, 2 * (cnt - 1)}, lo, qf, o, m, l, scale_log2);
+  // the diagonal block, causally by position (its keys may end before 128: ragged T)
+  for (int e = 0; e < 2; ++e) {
+    const int kbase = j * BLK + e * BN;
+    if (kbase >= T) break;
+    tl.issue(false, kbase, lds);
+    tl.issue(true, kbase, lds + Geo<D>::TILE);
     wait_tile_loads();
     __syncthreads();
-    if (e + 1 < n_ex) {
-      const int nbase = sl[(e + 1) >> 1] * BLK + ((e + 1) & 1) * BN;
-      uint16_t* nxt = lds + (cur ^ 1) * Geo<D>::STAGE;
-      issue_tile<D>(K, T, n_kv, g, nbase, nxt);
-      issue_tile<D>(V, T, n_kv, g, nbase, nxt + Geo<D>::TILE);
-    }
-    const uint16_t* kt = lds + cur * Geo<D>::STAGE;
-    const uint16_t* vt = kt + Geo<D>::TILE;
     cx.key0 = kbase;
     cx.kvalid = min(BN, T - kbase);
-    if (kbase >= j * BLK) {
-      // the diagonal block: causal by position; its keys may end before 64 (ragged T)
-      attn_step<D, MODE_CAUSAL, true>(kt, vt, nullptr, nullptr, lo, qf, o, m, l, cx);
-    } else {
-      attn_step<D, MODE_PLAIN, false>(kt, vt, nullptr, nullptr, lo, qf, o, m, l, cx);
-    }
-    cur ^= 1;
+    attn_step<D, MODE_CAUSAL, true>(lds, lds + Geo<D>::TILE, nullptr, nullptr, lo, qf, o, m, l, cx);
+    __syncthreads();
   }
-  wait_tile_loads();
-  __syncthreads();
 
   // pooled rows of the unselected visible blocks b < j, 64 per step
   uint16_t* khi = lds;
