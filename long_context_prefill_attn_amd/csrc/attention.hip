@@ -9,32 +9,37 @@
 // and an entry <= -30000 omits its key ("ANE Prefill Research", How the ANE
 // prefill path works; What worked, item 2).
 //
-// gfx950 mapping (one workgroup = 4 waves = 128 query rows of one query head):
+// gfx950 mapping. A workgroup is 8 waves; each wave owns 32 query rows of one
+// query head. The waves of a workgroup cover Hg query heads of one KV group
+// (grouped-query attention) x 256/Hg rows, so every K/V tile staged in LDS
+// feeds 8 waves' MFMAs.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16: A = a 32-key slice of the K tile
 //     (LDS), B = Q^T held in registers for the whole kernel. The accumulator
 //     puts query n = lane%32 in every lane, so each lane owns the softmax state
 //     of one query row; the row's other 16 keys of a 32-key slice sit in lane
 //     l^32 and one v_permlane32_swap completes each row reduction.
-//   * O^T = V^T P^T on the same MFMA: A = V^T from LDS (V is transposed while
-//     it is staged), B = P^T straight from the S^T accumulators (packed to
-//     bf16), so P never leaves registers and O^T lands with the row's head_dim
-//     values in the lane that owns the row's softmax state.
-//   * K/V tiles of 64 keys are double-buffered in LDS; the next tile's global
-//     loads are in flight while the current tile is computed.
+//   * O^T = V^T P^T on the same MFMA: A = V^T read from the row-major V tile
+//     with ds_read_b64_tr_b16, B = P^T straight from the S^T accumulators
+//     (packed to bf16), so P never leaves registers and O^T lands with the row's
+//     head_dim values in the lane that owns the row's softmax state.
+//   * K/V tiles of 64 keys go HBM -> LDS directly (buffer loads with the LDS
+//     bit) into 3-deep rings, issued two steps ahead of use; the QK^T of the
+//     next tile overlaps the softmax and PV of the current one.
 //   * Softmax in exp2 units with log2(e) folded into the scale. The running max
 //     is raised only when it grows by more than 2^8 (all weights stay <= 256),
 //     so the O rescale is rare; results are exact up to rounding either way.
-//   * Workgroup ids are remapped so that the workgroups of one query head run
-//     on one XCD (shared L2 for that KV head), longest query tiles first.
+//   * Workgroup ids are remapped so that the workgroups of one KV head run on
+//     one XCD (shared L2 for that head's K/V), longest query tiles first.
 #include <algorithm>
 
 #include "common.h"
 
 namespace pa {
 
-constexpr int BM = 128;         // query rows per workgroup
 constexpr int BN = 64;          // keys per inner step
-constexpr int NT = 256;         // threads per workgroup (4 waves)
+constexpr int NW = 8;           // waves per workgroup
+constexpr int NT = 64 * NW;     // threads per workgroup
+constexpr int KR = 3;           // K and V ring depth (tiles)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float SLACK = 8.0f;   // lazy-rescale threshold in log2 units
 
@@ -51,21 +56,15 @@ template <int D>
 struct Geo {
   static constexpr int CPR = D / 8;              // 16-byte chunks per row
   static constexpr int TILE = BN * D;            // halves of one K or V tile
-  static constexpr int STAGE = 2 * TILE;         // K tile then V tile
-  static constexpr size_t LDS_BYTES = 2 * STAGE * sizeof(uint16_t);  // two stages
+  static constexpr int RING = 2 * KR * TILE;     // K ring then V ring (halves)
+  static constexpr size_t LDS_BYTES = RING * sizeof(uint16_t);
   static constexpr int RPI = 64 / CPR;           // rows written by one wave-wide 16-byte load
-  static constexpr int NI = BN / RPI / 4;        // such loads per wave per tile
+  static constexpr int NIW = BN / RPI / NW;      // such loads per wave per tile
   static constexpr int KCH = BN * D / 8 / NT;    // 16-byte chunks per thread per tile
 };
 
 __device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
 
-// Direct HBM -> LDS loads of 64-key tiles of K or V for KV head g, through a
-// buffer resource whose range ends at row T: rows past T read as zeros (their
-// scores are masked). Lane l of a wave-wide 16-byte load lands at byte 16*l of
-// the 1 KB it writes, so each lane fetches the global chunk that belongs at
-// that swizzled position; the per-lane byte offsets are fixed for the whole
-// kernel and only the scalar row offset changes per tile.
 // One wave-wide 16-byte-per-lane buffer load into LDS. (Kept outside the
 // templates: hipcc's host pass drops kernel stubs when the buffer-resource type
 // appears inside templated device code.)
@@ -75,16 +74,21 @@ __device__ __forceinline__ void buffer_load_lds16(const void* base, uint32_t ran
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voff, soff, 0, 0);
 }
 
+// Direct HBM -> LDS loads of 64-key tiles of K or V for KV head g, through a
+// buffer resource whose range ends at row T: rows past T read as zeros (their
+// scores are masked). Lane l of a wave-wide 16-byte load lands at byte 16*l of
+// the 1 KB it writes, so each lane fetches the global chunk that belongs at
+// that swizzled position. Each of the 8 waves issues NIW such loads per tile.
 template <int D>
 struct TileLoader {
   const uint16_t* kptr;   // K + g*D
   const uint16_t* vptr;   // V + g*D
-  uint32_t range;          // bytes readable from kptr / vptr (rows 0..T-1)
-  uint32_t voff[Geo<D>::NI];   // per-lane byte offsets inside a tile
-  uint32_t row_bytes;           // bytes between consecutive tokens (n_kv * D * 2)
+  uint32_t range;         // bytes readable from kptr / vptr (rows 0..T-1)
+  uint32_t voff[Geo<D>::NIW];   // per-lane byte offsets inside a tile
+  uint32_t row_bytes;     // bytes between consecutive tokens (n_kv * D * 2)
 
   __device__ __forceinline__ void init(const uint16_t* K, const uint16_t* V, int T, int n_kv, int g) {
-    constexpr int CPR = Geo<D>::CPR, RPI = Geo<D>::RPI, NI = Geo<D>::NI;
+    constexpr int CPR = Geo<D>::CPR, RPI = Geo<D>::RPI, NIW = Geo<D>::NIW;
     row_bytes = (uint32_t)n_kv * D * 2;
     range = (uint32_t)T * row_bytes - (uint32_t)g * D * 2;
     kptr = K + (size_t)g * D;
@@ -92,26 +96,43 @@ struct TileLoader {
     const int lane = __lane_id(), wave = threadIdx.x >> 6;
     const int r_in = lane / CPR, pc = lane % CPR;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int row = (wave * NI + i) * RPI + r_in;
+    for (int i = 0; i < NIW; ++i) {
+      const int row = (wave * NIW + i) * RPI + r_in;
       voff[i] = (uint32_t)row * row_bytes + (uint32_t)((pc ^ swz(row)) * 16);
     }
   }
 
   __device__ __forceinline__ void issue(bool is_v, int kbase, uint16_t* tile) const {
-    constexpr int RPI = Geo<D>::RPI, NI = Geo<D>::NI;
+    constexpr int RPI = Geo<D>::RPI, NIW = Geo<D>::NIW;
     const int wave = threadIdx.x >> 6;
     // the tile's row offset goes into the per-lane offset, which the range check covers
     const uint32_t toff = (uint32_t)kbase * row_bytes;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      LDS_AS void* dst = (LDS_AS void*)(tile + (wave * NI + i) * RPI * D);
+    for (int i = 0; i < NIW; ++i) {
+      LDS_AS void* dst = (LDS_AS void*)(tile + (wave * NIW + i) * RPI * D);
       buffer_load_lds16(is_v ? vptr : kptr, range, dst, voff[i] + toff, 0);
     }
   }
 };
 
-__device__ __forceinline__ void wait_tile_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Workgroup barrier without a memory fence. Inside the pipelined loop the only
+// cross-wave data are the LDS-DMA tiles, whose arrival each wave has already
+// awaited with wait_vm, and every LDS read of an earlier tile has returned
+// (its value was consumed); a fenced barrier would also drain the tiles that
+// are deliberately still in flight.
+__device__ __forceinline__ void bare_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Wait until at most N of this wave's vector-memory loads are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+  asm volatile("" ::: "memory");
+}
 
 // Per-lane LDS offsets (in halves) of the MFMA operands inside a tile.
 template <int D>
@@ -276,17 +297,6 @@ __device__ __forceinline__ void attn_step(const uint16_t* __restrict__ kt, const
   }
 }
 
-// ---------------------------------------------------------------------------
-// Software-pipelined loop over "plain" 64-key steps (every key visible, no mask
-// to read). Iteration i computes S = K Q^T of step i+1 on the MFMA pipe while
-// the softmax of step i runs on the VALU, then O += V P of step i. K runs one
-// tile ahead of V, so two K buffers and two V buffers (64 KB for d = 128) hold
-// everything in flight:
-//   top of iteration i: V[i] and K[i+1] resident; issue K[i+2] (into K[i]'s
-//   buffer) and V[i+1] (into V[i-1]'s buffer) -- both free after the barrier.
-// Steps are visited in any order the source yields; the online softmax does not
-// depend on the order.
-// ---------------------------------------------------------------------------
 template <int D>
 __device__ __forceinline__ void qk_tile(const uint16_t* __restrict__ kt, const LaneOffs<D>& lo,
                                         const bf16x8 (&qf)[D / 16], f32x16 (&s)[2]) {
@@ -338,93 +348,131 @@ __device__ __forceinline__ void exp_pack(const f32x16 (&s)[2], float m, float sc
   }
 }
 
+// One hand-scheduled pipeline iteration body (after the barrier and the tile
+// loads): the QK^T MFMAs of the next tile, each with the K fragment read four
+// MFMAs ahead and a quarter-pair of the current tile's exp/pack work; then the
+// PV MFMAs of the current tile, each with its transposed V reads two MFMAs
+// ahead and a share of the next tile's row-max. sched_barrier fences keep the
+// compiler from regrouping the work. Returns the next tile's raw row max.
 template <int D>
-__device__ __forceinline__ void pv_tile(const uint16_t* __restrict__ vt, const LaneOffs<D>& lo,
-                                        const u32x4 (&P)[2][2], f32x16 (&o)[D / 32]) {
-#pragma unroll
-  for (int nb = 0; nb < D / 32; ++nb) {
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int off = lo.v[nb] + (kb * 32 + 16 * c) * D;
-        const v4i16 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt + off));
-        const v4i16 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt + off + 8 * D));
-        const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, P[kb][c]), o[nb], 0, 0, 0);
-      }
-    }
-  }
-}
+__device__ __forceinline__ float fused_step(const uint16_t* __restrict__ kt_next, const uint16_t* __restrict__ vt,
+                                            const LaneOffs<D>& lo, const bf16x8 (&qf)[D / 16],
+                                            const f32x16 (&sc)[2], f32x16 (&sn)[2], f32x16 (&o)[D / 32],
+                                            float m, float& l, float scale_log2) {
+  constexpr int NQK = 2 * (D / 16);     // QK^T MFMAs (k = 2*st + kb)
+  constexpr int NPV = 4 * (D / 32);     // PV MFMAs (k = 4*nb + 2*kb + c)
+  constexpr int KR = 4;                 // K fragment ring depth
+  const float nmu = (m == -__builtin_inff()) ? 0.f : -m;
 
-// Scheduling of one pipeline iteration: each QK^T MFMA of the next tile is paired
-// with its K fragment read and a share of the current tile's exp/pack VALU work;
-// each PV MFMA with its two transposed V reads and a share of the row-max work.
-template <int D>
-__device__ __forceinline__ void interleave_iteration() {
-  constexpr int NQK = 2 * (D / 16);   // QK^T MFMAs per step
-  constexpr int NPV = 4 * (D / 32);   // PV MFMAs per step
+  bf16x8 kf[KR];
+#pragma unroll
+  for (int k = 0; k < KR; ++k)
+    kf[k] = *reinterpret_cast<const bf16x8*>(kt_next + (k & 1) * 32 * D + lo.k[k >> 1]);
+  sn[0] = f32x16{};
+  sn[1] = f32x16{};
+  u32x4 P[2][2];
+  float psum = 0.f;
 #pragma unroll
   for (int k = 0; k < NQK; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);   // VALU
+    const bf16x8 a = kf[k % KR];
+    if (k + KR < NQK)
+      kf[k % KR] = *reinterpret_cast<const bf16x8*>(kt_next + ((k + KR) & 1) * 32 * D + lo.k[(k + KR) >> 1]);
+    sn[k & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[k >> 1], sn[k & 1], 0, 0, 0);
+    // exp/pack share: 16 packed pairs over NQK MFMAs
+#pragma unroll
+    for (int pi = k * 16 / NQK; pi < (k + 1) * 16 / NQK; ++pi) {
+      const int kb = pi >> 3, c = (pi >> 2) & 1, w = pi & 3;
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][8 * c + 2 * w], scale_log2, nmu));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][8 * c + 2 * w + 1], scale_log2, nmu));
+      P[kb][c][w] = pack_bf16x2(p0, p1);
+      psum += p0 + p1;
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
+  l += psum;
+
+  // PV: two transposed 8-byte reads per MFMA, two MFMAs ahead
+  v4i16 vf[4][2];
+  auto vread = [&](int k, v4i16 (&dst)[2]) {
+    const int nb = k >> 2, kb = (k >> 1) & 1, c = k & 1;
+    const int off = lo.v[nb] + (kb * 32 + 16 * c) * D;
+    dst[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt + off));
+    dst[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt + off + 8 * D));
+  };
+  vread(0, vf[0]);
+  vread(1, vf[1]);
+  float mx = -__builtin_inff();
 #pragma unroll
   for (int k = 0; k < NPV; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    if (k + 2 < NPV) vread(k + 2, vf[(k + 2) & 3]);
+    const int kb = (k >> 1) & 1, c = k & 1;
+    const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vf[k & 3][0], vf[k & 3][1], 0, 1, 2, 3, 4, 5, 6, 7));
+    o[k >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, P[kb][c]), o[k >> 2], 0, 0, 0);
+    // row-max share of the next tile: 32 values over NPV MFMAs
+#pragma unroll
+    for (int e = k * 32 / NPV; e < (k + 1) * 32 / NPV; ++e) mx = __builtin_fmaxf(mx, sn[e >> 4][e & 15]);
+    __builtin_amdgcn_sched_barrier(0);
   }
+  return __builtin_fmaxf(mx, partner32(mx));
 }
 
+// ---------------------------------------------------------------------------
+// Software-pipelined loop over "plain" 64-key steps (every key visible, no mask
+// to read). Iteration i computes S = K Q^T of step i+1 on the MFMA pipe while
+// the softmax of step i runs on the VALU, then O += V P of step i. Tiles are
+// issued two steps ahead into 3-deep rings:
+//   top of iteration i: wait for K[i+1] and V[i] (K[i+2], V[i+1] may still be in
+//   flight), barrier, then issue K[i+3] into K[i]'s slot and V[i+2] into
+//   V[i-1]'s slot -- both free after the barrier.
+// Steps are visited in any order the source yields; the online softmax does not
+// depend on the order. Loads past the last step re-read the first tile.
 // Src: int first(); int next(int st); int kbase(int st); a state < 0 ends the walk.
+// ---------------------------------------------------------------------------
 template <int D, class Src>
 __device__ __forceinline__ void plain_steps(const TileLoader<D>& tl, uint16_t* lds, const Src& src,
                                             const LaneOffs<D>& lo, const bf16x8 (&qf)[D / 16],
                                             f32x16 (&o)[D / 32], float& m, float& l, float scale_log2) {
-  constexpr int TL = Geo<D>::TILE;
-  uint16_t* kb0 = lds;
-  uint16_t* vb0 = lds + 2 * TL;
-  const int st0 = src.first();
-  if (st0 < 0) return;
-  const int kfb = src.kbase(st0);   // a valid tile to (re)load once the walk has ended
-  tl.issue(false, kfb, kb0);
-  tl.issue(true, kfb, vb0);
-  wait_tile_loads();
-  __syncthreads();
-  int st1 = src.next(st0);
-  tl.issue(false, st1 >= 0 ? src.kbase(st1) : kfb, kb0 + TL);
-  int i = 0;
-  // One pipeline iteration (see above); returns false after the last step. The
-  // loads are issued unconditionally so that the iteration is one basic block
-  // the scheduler can interleave. Unrolled by two below so the S registers
-  // ping-pong instead of being copied.
+  constexpr int TL = Geo<D>::TILE, NIW = Geo<D>::NIW;
+  uint16_t* kring = lds;
+  uint16_t* vring = lds + KR * TL;
+  const int s0 = src.first();
+  if (s0 < 0) return;
+  const int kfb = src.kbase(s0);
+  const int s1 = src.next(s0);
+  const int s2 = s1 >= 0 ? src.next(s1) : -1;
+  tl.issue(false, kfb, kring);
+  tl.issue(true, kfb, vring);
+  tl.issue(false, s1 >= 0 ? src.kbase(s1) : kfb, kring + TL);
+  tl.issue(true, s1 >= 0 ? src.kbase(s1) : kfb, vring + TL);
+  tl.issue(false, s2 >= 0 ? src.kbase(s2) : kfb, kring + 2 * TL);
+  wait_vm<3 * NIW>();   // K[0], V[0] landed
+  bare_barrier();
+  int t1 = s1, t2 = s2;   // steps i+1 and i+2
+  int ik = 1, iv = 0;     // ring slots of K[i+1] and V[i]
   auto iter = [&](const f32x16 (&sc)[2], float mxc, f32x16 (&sn)[2], float& mxn) -> bool {
     raise_max<D>(mxc, scale_log2, o, m, l);
-    wait_tile_loads();
-    __syncthreads();
-    const int st2 = st1 >= 0 ? src.next(st1) : -1;
-    tl.issue(false, st2 >= 0 ? src.kbase(st2) : kfb, kb0 + (i & 1) * TL);
-    tl.issue(true, st1 >= 0 ? src.kbase(st1) : kfb, vb0 + ((i + 1) & 1) * TL);
-    qk_tile<D>(kb0 + ((i + 1) & 1) * TL, lo, qf, sn);
-    u32x4 P[2][2];
-    exp_pack(sc, m, scale_log2, P, l);
-    pv_tile<D>(vb0 + (i & 1) * TL, lo, P, o);
-    mxn = row_max(sn);
-    interleave_iteration<D>();
-    if (st1 < 0) return false;
-    st1 = st2;
-    ++i;
+    wait_vm<2 * NIW>();   // K[i+1], V[i] landed
+    bare_barrier();
+    const int t3 = t2 >= 0 ? src.next(t2) : -1;
+    const int k3 = ik == 0 ? KR - 1 : ik - 1;          // K[i]'s slot
+    const int v2 = iv == 0 ? KR - 1 : iv - 1;          // V[i-1]'s slot
+    tl.issue(false, t3 >= 0 ? src.kbase(t3) : kfb, kring + k3 * TL);
+    tl.issue(true, t2 >= 0 ? src.kbase(t2) : kfb, vring + v2 * TL);
+    mxn = fused_step<D>(kring + ik * TL, vring + iv * TL, lo, qf, sc, sn, o, m, l, scale_log2);
+    if (t1 < 0) return false;
+    t1 = t2;
+    t2 = t3;
+    ik = ik == KR - 1 ? 0 : ik + 1;
+    iv = iv == KR - 1 ? 0 : iv + 1;
     return true;
   };
   f32x16 sa[2], sb[2];
   float mxa, mxb;
-  qk_tile<D>(kb0, lo, qf, sa);
+  qk_tile<D>(kring, lo, qf, sa);
   mxa = row_max(sa);
   while (iter(sa, mxa, sb, mxb) && iter(sb, mxb, sa, mxa)) {
   }
-  wait_tile_loads();
+  wait_vm<0>();
   __syncthreads();   // LDS free for whatever follows
 }
 
@@ -445,11 +493,11 @@ struct DenseSrc {
 
 // Block-sparse: the two 64-key halves of each selected block below the diagonal.
 struct SparseSrc {
-  const int32_t* sl;
+  const uint16_t* sl;   // selected block ids (LDS copy)
   int n;
   __device__ int first() const { return n > 0 ? 0 : -1; }
   __device__ int next(int e) const { return e + 1 < n ? e + 1 : -1; }
-  __device__ int kbase(int e) const { return sl[e >> 1] * 128 + (e & 1) * BN; }
+  __device__ int kbase(int e) const { return (int)sl[e >> 1] * 128 + (e & 1) * BN; }
 };
 
 // load this wave's 32 query rows as the B operand: lane holds Q[row n][dims 16st+8h .. +7]
@@ -490,6 +538,8 @@ __device__ __forceinline__ int remap_xcd(int bid, int nblk) {
 
 // ---------------------------------------------------------------------------
 // dense chunked prefill attention
+// Workgroup = (KV head g, head slice hs, query tile qt, key split). Its 8 waves
+// cover query heads g*group + hs*Hg .. +Hg-1 and rows qt*R .. qt*R+R-1, R = 256/Hg.
 // ---------------------------------------------------------------------------
 template <int D, bool SPLIT>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
@@ -497,26 +547,42 @@ attn_dense_kernel(const uint16_t* __restrict__ Q, int C, int n_q, const uint16_t
                   const uint16_t* __restrict__ V, int T, int n_kv, const uint16_t* __restrict__ mask,
                   int64_t mask_ld, float scale_log2, float* __restrict__ O,
                   const uint8_t* __restrict__ flags, int n_qt, int n_ktile, int splits,
-                  float* __restrict__ part_o, float* __restrict__ part_ml, int mask_vec) {
-  extern __shared__ uint16_t lds[];
+                  float* __restrict__ part_o, float* __restrict__ part_ml, int mask_vec, int hg_log2) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   __shared__ int s_lo, s_hi;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, n = lane & 31;
+  const int Hg = 1 << hg_log2;
+  const int R = 256 >> hg_log2;
+  const int group = n_q / n_kv;
+  const int n_hs = group >> hg_log2;
 
   const int bid = remap_xcd(blockIdx.x, gridDim.x);
-  const int per_head = n_qt * splits;
-  const int head = bid / per_head;
-  const int rem = bid % per_head;
+  const int per_unit = n_qt * splits;
+  const int unit = bid / per_unit;
+  const int g = unit / n_hs, hs = unit % n_hs;
+  const int rem = bid % per_unit;
   const int qt = n_qt - 1 - rem / splits;
   const int split = rem % splits;
-  const int g = head / (n_q / n_kv);
-  const uint8_t* frow = flags + (size_t)qt * n_ktile;
+  const int wph = R / 32;   // waves per head
+  const int head = g * group + hs * Hg + wave / wph;
 
-  // key range of this query tile: first..last tile that is not fully dropped
+  // the workgroup's rows' mask-tile flags, combined over the (one or two) flag
+  // rows they span and copied to LDS after the rings: walking the steps never
+  // waits on global memory
+  uint8_t* frow = reinterpret_cast<uint8_t*>(lds + Geo<D>::RING);
+  const int fr0 = (qt * R) / FLAG_TILE;
+  const int fr1 = (min(qt * R + R, C) - 1) / FLAG_TILE;
   if (tid == 0) { s_lo = n_ktile; s_hi = 0; }
   __syncthreads();
   for (int t = tid; t < n_ktile; t += NT) {
-    if (frow[t] != TILE_DROPPED) { atomicMin(&s_lo, t); atomicMax(&s_hi, t + 1); }
+    uint8_t f = flags[(size_t)fr0 * n_ktile + t];
+    for (int fr = fr0 + 1; fr <= fr1; ++fr) {
+      const uint8_t f2 = flags[(size_t)fr * n_ktile + t];
+      f = (f == f2) ? f : TILE_MIXED;
+    }
+    frow[t] = f;
+    if (f != TILE_DROPPED) { atomicMin(&s_lo, t); atomicMax(&s_hi, t + 1); }
   }
   __syncthreads();
   const int n_steps = (T + BN - 1) / BN;
@@ -526,7 +592,7 @@ attn_dense_kernel(const uint16_t* __restrict__ Q, int C, int n_q, const uint16_t
   const int a = st_lo + (int)((long)len * split / splits);
   const int b = st_lo + (int)((long)len * (split + 1) / splits);
 
-  const int qrow = qt * BM + wave * 32 + n;
+  const int qrow = qt * R + (wave % wph) * 32 + n;
   const bool qvalid = qrow < C;
   bf16x8 qf[D / 16];
   load_q<D>(Q, n_q, head, qrow, qvalid, qf);
@@ -543,10 +609,10 @@ attn_dense_kernel(const uint16_t* __restrict__ Q, int C, int n_q, const uint16_t
   cx.qpos = 0; cx.selbits = nullptr; cx.jlimit = 0; cx.pool_bias = 0.f;
 
   const LaneOffs<D> lo = lane_offsets<D>();
-
-  // 1) plain steps: tiles flagged ZERO whose 64 keys all lie below T
   TileLoader<D> tl;
   tl.init(K, V, T, n_kv, g);
+
+  // 1) plain steps: tiles flagged ZERO whose 64 keys all lie below T
   plain_steps<D>(tl, lds, DenseSrc{a, b, T, frow}, lo, qf, o, m, l, scale_log2);
 
   // 2) the remaining steps: mask tiles (MIXED) and a ragged last step
@@ -554,15 +620,15 @@ attn_dense_kernel(const uint16_t* __restrict__ Q, int C, int n_q, const uint16_t
     const uint8_t f = frow[st >> 1];
     if (f == TILE_DROPPED || (f == TILE_ZERO && (st + 1) * BN <= T)) continue;
     tl.issue(false, st * BN, lds);
-    tl.issue(true, st * BN, lds + Geo<D>::TILE);
-    wait_tile_loads();
+    tl.issue(true, st * BN, lds + KR * Geo<D>::TILE);
+    wait_vm<0>();
     __syncthreads();
     cx.key0 = st * BN;
     cx.kvalid = min(BN, T - st * BN);
     if (f == TILE_MIXED)
-      attn_step<D, MODE_GMASK, true>(lds, lds + Geo<D>::TILE, nullptr, nullptr, lo, qf, o, m, l, cx);
+      attn_step<D, MODE_GMASK, true>(lds, lds + KR * Geo<D>::TILE, nullptr, nullptr, lo, qf, o, m, l, cx);
     else
-      attn_step<D, MODE_PLAIN, true>(lds, lds + Geo<D>::TILE, nullptr, nullptr, lo, qf, o, m, l, cx);
+      attn_step<D, MODE_PLAIN, true>(lds, lds + KR * Geo<D>::TILE, nullptr, nullptr, lo, qf, o, m, l, cx);
     __syncthreads();
   }
 
@@ -583,11 +649,13 @@ attn_dense_kernel(const uint16_t* __restrict__ Q, int C, int n_q, const uint16_t
 
 // ---------------------------------------------------------------------------
 // block-sparse prefill attention: one workgroup per (query block of 128
-// positions, query head). Exact steps over the selected key blocks (the
-// diagonal block causally), then the pooled rows of the unselected visible
-// blocks with multiplicity `block` ("Porting FlashPrefill V2 to Apple
-// silicon", Compute the peaks, summarize the rest). Pooled keys/values are fp32;
-// they enter the bf16 MFMA as hi + lo bf16 pairs (about 16 significant bits).
+// positions, pair of query heads of one KV group). Exact steps over the
+// selected key blocks (the diagonal block causally), then the pooled rows of
+// the unselected visible blocks with multiplicity `block` ("Porting FlashPrefill
+// V2 to Apple silicon", Compute the peaks, summarize the rest). Pooled
+// keys/values are fp32; they enter the bf16 MFMA as hi + lo bf16 pairs (about
+// 16 significant bits). With an odd number of query heads per KV head, the
+// second half of the workgroup repeats the first head and does not store.
 // ---------------------------------------------------------------------------
 template <int D>
 __device__ __forceinline__ void split_hi_lo(float f, uint16_t& hi, uint16_t& lo) {
@@ -638,29 +706,36 @@ attn_blocksparse_kernel(const uint16_t* __restrict__ Q, int C, int q_start, int 
                         int n_kv, const float* __restrict__ Kp, const float* __restrict__ Vp,
                         int nb, int n_qblk, const int32_t* __restrict__ sel_idx,
                         const int32_t* __restrict__ sel_cnt, float scale_log2, float* __restrict__ O) {
-  extern __shared__ uint16_t lds[];
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   __shared__ uint32_t selbits[256];  // up to 8192 blocks
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, n = lane & 31;
   constexpr int BLK = 128;
+  const int group = n_q / n_kv;
+  const int hpw = (group % 2 == 0) ? 2 : 1;   // query heads per workgroup
 
   const int bid = remap_xcd(blockIdx.x, gridDim.x);
-  const int head = bid / n_qblk;
+  const int hp = bid / n_qblk;                  // head pair (or single head)
   const int jj = n_qblk - 1 - bid % n_qblk;
   const int j = q_start / BLK + jj;
-  const int g = head / (n_q / n_kv);
+  const int head = hp * hpw + (hpw == 2 ? (wave >> 2) : 0);
+  const bool storer = hpw == 2 || wave < 4;
+  const int g = (hp * hpw) / group;
   const int32_t* sl = sel_idx + ((size_t)g * n_qblk + jj) * nb;
   const int cnt = sel_cnt[(size_t)g * n_qblk + jj];
 
   const int nwords = (nb + 31) / 32;
   for (int w = tid; w < nwords; w += NT) selbits[w] = 0;
   __syncthreads();
+  // the selected block ids, copied to LDS (after the rings) for the step walk
+  uint16_t* sl_s = lds + Geo<D>::RING;
   for (int e = tid; e < cnt; e += NT) {
     const int bb = sl[e];
+    sl_s[e] = (uint16_t)bb;
     atomicOr(&selbits[bb >> 5], 1u << (bb & 31));
   }
 
-  const int qpos = j * BLK + wave * 32 + n;
+  const int qpos = j * BLK + (wave & 3) * 32 + n;
   const bool qvalid = qpos >= q_start && qpos < q_start + C;
   const int qrow = qpos - q_start;
   bf16x8 qf[D / 16];
@@ -674,36 +749,40 @@ attn_blocksparse_kernel(const uint16_t* __restrict__ Q, int C, int q_start, int 
   StepCtx cx;
   cx.scale_log2 = scale_log2;
   cx.mrow = nullptr;
+  cx.mask_vec = false;
   cx.qpos = qpos;
   cx.selbits = selbits;
   cx.jlimit = j;
   cx.pool_bias = __builtin_log2f((float)BLK);
 
-  // exact steps: two 64-key steps per selected block; every selected block but
-  // the last (the diagonal) lies fully below the query block
   const LaneOffs<D> lo = lane_offsets<D>();
   TileLoader<D> tl;
   tl.init(K, V, T, n_kv, g);
-  plain_steps<D>(tl, lds, SparseSrc{sl, 2 * (cnt - 1)}, lo, qf, o, m, l, scale_log2);
+  __syncthreads();
+  // exact steps: the two 64-key halves of every selected block but the last
+  // (the diagonal), which lie fully below the query block
+  plain_steps<D>(tl, lds, SparseSrc{sl_s, 2 * (cnt - 1)}, lo, qf, o, m, l, scale_log2);
   // the diagonal block, causally by position (its keys may end before 128: ragged T)
+  uint16_t* kt = lds;
+  uint16_t* vt = lds + KR * Geo<D>::TILE;
   for (int e = 0; e < 2; ++e) {
     const int kbase = j * BLK + e * BN;
     if (kbase >= T) break;
-    tl.issue(false, kbase, lds);
-    tl.issue(true, kbase, lds + Geo<D>::TILE);
-    wait_tile_loads();
+    tl.issue(false, kbase, kt);
+    tl.issue(true, kbase, vt);
+    wait_vm<0>();
     __syncthreads();
     cx.key0 = kbase;
     cx.kvalid = min(BN, T - kbase);
-    attn_step<D, MODE_CAUSAL, true>(lds, lds + Geo<D>::TILE, nullptr, nullptr, lo, qf, o, m, l, cx);
+    attn_step<D, MODE_CAUSAL, true>(kt, vt, nullptr, nullptr, lo, qf, o, m, l, cx);
     __syncthreads();
   }
 
   // pooled rows of the unselected visible blocks b < j, 64 per step
   uint16_t* khi = lds;
-  uint16_t* vhi = lds + Geo<D>::TILE;
-  uint16_t* klo = lds + Geo<D>::STAGE;
-  uint16_t* vlo = klo + Geo<D>::TILE;
+  uint16_t* klo = lds + Geo<D>::TILE;
+  uint16_t* vhi = lds + KR * Geo<D>::TILE;
+  uint16_t* vlo = vhi + Geo<D>::TILE;
   const float* kpg = Kp + (size_t)g * nb * D;
   const float* vpg = Vp + (size_t)g * nb * D;
   for (int pbase = 0; pbase < j; pbase += BN) {
@@ -717,7 +796,7 @@ attn_blocksparse_kernel(const uint16_t* __restrict__ Q, int C, int q_start, int 
   }
 
   const float lt = l + partner32(l);
-  if (!qvalid) return;
+  if (!qvalid || !storer) return;
   store_rows<D>(O + ((size_t)qrow * n_q + head) * D, o, lt > 0.f ? 1.f / lt : 0.f);
 }
 
@@ -737,20 +816,32 @@ static int num_cus() {
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// log2 of the query heads one workgroup packs: the largest power of two (<= 8)
+// that divides the group size n_q / n_kv
+static int hg_log2_for(int n_q, int n_kv) {
+  const int group = n_q / n_kv;
+  int lg = 0;
+  while (lg < 3 && group % (2 << lg) == 0) ++lg;
+  return lg;
+}
+
 DensePlan plan_dense(int C, int T, int n_q, int n_kv, int d) {
-  (void)n_kv;
+  (void)d;
   DensePlan p{};
-  p.n_qt = (C + BM - 1) / BM;
+  p.hg_log2 = hg_log2_for(n_q, n_kv);
+  const int R = 256 >> p.hg_log2;
+  p.n_qt = (C + R - 1) / R;
   p.n_ktile = (T + FLAG_TILE - 1) / FLAG_TILE;
-  const long wgs = (long)p.n_qt * n_q;
-  const int target = 2 * num_cus();             // two resident workgroups per CU
+  p.n_qft = (C + FLAG_TILE - 1) / FLAG_TILE;
+  const long wgs = (long)p.n_qt * (n_q >> p.hg_log2);
+  const int target = 2 * num_cus();             // two rounds of one resident workgroup per CU
   const int n_steps = (T + BN - 1) / BN;
   int splits = 1;
   if (wgs < target) splits = (int)((target + wgs - 1) / wgs);
   splits = std::max(1, std::min(splits, n_steps / 4));  // at least 4 steps (256 keys) per split
   splits = std::min(splits, 32);
   p.splits = splits;
-  p.flags_bytes = align256((size_t)p.n_qt * p.n_ktile);
+  p.flags_bytes = align256((size_t)p.n_qft * p.n_ktile);
   if (splits > 1) {
     p.part_o_bytes = align256((size_t)splits * C * n_q * d * sizeof(float));
     p.part_ml_bytes = align256((size_t)splits * C * n_q * 2 * sizeof(float));
@@ -765,21 +856,21 @@ static hipError_t dense_impl(const uint16_t* Q, int C, int n_q, const uint16_t* 
                              float* O, const DensePlan& p, const uint8_t* flags, float* part_o,
                              float* part_ml, hipStream_t stream) {
   const float sl2 = scale * LOG2E;
-  const int grid = p.n_qt * n_q * p.splits;
+  const int grid = p.n_qt * (n_q >> p.hg_log2) * p.splits;
+  const size_t lds = Geo<D>::LDS_BYTES + ((p.n_ktile + 15) & ~15);   // rings + flag row
   const int mask_vec = (mask_ld % 4 == 0) && (reinterpret_cast<uintptr_t>(mask) % 8 == 0);
-  const size_t lds = Geo<D>::LDS_BYTES;
   if (p.splits > 1) {
     hipFuncSetAttribute((const void*)attn_dense_kernel<D, true>,
                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     hipLaunchKernelGGL((attn_dense_kernel<D, true>), dim3(grid), dim3(NT), lds, stream, Q, C, n_q, K, V,
                        T, n_kv, mask, mask_ld, sl2, O, flags, p.n_qt, p.n_ktile, p.splits, part_o,
-                       part_ml, mask_vec);
+                       part_ml, mask_vec, p.hg_log2);
   } else {
     hipFuncSetAttribute((const void*)attn_dense_kernel<D, false>,
                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     hipLaunchKernelGGL((attn_dense_kernel<D, false>), dim3(grid), dim3(NT), lds, stream, Q, C, n_q, K,
                        V, T, n_kv, mask, mask_ld, sl2, O, flags, p.n_qt, p.n_ktile, 1, part_o,
-                       part_ml, mask_vec);
+                       part_ml, mask_vec, p.hg_log2);
   }
   return hipGetLastError();
 }
@@ -802,10 +893,11 @@ static hipError_t blocksparse_impl(const uint16_t* Q, int C, int q_start, int n_
                                    const int32_t* sel_cnt, float scale, float* O, hipStream_t stream) {
   const int nb = (T + block - 1) / block;
   const int n_qblk = (q_start + C - 1) / block - q_start / block + 1;
-  const size_t lds = Geo<D>::LDS_BYTES;
+  const int hpw = ((n_q / n_kv) % 2 == 0) ? 2 : 1;
+  const size_t lds = Geo<D>::LDS_BYTES + (((size_t)nb * 2 + 15) & ~(size_t)15);   // rings + selection list
   hipFuncSetAttribute((const void*)attn_blocksparse_kernel<D>,
                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  hipLaunchKernelGGL(attn_blocksparse_kernel<D>, dim3(n_qblk * n_q), dim3(NT), lds, stream, Q, C,
+  hipLaunchKernelGGL(attn_blocksparse_kernel<D>, dim3(n_qblk * (n_q / hpw)), dim3(NT), lds, stream, Q, C,
                      q_start, n_q, K, V, T, n_kv, Kp, Vp, nb, n_qblk, sel_idx, sel_cnt,
                      scale * LOG2E, O);
   return hipGetLastError();

@@ -64,9 +64,11 @@ hipError_t launch_mask_classify(const uint16_t* mask, int64_t mask_ld, int C, in
                                 uint8_t* flags, hipStream_t stream);
 
 struct DensePlan {
-  int n_qt;      // query tiles of 128 rows
+  int hg_log2;   // log2 of the query heads packed into one workgroup
+  int n_qt;      // query tiles of 256 >> hg_log2 rows
+  int n_qft;     // query rows of 128-row mask-flag tiles
   int n_ktile;   // flag tiles of 128 keys
-  int splits;    // key-range splits per (query tile, head)
+  int splits;    // key-range splits per (query tile, head slice)
   size_t flags_bytes, part_o_bytes, part_ml_bytes, total_bytes;
 };
 DensePlan plan_dense(int C, int T, int n_q, int n_kv, int d);

@@ -96,7 +96,7 @@ __global__ void __launch_bounds__(SEL_THREADS) select_kernel(
     const uint16_t* __restrict__ Q, int C, int q_start, int n_q, int n_kv,
     const float* __restrict__ Kp, int nb, int block, double theta, int vt_max,
     int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_cnt) {
-  extern __shared__ double smem[];
+  extern __shared__ __attribute__((aligned(16))) double smem[];
   const int g = blockIdx.y;
   const int jj = blockIdx.x;
   const int j0 = q_start / block;
