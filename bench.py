@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--workload", default="prefill32k", choices=["prefill32k", "dense128k"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 512 MiB device copy (reference for HBM byte counters)")
     ap.add_argument("--parts", default="dense,blocksparse",
                     help="subset of the step to run (for profiler runs); the default runs the whole step")
     return ap.parse_args()
@@ -146,6 +148,13 @@ def main():
         lp.build_pooled_index(K, V, B, K_pool=kp, V_pool=vp)
         lp.select_blocks(Q, kp, 0, B, s.alpha, scale, sel_idx=sel_idx, sel_cnt=sel_cnt)
         lp.prefill_attn_blocksparse(Q, K, V, kp, vp, sel_idx, sel_cnt, 0, B, scale, O=O_sparse)
+
+    if args.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         run_dense()
