@@ -88,6 +88,8 @@ def select_blocks(Q, K_pool, q_start: int, block: int, alpha: float, scale: floa
     C, n_q, d = Q.shape
     n_kv, nb, _ = K_pool.shape
     T = q_start + C
+    if nb != -(-T // block):
+        raise ValueError(f"K_pool has {nb} blocks; q_start + C = {T} needs {-(-T // block)}")
     n_qblk = (q_start + C - 1) // block - q_start // block + 1
     if sel_idx is None:
         sel_idx = torch.empty((n_kv, n_qblk, nb), dtype=torch.int32, device=Q.device)
@@ -112,8 +114,17 @@ def prefill_attn_blocksparse(Q, K, V, K_pool, V_pool, sel_idx, sel_cnt, q_start:
     _req(sel_cnt, "sel_cnt", torch.int32, 2)
     C, n_q, d = Q.shape
     T, n_kv, _ = K.shape
+    nb = -(-T // block)
+    n_qblk = (q_start + C - 1) // block - q_start // block + 1
+    if V.shape != K.shape or K.shape[2] != d:
+        raise ValueError("inconsistent Q/K/V shapes")
+    if tuple(K_pool.shape) != (n_kv, nb, d) or tuple(V_pool.shape) != (n_kv, nb, d):
+        raise ValueError(f"K_pool/V_pool must be {(n_kv, nb, d)}")
+    if tuple(sel_idx.shape) != (n_kv, n_qblk, nb) or tuple(sel_cnt.shape) != (n_kv, n_qblk):
+        raise ValueError(f"sel_idx/sel_cnt must be {(n_kv, n_qblk, nb)} / {(n_kv, n_qblk)}")
     if O is None:
         O = torch.empty((C, n_q, d), dtype=torch.float32, device=Q.device)
+    _req(O, "O", torch.float32, 3)
     check(lib().prefill_attn_blocksparse(Q.data_ptr(), C, q_start, n_q, K.data_ptr(), V.data_ptr(),
                                          T, n_kv, d, K_pool.data_ptr(), V_pool.data_ptr(), block,
                                          sel_idx.data_ptr(), sel_cnt.data_ptr(), float(scale),

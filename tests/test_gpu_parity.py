@@ -88,6 +88,87 @@ def test_select_bit_exact(lp, C, q_start, n_q, n_kv, d, block, alpha):
     assert np.array_equal(idx.cpu().numpy(), ridx)
 
 
+def _select_pooled(lp, q, kp, q_start, block, alpha, scale):
+    """Selection on a given pooled-key array, GPU vs oracle, bit-exact."""
+    import torch
+    idx, cnt = lp.select_blocks(dev_bf16(q), torch.from_numpy(np.ascontiguousarray(kp)).cuda(),
+                                q_start, block, alpha, scale)
+    torch.cuda.synchronize()
+    ridx, rcnt = select_ref(f64(q), kp, q_start, block, alpha, scale)
+    assert np.array_equal(cnt.cpu().numpy(), rcnt)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    return rcnt
+
+
+@pytest.mark.parametrize("n_q", [1, 16])   # 16 heads: the ambiguous list overflows
+def test_select_threshold_edge(lp, n_q):
+    """Pooled scores one to ten fp32 ulps either side of M + theta: the filter
+    cannot decide them, the fp64 re-evaluation must (strict >)."""
+    d, block, q_start, C = 128, 16, 640, 16
+    nb = (q_start + C) // block
+    scale = float(np.float32(1 / math.sqrt(d)))
+    alpha = 0.5
+    theta = math.log(alpha) / scale
+    q = np.zeros((C, n_q, d), dtype=np.float32)
+    q[:, :, 0] = 1.0
+    kp = np.zeros((1, nb, d), dtype=np.float32)
+    kp[0, 0, 0] = 1.0                                   # the row max M = 1
+    edge = np.float32(1.0 + theta)
+    vals = []
+    for s in range(-10, 10):                            # |s| fp32 ulps away from the edge
+        v = edge
+        for _ in range(abs(s)):
+            v = np.nextafter(v, np.float32(np.inf if s > 0 else -np.inf))
+        vals.append(v)
+    kp[0, 1:21, 0] = vals
+    kp[0, 21:31, 0] = 0.5                               # clearly kept
+    kp[0, 31:40, 0] = -100.0                            # clearly dropped
+    say("select threshold edge", n_q)
+    rcnt = _select_pooled(lp, bf16_bits(q), kp, q_start, block, alpha, scale)
+    assert 10 < rcnt[0, 0] - 1 < 30                     # both sides of the edge occur
+
+
+@pytest.mark.parametrize("n_q", [2, 8])    # 8 heads: more ambiguous pairs than the list holds
+def test_select_identical_pooled_keys(lp, n_q):
+    """All pooled keys equal and alpha = 1: every pair ties with the max, so every
+    pair is ambiguous and every voter has several near-max candidates."""
+    rng = np.random.default_rng(5)
+    C, q_start, n_kv, d, block = 200, 1000, 2, 128, 128
+    nb = -(-(q_start + C) // block)
+    q = rand_bits(rng, C, n_q, d)
+    row = rng.standard_normal(d).astype(np.float32)
+    kp = np.broadcast_to(row, (n_kv, nb, d)).copy()
+    scale = float(np.float32(1 / math.sqrt(d)))
+    say("select identical keys", n_q)
+    rcnt = _select_pooled(lp, q, kp, q_start, block, 1.0, scale)
+    assert np.all(rcnt == 1)
+
+
+def test_select_huge_magnitudes(lp):
+    """|q| |kbar| beyond the range of the filter's bound: decided in fp64 alone."""
+    rng = np.random.default_rng(6)
+    C, q_start, n_q, n_kv, d, block = 300, 700, 4, 2, 128, 64
+    T = q_start + C
+    q = rand_bits(rng, C, n_q, d, s=1e18)
+    k = rand_bits(rng, T, n_kv, d, s=1e15)
+    kp, _ = pooled_index_ref(f64(k), f64(k), block)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    say("select huge magnitudes")
+    rcnt = _select_pooled(lp, q, kp, q_start, block, 0.1, scale)
+    assert rcnt.min() >= 1
+
+
+def test_select_huge_theta(lp):
+    """ln(alpha)/scale beyond fp32's comfortable range: decided in fp64 alone."""
+    rng = np.random.default_rng(7)
+    C, q_start, n_q, n_kv, d, block = 256, 512, 4, 2, 64, 32
+    T = q_start + C
+    q, k = rand_bits(rng, C, n_q, d), rand_bits(rng, T, n_kv, d)
+    kp, _ = pooled_index_ref(f64(k), f64(k), block)
+    say("select huge theta")
+    _select_pooled(lp, q, kp, q_start, block, 1e-30, 1e-32)
+
+
 # ---------------------------------------------------------------- dense: configs
 @pytest.mark.parametrize("name", ["tiny", "gqa4k", "fold2k5"])
 def test_dense_configs(lp, name):
