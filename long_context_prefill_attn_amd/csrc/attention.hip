@@ -31,6 +31,7 @@
 //   * Workgroup ids are remapped so that the workgroups of one KV head run on
 //     one XCD (shared L2 for that head's K/V), longest query tiles first.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 
@@ -158,6 +159,14 @@ __device__ __forceinline__ LaneOffs<D> lane_offsets() {
   return o;
 }
 
+// acc + lo + hi of a packed bf16 pair (v_dot2_f32_bf16 against (1, 1), fp32
+// accumulate): the row sum is taken over the same rounded weights that enter
+// the PV product, so the normalised weights sum to one.
+__device__ __forceinline__ float row_sum_add(uint32_t packed, float acc) {
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), ones, acc, false);
+}
+
 struct StepCtx {
   float scale_log2;
   int kvalid;                        // keys of the step inside [0, T)
@@ -265,8 +274,8 @@ __device__ __forceinline__ void attn_step(const uint16_t* __restrict__ kt, const
       for (int w = 0; w < 4; ++w) {
         const float p0 = __builtin_amdgcn_exp2f(x[kb][8 * c + 2 * w] - mu);
         const float p1 = __builtin_amdgcn_exp2f(x[kb][8 * c + 2 * w + 1] - mu);
-        psum += p0 + p1;
         P[kb][c][w] = pack_bf16x2(p0, p1);
+        psum = row_sum_add(P[kb][c][w], psum);
       }
     }
   }
@@ -342,7 +351,7 @@ __device__ __forceinline__ void exp_pack(const f32x16 (&s)[2], float m, float sc
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * c + 2 * w], scale_log2, nmu));
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * c + 2 * w + 1], scale_log2, nmu));
         P[kb][c][w] = pack_bf16x2(p0, p1);
-        l += p0 + p1;
+        l = row_sum_add(P[kb][c][w], l);
       }
     }
   }
@@ -385,7 +394,7 @@ __device__ __forceinline__ float fused_step(const uint16_t* __restrict__ kt_next
       const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][8 * c + 2 * w], scale_log2, nmu));
       const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][8 * c + 2 * w + 1], scale_log2, nmu));
       P[kb][c][w] = pack_bf16x2(p0, p1);
-      psum += p0 + p1;
+      psum = row_sum_add(P[kb][c][w], psum);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -448,29 +457,36 @@ __device__ __forceinline__ void plain_steps(const TileLoader<D>& tl, uint16_t* l
   wait_vm<3 * NIW>();   // K[0], V[0] landed
   bare_barrier();
   int t1 = s1, t2 = s2;   // steps i+1 and i+2
-  int ik = 1, iv = 0;     // ring slots of K[i+1] and V[i]
-  auto iter = [&](const f32x16 (&sc)[2], float mxc, f32x16 (&sn)[2], float& mxn) -> bool {
+  // Iteration i uses ring slots IK = (i+1) % 3 for K[i+1] and IV = i % 3 for
+  // V[i]; six iterations cover both the 3-slot rings and the two S buffers, so
+  // the slots are compile-time constants and fold into the LDS offsets.
+  auto iter = [&](auto ikc, auto ivc, const f32x16 (&sc)[2], float mxc, f32x16 (&sn)[2],
+                  float& mxn) -> bool {
+    constexpr int IK = decltype(ikc)::value, IV = decltype(ivc)::value;
+    constexpr int K3 = IK == 0 ? KR - 1 : IK - 1;      // K[i]'s slot
+    constexpr int V2 = IV == 0 ? KR - 1 : IV - 1;      // V[i-1]'s slot
     raise_max<D>(mxc, scale_log2, o, m, l);
     wait_vm<2 * NIW>();   // K[i+1], V[i] landed
     bare_barrier();
     const int t3 = t2 >= 0 ? src.next(t2) : -1;
-    const int k3 = ik == 0 ? KR - 1 : ik - 1;          // K[i]'s slot
-    const int v2 = iv == 0 ? KR - 1 : iv - 1;          // V[i-1]'s slot
-    tl.issue(false, t3 >= 0 ? src.kbase(t3) : kfb, kring + k3 * TL);
-    tl.issue(true, t2 >= 0 ? src.kbase(t2) : kfb, vring + v2 * TL);
-    mxn = fused_step<D>(kring + ik * TL, vring + iv * TL, lo, qf, sc, sn, o, m, l, scale_log2);
+    tl.issue(false, t3 >= 0 ? src.kbase(t3) : kfb, kring + K3 * TL);
+    tl.issue(true, t2 >= 0 ? src.kbase(t2) : kfb, vring + V2 * TL);
+    mxn = fused_step<D>(kring + IK * TL, vring + IV * TL, lo, qf, sc, sn, o, m, l, scale_log2);
     if (t1 < 0) return false;
     t1 = t2;
     t2 = t3;
-    ik = ik == KR - 1 ? 0 : ik + 1;
-    iv = iv == KR - 1 ? 0 : iv + 1;
     return true;
   };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
   f32x16 sa[2], sb[2];
   float mxa, mxb;
   qk_tile<D>(kring, lo, qf, sa);
   mxa = row_max(sa);
-  while (iter(sa, mxa, sb, mxb) && iter(sb, mxb, sa, mxa)) {
+  while (iter(I1{}, I0{}, sa, mxa, sb, mxb) && iter(I2{}, I1{}, sb, mxb, sa, mxa) &&
+         iter(I0{}, I2{}, sa, mxa, sb, mxb) && iter(I1{}, I0{}, sb, mxb, sa, mxa) &&
+         iter(I2{}, I1{}, sa, mxa, sb, mxb) && iter(I0{}, I2{}, sb, mxb, sa, mxa)) {
   }
   wait_vm<0>();
   __syncthreads();   // LDS free for whatever follows
