@@ -360,8 +360,9 @@ __device__ __forceinline__ void exp_pack(const f32x16 (&s)[2], float m, float sc
 // One hand-scheduled pipeline iteration body (after the barrier and the tile
 // loads): the QK^T MFMAs of the next tile, each with the K fragment read four
 // MFMAs ahead and a quarter-pair of the current tile's exp/pack work; then the
-// PV MFMAs of the current tile, each with its transposed V reads two MFMAs
-// ahead and a share of the next tile's row-max. sched_barrier fences keep the
+// PV MFMAs of the current tile, each with its transposed V reads three MFMAs
+// ahead (the first three overlap the last QK^T MFMAs) and a share of the next
+// tile's row-max. sched_barrier fences keep the
 // compiler from regrouping the work. Returns the next tile's raw row max.
 template <int D>
 __device__ __forceinline__ float fused_step(const uint16_t* __restrict__ kt_next, const uint16_t* __restrict__ vt,
@@ -377,6 +378,16 @@ __device__ __forceinline__ float fused_step(const uint16_t* __restrict__ kt_next
 #pragma unroll
   for (int k = 0; k < KR; ++k)
     kf[k] = *reinterpret_cast<const bf16x8*>(kt_next + (k & 1) * 32 * D + lo.k[k >> 1]);
+  // PV operands: two transposed 8-byte reads per MFMA, kept VA MFMAs ahead;
+  // the first VA are issued during the last QK^T MFMAs
+  constexpr int VA = 3;
+  v4i16 vf[4][2];
+  auto vread = [&](int k, v4i16 (&dst)[2]) {
+    const int nb = k >> 2, kb = (k >> 1) & 1, c = k & 1;
+    const int off = lo.v[nb] + (kb * 32 + 16 * c) * D;
+    dst[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt + off));
+    dst[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt + off + 8 * D));
+  };
   sn[0] = f32x16{};
   sn[1] = f32x16{};
   u32x4 P[2][2];
@@ -386,6 +397,7 @@ __device__ __forceinline__ float fused_step(const uint16_t* __restrict__ kt_next
     const bf16x8 a = kf[k % KR];
     if (k + KR < NQK)
       kf[k % KR] = *reinterpret_cast<const bf16x8*>(kt_next + ((k + KR) & 1) * 32 * D + lo.k[(k + KR) >> 1]);
+    if (k >= NQK - VA) vread(k - (NQK - VA), vf[k - (NQK - VA)]);
     sn[k & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[k >> 1], sn[k & 1], 0, 0, 0);
     // exp/pack share: 16 packed pairs over NQK MFMAs
 #pragma unroll
@@ -400,20 +412,10 @@ __device__ __forceinline__ float fused_step(const uint16_t* __restrict__ kt_next
   }
   l += psum;
 
-  // PV: two transposed 8-byte reads per MFMA, two MFMAs ahead
-  v4i16 vf[4][2];
-  auto vread = [&](int k, v4i16 (&dst)[2]) {
-    const int nb = k >> 2, kb = (k >> 1) & 1, c = k & 1;
-    const int off = lo.v[nb] + (kb * 32 + 16 * c) * D;
-    dst[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt + off));
-    dst[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt + off + 8 * D));
-  };
-  vread(0, vf[0]);
-  vread(1, vf[1]);
   float mx = -__builtin_inff();
 #pragma unroll
   for (int k = 0; k < NPV; ++k) {
-    if (k + 2 < NPV) vread(k + 2, vf[(k + 2) & 3]);
+    if (k + VA < NPV) vread(k + VA, vf[(k + VA) & 3]);
     const int kb = (k >> 1) & 1, c = k & 1;
     const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vf[k & 3][0], vf[k & 3][1], 0, 1, 2, 3, 4, 5, 6, 7));
     o[k >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, P[kb][c]), o[k >> 2], 0, 0, 0);
