@@ -392,6 +392,7 @@ __device__ __forceinline__ float fused_step(const uint16_t* __restrict__ kt_next
   sn[1] = f32x16{};
   u32x4 P[2][2];
   float psum = 0.f;
+  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int k = 0; k < NQK; ++k) {
     const bf16x8 a = kf[k % KR];
@@ -410,6 +411,7 @@ __device__ __forceinline__ float fused_step(const uint16_t* __restrict__ kt_next
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+  __builtin_amdgcn_s_setprio(0);
   l += psum;
 
   float mx = -__builtin_inff();
