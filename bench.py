@@ -60,6 +60,17 @@ def source_hash(*names) -> str:
     return h.hexdigest()[:16]
 
 
+# sources each timed kernel is built from (a counter record is valid for one version)
+KERNEL_SOURCES = {
+    "attn_dense": ("attention.hip", "common.h"),
+    "attn_blocksparse": ("attention.hip", "common.h"),
+    "attn_combine": ("mask_combine.hip", "common.h"),
+    "mask_classify": ("mask_combine.hip", "common.h"),
+    "pool": ("pool_select.hip", "common.h"),
+    "select": ("pool_select.hip", "common.h"),
+}
+
+
 def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on the current kernel source (else None)."""
@@ -68,7 +79,7 @@ def measured_traffic(kernel: str, workload: str):
         return None
     with open(path) as f:
         rec = json.load(f).get(f"{kernel}:{workload}")
-    if not rec or rec.get("source_sha") != source_hash("attention.hip", "common.h"):
+    if not rec or rec.get("source_sha") != source_hash(*KERNEL_SOURCES[kernel]):
         return None
     return rec.get("bytes_per_launch")
 
