@@ -42,7 +42,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="prefill32k", choices=["prefill32k", "dense128k"])
+    ap.add_argument("--workload", default="prefill32k", choices=["prefill32k", "dense128k", "sparse128k"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -116,9 +116,17 @@ def main():
     def up_bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
+    # prefill32k: dense in 4,096-row chunks + one-shot block-sparse of the same 32K prompt
+    # sparse128k: dense and block-sparse, both in 4,096-row chunks over the growing history
+    # dense128k: dense in 4,096-row chunks only
+    chunked_sparse = args.workload == "sparse128k"
     if args.workload == "prefill32k":
         w = make_workload("sparse32k")
         chunks = chunk_list(w.N, 4096)
+        do_sparse = "blocksparse" in args.parts.split(",")
+    elif args.workload == "sparse128k":
+        w = make_workload("sparse128k")
+        chunks = w.spec.chunks
         do_sparse = "blocksparse" in args.parts.split(",")
     else:
         w = make_workload("dense128k")
@@ -136,8 +144,12 @@ def main():
     nb = -(-N // B)
     kp = torch.empty((Hkv, nb, d), dtype=torch.float32, device=dev)
     vp = torch.empty_like(kp)
-    sel_idx = torch.empty((Hkv, nb, nb), dtype=torch.int32, device=dev)
-    sel_cnt = torch.empty((Hkv, nb), dtype=torch.int32, device=dev)
+    sparse_calls = [(q0, C) for q0, C in chunks] if chunked_sparse else [(0, N)]
+    sel = []   # per call: (sel_idx, sel_cnt)
+    for q0, C in sparse_calls if do_sparse else []:
+        nbT, nq_blk = -(-(q0 + C) // B), (q0 + C - 1) // B - q0 // B + 1
+        sel.append((torch.empty((Hkv, nq_blk, nbT), dtype=torch.int32, device=dev),
+                    torch.empty((Hkv, nq_blk), dtype=torch.int32, device=dev)))
     O_sparse = torch.empty((N, Hq, d), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
@@ -156,9 +168,13 @@ def main():
             lp.prefill_attn_dense(Q[q0:T], K[:T], V[:T], m, scale, O=O_dense[q0:T], workspace=ws)
 
     def run_sparse():
-        lp.build_pooled_index(K, V, B, K_pool=kp, V_pool=vp)
-        lp.select_blocks(Q, kp, 0, B, s.alpha, scale, sel_idx=sel_idx, sel_cnt=sel_cnt)
-        lp.prefill_attn_blocksparse(Q, K, V, kp, vp, sel_idx, sel_cnt, 0, B, scale, O=O_sparse)
+        # one pooled index for the whole prompt, pooled incrementally chunk by chunk
+        for (q0, C), (si, sc) in zip(sparse_calls, sel):
+            T = q0 + C
+            lp.build_pooled_index(K[:T], V[:T], B, K_pool=kp, V_pool=vp, b_first=q0 // B)
+            lp.select_blocks(Q[q0:T], kp, q0, B, s.alpha, scale, sel_idx=si, sel_cnt=sc)
+            lp.prefill_attn_blocksparse(Q[q0:T], K[:T], V[:T], kp, vp, si, sc, q0, B, scale,
+                                        O=O_sparse[q0:T])
 
     if args.copy_calibration:
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
@@ -203,8 +219,8 @@ def main():
     assert torch.isfinite(O_dense).all().item(), "non-finite dense output"
     if do_sparse:
         assert torch.isfinite(O_sparse).all().item(), "non-finite block-sparse output"
-        visible = nb * (nb + 1) // 2 * Hkv
-        kept = int(sel_cnt.sum().item())
+        visible = nb * (nb + 1) // 2 * Hkv   # chunks cover each query block once (4,096 = 32 B)
+        kept = sum(int(sc.sum().item()) for _, sc in sel)
         sparsity = 1.0 - kept / visible
     tflops = (flops_dense + flops_sparse) / (ms_step * 1e-3) / 1e12
 
@@ -244,7 +260,9 @@ def main():
         "config": {"workload": args.workload, "tokens": N, "n_q": Hq, "n_kv": Hkv, "head_dim": d,
                    "chunk": 4096, "block": B if do_sparse else None,
                    "alpha": s.alpha if do_sparse else None,
-                   "step": "dense chunked + block-sparse prefill of the same prompt" if do_sparse
+                   "step": ("dense chunked + chunked block-sparse (incremental pooled index) prefill of "
+                            "the same prompt" if chunked_sparse else
+                            "dense chunked + block-sparse prefill of the same prompt") if do_sparse
                    else "dense chunked prefill", "parallelism": "none (1 GPU)"},
         "tokens_per_s": round((2 if do_sparse else 1) * N / (ms_step * 1e-3)),
         "pct_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),

@@ -6,6 +6,8 @@
  *   build_pooled_index        mean-pooled key/value blocks
  *   select_blocks             alpha-threshold block selection plus the local diagonal
  *   prefill_attn_blocksparse  exact attention on selected blocks + pooled correction
+ * and the last three have *_ld forms for chunked prefill over a growing history
+ * (a pooled index with spare capacity, pooled incrementally).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -154,6 +156,44 @@ int prefill_attn_blocksparse(const uint16_t* Q, int C, int q_start, int n_q,
                              const float* K_pool, const float* V_pool, int block,
                              const int32_t* sel_idx, const int32_t* sel_cnt,
                              float scale, float* O, void* stream);
+
+/*
+ * Chunked block-sparse prefill over a growing history: the same three steps
+ * with a pooled index that is built incrementally and kept between chunks.
+ * ("Porting FlashPrefill V2 to Apple silicon", Part I: the pooled index
+ * summarises the history by blocks; "ANE Prefill Research", How the ANE prefill
+ * path works: a prompt is prefilled chunk by chunk over the accumulated K/V.)
+ *
+ * Each takes the pooled arrays with a row capacity `pool_ld` per KV head:
+ *   K_pool, V_pool  fp32 [n_kv][pool_ld][d], pool_ld >= ceil(T/block)
+ * so one allocation sized for the longest history serves every chunk, and a
+ * block pooled once stays valid (its keys never change).
+ *
+ * build_pooled_index_ld -- pools blocks b_first .. ceil(T/block)-1 of K[0..T) and
+ *   V[0..T) (same arithmetic as build_pooled_index) and leaves blocks below
+ *   b_first untouched. For chunk after chunk, b_first = floor(T_prev/block)
+ *   re-pools the previous partial block, if any, with its new keys.
+ *   Requires 0 <= b_first <= ceil(T/block); b_first == ceil(T/block) enqueues nothing.
+ * select_blocks_ld, prefill_attn_blocksparse_ld -- as select_blocks and
+ *   prefill_attn_blocksparse, reading the pooled rows of blocks 0..ceil(T/block)-1
+ *   from arrays with row capacity pool_ld. sel_idx keeps its per-call layout
+ *   [n_kv][n_qblk][ceil(T/block)].
+ * select_blocks(...) is select_blocks_ld(..., pool_ld = ceil(T/block), ...), and
+ * likewise for the other two (b_first = 0).
+ * Errors: as the base calls; pool_ld < ceil(T/block) or b_first out of range is PA_EINVAL.
+ */
+int build_pooled_index_ld(const uint16_t* K, const uint16_t* V, int T, int n_kv, int d, int block,
+                          int b_first, float* K_pool, float* V_pool, int pool_ld, void* stream);
+
+int select_blocks_ld(const uint16_t* Q, int C, int q_start, int n_q, int n_kv, int d,
+                     const float* K_pool, int pool_ld, int T, int block, float alpha, float scale,
+                     int32_t* sel_idx, int32_t* sel_cnt, void* stream);
+
+int prefill_attn_blocksparse_ld(const uint16_t* Q, int C, int q_start, int n_q,
+                                const uint16_t* K, const uint16_t* V, int T, int n_kv, int d,
+                                const float* K_pool, const float* V_pool, int pool_ld, int block,
+                                const int32_t* sel_idx, const int32_t* sel_cnt,
+                                float scale, float* O, void* stream);
 
 /*
  * Kernel timing (instrumentation for benchmarks; off by default).

@@ -6,9 +6,13 @@ torch's current stream. Outputs are allocated with torch when not supplied.
 The calls are asynchronous, like the kernels they enqueue.
 
     prefill_attn_dense(Q, K, V, mask, scale)                  -> O
-    build_pooled_index(K, V, block)                            -> (K_pool, V_pool)
+    build_pooled_index(K, V, block[, K_pool, V_pool, b_first]) -> (K_pool, V_pool)
     select_blocks(Q, K_pool, q_start, block, alpha, scale)     -> (sel_idx, sel_cnt)
     prefill_attn_blocksparse(Q, K, V, K_pool, V_pool, sel_idx, sel_cnt, q_start, block, scale) -> O
+
+The pooled arrays may carry spare block rows ([n_kv][cap][d], cap >= ceil(T/block)):
+chunked prefill keeps one pooled index for the whole prompt and pools each chunk's
+new blocks with b_first (the *_ld entry points of the C ABI).
 """
 from __future__ import annotations
 
@@ -64,52 +68,70 @@ def prefill_attn_dense(Q, K, V, mask, scale: float, O=None, workspace=None):
     return O
 
 
-def build_pooled_index(K, V, block: int, K_pool=None, V_pool=None):
-    """K, V bf16 [T][n_kv][d] -> K_pool, V_pool fp32 [n_kv][ceil(T/block)][d]."""
+def _pooled(P, name, n_kv, nb, d, device):
+    """A pooled array [n_kv][cap][d] fp32 with cap >= nb; returns (tensor, cap)."""
+    if P is None:
+        return torch.empty((n_kv, nb, d), dtype=torch.float32, device=device), nb
+    _req(P, name, torch.float32, 3)
+    if P.shape[0] != n_kv or P.shape[2] != d or P.shape[1] < nb:
+        raise ValueError(f"{name} must be [{n_kv}][>= {nb}][{d}], got {tuple(P.shape)}")
+    return P, P.shape[1]
+
+
+def build_pooled_index(K, V, block: int, K_pool=None, V_pool=None, b_first: int = 0):
+    """K, V bf16 [T][n_kv][d] -> K_pool, V_pool fp32 [n_kv][cap][d] (cap >= ceil(T/block)).
+
+    Pools blocks b_first .. ceil(T/block)-1; given arrays with spare capacity keep
+    their other rows (chunked prefill: b_first = previous T // block)."""
     _req(K, "K", torch.bfloat16, 3)
     _req(V, "V", torch.bfloat16, 3)
     T, n_kv, d = K.shape
+    if V.shape != K.shape:
+        raise ValueError("K and V shapes differ")
     nb = -(-T // block)
-    if K_pool is None:
-        K_pool = torch.empty((n_kv, nb, d), dtype=torch.float32, device=K.device)
-    if V_pool is None:
-        V_pool = torch.empty((n_kv, nb, d), dtype=torch.float32, device=K.device)
-    check(lib().build_pooled_index(K.data_ptr(), V.data_ptr(), T, n_kv, d, block,
-                                   K_pool.data_ptr(), V_pool.data_ptr(), _stream()),
+    K_pool, cap = _pooled(K_pool, "K_pool", n_kv, nb, d, K.device)
+    V_pool, cap_v = _pooled(V_pool, "V_pool", n_kv, nb, d, K.device)
+    if cap_v != cap:
+        raise ValueError("K_pool and V_pool capacities differ")
+    check(lib().build_pooled_index_ld(K.data_ptr(), V.data_ptr(), T, n_kv, d, block, b_first,
+                                      K_pool.data_ptr(), V_pool.data_ptr(), cap, _stream()),
           "build_pooled_index")
     return K_pool, V_pool
 
 
 def select_blocks(Q, K_pool, q_start: int, block: int, alpha: float, scale: float,
                   sel_idx=None, sel_cnt=None):
-    """-> sel_idx int32 [n_kv][n_qblk][nb], sel_cnt int32 [n_kv][n_qblk]."""
+    """-> sel_idx int32 [n_kv][n_qblk][nb], sel_cnt int32 [n_kv][n_qblk] (nb = ceil(T/block)).
+
+    K_pool may have spare capacity: [n_kv][cap >= nb][d]."""
     _req(Q, "Q", torch.bfloat16, 3)
-    _req(K_pool, "K_pool", torch.float32, 3)
     C, n_q, d = Q.shape
-    n_kv, nb, _ = K_pool.shape
+    n_kv = K_pool.shape[0]
     T = q_start + C
-    if nb != -(-T // block):
-        raise ValueError(f"K_pool has {nb} blocks; q_start + C = {T} needs {-(-T // block)}")
+    nb = -(-T // block)
+    K_pool, cap = _pooled(K_pool, "K_pool", n_kv, nb, d, Q.device)
     n_qblk = (q_start + C - 1) // block - q_start // block + 1
     if sel_idx is None:
         sel_idx = torch.empty((n_kv, n_qblk, nb), dtype=torch.int32, device=Q.device)
     if sel_cnt is None:
         sel_cnt = torch.empty((n_kv, n_qblk), dtype=torch.int32, device=Q.device)
-    check(lib().select_blocks(Q.data_ptr(), C, q_start, n_q, n_kv, d, K_pool.data_ptr(), T, block,
-                              float(alpha), float(scale), sel_idx.data_ptr(), sel_cnt.data_ptr(),
-                              _stream()),
+    _req(sel_idx, "sel_idx", torch.int32, 3)
+    _req(sel_cnt, "sel_cnt", torch.int32, 2)
+    if tuple(sel_idx.shape) != (n_kv, n_qblk, nb) or tuple(sel_cnt.shape) != (n_kv, n_qblk):
+        raise ValueError(f"sel_idx/sel_cnt must be {(n_kv, n_qblk, nb)} / {(n_kv, n_qblk)}")
+    check(lib().select_blocks_ld(Q.data_ptr(), C, q_start, n_q, n_kv, d, K_pool.data_ptr(), cap, T,
+                                 block, float(alpha), float(scale), sel_idx.data_ptr(),
+                                 sel_cnt.data_ptr(), _stream()),
           "select_blocks")
     return sel_idx, sel_cnt
 
 
 def prefill_attn_blocksparse(Q, K, V, K_pool, V_pool, sel_idx, sel_cnt, q_start: int, block: int,
                              scale: float, O=None):
-    """Causal block-sparse attention -> O fp32 [C][n_q][d]."""
+    """Causal block-sparse attention -> O fp32 [C][n_q][d]. K_pool/V_pool may have spare capacity."""
     _req(Q, "Q", torch.bfloat16, 3)
     _req(K, "K", torch.bfloat16, 3)
     _req(V, "V", torch.bfloat16, 3)
-    _req(K_pool, "K_pool", torch.float32, 3)
-    _req(V_pool, "V_pool", torch.float32, 3)
     _req(sel_idx, "sel_idx", torch.int32, 3)
     _req(sel_cnt, "sel_cnt", torch.int32, 2)
     C, n_q, d = Q.shape
@@ -118,17 +140,19 @@ def prefill_attn_blocksparse(Q, K, V, K_pool, V_pool, sel_idx, sel_cnt, q_start:
     n_qblk = (q_start + C - 1) // block - q_start // block + 1
     if V.shape != K.shape or K.shape[2] != d:
         raise ValueError("inconsistent Q/K/V shapes")
-    if tuple(K_pool.shape) != (n_kv, nb, d) or tuple(V_pool.shape) != (n_kv, nb, d):
-        raise ValueError(f"K_pool/V_pool must be {(n_kv, nb, d)}")
+    K_pool, cap = _pooled(K_pool, "K_pool", n_kv, nb, d, Q.device)
+    V_pool, cap_v = _pooled(V_pool, "V_pool", n_kv, nb, d, Q.device)
+    if cap_v != cap:
+        raise ValueError("K_pool and V_pool capacities differ")
     if tuple(sel_idx.shape) != (n_kv, n_qblk, nb) or tuple(sel_cnt.shape) != (n_kv, n_qblk):
         raise ValueError(f"sel_idx/sel_cnt must be {(n_kv, n_qblk, nb)} / {(n_kv, n_qblk)}")
     if O is None:
         O = torch.empty((C, n_q, d), dtype=torch.float32, device=Q.device)
     _req(O, "O", torch.float32, 3)
-    check(lib().prefill_attn_blocksparse(Q.data_ptr(), C, q_start, n_q, K.data_ptr(), V.data_ptr(),
-                                         T, n_kv, d, K_pool.data_ptr(), V_pool.data_ptr(), block,
-                                         sel_idx.data_ptr(), sel_cnt.data_ptr(), float(scale),
-                                         O.data_ptr(), _stream()),
+    check(lib().prefill_attn_blocksparse_ld(Q.data_ptr(), C, q_start, n_q, K.data_ptr(), V.data_ptr(),
+                                            T, n_kv, d, K_pool.data_ptr(), V_pool.data_ptr(), cap,
+                                            block, sel_idx.data_ptr(), sel_cnt.data_ptr(),
+                                            float(scale), O.data_ptr(), _stream()),
           "prefill_attn_blocksparse")
     return O
 

@@ -146,20 +146,29 @@ int prefill_attn_dense(const uint16_t* Q, int C, int n_q, const uint16_t* K, con
   return PA_OK;
 }
 
-int build_pooled_index(const uint16_t* K, const uint16_t* V, int T, int n_kv, int d, int block,
-                       float* K_pool, float* V_pool, void* stream) {
+int build_pooled_index_ld(const uint16_t* K, const uint16_t* V, int T, int n_kv, int d, int block,
+                          int b_first, float* K_pool, float* V_pool, int pool_ld, void* stream) {
   if (!aligned16(K) || !aligned16(V) || !aligned16(K_pool) || !aligned16(V_pool)) return PA_EINVAL;
   if (T < 1 || n_kv < 1) return PA_EINVAL;
   if ((d != 64 && d != 128) || !pow2_block(block)) return PA_EUNSUPPORTED;
+  const int nb = (T + block - 1) / block;
+  if (b_first < 0 || b_first > nb || pool_ld < nb) return PA_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return hip_status(timed("pool", s, [&] {
-    return pa::launch_pool(K, V, T, n_kv, d, block, K_pool, V_pool, s);
+    return pa::launch_pool(K, V, T, n_kv, d, block, b_first, K_pool, V_pool, pool_ld, s);
   }));
 }
 
-int select_blocks(const uint16_t* Q, int C, int q_start, int n_q, int n_kv, int d,
-                  const float* K_pool, int T, int block, float alpha, float scale,
-                  int32_t* sel_idx, int32_t* sel_cnt, void* stream) {
+int build_pooled_index(const uint16_t* K, const uint16_t* V, int T, int n_kv, int d, int block,
+                       float* K_pool, float* V_pool, void* stream) {
+  if (T < 1 || !pow2_block(block)) return T < 1 ? PA_EINVAL : PA_EUNSUPPORTED;
+  return build_pooled_index_ld(K, V, T, n_kv, d, block, 0, K_pool, V_pool, (T + block - 1) / block,
+                               stream);
+}
+
+int select_blocks_ld(const uint16_t* Q, int C, int q_start, int n_q, int n_kv, int d,
+                     const float* K_pool, int pool_ld, int T, int block, float alpha, float scale,
+                     int32_t* sel_idx, int32_t* sel_cnt, void* stream) {
   if (!aligned16(Q) || !aligned16(K_pool) || !aligned16(sel_idx) || !aligned16(sel_cnt))
     return PA_EINVAL;
   if (C < 1 || q_start < 0 || n_q < 1 || n_kv < 1 || n_q % n_kv != 0) return PA_EINVAL;
@@ -168,18 +177,28 @@ int select_blocks(const uint16_t* Q, int C, int q_start, int n_q, int n_kv, int 
   if ((d != 64 && d != 128) || !pow2_block(block)) return PA_EUNSUPPORTED;
   const int nb = (T + block - 1) / block;
   if (nb > 8192) return PA_EUNSUPPORTED;
+  if (pool_ld < nb) return PA_EINVAL;
   // theta = ln(alpha)/scale in fp64; alpha = 0 keeps every block
   const double theta = alpha == 0.f ? -HUGE_VAL : std::log((double)alpha) / (double)scale;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return hip_status(timed("select", s, [&] {
-    return pa::launch_select(Q, C, q_start, n_q, n_kv, d, K_pool, T, block, theta, sel_idx, sel_cnt, s);
+    return pa::launch_select(Q, C, q_start, n_q, n_kv, d, K_pool, pool_ld, T, block, theta, sel_idx,
+                             sel_cnt, s);
   }));
 }
 
-int prefill_attn_blocksparse(const uint16_t* Q, int C, int q_start, int n_q, const uint16_t* K,
-                             const uint16_t* V, int T, int n_kv, int d, const float* K_pool,
-                             const float* V_pool, int block, const int32_t* sel_idx,
-                             const int32_t* sel_cnt, float scale, float* O, void* stream) {
+int select_blocks(const uint16_t* Q, int C, int q_start, int n_q, int n_kv, int d,
+                  const float* K_pool, int T, int block, float alpha, float scale,
+                  int32_t* sel_idx, int32_t* sel_cnt, void* stream) {
+  if (T < 1 || !pow2_block(block)) return T < 1 ? PA_EINVAL : PA_EUNSUPPORTED;
+  return select_blocks_ld(Q, C, q_start, n_q, n_kv, d, K_pool, (T + block - 1) / block, T, block,
+                          alpha, scale, sel_idx, sel_cnt, stream);
+}
+
+int prefill_attn_blocksparse_ld(const uint16_t* Q, int C, int q_start, int n_q, const uint16_t* K,
+                                const uint16_t* V, int T, int n_kv, int d, const float* K_pool,
+                                const float* V_pool, int pool_ld, int block, const int32_t* sel_idx,
+                                const int32_t* sel_cnt, float scale, float* O, void* stream) {
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(K_pool) || !aligned16(V_pool) ||
       !aligned16(sel_idx) || !aligned16(sel_cnt) || !aligned16(O))
     return PA_EINVAL;
@@ -190,11 +209,22 @@ int prefill_attn_blocksparse(const uint16_t* Q, int C, int q_start, int n_q, con
   if ((long long)T * n_kv * d * 2 >= (1LL << 31)) return PA_EUNSUPPORTED;   // 32-bit tile offsets
   const int nb = (T + block - 1) / block;
   if (nb > 8192) return PA_EUNSUPPORTED;
+  if (pool_ld < nb) return PA_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return hip_status(timed("attn_blocksparse", s, [&] {
-    return pa::launch_attn_blocksparse(Q, C, q_start, n_q, K, V, T, n_kv, d, K_pool, V_pool, block,
-                                       sel_idx, sel_cnt, scale, O, s);
+    return pa::launch_attn_blocksparse(Q, C, q_start, n_q, K, V, T, n_kv, d, K_pool, V_pool, pool_ld,
+                                       block, sel_idx, sel_cnt, scale, O, s);
   }));
+}
+
+int prefill_attn_blocksparse(const uint16_t* Q, int C, int q_start, int n_q, const uint16_t* K,
+                             const uint16_t* V, int T, int n_kv, int d, const float* K_pool,
+                             const float* V_pool, int block, const int32_t* sel_idx,
+                             const int32_t* sel_cnt, float scale, float* O, void* stream) {
+  if (T < 1 || block < 1) return PA_EINVAL;
+  return prefill_attn_blocksparse_ld(Q, C, q_start, n_q, K, V, T, n_kv, d, K_pool, V_pool,
+                                     (T + block - 1) / block, block, sel_idx, sel_cnt, scale, O,
+                                     stream);
 }
 
 int pa_timing_enable(int on) {

@@ -724,7 +724,7 @@ __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
 attn_blocksparse_kernel(const uint16_t* __restrict__ Q, int C, int q_start, int n_q,
                         const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, int T,
                         int n_kv, const float* __restrict__ Kp, const float* __restrict__ Vp,
-                        int nb, int n_qblk, const int32_t* __restrict__ sel_idx,
+                        int pool_ld, int nb, int n_qblk, const int32_t* __restrict__ sel_idx,
                         const int32_t* __restrict__ sel_cnt, float scale_log2, float* __restrict__ O) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   __shared__ uint32_t selbits[256];  // up to 8192 blocks
@@ -803,8 +803,8 @@ attn_blocksparse_kernel(const uint16_t* __restrict__ Q, int C, int q_start, int 
   uint16_t* klo = lds + Geo<D>::TILE;
   uint16_t* vhi = lds + KR * Geo<D>::TILE;
   uint16_t* vlo = vhi + Geo<D>::TILE;
-  const float* kpg = Kp + (size_t)g * nb * D;
-  const float* vpg = Vp + (size_t)g * nb * D;
+  const float* kpg = Kp + (size_t)g * pool_ld * D;
+  const float* vpg = Vp + (size_t)g * pool_ld * D;
   for (int pbase = 0; pbase < j; pbase += BN) {
     stage_pooled_one<D>(kpg, pbase, j, khi, klo);
     stage_pooled_one<D>(vpg, pbase, j, vhi, vlo);
@@ -909,7 +909,7 @@ hipError_t launch_attn_dense(const uint16_t* Q, int C, int n_q, const uint16_t* 
 template <int D>
 static hipError_t blocksparse_impl(const uint16_t* Q, int C, int q_start, int n_q, const uint16_t* K,
                                    const uint16_t* V, int T, int n_kv, const float* Kp,
-                                   const float* Vp, int block, const int32_t* sel_idx,
+                                   const float* Vp, int pool_ld, int block, const int32_t* sel_idx,
                                    const int32_t* sel_cnt, float scale, float* O, hipStream_t stream) {
   const int nb = (T + block - 1) / block;
   const int n_qblk = (q_start + C - 1) / block - q_start / block + 1;
@@ -918,21 +918,21 @@ static hipError_t blocksparse_impl(const uint16_t* Q, int C, int q_start, int n_
   hipFuncSetAttribute((const void*)attn_blocksparse_kernel<D>,
                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   hipLaunchKernelGGL(attn_blocksparse_kernel<D>, dim3(n_qblk * (n_q / hpw)), dim3(NT), lds, stream, Q, C,
-                     q_start, n_q, K, V, T, n_kv, Kp, Vp, nb, n_qblk, sel_idx, sel_cnt,
+                     q_start, n_q, K, V, T, n_kv, Kp, Vp, pool_ld, nb, n_qblk, sel_idx, sel_cnt,
                      scale * LOG2E, O);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_blocksparse(const uint16_t* Q, int C, int q_start, int n_q,
                                    const uint16_t* K, const uint16_t* V, int T, int n_kv, int d,
-                                   const float* K_pool, const float* V_pool, int block,
+                                   const float* K_pool, const float* V_pool, int pool_ld, int block,
                                    const int32_t* sel_idx, const int32_t* sel_cnt, float scale,
                                    float* O, hipStream_t stream) {
   if (d == 128)
-    return blocksparse_impl<128>(Q, C, q_start, n_q, K, V, T, n_kv, K_pool, V_pool, block, sel_idx,
-                                 sel_cnt, scale, O, stream);
-  return blocksparse_impl<64>(Q, C, q_start, n_q, K, V, T, n_kv, K_pool, V_pool, block, sel_idx,
-                              sel_cnt, scale, O, stream);
+    return blocksparse_impl<128>(Q, C, q_start, n_q, K, V, T, n_kv, K_pool, V_pool, pool_ld, block,
+                                 sel_idx, sel_cnt, scale, O, stream);
+  return blocksparse_impl<64>(Q, C, q_start, n_q, K, V, T, n_kv, K_pool, V_pool, pool_ld, block,
+                              sel_idx, sel_cnt, scale, O, stream);
 }
 
 }  // namespace pa

@@ -54,10 +54,10 @@ namespace pa {
 struct KernelTimer;  // opaque; see api.cpp
 
 hipError_t launch_pool(const uint16_t* K, const uint16_t* V, int T, int n_kv, int d, int block,
-                       float* K_pool, float* V_pool, hipStream_t stream);
+                       int b_first, float* K_pool, float* V_pool, int pool_ld, hipStream_t stream);
 
 hipError_t launch_select(const uint16_t* Q, int C, int q_start, int n_q, int n_kv, int d,
-                         const float* K_pool, int T, int block, double theta,
+                         const float* K_pool, int pool_ld, int T, int block, double theta,
                          int32_t* sel_idx, int32_t* sel_cnt, hipStream_t stream);
 
 hipError_t launch_mask_classify(const uint16_t* mask, int64_t mask_ld, int C, int T,
@@ -83,7 +83,7 @@ hipError_t launch_attn_combine(int C, int n_q, int d, int splits, const float* p
 
 hipError_t launch_attn_blocksparse(const uint16_t* Q, int C, int q_start, int n_q,
                                    const uint16_t* K, const uint16_t* V, int T, int n_kv, int d,
-                                   const float* K_pool, const float* V_pool, int block,
+                                   const float* K_pool, const float* V_pool, int pool_ld, int block,
                                    const int32_t* sel_idx, const int32_t* sel_cnt,
                                    float scale, float* O, hipStream_t stream);
 

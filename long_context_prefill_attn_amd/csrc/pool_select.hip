@@ -20,15 +20,17 @@ namespace pa {
 // build_pooled_index: one lane owns 8 adjacent columns (of the n_kv*d columns
 // of a token row) of one key block, and walks the block's tokens in order.
 // A wave reads 64 x 16 contiguous bytes per token: coalesced, HBM-bound.
-// grid = (ceil(cols8 / 64), n_blocks, 2 [K, V]), block = 64.
+// grid = (ceil(cols8 / 64), blocks b_first .. nb-1, 2 [K, V]), block = 64. The
+// pooled arrays hold pool_ld block rows per KV head.
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(64) pool_kernel(const uint16_t* __restrict__ K,
                                                   const uint16_t* __restrict__ V, int T,
-                                                  int cols8, int d, int block, int nb,
-                                                  float* __restrict__ Kp, float* __restrict__ Vp) {
+                                                  int cols8, int d, int block, int b_first,
+                                                  int pool_ld, float* __restrict__ Kp,
+                                                  float* __restrict__ Vp) {
   const int c8 = blockIdx.x * 64 + threadIdx.x;
   if (c8 >= cols8) return;
-  const int b = blockIdx.y;
+  const int b = b_first + (int)blockIdx.y;
   const uint16_t* X = blockIdx.z ? V : K;
   float* P = blockIdx.z ? Vp : Kp;
   const int t0 = b * block;
@@ -66,18 +68,19 @@ __global__ void __launch_bounds__(64) pool_kernel(const uint16_t* __restrict__ K
   float out[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) out[e] = (float)(acc[e] / dn);
-  float4* dst = reinterpret_cast<float4*>(P + ((size_t)g * nb + b) * d + dd);
+  float4* dst = reinterpret_cast<float4*>(P + ((size_t)g * pool_ld + b) * d + dd);
   dst[0] = make_float4(out[0], out[1], out[2], out[3]);
   dst[1] = make_float4(out[4], out[5], out[6], out[7]);
 }
 
 hipError_t launch_pool(const uint16_t* K, const uint16_t* V, int T, int n_kv, int d, int block,
-                       float* K_pool, float* V_pool, hipStream_t stream) {
+                       int b_first, float* K_pool, float* V_pool, int pool_ld, hipStream_t stream) {
   const int cols8 = n_kv * d / 8;
   const int nb = (T + block - 1) / block;
-  dim3 grid((cols8 + 63) / 64, nb, 2);
-  hipLaunchKernelGGL(pool_kernel, grid, dim3(64), 0, stream, K, V, T, cols8, d, block, nb, K_pool,
-                     V_pool);
+  if (b_first >= nb) return hipSuccess;   // nothing new to pool
+  dim3 grid((cols8 + 63) / 64, nb - b_first, 2);
+  hipLaunchKernelGGL(pool_kernel, grid, dim3(64), 0, stream, K, V, T, cols8, d, block, b_first,
+                     pool_ld, K_pool, V_pool);
   return hipGetLastError();
 }
 
@@ -106,9 +109,10 @@ hipError_t launch_pool(const uint16_t* K, const uint16_t* V, int T, int n_kv, in
 //     filtered gap lies more than 2E (+ 2^-22 |theta|) from theta is decided;
 //  2. lists the other pairs as ambiguous. The exact argmax of voter i is the
 //     filter's argmax unless another candidate came within 2E of the filtered
-//     max; such voters are flagged;
+//     max; such voters are flagged and their near-max pairs listed;
 //  3. re-evaluates the listed pairs in fp64 in the reference order: M_i
-//     exactly (the filter's argmax, or every candidate for a flagged voter),
+//     exactly (the filter's argmax, or the max over a flagged voter's near-max
+//     pairs),
 //     then each ambiguous pair against theta. Each exact dot product is done
 //     by a wave: one coalesced load of the two rows, the exact fp64 products
 //     staged in LDS, one lane summing them in order (4 pairs per wave at a
@@ -132,6 +136,7 @@ constexpr int SEL_CH = 64;               // candidates staged per chunk
 constexpr int SEL_MAX_NB = 8192;
 constexpr int SEL_AMB_CAP = 2048;        // ambiguous pairs per voter tile
 constexpr int SEL_JOB_CAP = 2048;        // exact max evaluations per voter tile
+constexpr int SEL_NEAR_CAP = 1024;       // near-max pairs of flagged voters per voter tile
 constexpr int SEL_JOBS = 4;              // exact dot products per wave at a time
 constexpr float SEL_ERR = 1.0e-4f;
 constexpr float SEL_ABS = 1.0e-30f;
@@ -194,13 +199,14 @@ struct SelShared {
   unsigned long long mxkey[SEL_VT];        // exact max (as dkey) of voters with ambiguous pairs
   uint32_t amb[SEL_AMB_CAP];               // (voter << 16) | block
   uint32_t jobs[SEL_JOB_CAP];              // pairs whose exact score enters a max
+  uint32_t nearl[SEL_NEAR_CAP];            // near-max pairs of flagged voters: (voter << 16) | block
   uint32_t flagw[SEL_MAX_NB / 32];
   uint32_t wsum[SEL_WAVES];
   uint16_t argb[SEL_VT];                   // the filter's argmax per voter
   uint8_t va[SEL_VT];                      // voter has ambiguous pairs
   uint8_t multi[SEL_VT];                   // several candidates came within 2E of the max
   float red[SEL_WAVES];
-  uint32_t amb_cnt, job_cnt;
+  uint32_t amb_cnt, job_cnt, near_cnt;
   uint32_t overflow;
 };
 
@@ -251,7 +257,8 @@ __device__ __forceinline__ void exact_pairs(SelShared<D>& S, const uint32_t* lis
 template <int D>
 __global__ void __launch_bounds__(SEL_THREADS) select_kernel(
     const uint16_t* __restrict__ Q, int C, int q_start, int n_q, int n_kv,
-    const float* __restrict__ Kp, int nb, int block, double theta, float theta_f, float theta_slack,
+    const float* __restrict__ Kp, int pool_ld, int nb, int block, double theta, float theta_f,
+    float theta_slack,
     int exact_only, int n_qblk, int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_cnt) {
   constexpr int NST = D / 16;   // MFMA k-steps
   constexpr int TPR = SEL_THREADS / SEL_CH;   // staging threads per candidate row
@@ -272,7 +279,7 @@ __global__ void __launch_bounds__(SEL_THREADS) select_kernel(
   const int nw = (nc + 31) >> 5;
 
   for (int i = tid; i < nw; i += SEL_THREADS) S.flagw[i] = 0;
-  const float* kg = Kp + (size_t)g * nb * D;
+  const float* kg = Kp + (size_t)g * pool_ld * D;
   const uint16_t* qg = Q + ((size_t)r0 * n_q + (size_t)g * group) * D;
   auto qptr = [&](int v) { return qg + ((size_t)(v / group) * n_q + (v % group)) * D; };
 
@@ -285,7 +292,7 @@ __global__ void __launch_bounds__(SEL_THREADS) select_kernel(
     for (int vt0 = 0; vt0 < nv; vt0 += SEL_VT) {
       __syncthreads();  // previous tile's readers of the shared state are done
       for (int i = tid; i < SEL_VT; i += SEL_THREADS) { S.va[i] = 0; S.mxkey[i] = 0; }
-      if (tid == 0) { S.amb_cnt = 0; S.job_cnt = 0; S.overflow = exact_only; }
+      if (tid == 0) { S.amb_cnt = 0; S.job_cnt = 0; S.near_cnt = 0; S.overflow = exact_only; }
 
       // B operand: q of the wave's 32 voters (voter = lane % 32), held for the whole tile
       const int vl = wave * 32 + col;  // voter within the tile
@@ -313,6 +320,7 @@ __global__ void __launch_bounds__(SEL_THREADS) select_kernel(
       // the voter's running max and second max over this lane's candidates
       float m1 = -__builtin_inff(), m2 = -__builtin_inff();
       float M = 0.f, tY = 0.f, tA = 0.f;  // the voter's max; yes above tY; ambiguous from tA
+      float tN = 0.f;                     // near-max from tN (recorded for flagged voters)
       int nidx = -1;                      // this lane's candidate equal to the max, if any
       bool multi = false;
       float mloc = 0.f;
@@ -423,6 +431,19 @@ __global__ void __launch_bounds__(SEL_THREADS) select_kernel(
                   }
                 }
               }
+              if (__builtin_amdgcn_ballot_w64(multi)) {
+                if (multi) {   // the exact max of a flagged voter is among these
+#pragma unroll
+                  for (int i = 0; i < 16; ++i) {
+                    const int c = cbase + 8 * (i >> 2) + (i & 3);
+                    if ((!RG || c < nc) & (acc[i] >= tN)) {
+                      const uint32_t k = atomicAdd(&S.near_cnt, 1u);
+                      if (k < SEL_NEAR_CAP) S.nearl[k] = ((uint32_t)vl << 16) | (uint32_t)c;
+                      else S.overflow = 1u;
+                    }
+                  }
+                }
+              }
               if (word != 0 && lane == 0) atomicOr(&S.flagw[cb >> 5], word);
             };
             if (cb + 32 > nc) tile(std::true_type{});
@@ -446,7 +467,8 @@ __global__ void __launch_bounds__(SEL_THREADS) select_kernel(
           const float nm = qn * mnorm;
           const bool bad = vok && !(qn <= SEL_MAG && mnorm <= SEL_MAG && nm <= SEL_MAG);
           const float e2 = 2.f * (SEL_ERR * nm + SEL_ABS * (qn + mnorm + 1.f));
-          multi = second >= M - e2;  // another candidate may hold the exact max
+          tN = M - e2;
+          multi = vok && second >= tN;  // another candidate may hold the exact max
           tY = M + (theta_f + (e2 + theta_slack));
           tA = M + (theta_f - (e2 + theta_slack));
           if (!vok) M = tY = tA = __builtin_inff();  // no voter: nothing passes any test
@@ -467,21 +489,20 @@ __global__ void __launch_bounds__(SEL_THREADS) select_kernel(
       __syncthreads();  // every thread has read the flags before they change again
       if (go) {
         // pairs whose exact score may be the max of a voter with ambiguous pairs:
-        // its argmax, or every candidate when several came within 2E
+        // its argmax, or its recorded near-max pairs when several came within 2E
         for (int v = tid; v < SEL_VT; v += SEL_THREADS) {
-          if (!S.va[v]) continue;
-          if (S.multi[v]) {
-            const uint32_t k = atomicAdd(&S.job_cnt, (uint32_t)nc);
-            if (k + nc <= SEL_JOB_CAP) {
-              for (int b = 0; b < nc; ++b) S.jobs[k + b] = ((uint32_t)v << 16) | (uint32_t)b;
-            } else {
-              S.overflow = 1u;
-            }
-          } else {
-            const uint32_t k = atomicAdd(&S.job_cnt, 1u);
-            if (k < SEL_JOB_CAP) S.jobs[k] = ((uint32_t)v << 16) | S.argb[v];
-            else S.overflow = 1u;
-          }
+          if (!S.va[v] || S.multi[v]) continue;
+          const uint32_t k = atomicAdd(&S.job_cnt, 1u);
+          if (k < SEL_JOB_CAP) S.jobs[k] = ((uint32_t)v << 16) | S.argb[v];
+          else S.overflow = 1u;
+        }
+        const int nn = (int)min(S.near_cnt, (uint32_t)SEL_NEAR_CAP);
+        for (int e = tid; e < nn; e += SEL_THREADS) {
+          const uint32_t pr = S.nearl[e];
+          if (!S.va[pr >> 16]) continue;
+          const uint32_t k = atomicAdd(&S.job_cnt, 1u);
+          if (k < SEL_JOB_CAP) S.jobs[k] = pr;
+          else S.overflow = 1u;
         }
         __syncthreads();
         if (!S.overflow) {
@@ -538,7 +559,7 @@ __global__ void __launch_bounds__(SEL_THREADS) select_kernel(
 }
 
 hipError_t launch_select(const uint16_t* Q, int C, int q_start, int n_q, int n_kv, int d,
-                         const float* K_pool, int T, int block, double theta,
+                         const float* K_pool, int pool_ld, int T, int block, double theta,
                          int32_t* sel_idx, int32_t* sel_cnt, hipStream_t stream) {
   const int nb = (T + block - 1) / block;
   const int j0 = q_start / block;
@@ -552,11 +573,11 @@ hipError_t launch_select(const uint16_t* Q, int C, int q_start, int n_q, int n_k
   dim3 grid(n_qblk * n_kv);
   if (d == 128)
     hipLaunchKernelGGL(select_kernel<128>, grid, dim3(SEL_THREADS), 0, stream, Q, C, q_start, n_q,
-                       n_kv, K_pool, nb, block, theta, theta_f, theta_slack, exact_only, n_qblk,
+                       n_kv, K_pool, pool_ld, nb, block, theta, theta_f, theta_slack, exact_only, n_qblk,
                        sel_idx, sel_cnt);
   else
     hipLaunchKernelGGL(select_kernel<64>, grid, dim3(SEL_THREADS), 0, stream, Q, C, q_start, n_q,
-                       n_kv, K_pool, nb, block, theta, theta_f, theta_slack, exact_only, n_qblk,
+                       n_kv, K_pool, pool_ld, nb, block, theta, theta_f, theta_slack, exact_only, n_qblk,
                        sel_idx, sel_cnt);
   return hipGetLastError();
 }

@@ -108,6 +108,22 @@ def test_pool_and_blocksparse_reject():
     assert bs(d=256) == _lib.PA_EUNSUPPORTED
 
 
+def test_ld_forms_reject():
+    """Pooled-index capacity and incremental range checks of the *_ld entry points."""
+    lib = _lib.lib()
+    # T = 1000, block 128 -> 8 blocks: capacity 7 is too small, b_first 9 is past the end
+    assert lib.build_pooled_index_ld(FAKE, FAKE, 1000, 2, 128, 128, 0, FAKE, FAKE, 7, None) == _lib.PA_EINVAL
+    assert lib.build_pooled_index_ld(FAKE, FAKE, 1000, 2, 128, 128, 9, FAKE, FAKE, 8, None) == _lib.PA_EINVAL
+    assert lib.build_pooled_index_ld(FAKE, FAKE, 1000, 2, 128, 128, -1, FAKE, FAKE, 8, None) == _lib.PA_EINVAL
+    assert lib.build_pooled_index_ld(FAKE, FAKE, 1000, 2, 128, 96, 0, FAKE, FAKE, 8, None) == _lib.PA_EUNSUPPORTED
+    assert lib.select_blocks_ld(FAKE, 256, 744, 4, 2, 128, FAKE, 7, 1000, 128, 0.1, 0.125, FAKE, FAKE,
+                                None) == _lib.PA_EINVAL
+    assert lib.prefill_attn_blocksparse_ld(FAKE, 256, 744, 4, FAKE, FAKE, 1000, 2, 128, FAKE, FAKE, 7,
+                                           128, FAKE, FAKE, 0.1, FAKE, None) == _lib.PA_EINVAL
+    assert lib.prefill_attn_blocksparse_ld(FAKE, 256, 744, 4, FAKE, FAKE, 1000, 2, 128, FAKE, FAKE, 8,
+                                           64, FAKE, FAKE, 0.1, FAKE, None) == _lib.PA_EUNSUPPORTED
+
+
 def test_timing_api_host_side():
     lib = _lib.lib()
     ms, n = ctypes.c_double(), ctypes.c_int64()

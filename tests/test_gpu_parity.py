@@ -323,3 +323,115 @@ def test_blocksparse_32k_sampled(lp):
     rows = np.array([j * B + o for j in qblocks for o in (0, 63, 127)])
     want = blocksparse_ref(Q64, K64, V64, rkp, rvp, ridx, rcnt, 0, B, s.scale, rows=rows)
     assert_close(got[rows], want, "sparse32k")
+
+
+# ---------------------------------------------------------------- chunked block-sparse
+def test_pool_incremental_bit_exact(lp):
+    """Pooling chunk by chunk into one array with spare rows equals pooling the
+    whole prefix: the partial block of each earlier chunk is re-pooled, rows past
+    the current length are left alone."""
+    import torch
+    rng = np.random.default_rng(21)
+    n_kv, d, block, cap = 2, 128, 128, 12
+    k, v = rand_bits(rng, 1400, n_kv, d), rand_bits(rng, 1400, n_kv, d, s=2.0)
+    Kd, Vd = dev_bf16(k), dev_bf16(v)
+    kp = torch.full((n_kv, cap, d), float("nan"), device="cuda")
+    vp = torch.full((n_kv, cap, d), float("nan"), device="cuda")
+    say("pool incremental")
+    prev = 0
+    for T in (300, 1000, 1000, 1400):            # 1000 twice: nothing new to pool
+        lp.build_pooled_index(Kd[:T], Vd[:T], block, K_pool=kp, V_pool=vp, b_first=prev // block)
+        prev = T
+    torch.cuda.synchronize()
+    rk, rv = pooled_index_ref(f64(k), f64(v), block)   # 11 blocks of the full 1400 keys
+    got_k, got_v = kp.cpu().numpy(), vp.cpu().numpy()
+    assert np.array_equal(got_k[:, :11].view(np.uint32), rk.view(np.uint32))
+    assert np.array_equal(got_v[:, :11].view(np.uint32), rv.view(np.uint32))
+    assert np.isnan(got_k[:, 11:]).all() and np.isnan(got_v[:, 11:]).all()
+
+
+def _chunked_sparse_gpu(lp, q, k, v, chunks, block, alpha, scale, cap):
+    """Chunk-by-chunk block-sparse prefill with one incrementally pooled index."""
+    import torch
+    Qd, Kd, Vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    n_kv, d = k.shape[1], k.shape[2]
+    kp = torch.empty((n_kv, cap, d), device="cuda")
+    vp = torch.empty_like(kp)
+    O = torch.empty((q.shape[0], q.shape[1], d), device="cuda")
+    sels = []
+    for q0, C in chunks:
+        T = q0 + C
+        lp.build_pooled_index(Kd[:T], Vd[:T], block, K_pool=kp, V_pool=vp, b_first=q0 // block)
+        idx, cnt = lp.select_blocks(Qd[q0:T], kp, q0, block, alpha, scale)
+        lp.prefill_attn_blocksparse(Qd[q0:T], Kd[:T], Vd[:T], kp, vp, idx, cnt, q0, block, scale,
+                                    O=O[q0:T])
+        sels.append((idx, cnt))
+    torch.cuda.synchronize()
+    return (kp.cpu().numpy(), vp.cpu().numpy(), [(i.cpu().numpy(), c.cpu().numpy()) for i, c in sels],
+            O.cpu().numpy())
+
+
+def test_blocksparse_chunked_unaligned(lp):
+    """Chunks of 1,000 rows (not a multiple of the 128-key block) over a growing
+    history: per chunk, selection bit-exact and every output row within tolerance."""
+    rng = np.random.default_rng(22)
+    N, n_q, n_kv, d, B = 3000, 4, 2, 128, 128
+    q, k, v = rand_bits(rng, N, n_q, d), rand_bits(rng, N, n_kv, d), rand_bits(rng, N, n_kv, d)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    chunks = ((0, 1000), (1000, 1000), (2000, 1000))
+    say("blocksparse chunked unaligned")
+    kp, vp, sels, got = _chunked_sparse_gpu(lp, q, k, v, chunks, B, 0.1, scale, cap=-(-N // B) + 3)
+    rkp, rvp = pooled_index_ref(f64(k), f64(v), B)
+    nb = rkp.shape[1]
+    assert np.array_equal(kp[:, :nb].view(np.uint32), rkp.view(np.uint32))
+    for (q0, C), (idx, cnt) in zip(chunks, sels):
+        T = q0 + C
+        nbT = -(-T // B)
+        # the pooled rows a chunk saw: blocks of its own prefix (the partial last block pooled over T keys)
+        pk, pv = pooled_index_ref(f64(k[:T]), f64(v[:T]), B)
+        ridx, rcnt = select_ref(f64(q[q0:T]), pk, q0, B, 0.1, scale)
+        assert np.array_equal(cnt, rcnt) and np.array_equal(idx, ridx), q0
+        want = blocksparse_ref(f64(q[q0:T]), f64(k[:T]), f64(v[:T]), pk, pv, ridx, rcnt, q0, B, scale)
+        assert_close(got[q0:T], want, f"chunk at {q0}")
+        assert pk.shape[1] == nbT
+
+
+@pytest.mark.timeout(600)
+def test_blocksparse_128k_chunked_sampled(lp):
+    """The planted 128K prompt in 32 chunks of 4,096 over the growing history, as
+    the bench runs it: full pooled index bit-exact, selection bit-exact on sampled
+    query blocks of sampled chunks, outputs on sampled rows."""
+    say("blocksparse 128K chunked: generating inputs")
+    w = make_workload("sparse128k")
+    s = w.spec
+    B = s.block
+    say("blocksparse 128K chunked: GPU")
+    nb = s.N // B
+    kp, vp, sels, got = _chunked_sparse_gpu(lp, w.Q, w.K, w.V, s.chunks, B, s.alpha, s.scale, cap=nb)
+    say("blocksparse 128K chunked: oracle")
+    K64, V64 = f64(w.K), f64(w.V)
+    rkp, rvp = pooled_index_ref(K64, V64, B)
+    assert np.array_equal(kp.view(np.uint32), rkp.view(np.uint32))
+    assert np.array_equal(vp.view(np.uint32), rvp.view(np.uint32))
+    kept = sum(int(c.sum()) for _, c in sels)
+    say("sparsity", 1.0 - kept / (nb * (nb + 1) // 2 * s.n_kv))
+    for ci in (0, 9, 31):
+        q0, C = s.chunks[ci]
+        T = q0 + C
+        idx, cnt = sels[ci]
+        j0 = q0 // B
+        qblocks = [j0, j0 + 13, j0 + 31]
+        Qc = f64(w.Q[q0:T])
+        sets = selection_sets(Qc, rkp, q0, B, s.alpha, s.scale, qblocks=qblocks)
+        nbT = T // B
+        ridx = np.zeros((s.n_kv, C // B, nbT), dtype=np.int32)
+        rcnt = np.zeros((s.n_kv, C // B), dtype=np.int32)
+        for (g, j), keep in sets.items():
+            ridx[g, j - j0, :len(keep)] = keep
+            rcnt[g, j - j0] = len(keep)
+            assert np.array_equal(idx[g, j - j0], ridx[g, j - j0]), (ci, g, j)
+            assert cnt[g, j - j0] == rcnt[g, j - j0], (ci, g, j)
+        rows = np.array([(j - j0) * B + o for j in qblocks for o in (0, 77, 127)])
+        want = blocksparse_ref(Qc, K64[:T], V64[:T], rkp[:, :nbT], rvp[:, :nbT], ridx, rcnt, q0, B,
+                               s.scale, rows=rows)
+        assert_close(got[q0 + rows], want, f"sparse128k chunk {ci}")

@@ -28,11 +28,21 @@ DROPPED = -30000.0  # fp16-exact sentinel for an omitted key
 # encodings
 # ----------------------------------------------------------------------------
 def bf16_bits(x) -> np.ndarray:
-    """Round float32 values to bf16 with round-to-nearest-even; return the bits."""
+    """Round float32 values to bf16 with round-to-nearest-even; return the bits.
+
+    Works through the array in slices so large inputs need no full-size temporaries."""
     x = np.ascontiguousarray(x, dtype=np.float32)
-    u = x.view(np.uint32)
-    bias = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
-    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+    flat = x.reshape(-1).view(np.uint32)
+    out = np.empty(flat.shape, dtype=np.uint16)
+    step = 1 << 22
+    for s0 in range(0, flat.size, step):
+        u = flat[s0:s0 + step]
+        t = (u >> np.uint32(16)) & np.uint32(1)
+        t += np.uint32(0x7FFF)
+        t += u
+        t >>= np.uint32(16)
+        out[s0:s0 + step] = t
+    return out.reshape(x.shape)
 
 
 def bf16_to_f32(bits) -> np.ndarray:
@@ -93,6 +103,12 @@ CONFIGS = {
                                    n_plants=4, min_j=20, min_gap=16)),
     # 128K dense causal prefill in 4,096-token chunks over the accumulated history
     "dense128k": Spec("dense128k", 5, 32, 8, 128, 131072, chunk_list(131072, 4096)),
+    # 128K block-sparse prefill in 4,096-token chunks over the accumulated history
+    # (incremental pooled index), same planted structure as the 32K case
+    "sparse128k": Spec("sparse128k", 6, 32, 8, 128, 131072, chunk_list(131072, 4096), mask="none",
+                       structure="planted",
+                       planted=dict(Aq=10.0, Ak=5.0, L=6000.0, gamma=6.0, shift=3.0,
+                                    n_plants=4, min_j=20, min_gap=16)),
 }
 
 
