@@ -178,15 +178,25 @@ int prefill_attn_blocksparse(const uint16_t* Q, int C, int q_start, int n_q,
  *   prefill_attn_blocksparse, reading the pooled rows of blocks 0..ceil(T/block)-1
  *   from arrays with row capacity pool_ld. sel_idx keeps its per-call layout
  *   [n_kv][n_qblk][ceil(T/block)].
- * select_blocks(...) is select_blocks_ld(..., pool_ld = ceil(T/block), ...), and
- * likewise for the other two (b_first = 0).
- * Errors: as the base calls; pool_ld < ceil(T/block) or b_first out of range is PA_EINVAL.
+ * select_blocks_ld also keeps blocks by rule ("Porting FlashPrefill V2 to Apple
+ *   silicon", figure "Where the kept blocks are": sinks, a local window and a
+ *   dense tail are kept whatever their scores). For query block j:
+ *     sink_tokens        every block b < j holding one of the first sink_tokens keys;
+ *     window_blocks      blocks j-window_blocks .. j-1;
+ *     dense_tail_blocks  every b < j when j is among the last dense_tail_blocks
+ *                        query blocks of this call's rows (pass it on the final chunk).
+ *   All three zero gives exactly select_blocks' selection.
+ * select_blocks(...) is select_blocks_ld(..., pool_ld = ceil(T/block), no rules, ...),
+ * and likewise for the other two (b_first = 0).
+ * Errors: as the base calls; pool_ld < ceil(T/block), b_first out of range or a
+ * negative rule count is PA_EINVAL.
  */
 int build_pooled_index_ld(const uint16_t* K, const uint16_t* V, int T, int n_kv, int d, int block,
                           int b_first, float* K_pool, float* V_pool, int pool_ld, void* stream);
 
 int select_blocks_ld(const uint16_t* Q, int C, int q_start, int n_q, int n_kv, int d,
                      const float* K_pool, int pool_ld, int T, int block, float alpha, float scale,
+                     int sink_tokens, int window_blocks, int dense_tail_blocks,
                      int32_t* sel_idx, int32_t* sel_cnt, void* stream);
 
 int prefill_attn_blocksparse_ld(const uint16_t* Q, int C, int q_start, int n_q,

@@ -100,10 +100,12 @@ def build_pooled_index(K, V, block: int, K_pool=None, V_pool=None, b_first: int 
 
 
 def select_blocks(Q, K_pool, q_start: int, block: int, alpha: float, scale: float,
-                  sel_idx=None, sel_cnt=None):
+                  sel_idx=None, sel_cnt=None, sink_tokens: int = 0, window_blocks: int = 0,
+                  dense_tail_blocks: int = 0):
     """-> sel_idx int32 [n_kv][n_qblk][nb], sel_cnt int32 [n_kv][n_qblk] (nb = ceil(T/block)).
 
-    K_pool may have spare capacity: [n_kv][cap >= nb][d]."""
+    K_pool may have spare capacity: [n_kv][cap >= nb][d]. The three rule counts
+    keep blocks whatever their scores (see select_blocks_ld in the header)."""
     _req(Q, "Q", torch.bfloat16, 3)
     C, n_q, d = Q.shape
     n_kv = K_pool.shape[0]
@@ -120,7 +122,8 @@ def select_blocks(Q, K_pool, q_start: int, block: int, alpha: float, scale: floa
     if tuple(sel_idx.shape) != (n_kv, n_qblk, nb) or tuple(sel_cnt.shape) != (n_kv, n_qblk):
         raise ValueError(f"sel_idx/sel_cnt must be {(n_kv, n_qblk, nb)} / {(n_kv, n_qblk)}")
     check(lib().select_blocks_ld(Q.data_ptr(), C, q_start, n_q, n_kv, d, K_pool.data_ptr(), cap, T,
-                                 block, float(alpha), float(scale), sel_idx.data_ptr(),
+                                 block, float(alpha), float(scale), int(sink_tokens),
+                                 int(window_blocks), int(dense_tail_blocks), sel_idx.data_ptr(),
                                  sel_cnt.data_ptr(), _stream()),
           "select_blocks")
     return sel_idx, sel_cnt

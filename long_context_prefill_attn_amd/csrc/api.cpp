@@ -4,6 +4,7 @@
 // fallback path: a request the kernels cannot serve is refused with a status.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -168,6 +169,7 @@ int build_pooled_index(const uint16_t* K, const uint16_t* V, int T, int n_kv, in
 
 int select_blocks_ld(const uint16_t* Q, int C, int q_start, int n_q, int n_kv, int d,
                      const float* K_pool, int pool_ld, int T, int block, float alpha, float scale,
+                     int sink_tokens, int window_blocks, int dense_tail_blocks,
                      int32_t* sel_idx, int32_t* sel_cnt, void* stream) {
   if (!aligned16(Q) || !aligned16(K_pool) || !aligned16(sel_idx) || !aligned16(sel_cnt))
     return PA_EINVAL;
@@ -178,12 +180,15 @@ int select_blocks_ld(const uint16_t* Q, int C, int q_start, int n_q, int n_kv, i
   const int nb = (T + block - 1) / block;
   if (nb > 8192) return PA_EUNSUPPORTED;
   if (pool_ld < nb) return PA_EINVAL;
+  if (sink_tokens < 0 || window_blocks < 0 || dense_tail_blocks < 0) return PA_EINVAL;
+  const int sink_blocks = (int)std::min<long long>(((long long)sink_tokens + block - 1) / block, nb);
   // theta = ln(alpha)/scale in fp64; alpha = 0 keeps every block
   const double theta = alpha == 0.f ? -HUGE_VAL : std::log((double)alpha) / (double)scale;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return hip_status(timed("select", s, [&] {
-    return pa::launch_select(Q, C, q_start, n_q, n_kv, d, K_pool, pool_ld, T, block, theta, sel_idx,
-                             sel_cnt, s);
+    return pa::launch_select(Q, C, q_start, n_q, n_kv, d, K_pool, pool_ld, T, block, theta,
+                             sink_blocks, std::min(window_blocks, nb), std::min(dense_tail_blocks, nb),
+                             sel_idx, sel_cnt, s);
   }));
 }
 
@@ -192,7 +197,7 @@ int select_blocks(const uint16_t* Q, int C, int q_start, int n_q, int n_kv, int 
                   int32_t* sel_idx, int32_t* sel_cnt, void* stream) {
   if (T < 1 || !pow2_block(block)) return T < 1 ? PA_EINVAL : PA_EUNSUPPORTED;
   return select_blocks_ld(Q, C, q_start, n_q, n_kv, d, K_pool, (T + block - 1) / block, T, block,
-                          alpha, scale, sel_idx, sel_cnt, stream);
+                          alpha, scale, 0, 0, 0, sel_idx, sel_cnt, stream);
 }
 
 int prefill_attn_blocksparse_ld(const uint16_t* Q, int C, int q_start, int n_q, const uint16_t* K,

@@ -58,6 +58,7 @@ hipError_t launch_pool(const uint16_t* K, const uint16_t* V, int T, int n_kv, in
 
 hipError_t launch_select(const uint16_t* Q, int C, int q_start, int n_q, int n_kv, int d,
                          const float* K_pool, int pool_ld, int T, int block, double theta,
+                         int sink_blocks, int window_blocks, int dense_tail_blocks,
                          int32_t* sel_idx, int32_t* sel_cnt, hipStream_t stream);
 
 hipError_t launch_mask_classify(const uint16_t* mask, int64_t mask_ld, int C, int T,

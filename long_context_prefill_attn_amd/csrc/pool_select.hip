@@ -172,6 +172,14 @@ __device__ __forceinline__ double dot_exact(const uint16_t* __restrict__ q, cons
   return acc;
 }
 
+// bits of positions [a, b) inside the 32-position word starting at lo
+__device__ __forceinline__ uint32_t range_bits(int lo, int a, int b) {
+  const int s0 = max(a - lo, 0), e0 = min(b - lo, 32);
+  if (s0 >= e0) return 0u;
+  const uint32_t upto = e0 == 32 ? 0xFFFFFFFFu : ((1u << e0) - 1u);
+  return upto & ~((1u << s0) - 1u);
+}
+
 __device__ __forceinline__ double wave_max(double v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v = fmax(v, __shfl_xor(v, off));
@@ -259,7 +267,8 @@ __global__ void __launch_bounds__(SEL_THREADS) select_kernel(
     const uint16_t* __restrict__ Q, int C, int q_start, int n_q, int n_kv,
     const float* __restrict__ Kp, int pool_ld, int nb, int block, double theta, float theta_f,
     float theta_slack,
-    int exact_only, int n_qblk, int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_cnt) {
+    int exact_only, int n_qblk, int sink_blocks, int window_blocks, int dense_tail_blocks,
+    int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_cnt) {
   constexpr int NST = D / 16;   // MFMA k-steps
   constexpr int TPR = SEL_THREADS / SEL_CH;   // staging threads per candidate row
   constexpr int DPT = D / TPR;                // staged dims per thread
@@ -529,6 +538,16 @@ __global__ void __launch_bounds__(SEL_THREADS) select_kernel(
     }
   }
   __syncthreads();
+  // kept by rule: sink blocks, a local window below the diagonal, and every
+  // visible block for the call's last query blocks
+  if (sink_blocks > 0 || window_blocks > 0 || dense_tail_blocks > 0) {
+    const bool tail = jj > n_qblk - 1 - dense_tail_blocks;
+    const int s_end = tail ? nc : min(sink_blocks, nc);
+    const int w_beg = max(0, nc - window_blocks);
+    for (int i = tid; i < nw; i += SEL_THREADS)
+      S.flagw[i] |= range_bits(i * 32, 0, s_end) | range_bits(i * 32, w_beg, nc);
+    __syncthreads();
+  }
   // ascending compaction: thread t owns flag word t (nc <= 8191 -> at most 256 words)
   const uint32_t word = tid < nw ? S.flagw[tid] : 0u;
   const uint32_t cnt = __popc(word);
@@ -560,6 +579,7 @@ __global__ void __launch_bounds__(SEL_THREADS) select_kernel(
 
 hipError_t launch_select(const uint16_t* Q, int C, int q_start, int n_q, int n_kv, int d,
                          const float* K_pool, int pool_ld, int T, int block, double theta,
+                         int sink_blocks, int window_blocks, int dense_tail_blocks,
                          int32_t* sel_idx, int32_t* sel_cnt, hipStream_t stream) {
   const int nb = (T + block - 1) / block;
   const int j0 = q_start / block;
@@ -574,11 +594,11 @@ hipError_t launch_select(const uint16_t* Q, int C, int q_start, int n_q, int n_k
   if (d == 128)
     hipLaunchKernelGGL(select_kernel<128>, grid, dim3(SEL_THREADS), 0, stream, Q, C, q_start, n_q,
                        n_kv, K_pool, pool_ld, nb, block, theta, theta_f, theta_slack, exact_only, n_qblk,
-                       sel_idx, sel_cnt);
+                       sink_blocks, window_blocks, dense_tail_blocks, sel_idx, sel_cnt);
   else
     hipLaunchKernelGGL(select_kernel<64>, grid, dim3(SEL_THREADS), 0, stream, Q, C, q_start, n_q,
                        n_kv, K_pool, pool_ld, nb, block, theta, theta_f, theta_slack, exact_only, n_qblk,
-                       sel_idx, sel_cnt);
+                       sink_blocks, window_blocks, dense_tail_blocks, sel_idx, sel_cnt);
   return hipGetLastError();
 }
 

@@ -18,5 +18,5 @@ closed forms, library routines or invariants that the method fixes.
 """
 from .dense import attention_weights, dense_ref  # noqa: F401
 from .blocksparse import (  # noqa: F401
-    pooled_index_ref, selection_votes_ref, select_ref, blocksparse_ref, selection_sets,
+    pooled_index_ref, selection_votes_ref, select_ref, blocksparse_ref, selection_sets, rule_blocks,
 )

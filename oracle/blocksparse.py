@@ -105,13 +105,33 @@ def selection_votes_ref(q_rows, kbar_visible, alpha: float, scale: float) -> np.
     return (r - M) > threshold(alpha, scale)
 
 
+def rule_blocks(j: int, j_last: int, block: int, sink_tokens: int = 0, window_blocks: int = 0,
+                dense_tail_blocks: int = 0) -> set:
+    """Blocks b < j kept by rule for query block j (figure "Where the kept blocks
+    are": the first tokens as attention sinks, a local window next to the
+    diagonal, and the last query tiles attending densely).
+
+    sinks:  every b < ceil(sink_tokens / block);
+    window: j - window_blocks <= b < j;
+    tail:   every b < j when j > j_last - dense_tail_blocks, j_last being the last
+            query block of the call's rows.
+    """
+    if j > j_last - dense_tail_blocks:
+        return set(range(j))
+    sinks = set(range(min(j, -(-sink_tokens // block))))
+    window = set(range(max(0, j - window_blocks), j))
+    return sinks | window
+
+
 def selection_sets(Q, K_pool, q_start: int, block: int, alpha: float, scale: float,
-                   qblocks=None) -> dict:
+                   qblocks=None, sink_tokens: int = 0, window_blocks: int = 0,
+                   dense_tail_blocks: int = 0) -> dict:
     """{(g, j): sorted list of kept block ids} for the query blocks of a chunk.
 
     Q [C][Hq][d] holds the chunk's rows at absolute positions q_start..q_start+C-1;
     K_pool [Hkv][Nb][d].  ``qblocks`` optionally restricts the absolute query
-    blocks evaluated.  Only rows of this chunk vote.
+    blocks evaluated.  Only rows of this chunk vote.  The kept-by-rule blocks of
+    ``rule_blocks`` join the voted ones (all rules off by default).
     """
     C, Hq, d = Q.shape
     Hkv = K_pool.shape[0]
@@ -126,12 +146,14 @@ def selection_sets(Q, K_pool, q_start: int, block: int, alpha: float, scale: flo
             r1 = min((j + 1) * block, q_start + C) - q_start
             rows = Q[r0:r1, g * group:(g + 1) * group, :].transpose(1, 0, 2).reshape(-1, d)
             votes = selection_votes_ref(rows, K_pool[g, :j, :], alpha, scale)
-            kept = [int(b) for b in np.nonzero(votes.any(axis=0))[0]]
-            out[(g, j)] = kept + [j]            # the diagonal block is always kept
+            kept = {int(b) for b in np.nonzero(votes.any(axis=0))[0]}
+            kept |= rule_blocks(j, j1, block, sink_tokens, window_blocks, dense_tail_blocks)
+            out[(g, j)] = sorted(kept) + [j]    # the diagonal block is always kept
     return out
 
 
-def select_ref(Q, K_pool, q_start: int, block: int, alpha: float, scale: float):
+def select_ref(Q, K_pool, q_start: int, block: int, alpha: float, scale: float,
+               sink_tokens: int = 0, window_blocks: int = 0, dense_tail_blocks: int = 0):
     """Compacted selection arrays, as the library returns them.
 
     sel_idx [Hkv][n_qblk][Nb] int32: kept block ids ascending (so the diagonal
@@ -144,7 +166,8 @@ def select_ref(Q, K_pool, q_start: int, block: int, alpha: float, scale: float):
     nb = -(-T // block)
     j0 = q_start // block
     n_qblk = (q_start + C - 1) // block - j0 + 1
-    sets = selection_sets(Q, K_pool, q_start, block, alpha, scale)
+    sets = selection_sets(Q, K_pool, q_start, block, alpha, scale, sink_tokens=sink_tokens,
+                          window_blocks=window_blocks, dense_tail_blocks=dense_tail_blocks)
     sel_idx = np.zeros((Hkv, n_qblk, nb), dtype=np.int32)
     sel_cnt = np.zeros((Hkv, n_qblk), dtype=np.int32)
     for (g, j), kept in sets.items():

@@ -116,8 +116,11 @@ def test_ld_forms_reject():
     assert lib.build_pooled_index_ld(FAKE, FAKE, 1000, 2, 128, 128, 9, FAKE, FAKE, 8, None) == _lib.PA_EINVAL
     assert lib.build_pooled_index_ld(FAKE, FAKE, 1000, 2, 128, 128, -1, FAKE, FAKE, 8, None) == _lib.PA_EINVAL
     assert lib.build_pooled_index_ld(FAKE, FAKE, 1000, 2, 128, 96, 0, FAKE, FAKE, 8, None) == _lib.PA_EUNSUPPORTED
-    assert lib.select_blocks_ld(FAKE, 256, 744, 4, 2, 128, FAKE, 7, 1000, 128, 0.1, 0.125, FAKE, FAKE,
-                                None) == _lib.PA_EINVAL
+    assert lib.select_blocks_ld(FAKE, 256, 744, 4, 2, 128, FAKE, 7, 1000, 128, 0.1, 0.125, 0, 0, 0,
+                                FAKE, FAKE, None) == _lib.PA_EINVAL
+    for rules in ((-1, 0, 0), (0, -1, 0), (0, 0, -1)):
+        assert lib.select_blocks_ld(FAKE, 256, 744, 4, 2, 128, FAKE, 8, 1000, 128, 0.1, 0.125, *rules,
+                                    FAKE, FAKE, None) == _lib.PA_EINVAL
     assert lib.prefill_attn_blocksparse_ld(FAKE, 256, 744, 4, FAKE, FAKE, 1000, 2, 128, FAKE, FAKE, 7,
                                            128, FAKE, FAKE, 0.1, FAKE, None) == _lib.PA_EINVAL
     assert lib.prefill_attn_blocksparse_ld(FAKE, 256, 744, 4, FAKE, FAKE, 1000, 2, 128, FAKE, FAKE, 8,

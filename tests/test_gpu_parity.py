@@ -435,3 +435,52 @@ def test_blocksparse_128k_chunked_sampled(lp):
         want = blocksparse_ref(Qc, K64[:T], V64[:T], rkp[:, :nbT], rvp[:, :nbT], ridx, rcnt, q0, B,
                                s.scale, rows=rows)
         assert_close(got[q0 + rows], want, f"sparse128k chunk {ci}")
+
+
+# ---------------------------------------------------------------- kept-by-rule selection
+@pytest.mark.parametrize("C,q_start,block,alpha,sink,window,tail", [
+    (512, 0, 128, 0.1, 256, 2, 0),         # the page's 256-token sinks
+    (300, 700, 64, 0.2, 100, 5, 2),        # a partial sink block, a dense tail of two query blocks
+    (256, 1024, 32, 1.0, 0, 3, 0),         # alpha 1: window and diagonal only
+    (200, 1000, 128, 0.05, 5000, 0, 1),    # sinks past the diagonal are clipped to it
+])
+def test_select_kept_by_rule_bit_exact(lp, C, q_start, block, alpha, sink, window, tail):
+    rng = np.random.default_rng(C + sink)
+    T = q_start + C
+    n_q, n_kv, d = 4, 2, 128
+    q, k = rand_bits(rng, C, n_q, d, s=2.0), rand_bits(rng, T, n_kv, d, s=2.0)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    say("select rules", C, q_start, block, alpha, sink, window, tail)
+    kp, _ = lp.build_pooled_index(dev_bf16(k), dev_bf16(k), block)
+    idx, cnt = lp.select_blocks(dev_bf16(q), kp, q_start, block, alpha, scale, sink_tokens=sink,
+                                window_blocks=window, dense_tail_blocks=tail)
+    import torch
+    torch.cuda.synchronize()
+    rkp, _ = pooled_index_ref(f64(k), f64(k), block)
+    ridx, rcnt = select_ref(f64(q), rkp, q_start, block, alpha, scale, sink_tokens=sink,
+                            window_blocks=window, dense_tail_blocks=tail)
+    assert np.array_equal(cnt.cpu().numpy(), rcnt)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+
+
+def test_blocksparse_with_kept_by_rule_selection(lp):
+    """Attention over a selection that includes sinks, a window and a dense tail."""
+    import torch
+    rng = np.random.default_rng(31)
+    N, q_start, n_q, n_kv, d, B = 2048, 1024, 4, 2, 128, 128
+    q = rand_bits(rng, N - q_start, n_q, d)
+    k, v = rand_bits(rng, N, n_kv, d), rand_bits(rng, N, n_kv, d)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    Qd, Kd, Vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    say("blocksparse rules")
+    kp, vp = lp.build_pooled_index(Kd, Vd, B)
+    idx, cnt = lp.select_blocks(Qd, kp, q_start, B, 0.2, scale, sink_tokens=256, window_blocks=2,
+                                dense_tail_blocks=1)
+    O = lp.prefill_attn_blocksparse(Qd, Kd, Vd, kp, vp, idx, cnt, q_start, B, scale)
+    torch.cuda.synchronize()
+    rkp, rvp = pooled_index_ref(f64(k), f64(v), B)
+    ridx, rcnt = select_ref(f64(q), rkp, q_start, B, 0.2, scale, sink_tokens=256, window_blocks=2,
+                            dense_tail_blocks=1)
+    assert np.array_equal(cnt.cpu().numpy(), rcnt) and np.array_equal(idx.cpu().numpy(), ridx)
+    want = blocksparse_ref(f64(q), f64(k), f64(v), rkp, rvp, ridx, rcnt, q_start, B, scale)
+    assert_close(O.cpu().numpy(), want, "blocksparse rules")

@@ -130,6 +130,32 @@ def test_selection_limits_and_monotonicity():
         assert votes[0, int(np.argmax(pooled_scores(Q[i:i + 1, 0], kp[0, :j])))]
 
 
+def test_kept_by_rule_closed_forms():
+    """With alpha = 1 no row votes, so the selection is exactly the rule sets plus
+    the diagonal (figure "Where the kept blocks are": sinks = the first 256
+    tokens, a local window next to the diagonal, the last tiles dense)."""
+    rng = np.random.default_rng(8)
+    B, d, C, q_start = 128, 16, 3 * 128, 9 * 128         # query blocks 9, 10, 11 over 12 key blocks
+    Q = _bf16(rng, C, 2, d)
+    kp = _bf16(rng, 1, 12, d).astype(np.float32)
+    sets = selection_sets(Q, kp, q_start, B, 1.0, 0.25, sink_tokens=256, window_blocks=3)
+    assert sets[(0, 9)] == [0, 1, 6, 7, 8, 9]
+    assert sets[(0, 10)] == [0, 1, 7, 8, 9, 10]
+    assert sets[(0, 11)] == [0, 1, 8, 9, 10, 11]
+    # a sink that is not a whole block keeps the block it starts; the window stops at 0
+    assert selection_sets(Q, kp, q_start, B, 1.0, 0.25, sink_tokens=1, window_blocks=20)[(0, 9)] == \
+        list(range(10))
+    # the last two query blocks of the call attend densely
+    tail = selection_sets(Q, kp, q_start, B, 1.0, 0.25, dense_tail_blocks=2)
+    assert tail[(0, 9)] == [9] and tail[(0, 10)] == list(range(11)) and tail[(0, 11)] == list(range(12))
+    # rules only add: every voted block stays kept
+    plain = selection_sets(Q, kp, q_start, B, 0.3, 0.25)
+    ruled = selection_sets(Q, kp, q_start, B, 0.3, 0.25, sink_tokens=300, window_blocks=2,
+                           dense_tail_blocks=1)
+    for key in plain:
+        assert set(plain[key]) <= set(ruled[key])
+
+
 def test_select_ref_arrays_layout():
     rng = np.random.default_rng(4)
     B, d, Hq, Hkv, C, q_start = 8, 8, 2, 1, 30, 13
