@@ -42,7 +42,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="prefill32k", choices=["prefill32k", "dense128k", "sparse128k"])
+    ap.add_argument("--workload", default="prefill32k",
+                    choices=["prefill32k", "dense128k", "sparse128k", "fold2k5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -128,6 +129,12 @@ def main():
         w = make_workload("sparse128k")
         chunks = w.spec.chunks
         do_sparse = "blocksparse" in args.parts.split(",")
+    elif args.workload == "fold2k5":
+        # the ~2,500-token narrow-chunk prompt; each step folds the indexer's keep
+        # lists into the chunk masks on the device, then runs dense attention
+        w = make_workload("fold2k5")
+        chunks = w.spec.chunks
+        do_sparse = False
     else:
         w = make_workload("dense128k")
         chunks = w.spec.chunks
@@ -138,6 +145,7 @@ def main():
 
     Q, K, V = up_bf16(w.Q), up_bf16(w.K), up_bf16(w.V)
     masks = [torch.from_numpy(causal_mask(q0, C)).to(dev) for q0, C in chunks]
+    keeps = [fold_lists(w, q0, C, dev) for q0, C in chunks] if args.workload == "fold2k5" else []
     O_dense = torch.empty((N, Hq, d), dtype=torch.float32, device=dev)
     ws_bytes = max(lp.prefill_attn_dense_workspace(C, q0 + C, Hq, Hkv, d) for q0, C in chunks)
     ws = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
@@ -163,8 +171,10 @@ def main():
     def run_dense():
         if not run_dense_part:
             return
-        for (q0, C), m in zip(chunks, masks):
+        for ci, ((q0, C), m) in enumerate(zip(chunks, masks)):
             T = q0 + C
+            if keeps:
+                lp.fold_keep_mask(keeps[ci][0], keeps[ci][1], q0, T, s.fold_width, s.fold_recent, mask=m)
             lp.prefill_attn_dense(Q[q0:T], K[:T], V[:T], m, scale, O=O_dense[q0:T], workspace=ws)
 
     def run_sparse():
@@ -211,7 +221,7 @@ def main():
     dense_ms = float(np.median([a.elapsed_time(b) for a, b, _ in part_ev]))
     sparse_ms = float(np.median([b.elapsed_time(c) for _, b, c in part_ev])) if do_sparse else 0.0
     kern = {}
-    for name in ("attn_dense", "mask_classify", "attn_combine", "attn_blocksparse", "pool", "select"):
+    for name in ("attn_dense", "mask_classify", "attn_combine", "attn_blocksparse", "pool", "select", "fold"):
         tot, n = lp.timing.read(name)
         if n:
             kern[name] = {"avg_ms": tot / n, "launches_per_step": n // args.steps, "ms_per_step": tot / args.steps}
@@ -239,6 +249,11 @@ def main():
                           "tflops": round(flops_dense / (dense_ms * 1e-3) / 1e12, 2),
                           "pct_peak": round(100 * flops_dense / (dense_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
                           "tokens_per_s": round(N / (dense_ms * 1e-3))}
+    if keeps:
+        fold_bytes = sum(2 * C * (q0 + C) + 4 * keeps[i][0].numel() for i, (q0, C) in enumerate(chunks))
+        fold_ms = kern["fold"]["ms_per_step"]
+        parts["fold"] = {"ms": round(fold_ms, 4), "GB_per_s": round(fold_bytes / (fold_ms * 1e-3) / 1e9, 1),
+                         "bytes_per_step": fold_bytes, "hbm_peak_GB_per_s": 8000}
     if do_sparse:
         parts["blocksparse"] = {"ms": round(sparse_ms, 3),
                                 "tflops_dense_equiv": round(flops_sparse / (sparse_ms * 1e-3) / 1e12, 2),
@@ -263,13 +278,30 @@ def main():
                    "step": ("dense chunked + chunked block-sparse (incremental pooled index) prefill of "
                             "the same prompt" if chunked_sparse else
                             "dense chunked + block-sparse prefill of the same prompt") if do_sparse
-                   else "dense chunked prefill", "parallelism": "none (1 GPU)"},
+                   else ("indexer keep lists folded into the masks on the device + dense chunked prefill"
+                         if keeps else "dense chunked prefill"), "parallelism": "none (1 GPU)"},
         "tokens_per_s": round((2 if do_sparse else 1) * N / (ms_step * 1e-3)),
         "pct_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "parts": parts, "kernels": kern, "roofline": roofline, "cpu_baseline": cpu,
         "device": {"name": props.name, "cus": props.multi_processor_count},
     }
     print(json.dumps(line), flush=True)
+
+
+def fold_lists(w, q0, C, dev):
+    """Compacted keep lists (blocks of fold_width keys) of the chunk's rows, as a
+    sparse indexer would return them: every block up to the row while the row
+    sees at most the budget, else the drawn blocks (the recent keys are added by
+    the fold itself)."""
+    import torch
+    s = w.spec
+    rows = [list(range(p // s.fold_width + 1)) if p + 1 <= s.fold_budget
+            else [int(c) for c in w.keep_blocks[p]] for p in range(q0, q0 + C)]
+    idx = np.zeros((C, max(len(r) for r in rows)), dtype=np.int32)
+    for i, r in enumerate(rows):
+        idx[i, :len(r)] = r
+    cnt = np.array([len(r) for r in rows], dtype=np.int32)
+    return torch.from_numpy(idx).to(dev), torch.from_numpy(cnt).to(dev)
 
 
 def cpu_baseline(w, chunks, budget_s):

@@ -158,6 +158,27 @@ int prefill_attn_blocksparse(const uint16_t* Q, int C, int q_start, int n_q,
                              float scale, float* O, void* stream);
 
 /*
+ * fold_keep_mask -- a sparse indexer's compacted selection folded into the
+ * additive mask that prefill_attn_dense consumes. ("ANE Prefill Research",
+ * What worked, item 2: the runtime folds keepIndices / keepCounts into the mask
+ * as -30000, which contributes exactly nothing.)
+ *
+ *   keep_idx  int32 [C][keep_ld]  per row, the kept blocks of `width` keys (block c = keys
+ *                                 c*width .. c*width+width-1); may be NULL when keep_ld == 0
+ *   keep_cnt  int32 [C]           entries used in each row (clamped to 0 .. keep_ld)
+ *   mask      fp16 [C][mask_ld]   output; columns 0..T-1 written, the rest untouched
+ *
+ * Row i sits at position p = q_start + i. mask[i][t] = 0 when t <= p and t lies in
+ * a listed block or among the `recent` keys ending at p; otherwise -30000.
+ * Listed blocks outside [0, ceil(T/width)) are ignored.
+ * Requires C >= 1, q_start >= 0, q_start + C <= T <= mask_ld, width >= 1, recent >= 0.
+ * Errors: PA_EINVAL, PA_EHIP.
+ */
+int fold_keep_mask(const int32_t* keep_idx, int64_t keep_ld, const int32_t* keep_cnt, int C,
+                   int q_start, int T, int width, int recent, uint16_t* mask, int64_t mask_ld,
+                   void* stream);
+
+/*
  * Chunked block-sparse prefill over a growing history: the same three steps
  * with a pooled index that is built incrementally and kept between chunks.
  * ("Porting FlashPrefill V2 to Apple silicon", Part I: the pooled index
@@ -210,7 +231,7 @@ int prefill_attn_blocksparse_ld(const uint16_t* Q, int C, int q_start, int n_q,
  * When enabled, each launch of the named kernels is bracketed by HIP events
  * recorded on the launch stream. pa_timing_read synchronises those events and
  * returns the summed milliseconds and launch count for `kernel`, one of
- * "attn_dense", "attn_blocksparse", "mask_classify", "attn_combine", "pool", "select".
+ * "attn_dense", "attn_blocksparse", "mask_classify", "attn_combine", "pool", "select", "fold".
  * pa_timing_reset clears the totals. Returns PA_OK or PA_EINVAL/PA_EHIP.
  */
 int pa_timing_enable(int on);

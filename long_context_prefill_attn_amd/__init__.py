@@ -6,6 +6,7 @@ torch's current stream. Outputs are allocated with torch when not supplied.
 The calls are asynchronous, like the kernels they enqueue.
 
     prefill_attn_dense(Q, K, V, mask, scale)                  -> O
+    fold_keep_mask(keep_idx, keep_cnt, q_start, T, width, recent) -> fp16 mask
     build_pooled_index(K, V, block[, K_pool, V_pool, b_first]) -> (K_pool, V_pool)
     select_blocks(Q, K_pool, q_start, block, alpha, scale)     -> (sel_idx, sel_cnt)
     prefill_attn_blocksparse(Q, K, V, K_pool, V_pool, sel_idx, sel_cnt, q_start, block, scale) -> O
@@ -21,7 +22,7 @@ import torch
 from ._lib import PrefillAttnError, check, lib  # noqa: F401
 
 __all__ = ["prefill_attn_dense", "prefill_attn_dense_workspace", "build_pooled_index",
-           "select_blocks", "prefill_attn_blocksparse", "PrefillAttnError", "timing"]
+           "select_blocks", "prefill_attn_blocksparse", "fold_keep_mask", "PrefillAttnError", "timing"]
 
 
 def _stream() -> int:
@@ -66,6 +67,26 @@ def prefill_attn_dense(Q, K, V, mask, scale: float, O=None, workspace=None):
                                    workspace.data_ptr(), workspace.numel(), _stream()),
           "prefill_attn_dense")
     return O
+
+
+def fold_keep_mask(keep_idx, keep_cnt, q_start: int, T: int, width: int, recent: int, mask=None):
+    """Fold an indexer's compacted selection into an fp16 mask [C][ld >= T].
+
+    keep_idx int32 [C][K] (kept blocks of `width` keys per row), keep_cnt int32 [C]."""
+    _req(keep_idx, "keep_idx", torch.int32, 2)
+    _req(keep_cnt, "keep_cnt", torch.int32, 1)
+    C, K = keep_idx.shape
+    if keep_cnt.shape[0] != C:
+        raise ValueError("keep_cnt must have one entry per row")
+    if mask is None:
+        mask = torch.empty((C, T), dtype=torch.float16, device=keep_idx.device)
+    _req(mask, "mask", torch.float16, 2)
+    if mask.shape[0] != C or mask.shape[1] < T:
+        raise ValueError(f"mask must be [{C}][>= {T}]")
+    check(lib().fold_keep_mask(keep_idx.data_ptr() if K else None, K, keep_cnt.data_ptr(), C, q_start,
+                               T, width, recent, mask.data_ptr(), mask.stride(0), _stream()),
+          "fold_keep_mask")
+    return mask
 
 
 def _pooled(P, name, n_kv, nb, d, device):

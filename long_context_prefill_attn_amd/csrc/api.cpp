@@ -40,7 +40,7 @@ struct TimedKernel {
 std::mutex g_timing_mu;
 bool g_timing_on = false;
 TimedKernel g_timed[] = {{"attn_dense"}, {"attn_blocksparse"}, {"mask_classify"},
-                         {"attn_combine"}, {"pool"}, {"select"}};
+                         {"attn_combine"}, {"pool"}, {"select"}, {"fold"}};
 std::vector<hipEvent_t> g_event_pool;
 
 hipEvent_t take_event() {
@@ -145,6 +145,21 @@ int prefill_attn_dense(const uint16_t* Q, int C, int n_q, const uint16_t* K, con
     if (e != hipSuccess) return hip_status(e);
   }
   return PA_OK;
+}
+
+int fold_keep_mask(const int32_t* keep_idx, int64_t keep_ld, const int32_t* keep_cnt, int C,
+                   int q_start, int T, int width, int recent, uint16_t* mask, int64_t mask_ld,
+                   void* stream) {
+  if (!aligned16(keep_cnt) || !aligned16(mask) || (keep_ld > 0 && !aligned16(keep_idx)))
+    return PA_EINVAL;
+  if (C < 1 || q_start < 0 || (long long)q_start + C > T || width < 1 || recent < 0 || keep_ld < 0)
+    return PA_EINVAL;
+  if (mask_ld < T) return PA_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(timed("fold", s, [&] {
+    return pa::launch_fold_keep(keep_idx, keep_ld, keep_cnt, C, q_start, T, width, recent, mask,
+                                mask_ld, s);
+  }));
 }
 
 int build_pooled_index_ld(const uint16_t* K, const uint16_t* V, int T, int n_kv, int d, int block,

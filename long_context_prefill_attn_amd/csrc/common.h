@@ -64,6 +64,10 @@ hipError_t launch_select(const uint16_t* Q, int C, int q_start, int n_q, int n_k
 hipError_t launch_mask_classify(const uint16_t* mask, int64_t mask_ld, int C, int T,
                                 uint8_t* flags, hipStream_t stream);
 
+hipError_t launch_fold_keep(const int32_t* keep_idx, int64_t keep_ld, const int32_t* keep_cnt, int C,
+                            int q_start, int T, int width, int recent, uint16_t* mask, int64_t mask_ld,
+                            hipStream_t stream);
+
 struct DensePlan {
   int hg_log2;   // log2 of the query heads packed into one workgroup
   int n_qt;      // query tiles of 256 >> hg_log2 rows

@@ -50,6 +50,64 @@ __global__ void __launch_bounds__(256) mask_classify_kernel(const uint16_t* __re
     flags[(size_t)qt * gridDim.x + kt] = dr ? TILE_DROPPED : (z ? TILE_ZERO : TILE_MIXED);
 }
 
+// ---------------------------------------------------------------------------
+// fold_keep_mask: an indexer's compacted selection into the additive mask
+// ("ANE Prefill Research", What worked, item 2). One workgroup per query row:
+// the row's columns 0..T-1 are first set to -30000 (16-byte stores where the
+// row is aligned), then, after a barrier, the kept keys are zeroed: every key of
+// each listed `width`-key block and the `recent` keys ending at the row's own
+// position p, both clipped to t <= p. Listed blocks outside [0, ceil(T/width))
+// are ignored; at most keep_ld entries of a row are read.
+// grid = C, block = 256.
+// ---------------------------------------------------------------------------
+constexpr uint16_t F16_M30000 = 0xF753;   // -30000 in fp16
+
+template <bool VEC>
+__global__ void __launch_bounds__(256) fold_keep_kernel(const int32_t* __restrict__ keep_idx,
+                                                        int64_t keep_ld,
+                                                        const int32_t* __restrict__ keep_cnt,
+                                                        int q_start, int T, int width, int recent,
+                                                        uint16_t* __restrict__ mask, int64_t mask_ld) {
+  const int i = blockIdx.x;
+  const int tid = threadIdx.x;
+  uint16_t* row = mask + (size_t)i * mask_ld;
+  if (VEC) {
+    const uint32_t d2 = (uint32_t)F16_M30000 | ((uint32_t)F16_M30000 << 16);
+    const u32x4 v = {d2, d2, d2, d2};
+    const int n8 = T / 8;
+    for (int c = tid; c < n8; c += 256) *reinterpret_cast<u32x4*>(row + 8 * c) = v;
+    for (int t = 8 * n8 + tid; t < T; t += 256) row[t] = F16_M30000;
+  } else {
+    for (int t = tid; t < T; t += 256) row[t] = F16_M30000;
+  }
+  __syncthreads();
+  const int p = q_start + i;
+  const int last = min(p, T - 1);            // no key past the row's own position
+  const int nblk = (T + width - 1) / width;
+  const int cnt = (int)min((int64_t)max(keep_cnt[i], 0), keep_ld);
+  const int32_t* ki = keep_idx + (size_t)i * keep_ld;
+  for (int e = tid; e < cnt; e += 256) {
+    const int c = ki[e];
+    if (c < 0 || c >= nblk) continue;
+    const int t1 = min(c * width + width - 1, last);
+    for (int t = c * width; t <= t1; ++t) row[t] = 0;
+  }
+  for (int t = max(0, p - recent + 1) + tid; t <= last; t += 256) row[t] = 0;
+}
+
+hipError_t launch_fold_keep(const int32_t* keep_idx, int64_t keep_ld, const int32_t* keep_cnt, int C,
+                            int q_start, int T, int width, int recent, uint16_t* mask, int64_t mask_ld,
+                            hipStream_t stream) {
+  const bool vec = (mask_ld % 8) == 0 && (reinterpret_cast<uintptr_t>(mask) % 16) == 0;
+  if (vec)
+    hipLaunchKernelGGL(fold_keep_kernel<true>, dim3(C), dim3(256), 0, stream, keep_idx, keep_ld,
+                       keep_cnt, q_start, T, width, recent, mask, mask_ld);
+  else
+    hipLaunchKernelGGL(fold_keep_kernel<false>, dim3(C), dim3(256), 0, stream, keep_idx, keep_ld,
+                       keep_cnt, q_start, T, width, recent, mask, mask_ld);
+  return hipGetLastError();
+}
+
 hipError_t launch_mask_classify(const uint16_t* mask, int64_t mask_ld, int C, int T,
                                 uint8_t* flags, hipStream_t stream) {
   dim3 grid((T + FLAG_TILE - 1) / FLAG_TILE, (C + FLAG_TILE - 1) / FLAG_TILE);

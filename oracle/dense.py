@@ -91,3 +91,27 @@ def dense_ref(Q, K, V, mask, scale, rows=None, heads=None, slab: int = 256) -> n
             w = attention_weights(Q[r, h, :], kg, mask[r, :T], scale)
             out[s0:s0 + slab, hi, :] = w @ vg
     return out
+
+
+def fold_mask_ref(keep_idx, keep_cnt, q_start: int, T: int, width: int, recent: int) -> np.ndarray:
+    """The additive fp16 mask [C][T] of an indexer's compacted selection.
+
+    "ANE Prefill Research", What worked, item 2: the kept keys (keepIndices /
+    keepCounts) stay visible and every other key is folded in as -30000.  Row i
+    (position p = q_start + i) keeps each key of the listed blocks of `width`
+    keys and the `recent` keys ending at p, never a key past p.  Listed blocks
+    outside [0, ceil(T/width)) are ignored; at most keep_idx.shape[1] entries of
+    a row are read.
+    """
+    keep_idx = np.asarray(keep_idx)
+    C, K = keep_idx.shape if keep_idx.ndim == 2 else (len(keep_cnt), 0)
+    nblk = -(-T // width)
+    m = np.full((C, T), np.float16(DROP_AT), dtype=np.float16)
+    for i in range(C):
+        p = q_start + i
+        for e in range(min(max(int(keep_cnt[i]), 0), K)):
+            c = int(keep_idx[i, e])
+            if 0 <= c < nblk:
+                m[i, c * width:min(c * width + width, p + 1, T)] = 0
+        m[i, max(0, p - recent + 1):min(p + 1, T)] = 0
+    return m

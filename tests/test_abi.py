@@ -127,6 +127,21 @@ def test_ld_forms_reject():
                                            64, FAKE, FAKE, 0.1, FAKE, None) == _lib.PA_EUNSUPPORTED
 
 
+def test_fold_rejects():
+    lib = _lib.lib()
+    f = lambda **kw: lib.fold_keep_mask(kw.get("idx", FAKE), kw.get("K", 8), kw.get("cnt", FAKE),
+                                        kw.get("C", 16), kw.get("q0", 100), kw.get("T", 116),
+                                        kw.get("width", 4), kw.get("recent", 3), kw.get("mask", FAKE),
+                                        kw.get("ld", 116), None)
+    assert f(T=115) == _lib.PA_EINVAL          # rows past the mask's columns
+    assert f(width=0) == _lib.PA_EINVAL
+    assert f(recent=-1) == _lib.PA_EINVAL
+    assert f(ld=100) == _lib.PA_EINVAL
+    assert f(K=-1) == _lib.PA_EINVAL
+    assert f(cnt=None) == _lib.PA_EINVAL
+    assert f(mask=FAKE + 4) == _lib.PA_EINVAL   # misaligned
+
+
 def test_timing_api_host_side():
     lib = _lib.lib()
     ms, n = ctypes.c_double(), ctypes.c_int64()

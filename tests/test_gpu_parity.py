@@ -11,7 +11,7 @@ import sys
 import numpy as np
 import pytest
 
-from oracle import blocksparse_ref, dense_ref, pooled_index_ref, select_ref, selection_sets
+from oracle import blocksparse_ref, dense_ref, fold_mask_ref, pooled_index_ref, select_ref, selection_sets
 from workloads import CONFIGS, bf16_bits, causal_mask, make_workload
 from _util import assert_close, dev_bf16, dev_f16, f64
 
@@ -484,3 +484,63 @@ def test_blocksparse_with_kept_by_rule_selection(lp):
     assert np.array_equal(cnt.cpu().numpy(), rcnt) and np.array_equal(idx.cpu().numpy(), ridx)
     want = blocksparse_ref(f64(q), f64(k), f64(v), rkp, rvp, ridx, rcnt, q_start, B, scale)
     assert_close(O.cpu().numpy(), want, "blocksparse rules")
+
+
+# ---------------------------------------------------------------- folded selection
+def _keep_lists(w, q_start, C):
+    s = w.spec
+    rows = [list(range(p // s.fold_width + 1)) if p + 1 <= s.fold_budget
+            else [int(c) for c in w.keep_blocks[p]] for p in range(q_start, q_start + C)]
+    idx = np.zeros((C, max(len(r) for r in rows)), dtype=np.int32)
+    for i, r in enumerate(rows):
+        idx[i, :len(r)] = r
+    return idx, np.array([len(r) for r in rows], dtype=np.int32)
+
+
+@pytest.mark.parametrize("pad", [0, 3])     # pad 3: rows not 16-byte aligned, scalar stores
+def test_fold_keep_mask_bit_exact(lp, pad):
+    """The folded fp16 mask equals the oracle's bit for bit on the fold2k5 chunks,
+    and dense attention over it equals attention over the host-built mask."""
+    import torch
+    w = make_workload("fold2k5")
+    s = w.spec
+    for q_start, C in s.chunks:
+        T = q_start + C
+        idx, cnt = _keep_lists(w, q_start, C)
+        say("fold", q_start, C, pad)
+        buf = torch.full((C, T + pad), 7.0, dtype=torch.float16, device="cuda")
+        m = lp.fold_keep_mask(torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda(), q_start, T,
+                              s.fold_width, s.fold_recent, mask=buf)
+        torch.cuda.synchronize()
+        want = fold_mask_ref(idx, cnt, q_start, T, s.fold_width, s.fold_recent)
+        got = m.cpu().numpy()
+        assert np.array_equal(got[:, :T].view(np.uint16), want.view(np.uint16)), q_start
+        assert np.all(got[:, T:] == 7.0)                     # columns past T untouched
+    # attention over the device-built mask: identical to the host-built one
+    q0, C = s.chunks[-1]
+    T = q0 + C
+    q, k, v = w.Q[q0:T], w.K[:T], w.V[:T]
+    a = gpu_dense(lp, q, k, v, w.mask(q0, C), s.scale)
+    idx, cnt = _keep_lists(w, q0, C)
+    m = lp.fold_keep_mask(torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda(), q0, T,
+                          s.fold_width, s.fold_recent)
+    b = lp.prefill_attn_dense(dev_bf16(q), dev_bf16(k), dev_bf16(v), m, s.scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(a.view(np.uint32), b.cpu().numpy().view(np.uint32))
+
+
+def test_fold_keep_mask_malformed_lists(lp):
+    """Out-of-range and duplicate block ids, counts past the list width or
+    negative, blocks reaching past the row's position."""
+    import torch
+    rng = np.random.default_rng(41)
+    C, q_start, T, width, recent, K = 300, 500, 900, 8, 5, 40
+    idx = rng.integers(-5, T // width + 10, size=(C, K)).astype(np.int32)
+    idx[:, 5] = idx[:, 4]                                    # duplicates
+    cnt = rng.integers(-3, K + 20, size=C).astype(np.int32)
+    say("fold malformed")
+    m = lp.fold_keep_mask(torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda(), q_start, T,
+                          width, recent)
+    torch.cuda.synchronize()
+    want = fold_mask_ref(idx, cnt, q_start, T, width, recent)
+    assert np.array_equal(m.cpu().numpy().view(np.uint16), want.view(np.uint16))

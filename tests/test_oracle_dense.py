@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attention_weights, dense_ref
+from oracle import attention_weights, dense_ref, fold_mask_ref
 from workloads import CONFIGS, bf16_to_f32, causal_mask, dense_equiv_pairs, make_workload
 
 DROP = -30000.0
@@ -235,3 +235,49 @@ def test_dense_equiv_pair_counts():
     assert sum(dense_equiv_pairs(s, c) for s, c in CONFIGS["fold2k5"].chunks) == 3126250
     assert sum(dense_equiv_pairs(s, c) for s, c in CONFIGS["sparse32k"].chunks) == 536887296
     assert sum(dense_equiv_pairs(s, c) for s, c in CONFIGS["dense128k"].chunks) == 8590000128
+
+
+# ---------------------------------------------------------------- folded selection
+def _fold_lists(w, q_start, C):
+    """Keep lists (blocks of 4 keys) reproducing the fold generator's selection."""
+    s = w.spec
+    rows = []
+    for i in range(C):
+        p = q_start + i
+        rows.append(list(range(p // s.fold_width + 1)) if p + 1 <= s.fold_budget
+                    else [int(c) for c in w.keep_blocks[p]])
+    K = max(len(r) for r in rows)
+    idx = np.zeros((C, K), dtype=np.int32)
+    cnt = np.array([len(r) for r in rows], dtype=np.int32)
+    for i, r in enumerate(rows):
+        idx[i, :len(r)] = r
+    return idx, cnt
+
+
+def test_fold_mask_equals_generator_mask():
+    """Two independent constructions of the folded mask agree bit for bit: the
+    generator's per-row column list and the fold of the compacted keep lists."""
+    w = make_workload("fold2k5")
+    s = w.spec
+    for q_start, C in s.chunks:
+        idx, cnt = _fold_lists(w, q_start, C)
+        got = fold_mask_ref(idx, cnt, q_start, q_start + C, s.fold_width, s.fold_recent)
+        assert np.array_equal(got.view(np.uint16), w.mask(q_start, C).view(np.uint16)), q_start
+
+
+def test_fold_mask_closed_forms():
+    # 2 rows at positions 9, 10 over T = 12 keys, blocks of 4, 2 recent keys
+    idx = np.array([[0, 2, -1, 7, 0], [1, 2, 9, 9, 9]], dtype=np.int32)
+    cnt = np.array([4, 2], dtype=np.int32)     # row 0 reads 4 entries, row 1 two
+    m = fold_mask_ref(idx, cnt, 9, 12, 4, 2)
+    keep0 = {0, 1, 2, 3, 8, 9}                  # block 0; block 2 clipped at p = 9; -1 and 7 ignored
+    keep1 = {4, 5, 6, 7, 8, 9, 10}              # blocks 1 and 2 (clipped at 10); recent 9, 10
+    for i, keep in ((0, keep0), (1, keep1)):
+        want = np.array([0.0 if t in keep else -30000.0 for t in range(12)], dtype=np.float16)
+        assert np.array_equal(m[i], want), i
+    # a full-budget row: 512 blocks below the 3 recent keys plus those keys = 2,051 visible
+    rng = np.random.default_rng(3)
+    p = 5000
+    blocks = np.sort(rng.choice((p - 2) // 4, size=512, replace=False)).astype(np.int32)
+    m = fold_mask_ref(blocks[None, :], np.array([512], np.int32), p, p + 1, 4, 3)
+    assert int((m[0] == 0).sum()) == 2051
