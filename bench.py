@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--workload", default="prefill32k",
                     choices=["prefill32k", "dense128k", "sparse128k", "fold2k5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--dense-entry", default="mask", choices=["mask", "causal"],
+                    help="dense part: prefill_attn_dense over a causal fp16 mask (default) or "
+                         "prefill_attn_dense_causal (no mask buffer)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 512 MiB device copy (reference for HBM byte counters)")
@@ -175,7 +178,10 @@ def main():
             T = q0 + C
             if keeps:
                 lp.fold_keep_mask(keeps[ci][0], keeps[ci][1], q0, T, s.fold_width, s.fold_recent, mask=m)
-            lp.prefill_attn_dense(Q[q0:T], K[:T], V[:T], m, scale, O=O_dense[q0:T], workspace=ws)
+            if args.dense_entry == "causal" and not keeps:
+                lp.prefill_attn_dense_causal(Q[q0:T], K[:T], V[:T], q0, scale, O=O_dense[q0:T], workspace=ws)
+            else:
+                lp.prefill_attn_dense(Q[q0:T], K[:T], V[:T], m, scale, O=O_dense[q0:T], workspace=ws)
 
     def run_sparse():
         # one pooled index for the whole prompt, pooled incrementally chunk by chunk
@@ -272,7 +278,8 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded; planted block structure)" if do_sparse else "synthetic (seeded N(0,1))",
-        "config": {"workload": args.workload, "tokens": N, "n_q": Hq, "n_kv": Hkv, "head_dim": d,
+        "config": {"workload": args.workload, "dense_entry": args.dense_entry, "tokens": N, "n_q": Hq,
+                   "n_kv": Hkv, "head_dim": d,
                    "chunk": 4096, "block": B if do_sparse else None,
                    "alpha": s.alpha if do_sparse else None,
                    "step": ("dense chunked + chunked block-sparse (incremental pooled index) prefill of "

@@ -3,6 +3,7 @@
  *
  * Four operations make up the path:
  *   prefill_attn_dense        chunked prefill attention under an arbitrary additive mask
+ *                             (prefill_attn_dense_causal: causal by position, no mask buffer)
  *   build_pooled_index        mean-pooled key/value blocks
  *   select_blocks             alpha-threshold block selection plus the local diagonal
  *   prefill_attn_blocksparse  exact attention on selected blocks + pooled correction
@@ -94,6 +95,29 @@ int prefill_attn_dense(const uint16_t* Q, int C, int n_q,
 
 /* Workspace bytes prefill_attn_dense needs for these sizes (0 for invalid sizes). */
 size_t prefill_attn_dense_workspace(int C, int T, int n_q, int n_kv, int d);
+
+/*
+ * prefill_attn_dense_causal -- prefill_attn_dense for a causal chunk without a
+ * [C][T] mask buffer, optionally with a per-key mask broadcast over the rows.
+ * ("The Four Principles for Optimizing Transformers on the ANE", Principle 3:
+ * additive pre-softmax masks, a per-(query, key) mask and a per-key padding
+ * mask composed by addition.)
+ *
+ *   rows are at positions q_start .. q_start+C-1; row i sees key t iff t <= q_start + i
+ *   kmask    fp16 [T] or NULL    per-key additive mask (e.g. padding), shared by every row;
+ *                                an entry <= -30000 (or -inf) omits the key
+ *
+ * Equals prefill_attn_dense with mask[i][t] = (t > q_start+i or kmask[t] <= -30000)
+ * ? -30000 : kmask[t] (0 without kmask). The causal tile structure is computed,
+ * not read, so no C x T mask is stored or scanned.
+ * Requires q_start >= 0 and q_start + C <= T; other requirements and the
+ * workspace (prefill_attn_dense_workspace) as prefill_attn_dense.
+ * Errors: PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP.
+ */
+int prefill_attn_dense_causal(const uint16_t* Q, int C, int q_start, int n_q,
+                              const uint16_t* K, const uint16_t* V, int T, int n_kv, int d,
+                              const uint16_t* kmask, float scale, float* O,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * build_pooled_index -- mean of each block of `block` consecutive keys (and values).

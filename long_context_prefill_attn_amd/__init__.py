@@ -6,6 +6,7 @@ torch's current stream. Outputs are allocated with torch when not supplied.
 The calls are asynchronous, like the kernels they enqueue.
 
     prefill_attn_dense(Q, K, V, mask, scale)                  -> O
+    prefill_attn_dense_causal(Q, K, V, q_start, scale[, kmask]) -> O
     fold_keep_mask(keep_idx, keep_cnt, q_start, T, width, recent) -> fp16 mask
     build_pooled_index(K, V, block[, K_pool, V_pool, b_first]) -> (K_pool, V_pool)
     select_blocks(Q, K_pool, q_start, block, alpha, scale)     -> (sel_idx, sel_cnt)
@@ -21,7 +22,8 @@ import torch
 
 from ._lib import PrefillAttnError, check, lib  # noqa: F401
 
-__all__ = ["prefill_attn_dense", "prefill_attn_dense_workspace", "build_pooled_index",
+__all__ = ["prefill_attn_dense", "prefill_attn_dense_causal", "prefill_attn_dense_workspace",
+           "build_pooled_index",
            "select_blocks", "prefill_attn_blocksparse", "fold_keep_mask", "PrefillAttnError", "timing"]
 
 
@@ -66,6 +68,36 @@ def prefill_attn_dense(Q, K, V, mask, scale: float, O=None, workspace=None):
                                    mask.data_ptr(), mask.stride(0), float(scale), O.data_ptr(),
                                    workspace.data_ptr(), workspace.numel(), _stream()),
           "prefill_attn_dense")
+    return O
+
+
+def prefill_attn_dense_causal(Q, K, V, q_start: int, scale: float, kmask=None, O=None, workspace=None):
+    """Causal chunk at positions q_start..q_start+C-1 without a mask buffer.
+
+    Q bf16 [C][n_q][d]; K, V bf16 [T][n_kv][d]; kmask optional fp16 [T] (per-key,
+    shared by all rows) -> O fp32 [C][n_q][d]."""
+    _req(Q, "Q", torch.bfloat16, 3)
+    _req(K, "K", torch.bfloat16, 3)
+    _req(V, "V", torch.bfloat16, 3)
+    C, n_q, d = Q.shape
+    T, n_kv, _ = K.shape
+    if V.shape != K.shape or K.shape[2] != d:
+        raise ValueError("inconsistent shapes")
+    if kmask is not None:
+        _req(kmask, "kmask", torch.float16, 1)
+        if kmask.shape[0] != T:
+            raise ValueError(f"kmask must have T = {T} entries")
+    if O is None:
+        O = torch.empty((C, n_q, d), dtype=torch.float32, device=Q.device)
+    _req(O, "O", torch.float32, 3)
+    need = prefill_attn_dense_workspace(C, T, n_q, n_kv, d)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=Q.device)
+    check(lib().prefill_attn_dense_causal(Q.data_ptr(), C, q_start, n_q, K.data_ptr(), V.data_ptr(), T,
+                                          n_kv, d, kmask.data_ptr() if kmask is not None else None,
+                                          float(scale), O.data_ptr(), workspace.data_ptr(),
+                                          workspace.numel(), _stream()),
+          "prefill_attn_dense_causal")
     return O
 
 

@@ -135,7 +135,49 @@ int prefill_attn_dense(const uint16_t* Q, int C, int n_q, const uint16_t* K, con
   if (e != hipSuccess) return hip_status(e);
   e = timed("attn_dense", s, [&] {
     return pa::launch_attn_dense(Q, C, n_q, K, V, T, n_kv, d, mask, mask_ld, scale, O, plan, flags,
-                                 part_o, part_ml, s);
+                                 part_o, part_ml, -1, s);
+  });
+  if (e != hipSuccess) return hip_status(e);
+  if (plan.splits > 1) {
+    e = timed("attn_combine", s, [&] {
+      return pa::launch_attn_combine(C, n_q, d, plan.splits, part_o, part_ml, O, s);
+    });
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return PA_OK;
+}
+
+int prefill_attn_dense_causal(const uint16_t* Q, int C, int q_start, int n_q, const uint16_t* K,
+                              const uint16_t* V, int T, int n_kv, int d, const uint16_t* kmask,
+                              float scale, float* O, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return PA_EINVAL;
+  if (kmask != nullptr && !aligned16(kmask)) return PA_EINVAL;
+  if (C < 1 || q_start < 0 || n_q < 1 || n_kv < 1 || n_q % n_kv != 0) return PA_EINVAL;
+  if ((long long)q_start + C > T || !good_scale(scale)) return PA_EINVAL;
+  if (d != 64 && d != 128) return PA_EUNSUPPORTED;
+  if (T > (1 << 22)) return PA_EUNSUPPORTED;
+  if ((long long)T * n_kv * d * 2 >= (1LL << 31)) return PA_EUNSUPPORTED;   // 32-bit tile offsets
+  const pa::DensePlan plan = pa::plan_dense(C, T, n_q, n_kv, d);
+  if ((long long)plan.n_qt * n_q * plan.splits >= (1LL << 31)) return PA_EUNSUPPORTED;
+  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
+      workspace_bytes < plan.total_bytes)
+    return PA_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* flags = static_cast<uint8_t*>(workspace);
+  float* part_o = plan.splits > 1 ? reinterpret_cast<float*>(flags + plan.flags_bytes) : nullptr;
+  float* part_ml =
+      plan.splits > 1 ? reinterpret_cast<float*>(flags + plan.flags_bytes + plan.part_o_bytes) : nullptr;
+  hipError_t e = hipSuccess;
+  if (kmask != nullptr) {   // one-row classification of the per-key mask's 128-key tiles
+    e = timed("mask_classify", s, [&] {
+      return pa::launch_mask_classify(kmask, ((int64_t)T + 7) / 8 * 8, 1, T, flags, s);
+    });
+    if (e != hipSuccess) return hip_status(e);
+  }
+  e = timed("attn_dense", s, [&] {
+    return pa::launch_attn_dense(Q, C, n_q, K, V, T, n_kv, d, kmask, T, scale, O, plan,
+                                 kmask != nullptr ? flags : nullptr, part_o, part_ml, q_start, s);
   });
   if (e != hipSuccess) return hip_status(e);
   if (plan.splits > 1) {

@@ -47,7 +47,7 @@ constexpr float SLACK = 8.0f;   // lazy-rescale threshold in log2 units
 #define LDS_AS __attribute__((address_space(3)))
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
-enum { MODE_PLAIN = 0, MODE_GMASK = 1, MODE_CAUSAL = 2, MODE_POOLED = 3 };
+enum { MODE_PLAIN = 0, MODE_GMASK = 1, MODE_CAUSAL = 2, MODE_POOLED = 3, MODE_CAUSAL_K = 4 };
 
 // LDS tiles are row-major [64 keys][D] bf16 with no padding; the 16-byte chunk c
 // of row r sits at chunk position c ^ swz(r). The swizzle spreads the 8 rows a
@@ -242,6 +242,16 @@ __device__ __forceinline__ void attn_step(const uint16_t* __restrict__ kt, const
                                : __builtin_fmaf((float)__builtin_bit_cast(_Float16, mv[i]), LOG2E, v);
       } else if (MODE == MODE_CAUSAL) {
         if (cx.key0 + kk > cx.qpos) v = -__builtin_inff();
+      } else if (MODE == MODE_CAUSAL_K) {
+        // causal by position, plus the per-key mask (cx.mrow, shared by all rows) if any
+        const int key = cx.key0 + kk;
+        if (key > cx.qpos) {
+          v = -__builtin_inff();
+        } else if (cx.mrow != nullptr && kk < cx.kvalid) {
+          const uint16_t hv = cx.mrow[key];
+          v = f16_dropped(hv) ? -__builtin_inff()
+                              : __builtin_fmaf((float)__builtin_bit_cast(_Float16, hv), LOG2E, v);
+        }
       } else if (MODE == MODE_POOLED) {
         const int b = cx.key0 + kk;
         bool live = false;
@@ -567,7 +577,8 @@ attn_dense_kernel(const uint16_t* __restrict__ Q, int C, int n_q, const uint16_t
                   const uint16_t* __restrict__ V, int T, int n_kv, const uint16_t* __restrict__ mask,
                   int64_t mask_ld, float scale_log2, float* __restrict__ O,
                   const uint8_t* __restrict__ flags, int n_qt, int n_ktile, int splits,
-                  float* __restrict__ part_o, float* __restrict__ part_ml, int mask_vec, int hg_log2) {
+                  float* __restrict__ part_o, float* __restrict__ part_ml, int mask_vec, int hg_log2,
+                  int causal_q0) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   __shared__ int s_lo, s_hi;
   const int tid = threadIdx.x;
@@ -596,10 +607,25 @@ attn_dense_kernel(const uint16_t* __restrict__ Q, int C, int n_q, const uint16_t
   if (tid == 0) { s_lo = n_ktile; s_hi = 0; }
   __syncthreads();
   for (int t = tid; t < n_ktile; t += NT) {
-    uint8_t f = flags[(size_t)fr0 * n_ktile + t];
-    for (int fr = fr0 + 1; fr <= fr1; ++fr) {
-      const uint8_t f2 = flags[(size_t)fr * n_ktile + t];
-      f = (f == f2) ? f : TILE_MIXED;
+    uint8_t f;
+    if (causal_q0 >= 0) {
+      // causal by position: rows causal_q0 + [qt*R, min(qt*R + R, C)); flags (if any)
+      // classify the per-key mask's 128-key tiles
+      const int rmin = causal_q0 + qt * R, rmax = causal_q0 + min(qt * R + R, C) - 1;
+      const int k0 = t * FLAG_TILE, k1 = k0 + FLAG_TILE - 1;
+      f = k0 > rmax ? TILE_DROPPED : (k1 <= rmin ? TILE_ZERO : TILE_MIXED);
+      if (flags != nullptr) {
+        const uint8_t kf = flags[t];
+        f = (f == TILE_DROPPED || kf == TILE_DROPPED) ? TILE_DROPPED
+            : (f == TILE_ZERO && kf == TILE_ZERO)      ? TILE_ZERO
+                                                       : TILE_MIXED;
+      }
+    } else {
+      f = flags[(size_t)fr0 * n_ktile + t];
+      for (int fr = fr0 + 1; fr <= fr1; ++fr) {
+        const uint8_t f2 = flags[(size_t)fr * n_ktile + t];
+        f = (f == f2) ? f : TILE_MIXED;
+      }
     }
     frow[t] = f;
     if (f != TILE_DROPPED) { atomicMin(&s_lo, t); atomicMax(&s_hi, t + 1); }
@@ -624,9 +650,15 @@ attn_dense_kernel(const uint16_t* __restrict__ Q, int C, int n_q, const uint16_t
 
   StepCtx cx;
   cx.scale_log2 = scale_log2;
-  cx.mrow = qvalid ? mask + (size_t)qrow * mask_ld : nullptr;
+  if (causal_q0 >= 0) {
+    cx.mrow = mask;   // the per-key mask (or null)
+    cx.qpos = causal_q0 + qrow;
+  } else {
+    cx.mrow = qvalid ? mask + (size_t)qrow * mask_ld : nullptr;
+    cx.qpos = 0;
+  }
   cx.mask_vec = mask_vec != 0;
-  cx.qpos = 0; cx.selbits = nullptr; cx.jlimit = 0; cx.pool_bias = 0.f;
+  cx.selbits = nullptr; cx.jlimit = 0; cx.pool_bias = 0.f;
 
   const LaneOffs<D> lo = lane_offsets<D>();
   TileLoader<D> tl;
@@ -645,7 +677,9 @@ attn_dense_kernel(const uint16_t* __restrict__ Q, int C, int n_q, const uint16_t
     __syncthreads();
     cx.key0 = st * BN;
     cx.kvalid = min(BN, T - st * BN);
-    if (f == TILE_MIXED)
+    if (f == TILE_MIXED && causal_q0 >= 0)
+      attn_step<D, MODE_CAUSAL_K, true>(lds, lds + KR * Geo<D>::TILE, nullptr, nullptr, lo, qf, o, m, l, cx);
+    else if (f == TILE_MIXED)
       attn_step<D, MODE_GMASK, true>(lds, lds + KR * Geo<D>::TILE, nullptr, nullptr, lo, qf, o, m, l, cx);
     else
       attn_step<D, MODE_PLAIN, true>(lds, lds + KR * Geo<D>::TILE, nullptr, nullptr, lo, qf, o, m, l, cx);
@@ -874,7 +908,7 @@ template <int D>
 static hipError_t dense_impl(const uint16_t* Q, int C, int n_q, const uint16_t* K, const uint16_t* V,
                              int T, int n_kv, const uint16_t* mask, int64_t mask_ld, float scale,
                              float* O, const DensePlan& p, const uint8_t* flags, float* part_o,
-                             float* part_ml, hipStream_t stream) {
+                             float* part_ml, int causal_q0, hipStream_t stream) {
   const float sl2 = scale * LOG2E;
   const int grid = p.n_qt * (n_q >> p.hg_log2) * p.splits;
   const size_t lds = Geo<D>::LDS_BYTES + ((p.n_ktile + 15) & ~15);   // rings + flag row
@@ -884,13 +918,13 @@ static hipError_t dense_impl(const uint16_t* Q, int C, int n_q, const uint16_t* 
                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     hipLaunchKernelGGL((attn_dense_kernel<D, true>), dim3(grid), dim3(NT), lds, stream, Q, C, n_q, K, V,
                        T, n_kv, mask, mask_ld, sl2, O, flags, p.n_qt, p.n_ktile, p.splits, part_o,
-                       part_ml, mask_vec, p.hg_log2);
+                       part_ml, mask_vec, p.hg_log2, causal_q0);
   } else {
     hipFuncSetAttribute((const void*)attn_dense_kernel<D, false>,
                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     hipLaunchKernelGGL((attn_dense_kernel<D, false>), dim3(grid), dim3(NT), lds, stream, Q, C, n_q, K,
                        V, T, n_kv, mask, mask_ld, sl2, O, flags, p.n_qt, p.n_ktile, 1, part_o,
-                       part_ml, mask_vec, p.hg_log2);
+                       part_ml, mask_vec, p.hg_log2, causal_q0);
   }
   return hipGetLastError();
 }
@@ -898,12 +932,12 @@ static hipError_t dense_impl(const uint16_t* Q, int C, int n_q, const uint16_t* 
 hipError_t launch_attn_dense(const uint16_t* Q, int C, int n_q, const uint16_t* K, const uint16_t* V,
                              int T, int n_kv, int d, const uint16_t* mask, int64_t mask_ld,
                              float scale, float* O, const DensePlan& plan, const uint8_t* flags,
-                             float* part_o, float* part_ml, hipStream_t stream) {
+                             float* part_o, float* part_ml, int causal_q0, hipStream_t stream) {
   if (d == 128)
     return dense_impl<128>(Q, C, n_q, K, V, T, n_kv, mask, mask_ld, scale, O, plan, flags, part_o,
-                           part_ml, stream);
+                           part_ml, causal_q0, stream);
   return dense_impl<64>(Q, C, n_q, K, V, T, n_kv, mask, mask_ld, scale, O, plan, flags, part_o,
-                        part_ml, stream);
+                        part_ml, causal_q0, stream);
 }
 
 template <int D>

@@ -81,7 +81,7 @@ DensePlan plan_dense(int C, int T, int n_q, int n_kv, int d);
 hipError_t launch_attn_dense(const uint16_t* Q, int C, int n_q, const uint16_t* K, const uint16_t* V,
                              int T, int n_kv, int d, const uint16_t* mask, int64_t mask_ld,
                              float scale, float* O, const DensePlan& plan, const uint8_t* flags,
-                             float* part_o, float* part_ml, hipStream_t stream);
+                             float* part_o, float* part_ml, int causal_q0, hipStream_t stream);
 
 hipError_t launch_attn_combine(int C, int n_q, int d, int splits, const float* part_o,
                                const float* part_ml, float* O, hipStream_t stream);

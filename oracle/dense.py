@@ -115,3 +115,17 @@ def fold_mask_ref(keep_idx, keep_cnt, q_start: int, T: int, width: int, recent: 
                 m[i, c * width:min(c * width + width, p + 1, T)] = 0
         m[i, max(0, p - recent + 1):min(p + 1, T)] = 0
     return m
+
+
+def causal_kmask_ref(q_start: int, C: int, T: int, kmask=None) -> np.ndarray:
+    """fp16 [C][T]: the causal mask of rows at q_start.. composed by addition with
+    a per-key mask kmask [T] ("The Four Principles for Optimizing Transformers on
+    the ANE", Principle 3: a (query, key) mask and a per-key padding mask, both
+    additive).  Reading: a key dropped by either part (<= -30000) stays dropped;
+    otherwise the entry is the per-key bias (the causal part is 0 there)."""
+    p = np.arange(q_start, q_start + C)[:, None]
+    t = np.arange(T)[None, :]
+    k = np.zeros(T, dtype=np.float16) if kmask is None else np.asarray(kmask, dtype=np.float16)
+    kdrop = k.astype(np.float64) <= DROP_AT
+    drop = (t > p) | kdrop[None, :]
+    return np.where(drop, np.float16(DROP_AT), k[None, :]).astype(np.float16)

@@ -11,7 +11,8 @@ import sys
 import numpy as np
 import pytest
 
-from oracle import blocksparse_ref, dense_ref, fold_mask_ref, pooled_index_ref, select_ref, selection_sets
+from oracle import (blocksparse_ref, causal_kmask_ref, dense_ref, fold_mask_ref, pooled_index_ref,
+                    select_ref, selection_sets)
 from workloads import CONFIGS, bf16_bits, causal_mask, make_workload
 from _util import assert_close, dev_bf16, dev_f16, f64
 
@@ -544,3 +545,51 @@ def test_fold_keep_mask_malformed_lists(lp):
     torch.cuda.synchronize()
     want = fold_mask_ref(idx, cnt, q_start, T, width, recent)
     assert np.array_equal(m.cpu().numpy().view(np.uint16), want.view(np.uint16))
+
+
+# ---------------------------------------------------------------- causal entry, per-key mask
+def test_dense_causal_gqa4k(lp):
+    """The causal entry (no mask buffer) on both gqa4k chunks."""
+    import torch
+    w = make_workload("gqa4k")
+    s = w.spec
+    for ci, (q0, C) in enumerate(s.chunks):
+        T = q0 + C
+        say("dense causal gqa4k chunk", ci)
+        O = lp.prefill_attn_dense_causal(dev_bf16(w.Q[q0:T]), dev_bf16(w.K[:T]), dev_bf16(w.V[:T]), q0,
+                                         s.scale)
+        torch.cuda.synchronize()
+        heads = np.arange(0, s.n_q, 3)
+        want = dense_ref(f64(w.Q[q0:T]), f64(w.K[:T]), f64(w.V[:T]), causal_mask(q0, C), s.scale,
+                         heads=heads)
+        assert_close(O.cpu().numpy()[:, heads], want, f"causal gqa4k chunk {ci}")
+
+
+@pytest.mark.parametrize("C,q_start,T,n_q,n_kv,d,pad_from", [
+    (700, 300, 1000, 4, 2, 128, None),     # padding and biases scattered over the keys
+    (512, 1000, 1700, 8, 2, 128, None),    # T beyond the chunk: keys past each row stay dropped
+    (16, 5000, 5016, 4, 1, 128, None),     # few rows: split-key path
+    (300, 0, 300, 2, 2, 64, 0),            # leading keys padded: early rows see nothing -> zeros
+])
+def test_dense_causal_kmask(lp, C, q_start, T, n_q, n_kv, d, pad_from):
+    import torch
+    rng = np.random.default_rng(C + T)
+    q, k, v = rand_bits(rng, C, n_q, d), rand_bits(rng, T, n_kv, d), rand_bits(rng, T, n_kv, d)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    km = np.zeros(T, np.float16)
+    if pad_from is None:
+        km[rng.random(T) < 0.1] = -30000
+        km[rng.random(T) < 0.05] = np.float16(-1e4)
+        sel = rng.random(T) < 0.1
+        km[sel] = rng.uniform(-3, 2, size=int(sel.sum())).astype(np.float16)
+    else:
+        km[pad_from:pad_from + 100] = -30000
+    say("dense causal kmask", C, q_start, T, n_q, n_kv, d)
+    O = lp.prefill_attn_dense_causal(dev_bf16(q), dev_bf16(k), dev_bf16(v), q_start, scale,
+                                     kmask=torch.from_numpy(km).cuda())
+    torch.cuda.synchronize()
+    want = dense_ref(f64(q), f64(k), f64(v), causal_kmask_ref(q_start, C, T, km), scale)
+    got = O.cpu().numpy()
+    assert_close(got, want, "causal kmask")
+    if pad_from is not None:
+        assert np.all(got[:100] == 0)

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attention_weights, dense_ref, fold_mask_ref
+from oracle import attention_weights, causal_kmask_ref, dense_ref, fold_mask_ref
 from workloads import CONFIGS, bf16_to_f32, causal_mask, dense_equiv_pairs, make_workload
 
 DROP = -30000.0
@@ -281,3 +281,28 @@ def test_fold_mask_closed_forms():
     blocks = np.sort(rng.choice((p - 2) // 4, size=512, replace=False)).astype(np.int32)
     m = fold_mask_ref(blocks[None, :], np.array([512], np.int32), p, p + 1, 4, 3)
     assert int((m[0] == 0).sum()) == 2051
+
+
+# ---------------------------------------------------------------- per-key mask
+def test_causal_kmask_composition():
+    """Without a per-key mask the composition is the causal mask; dropping keys
+    through it equals gathering the others; a finite per-key bias b scales that
+    key's weight by e^b (checked against an explicit softmax)."""
+    from workloads import causal_mask
+    assert np.array_equal(causal_kmask_ref(5, 7, 12).view(np.uint16), causal_mask(5, 7).view(np.uint16))
+    rng = np.random.default_rng(12)
+    C, T, d, q0 = 6, 14, 8, 8
+    q, k, v = rng.standard_normal((C, 1, d)), rng.standard_normal((T, 1, d)), rng.standard_normal((T, 1, d))
+    km = np.zeros(T, np.float16)
+    km[[2, 5, 11]] = -30000                      # padding keys
+    km[7] = np.float16(np.log(3.0))              # a finite bias
+    got = dense_ref(q, k, v, causal_kmask_ref(q0, C, T, km), 0.5)
+    for i in range(C):
+        p = q0 + i
+        keep = [t for t in range(p + 1) if t not in (2, 5, 11)]
+        s = 0.5 * (k[keep, 0] @ q[i, 0]) + np.array([float(km[t]) for t in keep])
+        w = np.exp(s - s.max())
+        assert np.allclose(got[i, 0], w @ v[keep, 0] / w.sum(), rtol=1e-13, atol=1e-13)
+    # every visible key padded: the row outputs zeros
+    km_all = np.full(T, -30000, np.float16)
+    assert np.all(dense_ref(q, k, v, causal_kmask_ref(q0, C, T, km_all), 0.5) == 0)
