@@ -80,7 +80,7 @@ const char* pa_status_string(int status);
  *
  *   O[i][h] = sum_t w_t V[t][g(h)],  w = softmax_t(scale * Q[i][h].K[t][g(h)] + mask[i][t])
  *
- * Requires C >= 1, 1 <= T <= 2^22, T*n_kv*d*2 < 2^31 (K and V below 2 GiB each), mask_ld >= T. The mask alone decides visibility; the
+ * Requires C >= 1, 1 <= T <= 2^22, mask_ld >= T (K and V may be any size). The mask alone decides visibility; the
  * library assumes nothing about causality. `workspace` must hold at least
  * prefill_attn_dense_workspace(C, T, n_q, n_kv, d) bytes (tile flags and, when
  * the key range is split across workgroups, partial results); it is scratch,
@@ -172,7 +172,7 @@ int select_blocks(const uint16_t* Q, int C, int q_start, int n_q, int n_kv, int 
  * (K_pool[g][b], V_pool[g][b]) with weight block * exp(scale*Q.K_pool - m):
  * a skipped block stands for its `block` keys. All terms share one softmax.
  * The selection arrays must come from select_blocks for the same chunk.
- * Requires block == 128 and T*n_kv*d*2 < 2^31 (else PA_EUNSUPPORTED).
+ * Requires block == 128 (else PA_EUNSUPPORTED).
  * Errors: PA_EINVAL, PA_EUNSUPPORTED, PA_EHIP.
  */
 int prefill_attn_blocksparse(const uint16_t* Q, int C, int q_start, int n_q,

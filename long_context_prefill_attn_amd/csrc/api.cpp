@@ -118,7 +118,6 @@ int prefill_attn_dense(const uint16_t* Q, int C, int n_q, const uint16_t* K, con
   if (mask_ld < T || !good_scale(scale)) return PA_EINVAL;
   if (d != 64 && d != 128) return PA_EUNSUPPORTED;
   if (T > (1 << 22)) return PA_EUNSUPPORTED;   // the per-tile flag row must fit in LDS
-  if ((long long)T * n_kv * d * 2 >= (1LL << 31)) return PA_EUNSUPPORTED;   // 32-bit tile offsets
   const pa::DensePlan plan = pa::plan_dense(C, T, n_q, n_kv, d);
   if ((long long)plan.n_qt * n_q * plan.splits >= (1LL << 31)) return PA_EUNSUPPORTED;
   if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
@@ -157,7 +156,6 @@ int prefill_attn_dense_causal(const uint16_t* Q, int C, int q_start, int n_q, co
   if ((long long)q_start + C > T || !good_scale(scale)) return PA_EINVAL;
   if (d != 64 && d != 128) return PA_EUNSUPPORTED;
   if (T > (1 << 22)) return PA_EUNSUPPORTED;
-  if ((long long)T * n_kv * d * 2 >= (1LL << 31)) return PA_EUNSUPPORTED;   // 32-bit tile offsets
   const pa::DensePlan plan = pa::plan_dense(C, T, n_q, n_kv, d);
   if ((long long)plan.n_qt * n_q * plan.splits >= (1LL << 31)) return PA_EUNSUPPORTED;
   if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
@@ -268,7 +266,6 @@ int prefill_attn_blocksparse_ld(const uint16_t* Q, int C, int q_start, int n_q, 
   if ((long long)q_start + C != T || !good_scale(scale)) return PA_EINVAL;
   if (d != 64 && d != 128) return PA_EUNSUPPORTED;
   if (block != 128) return PA_EUNSUPPORTED;  // the attention kernel tiles query blocks of 128
-  if ((long long)T * n_kv * d * 2 >= (1LL << 31)) return PA_EUNSUPPORTED;   // 32-bit tile offsets
   const int nb = (T + block - 1) / block;
   if (nb > 8192) return PA_EUNSUPPORTED;
   if (pool_ld < nb) return PA_EINVAL;

@@ -76,22 +76,28 @@ __device__ __forceinline__ void buffer_load_lds16(const void* base, uint32_t ran
 }
 
 // Direct HBM -> LDS loads of 64-key tiles of K or V for KV head g, through a
-// buffer resource whose range ends at row T: rows past T read as zeros (their
-// scores are masked). Lane l of a wave-wide 16-byte load lands at byte 16*l of
+// buffer resource per tile whose range ends at row T: rows past T read as zeros
+// (their scores are masked). Lane l of a wave-wide 16-byte load lands at byte 16*l of
 // the 1 KB it writes, so each lane fetches the global chunk that belongs at
 // that swizzled position. Each of the 8 waves issues NIW such loads per tile.
 template <int D>
 struct TileLoader {
   const uint16_t* kptr;   // K + g*D
   const uint16_t* vptr;   // V + g*D
-  uint32_t range;         // bytes readable from kptr / vptr (rows 0..T-1)
+  size_t row_elems;       // elements between consecutive tokens (n_kv * D)
+  uint32_t row_bytes;     // the same in bytes
+  uint32_t range;         // whole-tensor range (bytes readable from kptr / vptr, rows 0..T-1)
+  int T;
+  bool rebase;            // K/V too large for 32-bit offsets: one buffer resource per tile
   uint32_t voff[Geo<D>::NIW];   // per-lane byte offsets inside a tile
-  uint32_t row_bytes;     // bytes between consecutive tokens (n_kv * D * 2)
 
-  __device__ __forceinline__ void init(const uint16_t* K, const uint16_t* V, int T, int n_kv, int g) {
+  __device__ __forceinline__ void init(const uint16_t* K, const uint16_t* V, int T_, int n_kv, int g) {
     constexpr int CPR = Geo<D>::CPR, RPI = Geo<D>::RPI, NIW = Geo<D>::NIW;
+    row_elems = (size_t)n_kv * D;
     row_bytes = (uint32_t)n_kv * D * 2;
-    range = (uint32_t)T * row_bytes - (uint32_t)g * D * 2;
+    T = T_;
+    rebase = (uint64_t)T_ * row_bytes >= (1ull << 31);
+    range = rebase ? 0u : (uint32_t)T_ * row_bytes - (uint32_t)g * D * 2;
     kptr = K + (size_t)g * D;
     vptr = V + (size_t)g * D;
     const int lane = __lane_id(), wave = threadIdx.x >> 6;
@@ -103,15 +109,25 @@ struct TileLoader {
     }
   }
 
+  // Up to 2 GiB the buffer resource covers the whole tensor and the tile's row
+  // offset joins the per-lane offset. Beyond that the resource starts at the
+  // tile's first row (64-bit address) and its range ends with this head's slice
+  // of the tile's last valid row. Either way rows at or past T read as zeros.
   __device__ __forceinline__ void issue(bool is_v, int kbase, uint16_t* tile) const {
     constexpr int RPI = Geo<D>::RPI, NIW = Geo<D>::NIW;
     const int wave = threadIdx.x >> 6;
-    // the tile's row offset goes into the per-lane offset, which the range check covers
-    const uint32_t toff = (uint32_t)kbase * row_bytes;
+    const uint16_t* base = is_v ? vptr : kptr;
+    uint32_t rng = range, toff = (uint32_t)kbase * row_bytes;
+    if (rebase) {
+      base += (size_t)kbase * row_elems;
+      const int rows = min(T - kbase, BN);
+      rng = rows > 0 ? (uint32_t)(rows - 1) * row_bytes + D * 2 : 0u;
+      toff = 0;
+    }
 #pragma unroll
     for (int i = 0; i < NIW; ++i) {
       LDS_AS void* dst = (LDS_AS void*)(tile + (wave * NIW + i) * RPI * D);
-      buffer_load_lds16(is_v ? vptr : kptr, range, dst, voff[i] + toff, 0);
+      buffer_load_lds16(base, rng, dst, voff[i] + toff, 0);
     }
   }
 };

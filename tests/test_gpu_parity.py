@@ -593,3 +593,33 @@ def test_dense_causal_kmask(lp, C, q_start, T, n_q, n_kv, d, pad_from):
     assert_close(got, want, "causal kmask")
     if pad_from is not None:
         assert np.all(got[:100] == 0)
+
+
+@pytest.mark.timeout(900)
+def test_dense_causal_kv_beyond_2gib(lp):
+    """K and V of 1.1M tokens x 8 KV heads x d 128 (2.25 GB each): tiles are
+    addressed past 2^31 bytes. Sampled rows of two heads against the oracle."""
+    import torch
+    T, C, n_kv, d = 1_100_000, 64, 8, 128
+    q0 = T - C
+    rng = np.random.default_rng(77)
+    say("beyond 2 GiB: drawing K, V")
+    k = rand_bits(rng, T, n_kv, d)
+    v = rand_bits(rng, T, n_kv, d)
+    q = rand_bits(rng, C, n_kv, d)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    say("beyond 2 GiB: GPU")
+    Kd, Vd = dev_bf16(k), dev_bf16(v)
+    O = lp.prefill_attn_dense_causal(dev_bf16(q), Kd, Vd, q0, scale)
+    torch.cuda.synchronize()
+    got = O.cpu().numpy()
+    del Kd, Vd
+    say("beyond 2 GiB: oracle")
+    rows = np.array([0, 31, 63])
+    for g in (0, 7):
+        kg, vg = f64(k[:, g:g + 1, :]), f64(v[:, g:g + 1, :])
+        qg = f64(q[rows][:, g:g + 1, :])
+        for r_i, r in enumerate(rows):
+            p = q0 + r
+            want = dense_ref(qg[r_i:r_i + 1], kg[:p + 1], vg[:p + 1], np.zeros((1, p + 1), np.float16), scale)
+            assert_close(got[r, g:g + 1], want[0], f"row {r} head {g}")
