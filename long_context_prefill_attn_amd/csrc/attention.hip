@@ -683,10 +683,21 @@ attn_dense_kernel(const uint16_t* __restrict__ Q, int C, int n_q, const uint16_t
   // 1) plain steps: tiles flagged ZERO whose 64 keys all lie below T
   plain_steps<D>(tl, lds, DenseSrc{a, b, T, frow}, lo, qf, o, m, l, scale_log2);
 
-  // 2) the remaining steps: mask tiles (MIXED) and a ragged last step
-  for (int st = a; st < b; ++st) {
+  // 2) the remaining steps: mask tiles (MIXED) and a ragged last step. The next
+  // one is found 64 steps at a time by a wave-wide ballot over the LDS flags
+  // (every wave forms the same mask, so the barriers inside the steps stay
+  // uniform); the walk between them carries nothing but the step index.
+  auto next_special = [&](int st) -> int {
+    for (int base = st; base < b; base += 64) {
+      const int sl = base + lane;
+      const uint8_t fl = sl < b ? frow[sl >> 1] : TILE_DROPPED;
+      const uint64_t hit = __ballot(!(fl == TILE_DROPPED || (fl == TILE_ZERO && (sl + 1) * BN <= T)));
+      if (hit != 0) return base + __builtin_ctzll(hit);
+    }
+    return b;
+  };
+  for (int st = next_special(a); st < b; st = next_special(st + 1)) {
     const uint8_t f = frow[st >> 1];
-    if (f == TILE_DROPPED || (f == TILE_ZERO && (st + 1) * BN <= T)) continue;
     tl.issue(false, st * BN, lds);
     tl.issue(true, st * BN, lds + KR * Geo<D>::TILE);
     wait_vm<0>();
