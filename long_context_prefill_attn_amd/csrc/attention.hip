@@ -23,11 +23,15 @@
 //     (packed to bf16), so P never leaves registers and O^T lands with the row's
 //     head_dim values in the lane that owns the row's softmax state.
 //   * K/V tiles of 64 keys go HBM -> LDS directly (buffer loads with the LDS
-//     bit) into 3-deep rings, issued two steps ahead of use; the QK^T of the
-//     next tile overlaps the softmax and PV of the current one.
+//     bit) into 4-deep (K) and 3-deep (V) rings, issued two steps ahead of use.
+//     One loop iteration alternates the QK^T MFMAs of the next step with the PV
+//     MFMAs of the previous one and forms the current step's weights between
+//     them, so the softmax VALU work is spread evenly over all MFMAs.
 //   * Softmax in exp2 units with log2(e) folded into the scale. The running max
-//     is raised only when it grows by more than 2^8 (all weights stay <= 256),
-//     so the O rescale is rare; results are exact up to rounding either way.
+//     starts at the first tile's max and is raised only when a row's weights
+//     for a tile sum past 2^12, so the O rescale is rare and no per-tile max is
+//     taken; results are exact up to rounding either way. (Masked steps take
+//     their max and raise it when it grows by more than 2^8.)
 //   * Workgroup ids are remapped so that the workgroups of one KV head run on
 //     one XCD (shared L2 for that head's K/V), longest query tiles first.
 #include <algorithm>
@@ -40,7 +44,8 @@ namespace pa {
 constexpr int BN = 64;          // keys per inner step
 constexpr int NW = 8;           // waves per workgroup
 constexpr int NT = 64 * NW;     // threads per workgroup
-constexpr int KR = 3;           // K and V ring depth (tiles)
+constexpr int KRK = 4;          // K ring depth (tiles)
+constexpr int KRV = 3;          // V ring depth (tiles)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float SLACK = 8.0f;   // lazy-rescale threshold in log2 units
 
@@ -57,12 +62,20 @@ template <int D>
 struct Geo {
   static constexpr int CPR = D / 8;              // 16-byte chunks per row
   static constexpr int TILE = BN * D;            // halves of one K or V tile
-  static constexpr int RING = 2 * KR * TILE;     // K ring then V ring (halves)
+  static constexpr int RING = (KRK + KRV) * TILE;  // K ring then V ring (halves)
   static constexpr size_t LDS_BYTES = RING * sizeof(uint16_t);
   static constexpr int RPI = 64 / CPR;           // rows written by one wave-wide 16-byte load
   static constexpr int NIW = BN / RPI / NW;      // such loads per wave per tile
   static constexpr int KCH = BN * D / 8 / NT;    // 16-byte chunks per thread per tile
 };
+
+// The lane id, opaque to the optimiser: what is derived from it after the long
+// step loop is recomputed there instead of being held in registers through it.
+__device__ __forceinline__ int fresh_lane_id() {
+  int l = __lane_id();
+  asm volatile("" : "+v"(l));
+  return l;
+}
 
 __device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
 
@@ -96,7 +109,8 @@ struct TileLoader {
     row_elems = (size_t)n_kv * D;
     row_bytes = (uint32_t)n_kv * D * 2;
     T = T_;
-    rebase = (uint64_t)T_ * row_bytes >= (1ull << 31);
+    // T * row_bytes >= 2^31, in 32-bit scalar arithmetic
+    rebase = ((__umulhi((uint32_t)T_, row_bytes) | (((uint32_t)T_ * row_bytes) >> 31)) != 0);
     range = rebase ? 0u : (uint32_t)T_ * row_bytes - (uint32_t)g * D * 2;
     kptr = K + (size_t)g * D;
     vptr = V + (size_t)g * D;
@@ -154,21 +168,26 @@ __device__ __forceinline__ void wait_vm() {
 // Per-lane LDS offsets (in halves) of the MFMA operands inside a tile.
 template <int D>
 struct LaneOffs {
-  int k[D / 16];   // K slice rows n, dims 16*st + 8*h .. +7
-  int v[D / 32];   // transposed V read: see attn_step
+  // The swizzle only permutes the low 3 bits of a chunk index, so chunk c + 8
+  // sits exactly 8 chunks (64 halves) after chunk c: four K and two V base
+  // offsets serve every slice, the rest being immediate offsets.
+  int k[4];   // K slice rows n, dims 16*st + 8*h .. +7 for st < 4
+  int v[2];   // transposed V read for output blocks 0 and 1 (see attn_step)
+  __device__ __forceinline__ int kofs(int st) const { return k[st & 3] + (st >> 2) * 64; }
+  __device__ __forceinline__ int vofs(int nb) const { return v[nb & 1] + (nb >> 1) * 64; }
 };
 
 template <int D>
 __device__ __forceinline__ LaneOffs<D> lane_offsets() {
   LaneOffs<D> o;
-  const int lane = __lane_id();
+  const int lane = fresh_lane_id();
   const int n = lane & 31, h = lane >> 5;
 #pragma unroll
-  for (int st = 0; st < D / 16; ++st) o.k[st] = n * D + (((2 * st + h) ^ swz(n)) * 8);
+  for (int st = 0; st < 4; ++st) o.k[st] = n * D + (((2 * st + h) ^ swz(n)) * 8);
   const int blk = lane >> 4, s = lane & 15, r = s >> 2, q = s & 3;
   const int vrow = 4 * (blk >> 1) + r;   // row inside each 8-row group
 #pragma unroll
-  for (int nb = 0; nb < D / 32; ++nb) {
+  for (int nb = 0; nb < 2; ++nb) {
     const int chunk = nb * 4 + (blk & 1) * 2 + (q >> 1);
     o.v[nb] = vrow * D + ((chunk ^ swz(vrow)) * 8) + (q & 1) * 4;
   }
@@ -200,7 +219,7 @@ __device__ __forceinline__ f32x16 qk_slice(const uint16_t* __restrict__ kt, cons
                                            const bf16x8 (&qf)[D / 16], f32x16 s) {
 #pragma unroll
   for (int st = 0; st < D / 16; ++st) {
-    const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + lo.k[st]);
+    const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + lo.kofs(st));
     s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s, 0, 0, 0);
   }
   return s;
@@ -218,7 +237,7 @@ __device__ __forceinline__ void attn_step(const uint16_t* __restrict__ kt, const
                                           const uint16_t* __restrict__ vt2, const LaneOffs<D>& lo,
                                           const bf16x8 (&qf)[D / 16], f32x16 (&o)[D / 32], float& m,
                                           float& l, const StepCtx& cx) {
-  const int lane = __lane_id();
+  const int lane = fresh_lane_id();
   const int h = lane >> 5;
 
   f32x16 s[2];
@@ -313,7 +332,7 @@ __device__ __forceinline__ void attn_step(const uint16_t* __restrict__ kt, const
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const int off = lo.v[nb] + (kb * 32 + 16 * c) * D;
+        const int off = lo.vofs(nb) + (kb * 32 + 16 * c) * D;
         const bf16x8 b = __builtin_bit_cast(bf16x8, P[kb][c]);
         {
           const v4i16 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt + off));
@@ -349,21 +368,6 @@ __device__ __forceinline__ float row_max(const f32x16 (&s)[2]) {
   return __builtin_fmaxf(mx, partner32(mx));
 }
 
-// Raise the running max (log2 units) when a tile's max exceeds it by more than
-// the slack; rare after the first tiles, so it is a real branch.
-template <int D>
-__device__ __forceinline__ void raise_max(float mx_raw, float scale_log2, f32x16 (&o)[D / 32], float& m,
-                                          float& l) {
-  const float m_new = __builtin_fmaxf(m, mx_raw * scale_log2);
-  if (__builtin_expect(__any(m_new > m + SLACK), 0)) {
-    const float alpha = (m_new == -__builtin_inff()) ? 1.f : exp2f(m - m_new);
-#pragma unroll
-    for (int nb = 0; nb < D / 32; ++nb) o[nb] *= alpha;
-    l *= alpha;
-    m = m_new;
-  }
-}
-
 // P = 2^(S*scale_log2 - m) packed to bf16 in PV-operand order; l += sum of the packed values
 __device__ __forceinline__ void exp_pack(const f32x16 (&s)[2], float m, float scale_log2, u32x4 (&P)[2][2],
                                          float& l) {
@@ -383,86 +387,103 @@ __device__ __forceinline__ void exp_pack(const f32x16 (&s)[2], float m, float sc
   }
 }
 
-// One hand-scheduled pipeline iteration body (after the barrier and the tile
-// loads): the QK^T MFMAs of the next tile, each with the K fragment read four
-// MFMAs ahead and a quarter-pair of the current tile's exp/pack work; then the
-// PV MFMAs of the current tile, each with its transposed V reads three MFMAs
-// ahead (the first three overlap the last QK^T MFMAs) and a share of the next
-// tile's row-max. sched_barrier fences keep the
-// compiler from regrouping the work. Returns the next tile's raw row max.
-template <int D>
-__device__ __forceinline__ float fused_step(const uint16_t* __restrict__ kt_next, const uint16_t* __restrict__ vt,
-                                            const LaneOffs<D>& lo, const bf16x8 (&qf)[D / 16],
-                                            const f32x16 (&sc)[2], f32x16 (&sn)[2], f32x16 (&o)[D / 32],
-                                            float m, float& l, float scale_log2) {
-  constexpr int NQK = 2 * (D / 16);     // QK^T MFMAs (k = 2*st + kb)
-  constexpr int NPV = 4 * (D / 32);     // PV MFMAs (k = 4*nb + 2*kb + c)
-  constexpr int KR = 4;                 // K fragment ring depth
+// Lazy rescaling in the pipelined loop: a tile's weights are formed against the
+// running max m as it stands; m is raised (and O, l rescaled) only when a row's
+// weights for the tile sum to more than this, so every weight stays <= 2^12.
+constexpr float PSUM_LIMIT = 4096.0f;
+
+// One pipeline iteration for step i: the QK^T MFMAs of step i+1 alternate with
+// the PV MFMAs of step i-1 (whose weights were formed in the previous
+// iteration), and each MFMA pair carries one packed pair of step i's weights
+// (fma, exp2, pack, row-sum). The VALU work is thereby spread evenly over all
+// MFMAs of the iteration. K fragments are read KA MFMAs ahead, V fragments VA
+// ahead; sched_barrier fences keep the compiler from regrouping the work.
+//   S^T accumulator kb (keys 32kb .. +31) takes its MFMAs in slots kb*NS/2 ..;
+//   PV slot k uses weight fragment f = k / (D/32) (keys 16f .. +15) and output
+//   block nb = k % (D/32), so fragment f is dead after its D/32 MFMAs.
+// Returns the row's sum of step i's packed weights.
+template <int D, bool PV>
+__device__ __forceinline__ float pipe_step(const uint16_t* __restrict__ kt_next, const uint16_t* __restrict__ vt_prev,
+                                           const LaneOffs<D>& lo, const bf16x8 (&qf)[D / 16],
+                                           const f32x16 (&sc)[2], f32x16 (&sn)[2], const u32x4 (&pp)[2][2],
+                                           u32x4 (&pc)[2][2], f32x16 (&o)[D / 32], float m, float scale_log2) {
+  constexpr int NS = D / 8;             // QK^T MFMAs = PV MFMAs per step
+  constexpr int HS = NS / 2;            // QK^T MFMAs per S^T accumulator
+  constexpr int NB = D / 32;            // output blocks
+  constexpr int KA = 3;                 // K fragments in flight
+  constexpr int VA = 2;                 // V fragment pairs in flight
   const float nmu = (m == -__builtin_inff()) ? 0.f : -m;
 
-  bf16x8 kf[KR];
-#pragma unroll
-  for (int k = 0; k < KR; ++k)
-    kf[k] = *reinterpret_cast<const bf16x8*>(kt_next + (k & 1) * 32 * D + lo.k[k >> 1]);
-  // PV operands: two transposed 8-byte reads per MFMA, kept VA MFMAs ahead;
-  // the first VA are issued during the last QK^T MFMAs
-  constexpr int VA = 3;
-  v4i16 vf[4][2];
-  auto vread = [&](int k, v4i16 (&dst)[2]) {
-    const int nb = k >> 2, kb = (k >> 1) & 1, c = k & 1;
-    const int off = lo.v[nb] + (kb * 32 + 16 * c) * D;
-    dst[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt + off));
-    dst[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt + off + 8 * D));
+  auto kread = [&](int k) {
+    return *reinterpret_cast<const bf16x8*>(kt_next + (k / HS) * 32 * D + lo.kofs(k % HS));
   };
-  sn[0] = f32x16{};
-  sn[1] = f32x16{};
-  u32x4 P[2][2];
+  auto vread = [&](int k, v4i16 (&dst)[2]) {
+    const int f = k / NB, nb = k % NB;
+    const int off = lo.vofs(nb) + ((f >> 1) * 32 + 16 * (f & 1)) * D;
+    dst[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt_prev + off));
+    dst[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt_prev + off + 8 * D));
+  };
+  bf16x8 kf[KA];
+#pragma unroll
+  for (int k = 0; k < KA; ++k) kf[k] = kread(k);
+  v4i16 vf[VA + 1][2];
+  if (PV) {
+#pragma unroll
+    for (int k = 0; k < VA; ++k) vread(k, vf[k]);
+  }
   float psum = 0.f;
-  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-  for (int k = 0; k < NQK; ++k) {
-    const bf16x8 a = kf[k % KR];
-    if (k + KR < NQK)
-      kf[k % KR] = *reinterpret_cast<const bf16x8*>(kt_next + ((k + KR) & 1) * 32 * D + lo.k[(k + KR) >> 1]);
-    if (k >= NQK - VA) vread(k - (NQK - VA), vf[k - (NQK - VA)]);
-    sn[k & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[k >> 1], sn[k & 1], 0, 0, 0);
-    // exp/pack share: 16 packed pairs over NQK MFMAs
+  for (int k = 0; k < NS; ++k) {
+    const bf16x8 a = kf[k % KA];
+    if (k + KA < NS) kf[k % KA] = kread(k + KA);
+    if (PV && k + VA < NS) vread(k + VA, vf[(k + VA) % (VA + 1)]);
+    sn[k / HS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[k % HS], k % HS == 0 ? f32x16{} : sn[k / HS], 0, 0, 0);
+    if (PV) {
+      const int f = k / NB;
+      const v4i16 (&v)[2] = vf[k % (VA + 1)];
+      const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
+      o[k % NB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, __builtin_bit_cast(bf16x8, pp[f >> 1][f & 1]),
+                                                          o[k % NB], 0, 0, 0);
+    }
 #pragma unroll
-    for (int pi = k * 16 / NQK; pi < (k + 1) * 16 / NQK; ++pi) {
+    for (int pi = k * 16 / NS; pi < (k + 1) * 16 / NS; ++pi) {
       const int kb = pi >> 3, c = (pi >> 2) & 1, w = pi & 3;
       const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][8 * c + 2 * w], scale_log2, nmu));
       const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][8 * c + 2 * w + 1], scale_log2, nmu));
-      P[kb][c][w] = pack_bf16x2(p0, p1);
-      psum = row_sum_add(P[kb][c][w], psum);
+      pc[kb][c][w] = pack_bf16x2(p0, p1);
+      psum = row_sum_add(pc[kb][c][w], psum);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  __builtin_amdgcn_s_setprio(0);
-  l += psum;
+  return psum;
+}
 
-  float mx = -__builtin_inff();
+// The PV MFMAs of one step on their own (the pipeline's last step).
+template <int D>
+__device__ __forceinline__ void pv_only(const uint16_t* __restrict__ vt, const LaneOffs<D>& lo,
+                                        const u32x4 (&P)[2][2], f32x16 (&o)[D / 32]) {
+  constexpr int NS = D / 8, NB = D / 32;
 #pragma unroll
-  for (int k = 0; k < NPV; ++k) {
-    if (k + VA < NPV) vread(k + VA, vf[(k + VA) & 3]);
-    const int kb = (k >> 1) & 1, c = k & 1;
-    const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vf[k & 3][0], vf[k & 3][1], 0, 1, 2, 3, 4, 5, 6, 7));
-    o[k >> 2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(bf16x8, P[kb][c]), o[k >> 2], 0, 0, 0);
-    // row-max share of the next tile: 32 values over NPV MFMAs
-#pragma unroll
-    for (int e = k * 32 / NPV; e < (k + 1) * 32 / NPV; ++e) mx = __builtin_fmaxf(mx, sn[e >> 4][e & 15]);
-    __builtin_amdgcn_sched_barrier(0);
+  for (int k = 0; k < NS; ++k) {
+    const int f = k / NB, nb = k % NB;
+    const int off = lo.vofs(nb) + ((f >> 1) * 32 + 16 * (f & 1)) * D;
+    const v4i16 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt + off));
+    const v4i16 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt + off + 8 * D));
+    const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+    o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, __builtin_bit_cast(bf16x8, P[f >> 1][f & 1]), o[nb], 0, 0, 0);
   }
-  return __builtin_fmaxf(mx, partner32(mx));
 }
 
 // ---------------------------------------------------------------------------
 // Software-pipelined loop over "plain" 64-key steps (every key visible, no mask
-// to read). Iteration i computes S = K Q^T of step i+1 on the MFMA pipe while
-// the softmax of step i runs on the VALU, then O += V P of step i. Tiles are
-// issued two steps ahead into 3-deep rings:
-//   top of iteration i: wait for K[i+1] and V[i] (K[i+2], V[i+1] may still be in
-//   flight), barrier, then issue K[i+3] into K[i]'s slot and V[i+2] into
-//   V[i-1]'s slot -- both free after the barrier.
+// to read). Iteration i runs S = K Q^T of step i+1 and O += V P of step i-1 on
+// the MFMA pipe while step i's weights are formed on the VALU. K tile j sits in
+// slot j % 4 of the K ring and V tile j in slot j % 3 of the V ring; each is
+// issued two iterations before the one that reads it:
+//   top of iteration i: wait for K[i+1] and V[i-1] (K[i+2], V[i] may still be
+//   in flight), barrier, then issue K[i+3] into K[i-1]'s slot and V[i+1] into
+//   V[i-2]'s slot -- both free after the barrier. K[i] stays in place for the
+//   whole iteration, so a rescale can form step i's scores again.
 // Steps are visited in any order the source yields; the online softmax does not
 // depend on the order. Loads past the last step re-read the first tile.
 // Src: int first(); int next(int st); int kbase(int st); a state < 0 ends the walk.
@@ -473,52 +494,115 @@ __device__ __forceinline__ void plain_steps(const TileLoader<D>& tl, uint16_t* l
                                             f32x16 (&o)[D / 32], float& m, float& l, float scale_log2) {
   constexpr int TL = Geo<D>::TILE, NIW = Geo<D>::NIW;
   uint16_t* kring = lds;
-  uint16_t* vring = lds + KR * TL;
+  uint16_t* vring = lds + KRK * TL;
   const int s0 = src.first();
   if (s0 < 0) return;
   const int kfb = src.kbase(s0);
   const int s1 = src.next(s0);
   const int s2 = s1 >= 0 ? src.next(s1) : -1;
-  tl.issue(false, kfb, kring);
-  tl.issue(true, kfb, vring);
-  tl.issue(false, s1 >= 0 ? src.kbase(s1) : kfb, kring + TL);
-  tl.issue(true, s1 >= 0 ? src.kbase(s1) : kfb, vring + TL);
-  tl.issue(false, s2 >= 0 ? src.kbase(s2) : kfb, kring + 2 * TL);
-  wait_vm<3 * NIW>();   // K[0], V[0] landed
+  tl.issue(false, kfb, kring);                                      // K[0]
+  tl.issue(false, s1 >= 0 ? src.kbase(s1) : kfb, kring + TL);       // K[1]
+  tl.issue(true, kfb, vring);                                       // V[0]
+  tl.issue(false, s2 >= 0 ? src.kbase(s2) : kfb, kring + 2 * TL);   // K[2]
+  wait_vm<3 * NIW>();   // K[0] landed
   bare_barrier();
   int t1 = s1, t2 = s2;   // steps i+1 and i+2
-  // Iteration i uses ring slots IK = (i+1) % 3 for K[i+1] and IV = i % 3 for
-  // V[i]; six iterations cover both the 3-slot rings and the two S buffers, so
-  // the slots are compile-time constants and fold into the LDS offsets.
-  auto iter = [&](auto ikc, auto ivc, const f32x16 (&sc)[2], float mxc, f32x16 (&sn)[2],
-                  float& mxn) -> bool {
-    constexpr int IK = decltype(ikc)::value, IV = decltype(ivc)::value;
-    constexpr int K3 = IK == 0 ? KR - 1 : IK - 1;      // K[i]'s slot
-    constexpr int V2 = IV == 0 ? KR - 1 : IV - 1;      // V[i-1]'s slot
-    raise_max<D>(mxc, scale_log2, o, m, l);
-    wait_vm<2 * NIW>();   // K[i+1], V[i] landed
+  int tail_slot = 0;      // V slot of the last step
+  bool tail_a = false;    // the last step's weights are in pa (else pb)
+  // Iteration i, given the ring slots of K[i] (i % 4) and V[i] (i % 3) either as
+  // compile-time constants (folded into the LDS offsets) or as run-time values.
+  auto iter = [&](auto pvc, auto kcc, auto vcc, const f32x16 (&sc)[2], f32x16 (&sn)[2],
+                  const u32x4 (&pp)[2][2], u32x4 (&pc)[2][2], auto pc_is_a) -> bool {
+    constexpr bool HAS_PV = decltype(pvc)::value;
+    const int kc = kcc, vc = vcc;
+    const int kn = (kc + 1) & 3;                   // K[i+1]
+    const int kf = (kc + 3) & 3;                   // K[i-1]'s slot, receives K[i+3]
+    const int vp = vc == 0 ? 2 : vc - 1;           // V[i-1]
+    const int vn = vc == 2 ? 0 : vc + 1;           // V[i-2]'s slot, receives V[i+1]
+    wait_vm<2 * NIW>();   // K[i+1], V[i-1] landed
     bare_barrier();
     const int t3 = t2 >= 0 ? src.next(t2) : -1;
-    tl.issue(false, t3 >= 0 ? src.kbase(t3) : kfb, kring + K3 * TL);
-    tl.issue(true, t2 >= 0 ? src.kbase(t2) : kfb, vring + V2 * TL);
-    mxn = fused_step<D>(kring + IK * TL, vring + IV * TL, lo, qf, sc, sn, o, m, l, scale_log2);
-    if (t1 < 0) return false;
+    tl.issue(false, t3 >= 0 ? src.kbase(t3) : kfb, kring + kf * TL);
+    tl.issue(true, t1 >= 0 ? src.kbase(t1) : kfb, vring + vn * TL);
+    float psum = pipe_step<D, HAS_PV>(kring + kn * TL, vring + vp * TL, lo, qf, sc, sn, pp, pc, o, m, scale_log2);
+    if (__builtin_expect(__any(psum > PSUM_LIMIT), 0)) {
+      // a row's weights outgrew the bound: raise m to the tile's max, rescale
+      // what has been accumulated, and form the tile's weights again from
+      // scores recomputed out of K[i]
+      f32x16 sr[2];
+      qk_tile<D>(kring + kc * TL, lo, qf, sr);
+      const float m_new = __builtin_fmaxf(m, row_max(sr) * scale_log2);
+      const float alpha = (m == -__builtin_inff()) ? 1.f : exp2f(m - m_new);
+#pragma unroll
+      for (int nb = 0; nb < D / 32; ++nb) o[nb] *= alpha;
+      l *= alpha;
+      m = m_new;
+      psum = 0.f;
+      exp_pack(sr, m, scale_log2, pc, psum);
+    }
+    l += psum;
+    if (t1 < 0) {   // step i was the last
+      tail_slot = vc;
+      tail_a = decltype(pc_is_a)::value;
+      return false;
+    }
     t1 = t2;
     t2 = t3;
     return true;
   };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
+  using PV0 = std::integral_constant<bool, false>;
+  using PV1 = std::integral_constant<bool, true>;
+  using A = std::integral_constant<bool, true>;
+  using B = std::integral_constant<bool, false>;
   f32x16 sa[2], sb[2];
-  float mxa, mxb;
+  u32x4 pa[2][2], pb[2][2];
   qk_tile<D>(kring, lo, qf, sa);
-  mxa = row_max(sa);
-  while (iter(I1{}, I0{}, sa, mxa, sb, mxb) && iter(I2{}, I1{}, sb, mxb, sa, mxa) &&
-         iter(I0{}, I2{}, sa, mxa, sb, mxb) && iter(I1{}, I0{}, sb, mxb, sa, mxa) &&
-         iter(I2{}, I1{}, sa, mxa, sb, mxb) && iter(I0{}, I2{}, sb, mxb, sa, mxa)) {
+  {
+    const float m_new = __builtin_fmaxf(m, row_max(sa) * scale_log2);
+    const float alpha = (m == -__builtin_inff()) ? 1.f : exp2f(m - m_new);
+#pragma unroll
+    for (int nb = 0; nb < D / 32; ++nb) o[nb] *= alpha;
+    l *= alpha;
+    m = m_new;
   }
+  // even i: S[i] in sa, weights into pa; odd i: S[i] in sb, weights into pb
+  if constexpr (D == 128) {
+    // twelve iterations per pass cover the 4- and 3-slot rings and both buffers
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    using C2 = std::integral_constant<int, 2>;
+    using C3 = std::integral_constant<int, 3>;
+    if (iter(PV0{}, C0{}, C0{}, sa, sb, pb, pa, A{})) {
+      while (iter(PV1{}, C1{}, C1{}, sb, sa, pa, pb, B{}) && iter(PV1{}, C2{}, C2{}, sa, sb, pb, pa, A{}) &&
+             iter(PV1{}, C3{}, C0{}, sb, sa, pa, pb, B{}) && iter(PV1{}, C0{}, C1{}, sa, sb, pb, pa, A{}) &&
+             iter(PV1{}, C1{}, C2{}, sb, sa, pa, pb, B{}) && iter(PV1{}, C2{}, C0{}, sa, sb, pb, pa, A{}) &&
+             iter(PV1{}, C3{}, C1{}, sb, sa, pa, pb, B{}) && iter(PV1{}, C0{}, C2{}, sa, sb, pb, pa, A{}) &&
+             iter(PV1{}, C1{}, C0{}, sb, sa, pa, pb, B{}) && iter(PV1{}, C2{}, C1{}, sa, sb, pb, pa, A{}) &&
+             iter(PV1{}, C3{}, C2{}, sb, sa, pa, pb, B{}) && iter(PV1{}, C0{}, C0{}, sa, sb, pb, pa, A{})) {
+      }
+    }
+  } else {
+    // two iterations per pass, run-time ring slots (a full unroll spills here)
+    int kc = 0, vc = 0;
+    auto adv = [&]() {
+      kc = (kc + 1) & 3;
+      vc = vc == 2 ? 0 : vc + 1;
+      return true;
+    };
+    if (iter(PV0{}, kc, vc, sa, sb, pb, pa, A{}) && adv()) {
+      while (iter(PV1{}, kc, vc, sb, sa, pa, pb, B{}) && adv() && iter(PV1{}, kc, vc, sa, sb, pb, pa, A{}) &&
+             adv()) {
+      }
+    }
+  }
+  // the last step's PV, once its V tile has landed
   wait_vm<0>();
+  bare_barrier();
+  const uint16_t* vt = vring + tail_slot * TL;
+  if (tail_a)
+    pv_only<D>(vt, lo, pa, o);
+  else
+    pv_only<D>(vt, lo, pb, o);
   __syncthreads();   // LDS free for whatever follows
 }
 
@@ -562,7 +646,7 @@ __device__ __forceinline__ void load_q(const uint16_t* __restrict__ Q, int n_q, 
 // write O (normalised) or the split partials for this wave's 32 rows
 template <int D>
 __device__ __forceinline__ void store_rows(float* __restrict__ dst, const f32x16 (&o)[D / 32], float scale) {
-  const int h = __lane_id() >> 5;
+  const int h = fresh_lane_id() >> 5;
 #pragma unroll
   for (int nb = 0; nb < D / 32; ++nb) {
 #pragma unroll
@@ -598,7 +682,7 @@ attn_dense_kernel(const uint16_t* __restrict__ Q, int C, int n_q, const uint16_t
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   __shared__ int s_lo, s_hi;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, n = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, n = lane & 31;
   const int Hg = 1 << hg_log2;
   const int R = 256 >> hg_log2;
   const int group = n_q / n_kv;
@@ -664,18 +748,6 @@ attn_dense_kernel(const uint16_t* __restrict__ Q, int C, int n_q, const uint16_t
   for (int nb = 0; nb < D / 32; ++nb) o[nb] = f32x16{};
   float m = -__builtin_inff(), l = 0.f;
 
-  StepCtx cx;
-  cx.scale_log2 = scale_log2;
-  if (causal_q0 >= 0) {
-    cx.mrow = mask;   // the per-key mask (or null)
-    cx.qpos = causal_q0 + qrow;
-  } else {
-    cx.mrow = qvalid ? mask + (size_t)qrow * mask_ld : nullptr;
-    cx.qpos = 0;
-  }
-  cx.mask_vec = mask_vec != 0;
-  cx.selbits = nullptr; cx.jlimit = 0; cx.pool_bias = 0.f;
-
   const LaneOffs<D> lo = lane_offsets<D>();
   TileLoader<D> tl;
   tl.init(K, V, T, n_kv, g);
@@ -683,13 +755,30 @@ attn_dense_kernel(const uint16_t* __restrict__ Q, int C, int n_q, const uint16_t
   // 1) plain steps: tiles flagged ZERO whose 64 keys all lie below T
   plain_steps<D>(tl, lds, DenseSrc{a, b, T, frow}, lo, qf, o, m, l, scale_log2);
 
+  // lane-derived values for what follows, formed afresh (see fresh_lane_id)
+  const int lane2 = fresh_lane_id();
+  const int qrow2 = qt * R + (wave % wph) * 32 + (lane2 & 31);
+  const bool qvalid2 = qrow2 < C;
+  const LaneOffs<D> lo2 = lane_offsets<D>();
+  StepCtx cx;
+  cx.scale_log2 = scale_log2;
+  if (causal_q0 >= 0) {
+    cx.mrow = mask;   // the per-key mask (or null)
+    cx.qpos = causal_q0 + qrow2;
+  } else {
+    cx.mrow = qvalid2 ? mask + (size_t)qrow2 * mask_ld : nullptr;
+    cx.qpos = 0;
+  }
+  cx.mask_vec = mask_vec != 0;
+  cx.selbits = nullptr; cx.jlimit = 0; cx.pool_bias = 0.f;
+
   // 2) the remaining steps: mask tiles (MIXED) and a ragged last step. The next
   // one is found 64 steps at a time by a wave-wide ballot over the LDS flags
   // (every wave forms the same mask, so the barriers inside the steps stay
   // uniform); the walk between them carries nothing but the step index.
   auto next_special = [&](int st) -> int {
     for (int base = st; base < b; base += 64) {
-      const int sl = base + lane;
+      const int sl = base + lane2;
       const uint8_t fl = sl < b ? frow[sl >> 1] : TILE_DROPPED;
       const uint64_t hit = __ballot(!(fl == TILE_DROPPED || (fl == TILE_ZERO && (sl + 1) * BN <= T)));
       if (hit != 0) return base + __builtin_ctzll(hit);
@@ -699,27 +788,27 @@ attn_dense_kernel(const uint16_t* __restrict__ Q, int C, int n_q, const uint16_t
   for (int st = next_special(a); st < b; st = next_special(st + 1)) {
     const uint8_t f = frow[st >> 1];
     tl.issue(false, st * BN, lds);
-    tl.issue(true, st * BN, lds + KR * Geo<D>::TILE);
+    tl.issue(true, st * BN, lds + KRK * Geo<D>::TILE);
     wait_vm<0>();
     __syncthreads();
     cx.key0 = st * BN;
     cx.kvalid = min(BN, T - st * BN);
     if (f == TILE_MIXED && causal_q0 >= 0)
-      attn_step<D, MODE_CAUSAL_K, true>(lds, lds + KR * Geo<D>::TILE, nullptr, nullptr, lo, qf, o, m, l, cx);
+      attn_step<D, MODE_CAUSAL_K, true>(lds, lds + KRK * Geo<D>::TILE, nullptr, nullptr, lo2, qf, o, m, l, cx);
     else if (f == TILE_MIXED)
-      attn_step<D, MODE_GMASK, true>(lds, lds + KR * Geo<D>::TILE, nullptr, nullptr, lo, qf, o, m, l, cx);
+      attn_step<D, MODE_GMASK, true>(lds, lds + KRK * Geo<D>::TILE, nullptr, nullptr, lo2, qf, o, m, l, cx);
     else
-      attn_step<D, MODE_PLAIN, true>(lds, lds + KR * Geo<D>::TILE, nullptr, nullptr, lo, qf, o, m, l, cx);
+      attn_step<D, MODE_PLAIN, true>(lds, lds + KRK * Geo<D>::TILE, nullptr, nullptr, lo2, qf, o, m, l, cx);
     __syncthreads();
   }
 
   const float lt = l + partner32(l);
-  if (!qvalid) return;
-  const size_t row = (size_t)qrow * n_q + head;
+  if (!qvalid2) return;
+  const size_t row = (size_t)qrow2 * n_q + head;
   if (SPLIT) {
     const size_t rows = (size_t)C * n_q;
     store_rows<D>(part_o + ((size_t)split * rows + row) * D, o, 1.f);
-    if (lane < 32) {
+    if (lane2 < 32) {
       float2* ml = reinterpret_cast<float2*>(part_ml + ((size_t)split * rows + row) * 2);
       *ml = make_float2(m == -__builtin_inff() ? 0.f : m, lt);
     }
@@ -827,15 +916,6 @@ attn_blocksparse_kernel(const uint16_t* __restrict__ Q, int C, int q_start, int 
   for (int q = 0; q < D / 32; ++q) o[q] = f32x16{};
   float m = -__builtin_inff(), l = 0.f;
 
-  StepCtx cx;
-  cx.scale_log2 = scale_log2;
-  cx.mrow = nullptr;
-  cx.mask_vec = false;
-  cx.qpos = qpos;
-  cx.selbits = selbits;
-  cx.jlimit = j;
-  cx.pool_bias = __builtin_log2f((float)BLK);
-
   const LaneOffs<D> lo = lane_offsets<D>();
   TileLoader<D> tl;
   tl.init(K, V, T, n_kv, g);
@@ -843,9 +923,22 @@ attn_blocksparse_kernel(const uint16_t* __restrict__ Q, int C, int q_start, int 
   // exact steps: the two 64-key halves of every selected block but the last
   // (the diagonal), which lie fully below the query block
   plain_steps<D>(tl, lds, SparseSrc{sl_s, 2 * (cnt - 1)}, lo, qf, o, m, l, scale_log2);
+
+  // lane-derived values for what follows, formed afresh (see fresh_lane_id)
+  const int qpos2 = j * BLK + (wave & 3) * 32 + (fresh_lane_id() & 31);
+  const bool qvalid2 = qpos2 >= q_start && qpos2 < q_start + C;
+  const LaneOffs<D> lo2 = lane_offsets<D>();
+  StepCtx cx;
+  cx.scale_log2 = scale_log2;
+  cx.mrow = nullptr;
+  cx.mask_vec = false;
+  cx.qpos = qpos2;
+  cx.selbits = selbits;
+  cx.jlimit = j;
+  cx.pool_bias = __builtin_log2f((float)BLK);
   // the diagonal block, causally by position (its keys may end before 128: ragged T)
   uint16_t* kt = lds;
-  uint16_t* vt = lds + KR * Geo<D>::TILE;
+  uint16_t* vt = lds + KRK * Geo<D>::TILE;
   for (int e = 0; e < 2; ++e) {
     const int kbase = j * BLK + e * BN;
     if (kbase >= T) break;
@@ -855,14 +948,14 @@ attn_blocksparse_kernel(const uint16_t* __restrict__ Q, int C, int q_start, int 
     __syncthreads();
     cx.key0 = kbase;
     cx.kvalid = min(BN, T - kbase);
-    attn_step<D, MODE_CAUSAL, true>(kt, vt, nullptr, nullptr, lo, qf, o, m, l, cx);
+    attn_step<D, MODE_CAUSAL, true>(kt, vt, nullptr, nullptr, lo2, qf, o, m, l, cx);
     __syncthreads();
   }
 
   // pooled rows of the unselected visible blocks b < j, 64 per step
   uint16_t* khi = lds;
   uint16_t* klo = lds + Geo<D>::TILE;
-  uint16_t* vhi = lds + KR * Geo<D>::TILE;
+  uint16_t* vhi = lds + KRK * Geo<D>::TILE;
   uint16_t* vlo = vhi + Geo<D>::TILE;
   const float* kpg = Kp + (size_t)g * pool_ld * D;
   const float* vpg = Vp + (size_t)g * pool_ld * D;
@@ -872,13 +965,13 @@ attn_blocksparse_kernel(const uint16_t* __restrict__ Q, int C, int q_start, int 
     __syncthreads();
     cx.key0 = pbase;
     cx.kvalid = min(BN, j - pbase);
-    attn_step<D, MODE_POOLED, true>(khi, vhi, klo, vlo, lo, qf, o, m, l, cx);
+    attn_step<D, MODE_POOLED, true>(khi, vhi, klo, vlo, lo2, qf, o, m, l, cx);
     __syncthreads();
   }
 
   const float lt = l + partner32(l);
-  if (!qvalid || !storer) return;
-  store_rows<D>(O + ((size_t)qrow * n_q + head) * D, o, lt > 0.f ? 1.f / lt : 0.f);
+  if (!qvalid2 || !storer) return;
+  store_rows<D>(O + ((size_t)(qpos2 - q_start) * n_q + head) * D, o, lt > 0.f ? 1.f / lt : 0.f);
 }
 
 // ---------------------------------------------------------------------------
