@@ -241,6 +241,36 @@ def test_dense_edge_cases(lp, C, T, n_q, n_kv, d, kind, ld):
         assert np.all(got[0] == 0.0)
 
 
+@pytest.mark.parametrize("kind", ["spike", "rising", "falling"])
+def test_dense_lazy_rescale(lp, kind):
+    """The step loop forms a tile's weights against the running max as it stands
+    and raises it only when a row's weights for the tile sum past its bound:
+    a late tile whose logits overflow exp2 against the old max ("spike"),
+    logits that keep growing ("rising", several raises), and a first tile far
+    above the rest ("falling", later weights underflow, no raise)."""
+    rng = np.random.default_rng({"spike": 1, "rising": 2, "falling": 3}[kind])
+    C, T, n_q, n_kv, d = 256, 4096, 4, 1, 128
+    u = rng.standard_normal(d).astype(np.float32)
+    q = rng.standard_normal((C, n_q, d)).astype(np.float32) + u
+    k = rng.standard_normal((T, n_kv, d)).astype(np.float32)
+    if kind == "spike":
+        # q.k near 10 |u|^2: ~160 above the rest in log2 units, nearly even across
+        # the tile so that many keys share the weight (bf16 weights, as in the method)
+        k[3000:3064] = 10.0 * u + 0.25 * k[3000:3064]
+    elif kind == "rising":
+        k += (np.arange(T, dtype=np.float32) / T * 3.0)[:, None, None] * u
+    else:
+        k[:64] += 6.0 * u
+    v = rng.standard_normal((T, n_kv, d)).astype(np.float32)
+    q, k, v = bf16_bits(q), bf16_bits(k), bf16_bits(v)
+    mask = np.zeros((C, T), dtype=np.float16)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    say("dense lazy rescale", kind)
+    got = gpu_dense(lp, q, k, v, mask, scale)
+    want = dense_ref(f64(q), f64(k), f64(v), mask, scale)
+    assert_close(got, want, f"lazy rescale {kind}")
+
+
 def test_dense_is_deterministic(lp):
     w = make_workload("gqa4k")
     q_start, C, T, q, k, v, mask = w.chunk(1)
