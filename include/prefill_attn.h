@@ -3,7 +3,8 @@
  *
  * Four operations make up the path:
  *   prefill_attn_dense        chunked prefill attention under an arbitrary additive mask
- *                             (prefill_attn_dense_causal: causal by position, no mask buffer)
+ *                             (prefill_attn_dense_causal: causal by position, no mask buffer;
+ *                              prefill_attn_dense_bits: a keep/drop mask packed one bit per key)
  *   build_pooled_index        mean-pooled key/value blocks
  *   select_blocks             alpha-threshold block selection plus the local diagonal
  *   prefill_attn_blocksparse  exact attention on selected blocks + pooled correction
@@ -95,6 +96,27 @@ int prefill_attn_dense(const uint16_t* Q, int C, int n_q,
 
 /* Workspace bytes prefill_attn_dense needs for these sizes (0 for invalid sizes). */
 size_t prefill_attn_dense_workspace(int C, int T, int n_q, int n_kv, int d);
+
+/*
+ * prefill_attn_dense_bits -- prefill_attn_dense with a keep/drop mask packed one
+ * bit per (row, key) instead of fp16 (16x less mask traffic).
+ * ("ANE Prefill Research", What worked, item 2: a -30000 entry drops a key, a 0
+ * entry keeps it; the compact mask form of a 0 / -30000 mask.)
+ *
+ *   mask_bits  uint32 [C][bits_ld]   bit (t % 32) of word t / 32 of row i set: key t
+ *                                    kept (additive 0); clear: key t dropped (as -30000).
+ *                                    Bits of keys >= T are ignored.
+ *
+ * Equals prefill_attn_dense with mask[i][t] = bit ? 0 : -30000 (bit-for-bit the
+ * same arithmetic). Requires bits_ld >= ceil(T / 32) (words); other requirements
+ * and the workspace (prefill_attn_dense_workspace) as prefill_attn_dense.
+ * Errors: PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP.
+ */
+int prefill_attn_dense_bits(const uint16_t* Q, int C, int n_q,
+                            const uint16_t* K, const uint16_t* V, int T, int n_kv, int d,
+                            const uint32_t* mask_bits, int64_t bits_ld,
+                            float scale, float* O,
+                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * prefill_attn_dense_causal -- prefill_attn_dense for a causal chunk without a

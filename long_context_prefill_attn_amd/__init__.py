@@ -22,7 +22,7 @@ import torch
 
 from ._lib import PrefillAttnError, check, lib  # noqa: F401
 
-__all__ = ["prefill_attn_dense", "prefill_attn_dense_causal", "prefill_attn_dense_workspace",
+__all__ = ["prefill_attn_dense", "prefill_attn_dense_bits", "prefill_attn_dense_causal", "prefill_attn_dense_workspace",
            "build_pooled_index",
            "select_blocks", "prefill_attn_blocksparse", "fold_keep_mask", "PrefillAttnError", "timing"]
 
@@ -68,6 +68,34 @@ def prefill_attn_dense(Q, K, V, mask, scale: float, O=None, workspace=None):
                                    mask.data_ptr(), mask.stride(0), float(scale), O.data_ptr(),
                                    workspace.data_ptr(), workspace.numel(), _stream()),
           "prefill_attn_dense")
+    return O
+
+
+def prefill_attn_dense_bits(Q, K, V, mask_bits, scale: float, O=None, workspace=None):
+    """Dense chunk under a bit-packed keep mask.
+
+    Q bf16 [C][n_q][d]; K, V bf16 [T][n_kv][d]; mask_bits int32 [C][ld >= ceil(T/32)]
+    (bit t%32 of word t//32 set = key t kept, clear = dropped) -> O fp32 [C][n_q][d]."""
+    _req(Q, "Q", torch.bfloat16, 3)
+    _req(K, "K", torch.bfloat16, 3)
+    _req(V, "V", torch.bfloat16, 3)
+    _req(mask_bits, "mask_bits", torch.int32, 2)
+    C, n_q, d = Q.shape
+    T, n_kv, _ = K.shape
+    if V.shape != K.shape or K.shape[2] != d or mask_bits.shape[0] != C:
+        raise ValueError("inconsistent shapes")
+    if mask_bits.shape[1] * 32 < T:
+        raise ValueError(f"mask_bits needs at least {(T + 31) // 32} words per row")
+    if O is None:
+        O = torch.empty((C, n_q, d), dtype=torch.float32, device=Q.device)
+    _req(O, "O", torch.float32, 3)
+    need = prefill_attn_dense_workspace(C, T, n_q, n_kv, d)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=Q.device)
+    check(lib().prefill_attn_dense_bits(Q.data_ptr(), C, n_q, K.data_ptr(), V.data_ptr(), T, n_kv, d,
+                                        mask_bits.data_ptr(), mask_bits.stride(0), float(scale),
+                                        O.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream()),
+          "prefill_attn_dense_bits")
     return O
 
 

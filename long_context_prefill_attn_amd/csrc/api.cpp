@@ -146,6 +146,44 @@ int prefill_attn_dense(const uint16_t* Q, int C, int n_q, const uint16_t* K, con
   return PA_OK;
 }
 
+int prefill_attn_dense_bits(const uint16_t* Q, int C, int n_q, const uint16_t* K, const uint16_t* V,
+                            int T, int n_kv, int d, const uint32_t* mask_bits, int64_t bits_ld,
+                            float scale, float* O, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(mask_bits) || !aligned16(O))
+    return PA_EINVAL;
+  if (C < 1 || T < 1 || n_q < 1 || n_kv < 1 || n_q % n_kv != 0) return PA_EINVAL;
+  if (bits_ld < ((int64_t)T + 31) / 32 || !good_scale(scale)) return PA_EINVAL;
+  if (d != 64 && d != 128) return PA_EUNSUPPORTED;
+  if (T > (1 << 22)) return PA_EUNSUPPORTED;   // the per-tile flag row must fit in LDS
+  const pa::DensePlan plan = pa::plan_dense(C, T, n_q, n_kv, d);
+  if ((long long)plan.n_qt * n_q * plan.splits >= (1LL << 31)) return PA_EUNSUPPORTED;
+  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
+      workspace_bytes < plan.total_bytes)
+    return PA_EWORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* flags = static_cast<uint8_t*>(workspace);
+  float* part_o = plan.splits > 1 ? reinterpret_cast<float*>(flags + plan.flags_bytes) : nullptr;
+  float* part_ml =
+      plan.splits > 1 ? reinterpret_cast<float*>(flags + plan.flags_bytes + plan.part_o_bytes) : nullptr;
+  hipError_t e = timed("mask_classify", s, [&] {
+    return pa::launch_mask_classify_bits(mask_bits, bits_ld, C, T, flags, s);
+  });
+  if (e != hipSuccess) return hip_status(e);
+  e = timed("attn_dense", s, [&] {
+    return pa::launch_attn_dense(Q, C, n_q, K, V, T, n_kv, d, reinterpret_cast<const uint16_t*>(mask_bits),
+                                 bits_ld, scale, O, plan, flags, part_o, part_ml, -1, s, true);
+  });
+  if (e != hipSuccess) return hip_status(e);
+  if (plan.splits > 1) {
+    e = timed("attn_combine", s, [&] {
+      return pa::launch_attn_combine(C, n_q, d, plan.splits, part_o, part_ml, O, s);
+    });
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return PA_OK;
+}
+
 int prefill_attn_dense_causal(const uint16_t* Q, int C, int q_start, int n_q, const uint16_t* K,
                               const uint16_t* V, int T, int n_kv, int d, const uint16_t* kmask,
                               float scale, float* O, void* workspace, size_t workspace_bytes,

@@ -52,7 +52,9 @@ constexpr float SLACK = 8.0f;   // lazy-rescale threshold in log2 units
 #define LDS_AS __attribute__((address_space(3)))
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
-enum { MODE_PLAIN = 0, MODE_GMASK = 1, MODE_CAUSAL = 2, MODE_POOLED = 3, MODE_CAUSAL_K = 4 };
+enum { MODE_PLAIN = 0, MODE_GMASK = 1, MODE_CAUSAL = 2, MODE_POOLED = 3, MODE_CAUSAL_K = 4, MODE_GBITS = 5 };
+// how the dense kernel reads its mask: fp16 (8-byte loads when aligned) or bit-packed
+enum { MASK_F16 = 0, MASK_F16_VEC = 1, MASK_BITS = 2 };
 
 // LDS tiles are row-major [64 keys][D] bf16 with no padding; the 16-byte chunk c
 // of row r sits at chunk position c ^ swz(r). The swizzle spreads the 8 rows a
@@ -206,6 +208,7 @@ struct StepCtx {
   float scale_log2;
   int kvalid;                        // keys of the step inside [0, T)
   const uint16_t* __restrict__ mrow; // MODE_GMASK: mask row of this lane's query (may be null)
+  const uint32_t* __restrict__ brow; // MODE_GBITS: bit-mask row of this lane's query (may be null)
   bool mask_vec;                     // MODE_GMASK: 8-byte aligned mask rows
   int key0;                          // absolute key (or pooled block) index of the step's first key
   int qpos;                          // MODE_CAUSAL: absolute position of this lane's query
@@ -251,6 +254,8 @@ __device__ __forceinline__ void attn_step(const uint16_t* __restrict__ kt, const
   float mx = -__builtin_inff();
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
+    uint32_t mw = ~0u;   // MODE_GBITS: the row's keep bits for keys key0 + 32kb .. +31
+    if (MODE == MODE_GBITS && cx.brow != nullptr && 32 * kb < cx.kvalid) mw = cx.brow[(cx.key0 >> 5) + kb];
     uint16_t mv[16];
     if (MODE == MODE_GMASK) {
 #pragma unroll
@@ -275,6 +280,8 @@ __device__ __forceinline__ void attn_step(const uint16_t* __restrict__ kt, const
       if (MODE == MODE_GMASK) {
         v = f16_dropped(mv[i]) ? -__builtin_inff()
                                : __builtin_fmaf((float)__builtin_bit_cast(_Float16, mv[i]), LOG2E, v);
+      } else if (MODE == MODE_GBITS) {
+        if (!((mw >> (kk - 32 * kb)) & 1u)) v = -__builtin_inff();
       } else if (MODE == MODE_CAUSAL) {
         if (cx.key0 + kk > cx.qpos) v = -__builtin_inff();
       } else if (MODE == MODE_CAUSAL_K) {
@@ -677,7 +684,7 @@ attn_dense_kernel(const uint16_t* __restrict__ Q, int C, int n_q, const uint16_t
                   const uint16_t* __restrict__ V, int T, int n_kv, const uint16_t* __restrict__ mask,
                   int64_t mask_ld, float scale_log2, float* __restrict__ O,
                   const uint8_t* __restrict__ flags, int n_qt, int n_ktile, int splits,
-                  float* __restrict__ part_o, float* __restrict__ part_ml, int mask_vec, int hg_log2,
+                  float* __restrict__ part_o, float* __restrict__ part_ml, int mask_mode, int hg_log2,
                   int causal_q0) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   __shared__ int s_lo, s_hi;
@@ -762,14 +769,19 @@ attn_dense_kernel(const uint16_t* __restrict__ Q, int C, int n_q, const uint16_t
   const LaneOffs<D> lo2 = lane_offsets<D>();
   StepCtx cx;
   cx.scale_log2 = scale_log2;
+  cx.brow = nullptr;
   if (causal_q0 >= 0) {
     cx.mrow = mask;   // the per-key mask (or null)
     cx.qpos = causal_q0 + qrow2;
+  } else if (mask_mode == MASK_BITS) {
+    cx.mrow = nullptr;
+    cx.brow = qvalid2 ? reinterpret_cast<const uint32_t*>(mask) + (size_t)qrow2 * mask_ld : nullptr;
+    cx.qpos = 0;
   } else {
     cx.mrow = qvalid2 ? mask + (size_t)qrow2 * mask_ld : nullptr;
     cx.qpos = 0;
   }
-  cx.mask_vec = mask_vec != 0;
+  cx.mask_vec = mask_mode == MASK_F16_VEC;
   cx.selbits = nullptr; cx.jlimit = 0; cx.pool_bias = 0.f;
 
   // 2) the remaining steps: mask tiles (MIXED) and a ragged last step. The next
@@ -795,6 +807,8 @@ attn_dense_kernel(const uint16_t* __restrict__ Q, int C, int n_q, const uint16_t
     cx.kvalid = min(BN, T - st * BN);
     if (f == TILE_MIXED && causal_q0 >= 0)
       attn_step<D, MODE_CAUSAL_K, true>(lds, lds + KRK * Geo<D>::TILE, nullptr, nullptr, lo2, qf, o, m, l, cx);
+    else if (f == TILE_MIXED && mask_mode == MASK_BITS)
+      attn_step<D, MODE_GBITS, true>(lds, lds + KRK * Geo<D>::TILE, nullptr, nullptr, lo2, qf, o, m, l, cx);
     else if (f == TILE_MIXED)
       attn_step<D, MODE_GMASK, true>(lds, lds + KRK * Geo<D>::TILE, nullptr, nullptr, lo2, qf, o, m, l, cx);
     else
@@ -931,6 +945,7 @@ attn_blocksparse_kernel(const uint16_t* __restrict__ Q, int C, int q_start, int 
   StepCtx cx;
   cx.scale_log2 = scale_log2;
   cx.mrow = nullptr;
+  cx.brow = nullptr;
   cx.mask_vec = false;
   cx.qpos = qpos2;
   cx.selbits = selbits;
@@ -1028,23 +1043,24 @@ template <int D>
 static hipError_t dense_impl(const uint16_t* Q, int C, int n_q, const uint16_t* K, const uint16_t* V,
                              int T, int n_kv, const uint16_t* mask, int64_t mask_ld, float scale,
                              float* O, const DensePlan& p, const uint8_t* flags, float* part_o,
-                             float* part_ml, int causal_q0, hipStream_t stream) {
+                             float* part_ml, int causal_q0, hipStream_t stream, bool mask_bits) {
   const float sl2 = scale * LOG2E;
   const int grid = p.n_qt * (n_q >> p.hg_log2) * p.splits;
   const size_t lds = Geo<D>::LDS_BYTES + ((p.n_ktile + 15) & ~15);   // rings + flag row
-  const int mask_vec = (mask_ld % 4 == 0) && (reinterpret_cast<uintptr_t>(mask) % 8 == 0);
+  const bool vec = (mask_ld % 4 == 0) && (reinterpret_cast<uintptr_t>(mask) % 8 == 0);
+  const int mask_mode = mask_bits ? MASK_BITS : vec ? MASK_F16_VEC : MASK_F16;
   if (p.splits > 1) {
     hipFuncSetAttribute((const void*)attn_dense_kernel<D, true>,
                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     hipLaunchKernelGGL((attn_dense_kernel<D, true>), dim3(grid), dim3(NT), lds, stream, Q, C, n_q, K, V,
                        T, n_kv, mask, mask_ld, sl2, O, flags, p.n_qt, p.n_ktile, p.splits, part_o,
-                       part_ml, mask_vec, p.hg_log2, causal_q0);
+                       part_ml, mask_mode, p.hg_log2, causal_q0);
   } else {
     hipFuncSetAttribute((const void*)attn_dense_kernel<D, false>,
                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     hipLaunchKernelGGL((attn_dense_kernel<D, false>), dim3(grid), dim3(NT), lds, stream, Q, C, n_q, K,
                        V, T, n_kv, mask, mask_ld, sl2, O, flags, p.n_qt, p.n_ktile, 1, part_o,
-                       part_ml, mask_vec, p.hg_log2, causal_q0);
+                       part_ml, mask_mode, p.hg_log2, causal_q0);
   }
   return hipGetLastError();
 }
@@ -1052,12 +1068,13 @@ static hipError_t dense_impl(const uint16_t* Q, int C, int n_q, const uint16_t* 
 hipError_t launch_attn_dense(const uint16_t* Q, int C, int n_q, const uint16_t* K, const uint16_t* V,
                              int T, int n_kv, int d, const uint16_t* mask, int64_t mask_ld,
                              float scale, float* O, const DensePlan& plan, const uint8_t* flags,
-                             float* part_o, float* part_ml, int causal_q0, hipStream_t stream) {
+                             float* part_o, float* part_ml, int causal_q0, hipStream_t stream,
+                             bool mask_bits) {
   if (d == 128)
     return dense_impl<128>(Q, C, n_q, K, V, T, n_kv, mask, mask_ld, scale, O, plan, flags, part_o,
-                           part_ml, causal_q0, stream);
+                           part_ml, causal_q0, stream, mask_bits);
   return dense_impl<64>(Q, C, n_q, K, V, T, n_kv, mask, mask_ld, scale, O, plan, flags, part_o,
-                        part_ml, causal_q0, stream);
+                        part_ml, causal_q0, stream, mask_bits);
 }
 
 template <int D>

@@ -64,6 +64,10 @@ hipError_t launch_select(const uint16_t* Q, int C, int q_start, int n_q, int n_k
 hipError_t launch_mask_classify(const uint16_t* mask, int64_t mask_ld, int C, int T,
                                 uint8_t* flags, hipStream_t stream);
 
+// Tile flags of a bit-packed mask: bit t % 32 of word t / 32 of a row set = key t kept.
+hipError_t launch_mask_classify_bits(const uint32_t* bits, int64_t bits_ld, int C, int T,
+                                     uint8_t* flags, hipStream_t stream);
+
 hipError_t launch_fold_keep(const int32_t* keep_idx, int64_t keep_ld, const int32_t* keep_cnt, int C,
                             int q_start, int T, int width, int recent, uint16_t* mask, int64_t mask_ld,
                             hipStream_t stream);
@@ -78,10 +82,13 @@ struct DensePlan {
 };
 DensePlan plan_dense(int C, int T, int n_q, int n_kv, int d);
 
+// mask: fp16 [C][mask_ld] (mask_bits false) or, with mask_bits true, uint32 words
+// [C][mask_ld] of a bit-packed mask (the pointer is reinterpreted).
 hipError_t launch_attn_dense(const uint16_t* Q, int C, int n_q, const uint16_t* K, const uint16_t* V,
                              int T, int n_kv, int d, const uint16_t* mask, int64_t mask_ld,
                              float scale, float* O, const DensePlan& plan, const uint8_t* flags,
-                             float* part_o, float* part_ml, int causal_q0, hipStream_t stream);
+                             float* part_o, float* part_ml, int causal_q0, hipStream_t stream,
+                             bool mask_bits = false);
 
 hipError_t launch_attn_combine(int C, int n_q, int d, int splits, const float* part_o,
                                const float* part_ml, float* O, hipStream_t stream);

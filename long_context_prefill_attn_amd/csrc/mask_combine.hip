@@ -108,6 +108,39 @@ hipError_t launch_fold_keep(const int32_t* keep_idx, int64_t keep_ld, const int3
   return hipGetLastError();
 }
 
+// mask_classify for a bit-packed mask: one workgroup per 128 x 128 tile (128 rows x
+// 4 words); only the bits of keys below T count.
+__global__ void __launch_bounds__(256) mask_classify_bits_kernel(const uint32_t* __restrict__ bits,
+                                                                 int64_t ld, int C, int T,
+                                                                 uint8_t* __restrict__ flags) {
+  const int kt = blockIdx.x, qt = blockIdx.y;
+  bool all_keep = true, all_drop = true;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int p = threadIdx.x + 256 * j;
+    const int r = qt * FLAG_TILE + (p >> 2);
+    const int wi = kt * (FLAG_TILE / 32) + (p & 3);
+    const int nvalid = min(max(T - 32 * wi, 0), 32);
+    if (r < C && nvalid > 0) {
+      const uint32_t vmask = nvalid == 32 ? ~0u : ((1u << nvalid) - 1u);
+      const uint32_t w = bits[(size_t)r * ld + wi] & vmask;
+      all_keep &= w == vmask;
+      all_drop &= w == 0u;
+    }
+  }
+  const int z = __syncthreads_and(all_keep);
+  const int dr = __syncthreads_and(all_drop);
+  if (threadIdx.x == 0)
+    flags[(size_t)qt * gridDim.x + kt] = dr ? TILE_DROPPED : (z ? TILE_ZERO : TILE_MIXED);
+}
+
+hipError_t launch_mask_classify_bits(const uint32_t* bits, int64_t bits_ld, int C, int T,
+                                     uint8_t* flags, hipStream_t stream) {
+  const dim3 grid((T + FLAG_TILE - 1) / FLAG_TILE, (C + FLAG_TILE - 1) / FLAG_TILE);
+  hipLaunchKernelGGL(mask_classify_bits_kernel, grid, dim3(256), 0, stream, bits, bits_ld, C, T, flags);
+  return hipGetLastError();
+}
+
 hipError_t launch_mask_classify(const uint16_t* mask, int64_t mask_ld, int C, int T,
                                 uint8_t* flags, hipStream_t stream) {
   dim3 grid((T + FLAG_TILE - 1) / FLAG_TILE, (C + FLAG_TILE - 1) / FLAG_TILE);

@@ -16,7 +16,7 @@ blocksparse  mean-pooled key index, alpha-threshold block selection plus the
 Every function is pinned by ``tests/test_oracle_*.py`` against brute force,
 closed forms, library routines or invariants that the method fixes.
 """
-from .dense import attention_weights, causal_kmask_ref, dense_ref, fold_mask_ref  # noqa: F401
+from .dense import attention_weights, bits_mask_ref, causal_kmask_ref, dense_ref, fold_mask_ref  # noqa: F401
 from .blocksparse import (  # noqa: F401
     pooled_index_ref, selection_votes_ref, select_ref, blocksparse_ref, selection_sets, rule_blocks,
 )

@@ -129,3 +129,20 @@ def causal_kmask_ref(q_start: int, C: int, T: int, kmask=None) -> np.ndarray:
     kdrop = k.astype(np.float64) <= DROP_AT
     drop = (t > p) | kdrop[None, :]
     return np.where(drop, np.float16(DROP_AT), k[None, :]).astype(np.float16)
+
+
+def bits_mask_ref(bits, T: int) -> np.ndarray:
+    """fp16 [C][T] additive mask of a keep/drop mask packed one bit per key.
+
+    "ANE Prefill Research", What worked, item 2: a kept key adds 0, a dropped key
+    -30000.  Packing (the library's compact form of such a mask): bit t % 32 of
+    the 32-bit word t // 32 of a row, set = kept.  Words are read as unsigned;
+    bits of keys >= T do not exist for the row.  Written out bit by bit.
+    """
+    w = np.asarray(bits).astype(np.int64) & 0xFFFFFFFF
+    C = w.shape[0]
+    m = np.empty((C, T), dtype=np.float16)
+    for t in range(T):
+        kept = (w[:, t // 32] >> (t % 32)) & 1
+        m[:, t] = np.where(kept == 1, np.float16(0.0), np.float16(DROP_AT))
+    return m

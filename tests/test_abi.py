@@ -61,6 +61,22 @@ def test_dense_rejects(kw, code):
     assert dense(**kw) == code
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(mask=FAKE + 4), _lib.PA_EINVAL),        # misaligned bits
+    (dict(ld=7), _lib.PA_EINVAL),                 # 7 words < ceil(256 / 32)
+    (dict(ld=8, d=96), _lib.PA_EUNSUPPORTED),
+    (dict(ld=8, T=(1 << 22) + 1), _lib.PA_EINVAL),   # ld too small for that T
+    (dict(ld=8), _lib.PA_EWORKSPACE),             # no workspace
+])
+def test_dense_bits_rejects(kw, code):
+    a = dict(Q=FAKE, C=64, n_q=4, K=FAKE, V=FAKE, T=256, n_kv=2, d=128, mask=FAKE, ld=8, scale=0.125,
+             O=FAKE, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    assert _lib.lib().prefill_attn_dense_bits(a["Q"], a["C"], a["n_q"], a["K"], a["V"], a["T"], a["n_kv"],
+                                              a["d"], a["mask"], a["ld"], a["scale"], a["O"], a["ws"],
+                                              a["ws_bytes"], a["stream"]) == code
+
+
 def test_dense_workspace_size():
     lib = _lib.lib()
     assert lib.prefill_attn_dense_workspace(64, 256, 4, 2, 128) >= 256

@@ -11,9 +11,9 @@ import sys
 import numpy as np
 import pytest
 
-from oracle import (blocksparse_ref, causal_kmask_ref, dense_ref, fold_mask_ref, pooled_index_ref,
-                    select_ref, selection_sets)
-from workloads import CONFIGS, bf16_bits, causal_mask, make_workload
+from oracle import (bits_mask_ref, blocksparse_ref, causal_kmask_ref, dense_ref, fold_mask_ref,
+                    pooled_index_ref, select_ref, selection_sets)
+from workloads import CONFIGS, bf16_bits, causal_mask, make_workload, pack_keep_bits
 from _util import assert_close, dev_bf16, dev_f16, f64
 
 pytestmark = pytest.mark.gpu
@@ -653,3 +653,58 @@ def test_dense_causal_kv_beyond_2gib(lp):
             p = q0 + r
             want = dense_ref(qg[r_i:r_i + 1], kg[:p + 1], vg[:p + 1], np.zeros((1, p + 1), np.float16), scale)
             assert_close(got[r, g:g + 1], want[0], f"row {r} head {g}")
+
+
+# ---------------------------------------------------------------- bit-packed masks
+def gpu_dense_bits(lp, q, k, v, bits, scale):
+    Bd = torch.from_numpy(np.ascontiguousarray(bits)).cuda()
+    O = lp.prefill_attn_dense_bits(dev_bf16(q), dev_bf16(k), dev_bf16(v), Bd, scale)
+    torch.cuda.synchronize()
+    return O.cpu().numpy()
+
+
+@pytest.mark.parametrize("C,T,n_q,n_kv,d,kind,words", [
+    (237, 4333, 16, 4, 128, "causal", None),     # the gqa4k tail chunk's shape
+    (129, 700, 8, 8, 64, "random", None),
+    (256, 4100, 4, 2, 128, "band", 136),          # padded rows: junk bits past T must be ignored
+    (37, 4100, 4, 4, 128, "random", None),        # split key range + combine
+    (300, 1000, 4, 1, 128, "sparse", None),       # ~8% kept: most tiles mixed, some dropped
+    (64, 64, 2, 2, 128, "dense", None),           # all kept: every tile plain
+])
+def test_dense_bits(lp, C, T, n_q, n_kv, d, kind, words):
+    rng = np.random.default_rng(C + T + d)
+    q, k, v = rand_bits(rng, C, n_q, d), rand_bits(rng, T, n_kv, d), rand_bits(rng, T, n_kv, d)
+    t = np.arange(T)[None, :]
+    p = (T - C + np.arange(C))[:, None]
+    if kind == "causal":
+        keep = t <= p
+    elif kind == "random":
+        keep = rng.random((C, T)) < 0.5
+        keep[0] = False                           # an all-dropped row outputs zeros
+    elif kind == "band":
+        keep = (t <= p) & (t > p - 1500)
+    elif kind == "sparse":
+        # ~80 keys per row; far fewer makes single bf16-rounded weights dominate
+        # and can exceed the tolerance (the same with an fp16 mask)
+        keep = rng.random((C, T)) < 0.08
+        keep[:, 0] = True
+        keep[:, 256:384] = False                  # a fully dropped column of tiles
+    else:
+        keep = np.ones((C, T), bool)
+    bits = pack_keep_bits(keep, words)
+    if words is not None:                         # set every bit past T
+        w = bits.astype(np.int64) & 0xFFFFFFFF
+        for c in range(T // 32, words):
+            lo = max(T - 32 * c, 0)
+            w[:, c] |= (0xFFFFFFFF >> lo) << lo if lo < 32 else 0
+        bits = w.astype(np.uint32).view(np.int32)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    say("dense bits", C, T, n_q, n_kv, d, kind, words)
+    got = gpu_dense_bits(lp, q, k, v, bits, scale)
+    want = dense_ref(f64(q), f64(k), f64(v), bits_mask_ref(bits, T), scale)
+    assert_close(got, want, f"bits {kind}")
+    if kind == "random":
+        assert np.all(got[0] == 0.0)
+    # the same keep pattern as an fp16 mask gives the same bits of output
+    same = gpu_dense(lp, q, k, v, np.where(keep, np.float16(0), np.float16(-30000)).astype(np.float16), scale)
+    assert np.array_equal(got.view(np.uint32), same.view(np.uint32))

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attention_weights, causal_kmask_ref, dense_ref, fold_mask_ref
+from oracle import attention_weights, bits_mask_ref, causal_kmask_ref, dense_ref, fold_mask_ref
 from workloads import CONFIGS, bf16_to_f32, causal_mask, dense_equiv_pairs, make_workload
 
 DROP = -30000.0
@@ -306,3 +306,44 @@ def test_causal_kmask_composition():
     # every visible key padded: the row outputs zeros
     km_all = np.full(T, -30000, np.float16)
     assert np.all(dense_ref(q, k, v, causal_kmask_ref(q0, C, T, km_all), 0.5) == 0)
+
+
+def test_bits_mask_hand_example_and_closed_forms():
+    """A hand-packed row: word 0 = 0b1011 keeps keys 0, 1, 3 and drops 2 and 4..31;
+    bit 31 of a word is key 31 (sign bit of the int32 word); bit 0 of word 1 is
+    key 32.  All bits set equals no mask; no bits set drops every key."""
+    T = 40
+    bits = np.zeros((3, 2), dtype=np.int32)
+    bits[0, 0] = 0b1011
+    bits[1, 0] = np.int32(-2 ** 31)             # only bit 31
+    bits[1, 1] = 1                              # key 32
+    bits[2, :] = -1                             # everything kept (bits past T ignored)
+    m = bits_mask_ref(bits, T)
+    assert m.shape == (3, T) and m.dtype == np.float16
+    assert [t for t in range(T) if m[0, t] == 0] == [0, 1, 3]
+    assert [t for t in range(T) if m[1, t] == 0] == [31, 32]
+    assert np.all(m[2] == 0)
+    assert np.all(m[m != 0] == np.float16(-30000.0))
+    rng = np.random.default_rng(4)
+    q, k, v = rng.standard_normal((3, 1, 8)), rng.standard_normal((T, 1, 8)), rng.standard_normal((T, 1, 8))
+    assert np.array_equal(dense_ref(q, k, v, m, 0.5)[2], dense_ref(q, k, v, np.zeros((3, T), np.float16), 0.5)[2])
+    assert np.all(dense_ref(q, k, v, bits_mask_ref(np.zeros((3, 2), np.int32), T), 0.5) == 0)
+
+
+def test_bits_mask_inverts_the_generator_packing():
+    """Two independent constructions: the generator packs a keep pattern with
+    numpy's little-endian bit packing, the oracle unpacks bit by bit; the round
+    trip gives back the pattern (causal, random, ragged T, padded word rows)."""
+    from workloads import pack_keep_bits
+    rng = np.random.default_rng(5)
+    for C, T, words in ((7, 100, None), (5, 64, 4), (3, 33, None), (2, 1, 3)):
+        keep = rng.random((C, T)) < 0.4
+        keep[0] = np.arange(T) <= T // 2            # a causal-like row
+        bits = pack_keep_bits(keep, words)
+        assert bits.dtype == np.int32 and bits.shape == (C, words or -(-T // 32))
+        assert np.array_equal(bits_mask_ref(bits, T) == 0, keep)
+        if words:                                   # padding words and bits past T are clear
+            w = bits.astype(np.int64) & 0xFFFFFFFF
+            assert np.all((w[:, -(-T // 32):]) == 0)
+    cm = causal_mask(300, 200, 640)
+    assert np.array_equal(bits_mask_ref(pack_keep_bits(cm == 0), 640).view(np.uint16), cm.view(np.uint16))

@@ -124,6 +124,20 @@ def causal_mask(q_start: int, C: int, T: int | None = None) -> np.ndarray:
     return np.where(t <= p, np.float16(0.0), np.float16(DROPPED)).astype(np.float16)
 
 
+def pack_keep_bits(keep, words: int | None = None) -> np.ndarray:
+    """int32 [C][words] packing of a boolean keep pattern [C][T]: bit t % 32 of
+    word t // 32 set where keep[i][t]; bits past T clear (words defaults to the
+    minimum ceil(T / 32))."""
+    keep = np.asarray(keep, dtype=bool)
+    C, T = keep.shape
+    if words is None:
+        words = -(-T // 32)
+    padded = np.zeros((C, words * 32), dtype=bool)
+    padded[:, :T] = keep
+    packed = np.packbits(padded, axis=1, bitorder="little")          # bytes, bit j of byte = key 8b + j
+    return packed.view("<u4").astype(np.uint32).view(np.int32).reshape(C, words)
+
+
 def folded_mask(q_start: int, C: int, keep_blocks: dict, spec: Spec, T: int | None = None):
     """fp16 [C][T] mask for the folded sparse-indexer selection.
 
