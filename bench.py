@@ -45,9 +45,10 @@ def parse():
     ap.add_argument("--workload", default="prefill32k",
                     choices=["prefill32k", "dense128k", "sparse128k", "fold2k5"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--dense-entry", default="mask", choices=["mask", "causal"],
-                    help="dense part: prefill_attn_dense over a causal fp16 mask (default) or "
-                         "prefill_attn_dense_causal (no mask buffer)")
+    ap.add_argument("--dense-entry", default="mask", choices=["mask", "causal", "bits"],
+                    help="dense part: prefill_attn_dense over a causal fp16 mask (default), "
+                         "prefill_attn_dense_causal (no mask buffer) or prefill_attn_dense_bits "
+                         "(the same causal masks packed one bit per key)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 512 MiB device copy (reference for HBM byte counters)")
@@ -109,7 +110,7 @@ def main():
 
     import torch
     import long_context_prefill_attn_amd as lp
-    from workloads import causal_mask, dense_equiv_pairs, make_workload
+    from workloads import causal_mask, dense_equiv_pairs, make_workload, pack_keep_bits
     from workloads.gen import chunk_list
 
     assert torch.cuda.is_available(), "bench.py needs the GPU"
@@ -148,6 +149,8 @@ def main():
 
     Q, K, V = up_bf16(w.Q), up_bf16(w.K), up_bf16(w.V)
     masks = [torch.from_numpy(causal_mask(q0, C)).to(dev) for q0, C in chunks]
+    if args.dense_entry == "bits":   # packed on the host before the timed region
+        mask_bits = [torch.from_numpy(pack_keep_bits(causal_mask(q0, C) == 0)).to(dev) for q0, C in chunks]
     keeps = [fold_lists(w, q0, C, dev) for q0, C in chunks] if args.workload == "fold2k5" else []
     O_dense = torch.empty((N, Hq, d), dtype=torch.float32, device=dev)
     ws_bytes = max(lp.prefill_attn_dense_workspace(C, q0 + C, Hq, Hkv, d) for q0, C in chunks)
@@ -180,6 +183,9 @@ def main():
                 lp.fold_keep_mask(keeps[ci][0], keeps[ci][1], q0, T, s.fold_width, s.fold_recent, mask=m)
             if args.dense_entry == "causal" and not keeps:
                 lp.prefill_attn_dense_causal(Q[q0:T], K[:T], V[:T], q0, scale, O=O_dense[q0:T], workspace=ws)
+            elif args.dense_entry == "bits" and not keeps:
+                lp.prefill_attn_dense_bits(Q[q0:T], K[:T], V[:T], mask_bits[ci], scale, O=O_dense[q0:T],
+                                           workspace=ws)
             else:
                 lp.prefill_attn_dense(Q[q0:T], K[:T], V[:T], m, scale, O=O_dense[q0:T], workspace=ws)
 
