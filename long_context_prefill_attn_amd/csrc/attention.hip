@@ -797,23 +797,42 @@ attn_dense_kernel(const uint16_t* __restrict__ Q, int C, int n_q, const uint16_t
     }
     return b;
   };
-  for (int st = next_special(a); st < b; st = next_special(st + 1)) {
-    const uint8_t f = frow[st >> 1];
-    tl.issue(false, st * BN, lds);
-    tl.issue(true, st * BN, lds + KRK * Geo<D>::TILE);
-    wait_vm<0>();
-    __syncthreads();
-    cx.key0 = st * BN;
-    cx.kvalid = min(BN, T - st * BN);
-    if (f == TILE_MIXED && causal_q0 >= 0)
-      attn_step<D, MODE_CAUSAL_K, true>(lds, lds + KRK * Geo<D>::TILE, nullptr, nullptr, lo2, qf, o, m, l, cx);
-    else if (f == TILE_MIXED && mask_mode == MASK_BITS)
-      attn_step<D, MODE_GBITS, true>(lds, lds + KRK * Geo<D>::TILE, nullptr, nullptr, lo2, qf, o, m, l, cx);
-    else if (f == TILE_MIXED)
-      attn_step<D, MODE_GMASK, true>(lds, lds + KRK * Geo<D>::TILE, nullptr, nullptr, lo2, qf, o, m, l, cx);
-    else
-      attn_step<D, MODE_PLAIN, true>(lds, lds + KRK * Geo<D>::TILE, nullptr, nullptr, lo2, qf, o, m, l, cx);
-    __syncthreads();
+  // Two buffers (the first two K and V ring slots): the next such step's tiles
+  // load while this one computes.
+  {
+    constexpr int TL = Geo<D>::TILE, NIW = Geo<D>::NIW;
+    int st = next_special(a), buf = 0;
+    if (st < b) {
+      tl.issue(false, st * BN, lds);
+      tl.issue(true, st * BN, lds + KRK * TL);
+    }
+    while (st < b) {
+      const int nx = next_special(st + 1);
+      if (nx < b) {
+        tl.issue(false, nx * BN, lds + (buf ^ 1) * TL);
+        tl.issue(true, nx * BN, lds + (KRK + (buf ^ 1)) * TL);
+        wait_vm<2 * NIW>();   // this step's tiles landed
+      } else {
+        wait_vm<0>();
+      }
+      __syncthreads();
+      const uint8_t f = frow[st >> 1];
+      const uint16_t* kt = lds + buf * TL;
+      const uint16_t* vt = lds + (KRK + buf) * TL;
+      cx.key0 = st * BN;
+      cx.kvalid = min(BN, T - st * BN);
+      if (f == TILE_MIXED && causal_q0 >= 0)
+        attn_step<D, MODE_CAUSAL_K, true>(kt, vt, nullptr, nullptr, lo2, qf, o, m, l, cx);
+      else if (f == TILE_MIXED && mask_mode == MASK_BITS)
+        attn_step<D, MODE_GBITS, true>(kt, vt, nullptr, nullptr, lo2, qf, o, m, l, cx);
+      else if (f == TILE_MIXED)
+        attn_step<D, MODE_GMASK, true>(kt, vt, nullptr, nullptr, lo2, qf, o, m, l, cx);
+      else
+        attn_step<D, MODE_PLAIN, true>(kt, vt, nullptr, nullptr, lo2, qf, o, m, l, cx);
+      __syncthreads();
+      st = nx;
+      buf ^= 1;
+    }
   }
 
   const float lt = l + partner32(l);
