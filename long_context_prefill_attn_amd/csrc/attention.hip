@@ -630,11 +630,11 @@ struct DenseSrc {
 
 // Block-sparse: the two 64-key halves of each selected block below the diagonal.
 struct SparseSrc {
-  const uint16_t* sl;   // selected block ids (LDS copy)
+  const int32_t* __restrict__ sl;   // selected block ids (global; uniform index, so scalar loads)
   int n;
   __device__ int first() const { return n > 0 ? 0 : -1; }
   __device__ int next(int e) const { return e + 1 < n ? e + 1 : -1; }
-  __device__ int kbase(int e) const { return (int)sl[e >> 1] * 128 + (e & 1) * BN; }
+  __device__ int kbase(int e) const { return sl[e >> 1] * 128 + (e & 1) * BN; }
 };
 
 // load this wave's 32 query rows as the B operand: lane holds Q[row n][dims 16st+8h .. +7]
@@ -930,11 +930,9 @@ attn_blocksparse_kernel(const uint16_t* __restrict__ Q, int C, int q_start, int 
   const int nwords = (nb + 31) / 32;
   for (int w = tid; w < nwords; w += NT) selbits[w] = 0;
   __syncthreads();
-  // the selected block ids, copied to LDS (after the rings) for the step walk
-  uint16_t* sl_s = lds + Geo<D>::RING;
+  // the selected blocks as a bitmap (the pooled steps skip them)
   for (int e = tid; e < cnt; e += NT) {
     const int bb = sl[e];
-    sl_s[e] = (uint16_t)bb;
     atomicOr(&selbits[bb >> 5], 1u << (bb & 31));
   }
 
@@ -955,7 +953,7 @@ attn_blocksparse_kernel(const uint16_t* __restrict__ Q, int C, int q_start, int 
   __syncthreads();
   // exact steps: the two 64-key halves of every selected block but the last
   // (the diagonal), which lie fully below the query block
-  plain_steps<D>(tl, lds, SparseSrc{sl_s, 2 * (cnt - 1)}, lo, qf, o, m, l, scale_log2);
+  plain_steps<D>(tl, lds, SparseSrc{sl, 2 * (cnt - 1)}, lo, qf, o, m, l, scale_log2);
 
   // lane-derived values for what follows, formed afresh (see fresh_lane_id)
   const int qpos2 = j * BLK + (wave & 3) * 32 + (fresh_lane_id() & 31);
@@ -1104,7 +1102,7 @@ static hipError_t blocksparse_impl(const uint16_t* Q, int C, int q_start, int n_
   const int nb = (T + block - 1) / block;
   const int n_qblk = (q_start + C - 1) / block - q_start / block + 1;
   const int hpw = ((n_q / n_kv) % 2 == 0) ? 2 : 1;
-  const size_t lds = Geo<D>::LDS_BYTES + (((size_t)nb * 2 + 15) & ~(size_t)15);   // rings + selection list
+  const size_t lds = Geo<D>::LDS_BYTES;   // the rings
   hipFuncSetAttribute((const void*)attn_blocksparse_kernel<D>,
                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   hipLaunchKernelGGL(attn_blocksparse_kernel<D>, dim3(n_qblk * (n_q / hpw)), dim3(NT), lds, stream, Q, C,
