@@ -81,7 +81,7 @@ const char* pa_status_string(int status);
  *
  *   O[i][h] = sum_t w_t V[t][g(h)],  w = softmax_t(scale * Q[i][h].K[t][g(h)] + mask[i][t])
  *
- * Requires C >= 1, 1 <= T <= 2^22, mask_ld >= T (K and V may be any size). The mask alone decides visibility; the
+ * Requires C >= 1, 1 <= T <= 2^22 - 4096, mask_ld >= T (K and V may be any size). The mask alone decides visibility; the
  * library assumes nothing about causality. `workspace` must hold at least
  * prefill_attn_dense_workspace(C, T, n_q, n_kv, d) bytes (tile flags and, when
  * the key range is split across workgroups, partial results); it is scratch,

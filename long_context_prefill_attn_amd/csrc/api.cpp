@@ -17,6 +17,10 @@
 
 namespace {
 
+// Longest key range of the dense entry points: the workgroup keeps one flag byte
+// per 128-key tile in LDS after its K/V rings (128 KB), within the 160 KB of a CU.
+constexpr int PA_MAX_T = (1 << 22) - 4096;
+
 thread_local std::string g_last_hip_error;
 
 int hip_status(hipError_t e) {
@@ -117,7 +121,7 @@ int prefill_attn_dense(const uint16_t* Q, int C, int n_q, const uint16_t* K, con
   if (C < 1 || T < 1 || n_q < 1 || n_kv < 1 || n_q % n_kv != 0) return PA_EINVAL;
   if (mask_ld < T || !good_scale(scale)) return PA_EINVAL;
   if (d != 64 && d != 128) return PA_EUNSUPPORTED;
-  if (T > (1 << 22)) return PA_EUNSUPPORTED;   // the per-tile flag row must fit in LDS
+  if (T > PA_MAX_T) return PA_EUNSUPPORTED;   // the per-tile flag row must fit in LDS
   const pa::DensePlan plan = pa::plan_dense(C, T, n_q, n_kv, d);
   if ((long long)plan.n_qt * n_q * plan.splits >= (1LL << 31)) return PA_EUNSUPPORTED;
   if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
@@ -155,7 +159,7 @@ int prefill_attn_dense_bits(const uint16_t* Q, int C, int n_q, const uint16_t* K
   if (C < 1 || T < 1 || n_q < 1 || n_kv < 1 || n_q % n_kv != 0) return PA_EINVAL;
   if (bits_ld < ((int64_t)T + 31) / 32 || !good_scale(scale)) return PA_EINVAL;
   if (d != 64 && d != 128) return PA_EUNSUPPORTED;
-  if (T > (1 << 22)) return PA_EUNSUPPORTED;   // the per-tile flag row must fit in LDS
+  if (T > PA_MAX_T) return PA_EUNSUPPORTED;   // the per-tile flag row must fit in LDS
   const pa::DensePlan plan = pa::plan_dense(C, T, n_q, n_kv, d);
   if ((long long)plan.n_qt * n_q * plan.splits >= (1LL << 31)) return PA_EUNSUPPORTED;
   if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
@@ -193,7 +197,7 @@ int prefill_attn_dense_causal(const uint16_t* Q, int C, int q_start, int n_q, co
   if (C < 1 || q_start < 0 || n_q < 1 || n_kv < 1 || n_q % n_kv != 0) return PA_EINVAL;
   if ((long long)q_start + C > T || !good_scale(scale)) return PA_EINVAL;
   if (d != 64 && d != 128) return PA_EUNSUPPORTED;
-  if (T > (1 << 22)) return PA_EUNSUPPORTED;
+  if (T > PA_MAX_T) return PA_EUNSUPPORTED;
   const pa::DensePlan plan = pa::plan_dense(C, T, n_q, n_kv, d);
   if ((long long)plan.n_qt * n_q * plan.splits >= (1LL << 31)) return PA_EUNSUPPORTED;
   if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||

@@ -23,7 +23,8 @@
 //     (packed to bf16), so P never leaves registers and O^T lands with the row's
 //     head_dim values in the lane that owns the row's softmax state.
 //   * K/V tiles of 64 keys go HBM -> LDS directly (buffer loads with the LDS
-//     bit) into 4-deep (K) and 3-deep (V) rings, issued two steps ahead of use.
+//     bit) into 4-deep K and V rings, issued one step-pair ahead of use (one
+//     workgroup barrier per pair of steps).
 //     One loop iteration alternates the QK^T MFMAs of the next step with the PV
 //     MFMAs of the previous one and forms the current step's weights between
 //     them, so the softmax VALU work is spread evenly over all MFMAs.
@@ -45,7 +46,7 @@ constexpr int BN = 64;          // keys per inner step
 constexpr int NW = 8;           // waves per workgroup
 constexpr int NT = 64 * NW;     // threads per workgroup
 constexpr int KRK = 4;          // K ring depth (tiles)
-constexpr int KRV = 3;          // V ring depth (tiles)
+constexpr int KRV = 4;          // V ring depth (tiles)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float SLACK = 8.0f;   // lazy-rescale threshold in log2 units
 
@@ -365,6 +366,27 @@ __device__ __forceinline__ void qk_tile(const uint16_t* __restrict__ kt, const L
   s[1] = qk_slice<D>(kt + 32 * D, lo, qf, f32x16{});
 }
 
+// The same scores with the K operands read straight from global memory (kg =
+// the tile's first row of this KV head; rows row_elems apart): the rare rescale
+// path, which may not rely on the tile still being in its ring slot.
+template <int D>
+__device__ __forceinline__ void qk_tile_global(const uint16_t* __restrict__ kg, size_t row_elems,
+                                               const bf16x8 (&qf)[D / 16], f32x16 (&s)[2]) {
+  const int lane = fresh_lane_id();
+  const int n = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const uint16_t* rp = kg + (size_t)(kb * 32 + n) * row_elems + 8 * h;
+    f32x16 acc = {};
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(rp + 16 * st);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], acc, 0, 0, 0);
+    }
+    s[kb] = acc;
+  }
+}
+
 // Row max of a raw (unscaled) S tile pair, completed across the two half-waves.
 __device__ __forceinline__ float row_max(const f32x16 (&s)[2]) {
   float mx = -__builtin_inff();
@@ -484,60 +506,68 @@ __device__ __forceinline__ void pv_only(const uint16_t* __restrict__ vt, const L
 // ---------------------------------------------------------------------------
 // Software-pipelined loop over "plain" 64-key steps (every key visible, no mask
 // to read). Iteration i runs S = K Q^T of step i+1 and O += V P of step i-1 on
-// the MFMA pipe while step i's weights are formed on the VALU. K tile j sits in
-// slot j % 4 of the K ring and V tile j in slot j % 3 of the V ring; each is
-// issued two iterations before the one that reads it:
-//   top of iteration i: wait for K[i+1] and V[i-1] (K[i+2], V[i] may still be
-//   in flight), barrier, then issue K[i+3] into K[i-1]'s slot and V[i+1] into
-//   V[i-2]'s slot -- both free after the barrier. K[i] stays in place for the
-//   whole iteration, so a rescale can form step i's scores again.
+// the MFMA pipe while step i's weights are formed on the VALU. Iterations go in
+// pairs (i even, i+1) with one workgroup barrier per pair; K tile j and V tile j
+// sit in slot j % 4 of their rings:
+//   top of pair i: wait for every load issued so far (K[i+1], K[i+2], V[i-1],
+//   V[i] were issued one pair earlier), barrier, then issue K[i+3], K[i+4] into
+//   the slots of K[i-1], K[i] and V[i+1], V[i+2] into those of V[i-3], V[i-2]:
+//   all were last read in the previous pair. A rescale (rare) recomputes step
+//   i's scores from K in global memory.
 // Steps are visited in any order the source yields; the online softmax does not
 // depend on the order. Loads past the last step re-read the first tile.
 // Src: int first(); int next(int st); int kbase(int st); a state < 0 ends the walk.
 // ---------------------------------------------------------------------------
 template <int D, class Src>
-__device__ __forceinline__ void plain_steps(const TileLoader<D>& tl, uint16_t* lds, const Src& src,
+__device__ __forceinline__ void plain_steps(const TileLoader<D>& tl, uint16_t* lds, Src& src,
                                             const LaneOffs<D>& lo, const bf16x8 (&qf)[D / 16],
                                             f32x16 (&o)[D / 32], float& m, float& l, float scale_log2) {
+  static_assert(KRK == 4 && KRV == 4, "ring slots are step % 4");
   constexpr int TL = Geo<D>::TILE, NIW = Geo<D>::NIW;
   uint16_t* kring = lds;
   uint16_t* vring = lds + KRK * TL;
   const int s0 = src.first();
   if (s0 < 0) return;
   const int kfb = src.kbase(s0);
-  const int s1 = src.next(s0);
-  const int s2 = s1 >= 0 ? src.next(s1) : -1;
-  tl.issue(false, kfb, kring);                                      // K[0]
-  tl.issue(false, s1 >= 0 ? src.kbase(s1) : kfb, kring + TL);       // K[1]
-  tl.issue(true, kfb, vring);                                       // V[0]
-  tl.issue(false, s2 >= 0 ? src.kbase(s2) : kfb, kring + 2 * TL);   // K[2]
+  auto kb = [&](int st) { return st >= 0 ? src.kbase(st) : kfb; };
+  int t0 = s0;                           // step i
+  int t1 = src.next(s0);                 // step i+1
+  int t2 = t1 >= 0 ? src.next(t1) : -1;  // step i+2
+  int t3 = -1, t4 = -1;
+  tl.issue(false, kfb, kring);              // K[0]
+  tl.issue(false, kb(t1), kring + TL);      // K[1]
+  tl.issue(true, kfb, vring);               // V[0]
+  tl.issue(false, kb(t2), kring + 2 * TL);  // K[2]
   wait_vm<3 * NIW>();   // K[0] landed
   bare_barrier();
-  int t1 = s1, t2 = s2;   // steps i+1 and i+2
   int tail_slot = 0;      // V slot of the last step
   bool tail_a = false;    // the last step's weights are in pa (else pb)
-  // Iteration i, given the ring slots of K[i] (i % 4) and V[i] (i % 3) either as
-  // compile-time constants (folded into the LDS offsets) or as run-time values.
-  auto iter = [&](auto pvc, auto kcc, auto vcc, const f32x16 (&sc)[2], f32x16 (&sn)[2],
-                  const u32x4 (&pp)[2][2], u32x4 (&pc)[2][2], auto pc_is_a) -> bool {
-    constexpr bool HAS_PV = decltype(pvc)::value;
-    const int kc = kcc, vc = vcc;
-    const int kn = (kc + 1) & 3;                   // K[i+1]
-    const int kf = (kc + 3) & 3;                   // K[i-1]'s slot, receives K[i+3]
-    const int vp = vc == 0 ? 2 : vc - 1;           // V[i-1]
-    const int vn = vc == 2 ? 0 : vc + 1;           // V[i-2]'s slot, receives V[i+1]
-    wait_vm<2 * NIW>();   // K[i+1], V[i-1] landed
+  // top of pair i, kc = i % 4 (0 or 2)
+  auto top = [&](auto kcc) {
+    const int kc = kcc;
+    wait_vm<0>();
     bare_barrier();
-    const int t3 = t2 >= 0 ? src.next(t2) : -1;
-    tl.issue(false, t3 >= 0 ? src.kbase(t3) : kfb, kring + kf * TL);
-    tl.issue(true, t1 >= 0 ? src.kbase(t1) : kfb, vring + vn * TL);
-    float psum = pipe_step<D, HAS_PV>(kring + kn * TL, vring + vp * TL, lo, qf, sc, sn, pp, pc, o, m, scale_log2);
+    t3 = t2 >= 0 ? src.next(t2) : -1;
+    t4 = t3 >= 0 ? src.next(t3) : -1;
+    tl.issue(false, kb(t3), kring + ((kc + 3) & 3) * TL);
+    tl.issue(false, kb(t4), kring + kc * TL);
+    tl.issue(true, kb(t1), vring + ((kc + 1) & 3) * TL);
+    tl.issue(true, kb(t2), vring + ((kc + 2) & 3) * TL);
+  };
+  // iteration i, kc = i % 4; ti = step i, tn = the step after it (< 0: step i is the last)
+  auto iter = [&](auto pvc, auto kcc, const f32x16 (&sc)[2], f32x16 (&sn)[2], const u32x4 (&pp)[2][2],
+                  u32x4 (&pc)[2][2], auto pc_is_a, int ti, int tn) -> bool {
+    constexpr bool HAS_PV = decltype(pvc)::value;
+    const int kc = kcc;
+    float psum = pipe_step<D, HAS_PV>(kring + ((kc + 1) & 3) * TL, vring + ((kc + 3) & 3) * TL, lo, qf, sc,
+                                      sn, pp, pc, o, m, scale_log2);
     if (__builtin_expect(__any(psum > PSUM_LIMIT), 0)) {
       // a row's weights outgrew the bound: raise m to the tile's max, rescale
       // what has been accumulated, and form the tile's weights again from
-      // scores recomputed out of K[i]
+      // scores recomputed out of K[i] (read from global memory: its ring slot
+      // may already be refilled, and sc's registers are reused inside pipe_step)
       f32x16 sr[2];
-      qk_tile<D>(kring + kc * TL, lo, qf, sr);
+      qk_tile_global<D>(tl.kptr + (size_t)kb(ti) * tl.row_elems, tl.row_elems, qf, sr);
       const float m_new = __builtin_fmaxf(m, row_max(sr) * scale_log2);
       const float alpha = (m == -__builtin_inff()) ? 1.f : exp2f(m - m_new);
 #pragma unroll
@@ -548,19 +578,27 @@ __device__ __forceinline__ void plain_steps(const TileLoader<D>& tl, uint16_t* l
       exp_pack(sr, m, scale_log2, pc, psum);
     }
     l += psum;
-    if (t1 < 0) {   // step i was the last
-      tail_slot = vc;
+    if (tn < 0) {   // step i was the last
+      tail_slot = kc;
       tail_a = decltype(pc_is_a)::value;
       return false;
     }
-    t1 = t2;
-    t2 = t3;
+    return true;
+  };
+  auto advance = [&]() {
+    t0 = t2;
+    t1 = t3;
+    t2 = t4;
     return true;
   };
   using PV0 = std::integral_constant<bool, false>;
   using PV1 = std::integral_constant<bool, true>;
   using A = std::integral_constant<bool, true>;
   using B = std::integral_constant<bool, false>;
+  using C0 = std::integral_constant<int, 0>;
+  using C1 = std::integral_constant<int, 1>;
+  using C2 = std::integral_constant<int, 2>;
+  using C3 = std::integral_constant<int, 3>;
   f32x16 sa[2], sb[2];
   u32x4 pa[2][2], pb[2][2];
   qk_tile<D>(kring, lo, qf, sa);
@@ -572,33 +610,32 @@ __device__ __forceinline__ void plain_steps(const TileLoader<D>& tl, uint16_t* l
     l *= alpha;
     m = m_new;
   }
-  // even i: S[i] in sa, weights into pa; odd i: S[i] in sb, weights into pb
+  // even i: S[i] in sa, weights into pa; odd i: S[i] in sb, weights into pb.
   if constexpr (D == 128) {
-    // twelve iterations per pass cover the 4- and 3-slot rings and both buffers
-    using C0 = std::integral_constant<int, 0>;
-    using C1 = std::integral_constant<int, 1>;
-    using C2 = std::integral_constant<int, 2>;
-    using C3 = std::integral_constant<int, 3>;
-    if (iter(PV0{}, C0{}, C0{}, sa, sb, pb, pa, A{})) {
-      while (iter(PV1{}, C1{}, C1{}, sb, sa, pa, pb, B{}) && iter(PV1{}, C2{}, C2{}, sa, sb, pb, pa, A{}) &&
-             iter(PV1{}, C3{}, C0{}, sb, sa, pa, pb, B{}) && iter(PV1{}, C0{}, C1{}, sa, sb, pb, pa, A{}) &&
-             iter(PV1{}, C1{}, C2{}, sb, sa, pa, pb, B{}) && iter(PV1{}, C2{}, C0{}, sa, sb, pb, pa, A{}) &&
-             iter(PV1{}, C3{}, C1{}, sb, sa, pa, pb, B{}) && iter(PV1{}, C0{}, C2{}, sa, sb, pb, pa, A{}) &&
-             iter(PV1{}, C1{}, C0{}, sb, sa, pa, pb, B{}) && iter(PV1{}, C2{}, C1{}, sa, sb, pb, pa, A{}) &&
-             iter(PV1{}, C3{}, C2{}, sb, sa, pa, pb, B{}) && iter(PV1{}, C0{}, C0{}, sa, sb, pb, pa, A{})) {
+    // four iterations (two pairs) per pass cover the ring slots and both
+    // buffers; the slots are compile-time constants folded into LDS offsets
+    top(C0{});
+    if (iter(PV0{}, C0{}, sa, sb, pb, pa, A{}, t0, t1) && iter(PV1{}, C1{}, sb, sa, pa, pb, B{}, t1, t2) &&
+        advance()) {
+      while ((top(C2{}), true) && iter(PV1{}, C2{}, sa, sb, pb, pa, A{}, t0, t1) &&
+             iter(PV1{}, C3{}, sb, sa, pa, pb, B{}, t1, t2) && advance() && (top(C0{}), true) &&
+             iter(PV1{}, C0{}, sa, sb, pb, pa, A{}, t0, t1) && iter(PV1{}, C1{}, sb, sa, pa, pb, B{}, t1, t2) &&
+             advance()) {
       }
     }
   } else {
-    // two iterations per pass, run-time ring slots (a full unroll spills here)
-    int kc = 0, vc = 0;
-    auto adv = [&]() {
-      kc = (kc + 1) & 3;
-      vc = vc == 2 ? 0 : vc + 1;
-      return true;
-    };
-    if (iter(PV0{}, kc, vc, sa, sb, pb, pa, A{}) && adv()) {
-      while (iter(PV1{}, kc, vc, sb, sa, pa, pb, B{}) && adv() && iter(PV1{}, kc, vc, sa, sb, pb, pa, A{}) &&
-             adv()) {
+    // one pair per pass with run-time ring slots (constant slots spill here)
+    int kc = 0;
+    top(kc);
+    if (iter(PV0{}, kc, sa, sb, pb, pa, A{}, t0, t1) && iter(PV1{}, kc + 1, sb, sa, pa, pb, B{}, t1, t2) &&
+        advance()) {
+      for (;;) {
+        kc ^= 2;
+        asm volatile("" : "+s"(kc));   // keep the slot a run-time value
+        top(kc);
+        if (!(iter(PV1{}, kc, sa, sb, pb, pa, A{}, t0, t1) && iter(PV1{}, kc + 1, sb, sa, pa, pb, B{}, t1, t2) &&
+              advance()))
+          break;
       }
     }
   }
@@ -615,16 +652,32 @@ __device__ __forceinline__ void plain_steps(const TileLoader<D>& tl, uint16_t* l
 
 // Plain-step sources (see plain_steps).
 // Dense: steps [a, b) whose 128-key flag tile is ZERO and whose 64 keys all lie below T.
+// The walk keeps a 64-step window of plain bits in scalar registers, filled by one
+// wave-wide ballot over the LDS flag row; finding the next step is scalar bit
+// arithmetic, so an iteration never waits on an LDS read for it (the walk only
+// moves forward, and every lane of the wave is active in the step loop).
 struct DenseSrc {
   int a, b, T;
   const uint8_t* frow;
-  __device__ bool plain(int st) const { return frow[st >> 1] == TILE_ZERO && (st + 1) * BN <= T; }
-  __device__ int scan(int st) const {
-    while (st < b && !plain(st)) ++st;
-    return st < b ? st : -1;
+  int wbase;        // first step of the window
+  uint64_t wmask;   // bit k: step wbase + k is plain
+  __device__ void fill(int base) {
+    const int sl = base + fresh_lane_id();
+    const bool p = sl < b && frow[sl >> 1] == TILE_ZERO && (sl + 1) * BN <= T;
+    wbase = base;
+    wmask = __ballot(p);
   }
-  __device__ int first() const { return scan(a); }
-  __device__ int next(int st) const { return scan(st + 1); }
+  __device__ int scan(int st) {
+    while (st < b) {
+      if (st < wbase || st >= wbase + 64) fill(st);
+      const uint64_t bits = wmask >> (st - wbase);
+      if (bits != 0) return st + __builtin_ctzll(bits);   // set bits lie below b
+      st = wbase + 64;
+    }
+    return -1;
+  }
+  __device__ int first() { return scan(a); }
+  __device__ int next(int st) { return scan(st + 1); }
   __device__ int kbase(int st) const { return st * BN; }
 };
 
@@ -760,7 +813,8 @@ attn_dense_kernel(const uint16_t* __restrict__ Q, int C, int n_q, const uint16_t
   tl.init(K, V, T, n_kv, g);
 
   // 1) plain steps: tiles flagged ZERO whose 64 keys all lie below T
-  plain_steps<D>(tl, lds, DenseSrc{a, b, T, frow}, lo, qf, o, m, l, scale_log2);
+  DenseSrc dsrc{a, b, T, frow, -64, 0};
+  plain_steps<D>(tl, lds, dsrc, lo, qf, o, m, l, scale_log2);
 
   // lane-derived values for what follows, formed afresh (see fresh_lane_id)
   const int lane2 = fresh_lane_id();
@@ -953,7 +1007,8 @@ attn_blocksparse_kernel(const uint16_t* __restrict__ Q, int C, int q_start, int 
   __syncthreads();
   // exact steps: the two 64-key halves of every selected block but the last
   // (the diagonal), which lie fully below the query block
-  plain_steps<D>(tl, lds, SparseSrc{sl, 2 * (cnt - 1)}, lo, qf, o, m, l, scale_log2);
+  SparseSrc ssrc{sl, 2 * (cnt - 1)};
+  plain_steps<D>(tl, lds, ssrc, lo, qf, o, m, l, scale_log2);
 
   // lane-derived values for what follows, formed afresh (see fresh_lane_id)
   const int qpos2 = j * BLK + (wave & 3) * 32 + (fresh_lane_id() & 31);
