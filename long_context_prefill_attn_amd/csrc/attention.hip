@@ -237,8 +237,7 @@ __device__ __forceinline__ f32x16 qk_slice(const uint16_t* __restrict__ kt, cons
 //   receives V[row base + 0..3][d0 + lane%16].
 template <int D, int MODE, bool TAIL>
 __device__ __forceinline__ void attn_step(const uint16_t* __restrict__ kt, const uint16_t* __restrict__ vt,
-                                          const uint16_t* __restrict__ kt2,
-                                          const uint16_t* __restrict__ vt2, const LaneOffs<D>& lo,
+                                          const LaneOffs<D>& lo,
                                           const bf16x8 (&qf)[D / 16], f32x16 (&o)[D / 32], float& m,
                                           float& l, const StepCtx& cx) {
   const int lane = fresh_lane_id();
@@ -248,7 +247,6 @@ __device__ __forceinline__ void attn_step(const uint16_t* __restrict__ kt, const
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     s[kb] = qk_slice<D>(kt + kb * 32 * D, lo, qf, f32x16{});
-    if (MODE == MODE_POOLED) s[kb] = qk_slice<D>(kt2 + kb * 32 * D, lo, qf, s[kb]);
   }
 
   float x[2][16];
@@ -345,12 +343,6 @@ __device__ __forceinline__ void attn_step(const uint16_t* __restrict__ kt, const
         {
           const v4i16 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt + off));
           const v4i16 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt + off + 8 * D));
-          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, o[nb], 0, 0, 0);
-        }
-        if (MODE == MODE_POOLED) {
-          const v4i16 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt2 + off));
-          const v4i16 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt2 + off + 8 * D));
           const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
           o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, o[nb], 0, 0, 0);
         }
@@ -876,13 +868,13 @@ attn_dense_kernel(const uint16_t* __restrict__ Q, int C, int n_q, const uint16_t
       cx.key0 = st * BN;
       cx.kvalid = min(BN, T - st * BN);
       if (f == TILE_MIXED && causal_q0 >= 0)
-        attn_step<D, MODE_CAUSAL_K, true>(kt, vt, nullptr, nullptr, lo2, qf, o, m, l, cx);
+        attn_step<D, MODE_CAUSAL_K, true>(kt, vt, lo2, qf, o, m, l, cx);
       else if (f == TILE_MIXED && mask_mode == MASK_BITS)
-        attn_step<D, MODE_GBITS, true>(kt, vt, nullptr, nullptr, lo2, qf, o, m, l, cx);
+        attn_step<D, MODE_GBITS, true>(kt, vt, lo2, qf, o, m, l, cx);
       else if (f == TILE_MIXED)
-        attn_step<D, MODE_GMASK, true>(kt, vt, nullptr, nullptr, lo2, qf, o, m, l, cx);
+        attn_step<D, MODE_GMASK, true>(kt, vt, lo2, qf, o, m, l, cx);
       else
-        attn_step<D, MODE_PLAIN, true>(kt, vt, nullptr, nullptr, lo2, qf, o, m, l, cx);
+        attn_step<D, MODE_PLAIN, true>(kt, vt, lo2, qf, o, m, l, cx);
       __syncthreads();
       st = nx;
       buf ^= 1;
@@ -906,55 +898,52 @@ attn_dense_kernel(const uint16_t* __restrict__ Q, int C, int n_q, const uint16_t
 
 // ---------------------------------------------------------------------------
 // block-sparse prefill attention: one workgroup per (query block of 128
-// positions, pair of query heads of one KV group). Exact steps over the
-// selected key blocks (the diagonal block causally), then the pooled rows of
-// the unselected visible blocks with multiplicity `block` ("Porting FlashPrefill
-// V2 to Apple silicon", Compute the peaks, summarize the rest). Pooled
-// keys/values are fp32; they enter the bf16 MFMA as hi + lo bf16 pairs (about
-// 16 significant bits). With an odd number of query heads per KV head, the
-// second half of the workgroup repeats the first head and does not store.
+// positions, pair of query heads of one KV group). The diagonal block first
+// (causally by position; its tiles load while the selection bitmap is built and
+// Q is read), then exact steps over the other selected key blocks, then the
+// pooled rows of the unselected visible blocks with multiplicity `block`
+// ("Porting FlashPrefill V2 to Apple silicon", Compute the peaks, summarize the
+// rest). Pooled keys/values are fp32 in memory and enter the bf16 MFMA rounded
+// to bf16 (as the keys and values themselves are); the next pooled tile's
+// global loads are in flight while the current one is computed. With an odd
+// number of query heads per KV head, the second half of the workgroup repeats
+// the first head and does not store.
 // ---------------------------------------------------------------------------
 template <int D>
-__device__ __forceinline__ void split_hi_lo(float f, uint16_t& hi, uint16_t& lo) {
-  const uint32_t hb = pack_bf16x2(f, 0.f) & 0xFFFFu;
-  const float rest = f - __uint_as_float(hb << 16);
-  hi = (uint16_t)hb;
-  lo = (uint16_t)(pack_bf16x2(rest, 0.f) & 0xFFFFu);
-}
+struct PooledFetch {
+  float4 f[Geo<D>::KCH][2];   // this thread's 16-byte destination chunks, as 8 fp32 each
 
-template <int D>
-__device__ __forceinline__ void stage_pooled_one(const float* __restrict__ src, int pbase, int jlimit,
-                                                 uint16_t* hi_tile, uint16_t* lo_tile) {
-  const int tid = threadIdx.x;
-  constexpr int CPR = Geo<D>::CPR;
+  // global loads of pooled rows pbase .. pbase+63 (rows >= jlimit read as zeros)
+  __device__ __forceinline__ void load(const float* __restrict__ src, int pbase, int jlimit) {
+    constexpr int CPR = Geo<D>::CPR;
 #pragma unroll
-  for (int i = 0; i < Geo<D>::KCH; ++i) {
-    const int c = tid + NT * i;
-    const int row = c / CPR, lc = c % CPR;
-    const int bb = pbase + row;
-    float f[8];
-    if (bb < jlimit) {
-      const float4 x0 = *reinterpret_cast<const float4*>(src + (size_t)bb * D + lc * 8);
-      const float4 x1 = *reinterpret_cast<const float4*>(src + (size_t)bb * D + lc * 8 + 4);
-      f[0] = x0.x; f[1] = x0.y; f[2] = x0.z; f[3] = x0.w; f[4] = x1.x; f[5] = x1.y; f[6] = x1.z; f[7] = x1.w;
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) f[e] = 0.f;
+    for (int i = 0; i < Geo<D>::KCH; ++i) {
+      const int c = threadIdx.x + NT * i;
+      const int row = c / CPR, lc = c % CPR;
+      const int bb = pbase + row;
+      const bool ok = bb < jlimit;   // row 0 exists whenever this is called (jlimit >= 1)
+      const float* rp = src + (size_t)(ok ? bb : 0) * D + lc * 8;
+      const float4 x0 = *reinterpret_cast<const float4*>(rp);
+      const float4 x1 = *reinterpret_cast<const float4*>(rp + 4);
+      const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+      f[i][0] = ok ? x0 : z;
+      f[i][1] = ok ? x1 : z;
     }
-    u32x4 H, L;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      uint16_t h0, l0, h1, l1;
-      split_hi_lo<D>(f[2 * w], h0, l0);
-      split_hi_lo<D>(f[2 * w + 1], h1, l1);
-      H[w] = h0 | ((uint32_t)h1 << 16);
-      L[w] = l0 | ((uint32_t)l1 << 16);
-    }
-    const int off = row * D + ((lc ^ swz(row)) * 8);
-    *reinterpret_cast<u32x4*>(hi_tile + off) = H;
-    *reinterpret_cast<u32x4*>(lo_tile + off) = L;
   }
-}
+
+  // the same chunks rounded to bf16 (nearest even) into a swizzled LDS tile
+  __device__ __forceinline__ void store(uint16_t* tile) const {
+    constexpr int CPR = Geo<D>::CPR;
+#pragma unroll
+    for (int i = 0; i < Geo<D>::KCH; ++i) {
+      const int c = threadIdx.x + NT * i;
+      const int row = c / CPR, lc = c % CPR;
+      const u32x4 h = {pack_bf16x2(f[i][0].x, f[i][0].y), pack_bf16x2(f[i][0].z, f[i][0].w),
+                       pack_bf16x2(f[i][1].x, f[i][1].y), pack_bf16x2(f[i][1].z, f[i][1].w)};
+      *reinterpret_cast<u32x4*>(tile + row * D + ((lc ^ swz(row)) * 8)) = h;
+    }
+  }
+};
 
 template <int D>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
@@ -965,6 +954,7 @@ attn_blocksparse_kernel(const uint16_t* __restrict__ Q, int C, int q_start, int 
                         const int32_t* __restrict__ sel_cnt, float scale_log2, float* __restrict__ O) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   __shared__ uint32_t selbits[256];  // up to 8192 blocks
+  constexpr int TL = Geo<D>::TILE;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, n = lane & 31;
   constexpr int BLK = 128;
@@ -980,6 +970,18 @@ attn_blocksparse_kernel(const uint16_t* __restrict__ Q, int C, int q_start, int 
   const int g = (hp * hpw) / group;
   const int32_t* sl = sel_idx + ((size_t)g * n_qblk + jj) * nb;
   const int cnt = sel_cnt[(size_t)g * n_qblk + jj];
+
+  // the diagonal block's tiles (its keys may end before 128: ragged T; its
+  // first key j*128 <= the chunk's last position < T)
+  TileLoader<D> tl;
+  tl.init(K, V, T, n_kv, g);
+  const int n_diag = (j * BLK + BN < T) ? 2 : 1;
+  tl.issue(false, j * BLK, lds);
+  tl.issue(true, j * BLK, lds + KRK * TL);
+  if (n_diag == 2) {
+    tl.issue(false, j * BLK + BN, lds + TL);
+    tl.issue(true, j * BLK + BN, lds + (KRK + 1) * TL);
+  }
 
   const int nwords = (nb + 31) / 32;
   for (int w = tid; w < nwords; w += NT) selbits[w] = 0;
@@ -1002,9 +1004,24 @@ attn_blocksparse_kernel(const uint16_t* __restrict__ Q, int C, int q_start, int 
   float m = -__builtin_inff(), l = 0.f;
 
   const LaneOffs<D> lo = lane_offsets<D>();
-  TileLoader<D> tl;
-  tl.init(K, V, T, n_kv, g);
+  StepCtx cx;
+  cx.scale_log2 = scale_log2;
+  cx.mrow = nullptr;
+  cx.brow = nullptr;
+  cx.mask_vec = false;
+  cx.qpos = qpos;
+  cx.selbits = selbits;
+  cx.jlimit = j;
+  cx.pool_bias = __builtin_log2f((float)BLK);
+  wait_vm<0>();
   __syncthreads();
+  for (int e = 0; e < n_diag; ++e) {
+    cx.key0 = j * BLK + e * BN;
+    cx.kvalid = min(BN, T - cx.key0);
+    attn_step<D, MODE_CAUSAL, true>(lds + e * TL, lds + (KRK + e) * TL, lo, qf, o, m, l, cx);
+  }
+  __syncthreads();
+
   // exact steps: the two 64-key halves of every selected block but the last
   // (the diagonal), which lie fully below the query block
   SparseSrc ssrc{sl, 2 * (cnt - 1)};
@@ -1014,46 +1031,31 @@ attn_blocksparse_kernel(const uint16_t* __restrict__ Q, int C, int q_start, int 
   const int qpos2 = j * BLK + (wave & 3) * 32 + (fresh_lane_id() & 31);
   const bool qvalid2 = qpos2 >= q_start && qpos2 < q_start + C;
   const LaneOffs<D> lo2 = lane_offsets<D>();
-  StepCtx cx;
-  cx.scale_log2 = scale_log2;
-  cx.mrow = nullptr;
-  cx.brow = nullptr;
-  cx.mask_vec = false;
-  cx.qpos = qpos2;
-  cx.selbits = selbits;
-  cx.jlimit = j;
-  cx.pool_bias = __builtin_log2f((float)BLK);
-  // the diagonal block, causally by position (its keys may end before 128: ragged T)
-  uint16_t* kt = lds;
-  uint16_t* vt = lds + KRK * Geo<D>::TILE;
-  for (int e = 0; e < 2; ++e) {
-    const int kbase = j * BLK + e * BN;
-    if (kbase >= T) break;
-    tl.issue(false, kbase, kt);
-    tl.issue(true, kbase, vt);
-    wait_vm<0>();
-    __syncthreads();
-    cx.key0 = kbase;
-    cx.kvalid = min(BN, T - kbase);
-    attn_step<D, MODE_CAUSAL, true>(kt, vt, nullptr, nullptr, lo2, qf, o, m, l, cx);
-    __syncthreads();
-  }
 
-  // pooled rows of the unselected visible blocks b < j, 64 per step
-  uint16_t* khi = lds;
-  uint16_t* klo = lds + Geo<D>::TILE;
-  uint16_t* vhi = lds + KRK * Geo<D>::TILE;
-  uint16_t* vlo = vhi + Geo<D>::TILE;
+  // pooled rows of the unselected visible blocks b < j, 64 per step, in two
+  // alternating LDS buffers (one barrier per step)
   const float* kpg = Kp + (size_t)g * pool_ld * D;
   const float* vpg = Vp + (size_t)g * pool_ld * D;
-  for (int pbase = 0; pbase < j; pbase += BN) {
-    stage_pooled_one<D>(kpg, pbase, j, khi, klo);
-    stage_pooled_one<D>(vpg, pbase, j, vhi, vlo);
+  const int n_pool = (j + BN - 1) / BN;
+  PooledFetch<D> fk, fv;
+  if (n_pool > 0) {
+    fk.load(kpg, 0, j);
+    fv.load(vpg, 0, j);
+  }
+  for (int p = 0; p < n_pool; ++p) {
+    uint16_t* kt = lds + (p & 1) * TL;
+    uint16_t* vt = lds + (KRK + (p & 1)) * TL;
+    fk.store(kt);
+    fv.store(vt);
     __syncthreads();
-    cx.key0 = pbase;
-    cx.kvalid = min(BN, j - pbase);
-    attn_step<D, MODE_POOLED, true>(khi, vhi, klo, vlo, lo2, qf, o, m, l, cx);
-    __syncthreads();
+    if (p + 1 < n_pool) {
+      fk.load(kpg, (p + 1) * BN, j);
+      fv.load(vpg, (p + 1) * BN, j);
+    }
+    cx.key0 = p * BN;
+    cx.kvalid = min(BN, j - p * BN);
+    cx.qpos = qpos2;
+    attn_step<D, MODE_POOLED, true>(kt, vt, lo2, qf, o, m, l, cx);
   }
 
   const float lt = l + partner32(l);
