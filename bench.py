@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 512 MiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--no-mfma-ceiling", action="store_true",
+                    help="skip the register-only MFMA calibration (random vs zero bf16 operands)")
     ap.add_argument("--parts", default="dense,blocksparse",
                     help="subset of the step to run (for profiler runs); the default runs the whole step")
     return ap.parse_args()
@@ -275,6 +277,10 @@ def main():
                                 "skipped_block_fraction": round(sparsity, 4),
                                 "speedup_vs_dense": round(dense_ms / sparse_ms, 3) if run_dense_part else None}
 
+    ceiling = None if args.no_mfma_ceiling else mfma_ceiling(lp, torch, dev, props.multi_processor_count)
+    if ceiling:
+        roofline["frac_of_random_operand_mfma_rate"] = round(achieved / ceiling["random_bf16_tflops"], 4)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, chunks, args.cpu_seconds)
@@ -295,10 +301,40 @@ def main():
                          if keeps else "dense chunked prefill"), "parallelism": "none (1 GPU)"},
         "tokens_per_s": round((2 if do_sparse else 1) * N / (ms_step * 1e-3)),
         "pct_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
-        "parts": parts, "kernels": kern, "roofline": roofline, "cpu_baseline": cpu,
+        "parts": parts, "kernels": kern, "roofline": roofline, "mfma_ceiling": ceiling, "cpu_baseline": cpu,
         "device": {"name": props.name, "cus": props.multi_processor_count},
     }
     print(json.dumps(line), flush=True)
+
+
+def mfma_ceiling(lp, torch, dev, cus):
+    """bf16 MFMA rate sustained from registers (pa_mfma_probe) with random N(0,1)
+    bf16 operands, as the attention kernels see, and with zero operands; best of
+    three ~30 ms runs each, after the timed region. The gap between the two is
+    the clock the matrix cores' operand-dependent power draw costs."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    rnd = torch.randn(1 << 19, device=dev, generator=g).to(torch.bfloat16)   # 1 MiB
+    zero = torch.zeros_like(rnd)
+    sink = torch.empty(4 * cus * 512, dtype=torch.float32, device=dev)
+    iters = 6000
+    flops = 4 * cus * 8 * iters * 32 * 32768.0
+    out = {}
+    for name, ops in (("random_bf16_tflops", rnd), ("zero_tflops", zero)):
+        lp.mfma_probe(ops, sink, 200)
+        best = float("inf")
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            lp.mfma_probe(ops, sink, iters)
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        out[name] = round(flops / (best * 1e-3) / 1e12, 1)
+    out["random_frac_of_peak"] = round(out["random_bf16_tflops"] / PEAK_BF16_TFLOPS, 4)
+    out["probe"] = (f"{4 * cus} workgroups x 8 waves, {iters} x 32 v_mfma_f32_32x32x16_bf16 per wave "
+                    "from registers, 4 independent accumulators")
+    return out
 
 
 def fold_lists(w, q0, C, dev):

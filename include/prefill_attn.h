@@ -277,12 +277,28 @@ int prefill_attn_blocksparse_ld(const uint16_t* Q, int C, int q_start, int n_q,
  * When enabled, each launch of the named kernels is bracketed by HIP events
  * recorded on the launch stream. pa_timing_read synchronises those events and
  * returns the summed milliseconds and launch count for `kernel`, one of
- * "attn_dense", "attn_blocksparse", "mask_classify", "attn_combine", "pool", "select", "fold".
+ * "attn_dense", "attn_blocksparse", "mask_classify", "attn_combine", "pool", "select", "fold",
+ * "mfma_probe".
  * pa_timing_reset clears the totals. Returns PA_OK or PA_EINVAL/PA_EHIP.
  */
 int pa_timing_enable(int on);
 int pa_timing_reset(void);
 int pa_timing_read(const char* kernel, double* total_ms, int64_t* launches);
+
+/*
+ * Matrix-core calibration (instrumentation for benchmarks, not part of the
+ * attention path): the bf16 MFMA rate the part sustains from registers for
+ * given operand data. Enqueues `grid` workgroups of 512 threads. Thread t takes
+ * the 16 operand slots operands[(16 t + i) mod 65536], i < 16, of 16 bytes each
+ * (so `operands` is a device buffer of 1 MiB, filled by the caller), runs
+ * `iters` x 32 v_mfma_f32_32x32x16_bf16 from registers on four independent
+ * accumulators, and writes one float to sink[t] (`sink`: grid * 512 floats).
+ * FLOPs = grid * 8 * iters * 32 * 32768. Random bf16 operands against zeros
+ * show how far the operand-dependent power draw of the matrix cores pulls the
+ * clock below the one the published peak assumes.
+ * Requires 16-byte aligned pointers, grid >= 1, iters >= 1. Errors: PA_EINVAL, PA_EHIP.
+ */
+int pa_mfma_probe(const uint16_t* operands, float* sink, int grid, int iters, void* stream);
 
 #ifdef __cplusplus
 }

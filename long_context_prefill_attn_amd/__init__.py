@@ -24,7 +24,7 @@ from ._lib import PrefillAttnError, check, lib  # noqa: F401
 
 __all__ = ["prefill_attn_dense", "prefill_attn_dense_bits", "prefill_attn_dense_causal", "prefill_attn_dense_workspace",
            "build_pooled_index",
-           "select_blocks", "prefill_attn_blocksparse", "fold_keep_mask", "PrefillAttnError", "timing"]
+           "select_blocks", "prefill_attn_blocksparse", "fold_keep_mask", "PrefillAttnError", "timing", "mfma_probe"]
 
 
 def _stream() -> int:
@@ -239,6 +239,18 @@ def prefill_attn_blocksparse(Q, K, V, K_pool, V_pool, sel_idx, sel_cnt, q_start:
                                             float(scale), O.data_ptr(), _stream()),
           "prefill_attn_blocksparse")
     return O
+
+
+def mfma_probe(operands, sink, iters: int) -> None:
+    """Matrix-core calibration (pa_mfma_probe): operands = 1 MiB device buffer of
+    bf16 bits (65,536 slots of 16 bytes), sink = fp32 [grid * 512]; enqueues
+    grid = sink.numel() // 512 workgroups of iters x 32 bf16 MFMAs per wave."""
+    if not (operands.is_cuda and sink.is_cuda and sink.dtype == torch.float32):
+        raise ValueError("operands and sink must be device tensors (sink fp32)")
+    if operands.numel() * operands.element_size() < (1 << 20) or sink.numel() < 512:
+        raise ValueError("operands needs 1 MiB, sink at least 512 floats")
+    check(lib().pa_mfma_probe(operands.data_ptr(), sink.data_ptr(), sink.numel() // 512, int(iters),
+                              _stream()), "pa_mfma_probe")
 
 
 class timing:

@@ -44,7 +44,7 @@ struct TimedKernel {
 std::mutex g_timing_mu;
 bool g_timing_on = false;
 TimedKernel g_timed[] = {{"attn_dense"}, {"attn_blocksparse"}, {"mask_classify"},
-                         {"attn_combine"}, {"pool"}, {"select"}, {"fold"}};
+                         {"attn_combine"}, {"pool"}, {"select"}, {"fold"}, {"mfma_probe"}};
 std::vector<hipEvent_t> g_event_pool;
 
 hipEvent_t take_event() {
@@ -326,6 +326,12 @@ int prefill_attn_blocksparse(const uint16_t* Q, int C, int q_start, int n_q, con
   return prefill_attn_blocksparse_ld(Q, C, q_start, n_q, K, V, T, n_kv, d, K_pool, V_pool,
                                      (T + block - 1) / block, block, sel_idx, sel_cnt, scale, O,
                                      stream);
+}
+
+int pa_mfma_probe(const uint16_t* operands, float* sink, int grid, int iters, void* stream) {
+  if (!aligned16(operands) || !aligned16(sink) || grid < 1 || iters < 1) return PA_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(timed("mfma_probe", s, [&] { return pa::launch_mfma_probe(operands, sink, grid, iters, s); }));
 }
 
 int pa_timing_enable(int on) {

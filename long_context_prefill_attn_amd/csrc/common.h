@@ -99,4 +99,6 @@ hipError_t launch_attn_blocksparse(const uint16_t* Q, int C, int q_start, int n_
                                    const int32_t* sel_idx, const int32_t* sel_cnt,
                                    float scale, float* O, hipStream_t stream);
 
+hipError_t launch_mfma_probe(const uint16_t* operands, float* sink, int grid, int iters, hipStream_t stream);
+
 }  // namespace pa

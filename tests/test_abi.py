@@ -165,3 +165,11 @@ def test_timing_api_host_side():
     assert lib.pa_timing_reset() == 0
     assert lib.pa_timing_read(b"attn_dense", ctypes.byref(ms), ctypes.byref(n)) == 0
     assert n.value == 0
+
+
+def test_mfma_probe_rejects():
+    f = _lib.lib().pa_mfma_probe
+    assert f(FAKE, FAKE, 0, 10, None) == _lib.PA_EINVAL      # no workgroups
+    assert f(FAKE, FAKE, 4, 0, None) == _lib.PA_EINVAL       # no iterations
+    assert f(FAKE + 8, FAKE, 4, 10, None) == _lib.PA_EINVAL  # misaligned operands
+    assert f(FAKE, None, 4, 10, None) == _lib.PA_EINVAL      # no sink

@@ -708,3 +708,17 @@ def test_dense_bits(lp, C, T, n_q, n_kv, d, kind, words):
     # the same keep pattern as an fp16 mask gives the same bits of output
     same = gpu_dense(lp, q, k, v, np.where(keep, np.float16(0), np.float16(-30000)).astype(np.float16), scale)
     assert np.array_equal(got.view(np.uint32), same.view(np.uint32))
+
+
+def test_mfma_probe_calibration_kernel(lp):
+    # the benchmark's matrix-core calibration: zero operands give exactly zero sums;
+    # unit operands add 16 per MFMA to each accumulator element, 8 MFMAs per chain
+    # per iteration, and the 64 elements of a lane's four chains are summed
+    import torch
+    sink = torch.full((2 * 512,), float("nan"), dtype=torch.float32, device="cuda")
+    lp.mfma_probe(torch.zeros(1 << 19, dtype=torch.bfloat16, device="cuda"), sink, 3)
+    torch.cuda.synchronize()
+    assert torch.equal(sink, torch.zeros_like(sink))
+    lp.mfma_probe(torch.ones(1 << 19, dtype=torch.bfloat16, device="cuda"), sink, 3)
+    torch.cuda.synchronize()
+    assert torch.equal(sink, torch.full_like(sink, 64.0 * 16 * 8 * 3))
