@@ -240,6 +240,18 @@ def main():
         if n:
             kern[name] = {"avg_ms": tot / n, "launches_per_step": n // args.steps, "ms_per_step": tot / args.steps}
 
+    # HBM-bound kernels: algorithmic bytes per step / their event time per step
+    hbm = {}
+    if "pool" in kern:   # K and V of the tokens pooled (bf16) in, pooled rows (fp32) out
+        pool_bytes = sum(2 * (q0 + C - (q0 // B) * B) * Hkv * d * 2 + 2 * (-(-(q0 + C) // B) - q0 // B) * Hkv * d * 4
+                         for q0, C in sparse_calls)
+        hbm["pool"] = pool_bytes
+    if "mask_classify" in kern and args.dense_entry == "mask" and not keeps:   # fp16 mask in, tile flags out
+        hbm["mask_classify"] = sum(2 * C * (q0 + C) + (-(-C // 128)) * (-(-(q0 + C) // 128)) for q0, C in chunks)
+    hbm_kernels = {k: {"bytes_per_step": b, "GB_per_s": round(b / (kern[k]["ms_per_step"] * 1e-3) / 1e9, 1),
+                       "frac_of_hbm_peak": round(b / (kern[k]["ms_per_step"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
+                   for k, b in hbm.items()}
+
     assert torch.isfinite(O_dense).all().item(), "non-finite dense output"
     if do_sparse:
         assert torch.isfinite(O_sparse).all().item(), "non-finite block-sparse output"
@@ -301,7 +313,8 @@ def main():
                          if keeps else "dense chunked prefill"), "parallelism": "none (1 GPU)"},
         "tokens_per_s": round((2 if do_sparse else 1) * N / (ms_step * 1e-3)),
         "pct_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
-        "parts": parts, "kernels": kern, "roofline": roofline, "mfma_ceiling": ceiling, "cpu_baseline": cpu,
+        "parts": parts, "kernels": kern, "roofline": roofline, "mfma_ceiling": ceiling,
+        "hbm_kernels": hbm_kernels, "cpu_baseline": cpu,
         "device": {"name": props.name, "cus": props.multi_processor_count},
     }
     print(json.dumps(line), flush=True)
