@@ -195,6 +195,25 @@ def test_dense_128k_sampled_rows(lp):
         assert_close(got[rows], want, f"dense128k chunk {idx}")
 
 
+def test_dense_planted_32k_sampled_rows(lp):
+    """The dense half of the default benchmark step: the planted 32K tensors in
+    4,096-row chunks under fp16 causal masks, launched as the bench launches them.
+    The planted positional and topic components give large, structured scores,
+    so the lazy-rescale path (scores recomputed from K in global memory) runs at
+    full size. Chunks 0, 3 and 7 on sampled rows of every head."""
+    w = make_workload("sparse32k")
+    s = w.spec
+    rows = np.concatenate([np.arange(0, 4096, 127), [4095]])
+    for ci in (0, 3, 7):
+        q0, C = 4096 * ci, 4096
+        T = q0 + C
+        mask = causal_mask(q0, C)
+        say("planted 32K dense chunk", ci, "T", T)
+        got = gpu_dense(lp, w.Q[q0:T], w.K[:T], w.V[:T], mask, s.scale)
+        want = dense_ref(f64(w.Q[q0:T][rows]), f64(w.K[:T]), f64(w.V[:T]), mask[rows], s.scale)
+        assert_close(got[rows], want, f"planted 32K dense chunk {ci}")
+
+
 # ---------------------------------------------------------------- dense: edge cases
 def _edge(seed, C, T, n_q, n_kv, d, kind):
     rng = np.random.default_rng(seed)
