@@ -105,8 +105,9 @@ def cpu_threads() -> int:
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the path is built and timed on a single MI355X "
-              "(multi-GPU sharding is described in DESIGN.md, not built). Run with --gpus 1.",
+        print("bench.py measures one GPU only: the path is built and timed on a single MI355X. "
+              "Sharding across GPUs (by KV head, or by key range with an LSE merge) is not built. "
+              "Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
 
