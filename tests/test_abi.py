@@ -53,6 +53,7 @@ def dense(**kw):
     (dict(scale=-1.0), _lib.PA_EINVAL),
     (dict(scale=float("inf")), _lib.PA_EINVAL),
     (dict(d=96), _lib.PA_EUNSUPPORTED),
+    (dict(T=(1 << 22) - 4095, ld=1 << 22), _lib.PA_EUNSUPPORTED),   # flag row would not fit in LDS
     (dict(), _lib.PA_EWORKSPACE),                 # no workspace
     (dict(ws=FAKE + 16, ws_bytes=1 << 30), _lib.PA_EWORKSPACE),  # workspace not 256-aligned
     (dict(ws=FAKE, ws_bytes=1), _lib.PA_EWORKSPACE),
@@ -66,6 +67,7 @@ def test_dense_rejects(kw, code):
     (dict(ld=7), _lib.PA_EINVAL),                 # 7 words < ceil(256 / 32)
     (dict(ld=8, d=96), _lib.PA_EUNSUPPORTED),
     (dict(ld=8, T=(1 << 22) + 1), _lib.PA_EINVAL),   # ld too small for that T
+    (dict(ld=1 << 17, T=(1 << 22) - 4095), _lib.PA_EUNSUPPORTED),  # longest key range exceeded
     (dict(ld=8), _lib.PA_EWORKSPACE),             # no workspace
 ])
 def test_dense_bits_rejects(kw, code):
