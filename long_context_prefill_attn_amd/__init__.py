@@ -24,7 +24,8 @@ from ._lib import PrefillAttnError, check, lib  # noqa: F401
 
 __all__ = ["prefill_attn_dense", "prefill_attn_dense_bits", "prefill_attn_dense_causal", "prefill_attn_dense_workspace",
            "build_pooled_index",
-           "select_blocks", "prefill_attn_blocksparse", "fold_keep_mask", "PrefillAttnError", "timing", "mfma_probe"]
+           "select_blocks", "prefill_attn_blocksparse", "fold_keep_mask", "PrefillAttnError", "timing", "mfma_probe",
+           "bisect_alpha", "calibrate_alpha"]
 
 
 def _stream() -> int:
@@ -239,6 +240,54 @@ def prefill_attn_blocksparse(Q, K, V, K_pool, V_pool, sel_idx, sel_cnt, q_start:
                                             float(scale), O.data_ptr(), _stream()),
           "prefill_attn_blocksparse")
     return O
+
+
+def bisect_alpha(skip_of, target: float, lo: float = 0.0, hi: float = 1.0, iters: int = 30):
+    """Smallest alpha in [lo, hi] whose skipped share reaches `target`, by bisection.
+
+    skip_of(alpha) -> skipped share of the visible blocks; it must be
+    non-decreasing in alpha. Selection sets shrink as alpha grows (a block kept
+    at some alpha is kept at every smaller one), so this holds for selections.
+    Returns (alpha, skip_of(alpha)). If even `hi` falls short, returns hi and its share."""
+    s_hi = skip_of(hi)
+    if s_hi < target:
+        return hi, s_hi
+    s_lo = skip_of(lo)
+    if s_lo >= target:
+        return lo, s_lo
+    for _ in range(iters):
+        mid = 0.5 * (lo + hi)
+        s = skip_of(mid)
+        if s >= target:
+            hi, s_hi = mid, s
+        else:
+            lo = mid
+    return hi, s_hi
+
+
+def calibrate_alpha(Q, K_pool, q_start: int, block: int, scale: float, target_skip: float,
+                    iters: int = 30, sink_tokens: int = 0, window_blocks: int = 0,
+                    dense_tail_blocks: int = 0):
+    """Per-prompt alpha: the smallest alpha whose selection skips at least
+    `target_skip` of this call's visible blocks. The FlashPrefill port picks alpha
+    per prompt length this way, to match a measured skip share ("Porting
+    FlashPrefill V2 to Apple silicon", A cheap map of where the attention lives).
+    Each probe is one select_blocks call on the device; only the per-block counts
+    (n_kv x n_qblk integers) come back to the host. Returns (alpha, skip)."""
+    C = Q.shape[0]
+    n_kv = K_pool.shape[0]
+    j0, j1 = q_start // block, (q_start + C - 1) // block
+    visible = n_kv * sum(j + 1 for j in range(j0, j1 + 1))
+    sel_idx = sel_cnt = None
+
+    def skip_of(alpha):
+        nonlocal sel_idx, sel_cnt
+        sel_idx, sel_cnt = select_blocks(Q, K_pool, q_start, block, alpha, scale, sel_idx, sel_cnt,
+                                         sink_tokens, window_blocks, dense_tail_blocks)
+        kept = int(sel_cnt.cpu().numpy().astype("int64").sum())
+        return 1.0 - kept / visible
+
+    return bisect_alpha(skip_of, target_skip, 0.0, 1.0, iters)
 
 
 def mfma_probe(operands, sink, iters: int) -> None:

@@ -175,3 +175,18 @@ def test_mfma_probe_rejects():
     assert f(FAKE, FAKE, 4, 0, None) == _lib.PA_EINVAL       # no iterations
     assert f(FAKE + 8, FAKE, 4, 10, None) == _lib.PA_EINVAL  # misaligned operands
     assert f(FAKE, None, 4, 10, None) == _lib.PA_EINVAL      # no sink
+
+
+def test_bisect_alpha_host_logic():
+    # a monotone step function with known jumps: the smallest alpha reaching each
+    # target is found to the bisection's resolution
+    import long_context_prefill_attn_amd as lp
+    steps = [(0.0, 0.0), (0.05, 0.30), (0.2, 0.62), (0.5, 0.85), (0.9, 0.97)]
+
+    def skip_of(a):
+        return max(s for x, s in steps if x <= a)
+    for target, want in [(0.3, 0.05), (0.6, 0.2), (0.85, 0.5), (0.9, 0.9)]:
+        a, s = lp.bisect_alpha(skip_of, target, iters=40)
+        assert abs(a - want) < 1e-9 and s >= target, (target, a, s)
+    assert lp.bisect_alpha(skip_of, 0.99) == (1.0, 0.97)    # unreachable: hi and its share
+    assert lp.bisect_alpha(skip_of, 0.0) == (0.0, 0.0)      # reached at lo

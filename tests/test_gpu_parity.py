@@ -375,6 +375,33 @@ def test_blocksparse_32k_sampled(lp):
     assert_close(got[rows], want, "sparse32k")
 
 
+def test_calibrate_alpha_planted_32k(lp):
+    """Per-prompt alpha on the planted 32K prompt: the share skipped at the
+    returned alpha reaches the target, a slightly smaller alpha falls short, and
+    the selection at the returned alpha equals the oracle's on sampled blocks."""
+    w = make_workload("sparse32k")
+    s = w.spec
+    B = s.block
+    Qd, Kd, Vd = dev_bf16(w.Q), dev_bf16(w.K), dev_bf16(w.V)
+    kp, _ = lp.build_pooled_index(Kd, Vd, B)
+    target = 0.80
+    a, skip = lp.calibrate_alpha(Qd, kp, 0, B, s.scale, target)
+    say("calibrated alpha", a, "skip", skip)
+    assert 0.0 < a < s.alpha and skip >= target
+    nb = s.N // B
+    visible = s.n_kv * nb * (nb + 1) // 2
+    _, cnt_below = lp.select_blocks(Qd, kp, 0, B, a * (1 - 1e-6), s.scale)
+    assert 1.0 - int(cnt_below.cpu().numpy().astype(np.int64).sum()) / visible < target
+    idx, cnt = lp.select_blocks(Qd, kp, 0, B, a, s.scale)
+    torch.cuda.synchronize()
+    idx, cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    rkp = pooled_index_ref(f64(w.K), f64(w.V), B)[0]
+    a32 = float(np.float32(a))   # the library takes alpha as fp32
+    sets = selection_sets(f64(w.Q), rkp, 0, B, a32, s.scale, qblocks=[20, 128, 255])
+    for (g, j), kept in sets.items():
+        assert cnt[g, j] == len(kept) and np.array_equal(idx[g, j, :len(kept)], kept), (g, j)
+
+
 # ---------------------------------------------------------------- chunked block-sparse
 def test_pool_incremental_bit_exact(lp):
     """Pooling chunk by chunk into one array with spare rows equals pooling the
