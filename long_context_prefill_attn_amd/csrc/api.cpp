@@ -17,8 +17,8 @@
 
 namespace {
 
-// Longest key range of the dense entry points: the workgroup keeps one flag byte
-// per 128-key tile in LDS after its K/V rings (128 KB), within the 160 KB of a CU.
+// Longest key range of the dense entry points: the workgroup keeps two flag bits
+// per 64-key step in LDS after its K/V rings (128 KB), within the 160 KB of a CU.
 constexpr int PA_MAX_T = (1 << 22) - 4096;
 
 thread_local std::string g_last_hip_error;

@@ -82,6 +82,13 @@ __device__ __forceinline__ int fresh_lane_id() {
 
 __device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
 
+static_assert(FLAG_KEYS == BN, "one mask-flag tile per key step");
+
+// The workgroup's flag row in LDS: two bits per 64-key step, 16 steps per word.
+__device__ __forceinline__ int step_flag(const uint32_t* frow, int st) {
+  return (int)((frow[st >> 4] >> (2 * (st & 15))) & 3u);
+}
+
 // One wave-wide 16-byte-per-lane buffer load into LDS. (Kept outside the
 // templates: hipcc's host pass drops kernel stubs when the buffer-resource type
 // appears inside templated device code.)
@@ -643,19 +650,19 @@ __device__ __forceinline__ void plain_steps(const TileLoader<D>& tl, uint16_t* l
 }
 
 // Plain-step sources (see plain_steps).
-// Dense: steps [a, b) whose 128-key flag tile is ZERO and whose 64 keys all lie below T.
+// Dense: steps [a, b) whose flag tile is ZERO and whose 64 keys all lie below T.
 // The walk keeps a 64-step window of plain bits in scalar registers, filled by one
 // wave-wide ballot over the LDS flag row; finding the next step is scalar bit
 // arithmetic, so an iteration never waits on an LDS read for it (the walk only
 // moves forward, and every lane of the wave is active in the step loop).
 struct DenseSrc {
   int a, b, T;
-  const uint8_t* frow;
+  const uint32_t* frow;
   int wbase;        // first step of the window
   uint64_t wmask;   // bit k: step wbase + k is plain
   __device__ void fill(int base) {
     const int sl = base + fresh_lane_id();
-    const bool p = sl < b && frow[sl >> 1] == TILE_ZERO && (sl + 1) * BN <= T;
+    const bool p = sl < b && step_flag(frow, sl) == TILE_ZERO && (sl + 1) * BN <= T;
     wbase = base;
     wmask = __ballot(p);
   }
@@ -750,21 +757,22 @@ attn_dense_kernel(const uint16_t* __restrict__ Q, int C, int n_q, const uint16_t
   const int wph = R / 32;   // waves per head
   const int head = g * group + hs * Hg + wave / wph;
 
-  // the workgroup's rows' mask-tile flags, combined over the (one or two) flag
-  // rows they span and copied to LDS after the rings: walking the steps never
-  // waits on global memory
-  uint8_t* frow = reinterpret_cast<uint8_t*>(lds + Geo<D>::RING);
-  const int fr0 = (qt * R) / FLAG_TILE;
-  const int fr1 = (min(qt * R + R, C) - 1) / FLAG_TILE;
+  // the workgroup's rows' mask-tile flags (one per 64-key step), combined over
+  // the (one or two) flag rows they span and copied to LDS after the rings, two
+  // bits each (16 steps per word): walking the steps never waits on global memory
+  uint32_t* frow = reinterpret_cast<uint32_t*>(lds + Geo<D>::RING);
+  const int fr0 = (qt * R) / FLAG_ROWS;
+  const int fr1 = (min(qt * R + R, C) - 1) / FLAG_ROWS;
   if (tid == 0) { s_lo = n_ktile; s_hi = 0; }
+  for (int wd = tid; wd < (n_ktile + 15) / 16; wd += NT) frow[wd] = 0u;
   __syncthreads();
   for (int t = tid; t < n_ktile; t += NT) {
     uint8_t f;
     if (causal_q0 >= 0) {
       // causal by position: rows causal_q0 + [qt*R, min(qt*R + R, C)); flags (if any)
-      // classify the per-key mask's 128-key tiles
+      // classify the per-key mask's 64-key tiles
       const int rmin = causal_q0 + qt * R, rmax = causal_q0 + min(qt * R + R, C) - 1;
-      const int k0 = t * FLAG_TILE, k1 = k0 + FLAG_TILE - 1;
+      const int k0 = t * FLAG_KEYS, k1 = k0 + FLAG_KEYS - 1;
       f = k0 > rmax ? TILE_DROPPED : (k1 <= rmin ? TILE_ZERO : TILE_MIXED);
       if (flags != nullptr) {
         const uint8_t kf = flags[t];
@@ -779,13 +787,13 @@ attn_dense_kernel(const uint16_t* __restrict__ Q, int C, int n_q, const uint16_t
         f = (f == f2) ? f : TILE_MIXED;
       }
     }
-    frow[t] = f;
+    if (f != TILE_ZERO) atomicOr(&frow[t >> 4], (uint32_t)f << (2 * (t & 15)));
     if (f != TILE_DROPPED) { atomicMin(&s_lo, t); atomicMax(&s_hi, t + 1); }
   }
   __syncthreads();
   const int n_steps = (T + BN - 1) / BN;
-  const int st_lo = s_lo * (FLAG_TILE / BN);
-  const int st_hi = min(s_hi * (FLAG_TILE / BN), n_steps);
+  const int st_lo = s_lo;
+  const int st_hi = min(s_hi, n_steps);
   const int len = max(st_hi - st_lo, 0);
   const int a = st_lo + (int)((long)len * split / splits);
   const int b = st_lo + (int)((long)len * (split + 1) / splits);
@@ -837,7 +845,7 @@ attn_dense_kernel(const uint16_t* __restrict__ Q, int C, int n_q, const uint16_t
   auto next_special = [&](int st) -> int {
     for (int base = st; base < b; base += 64) {
       const int sl = base + lane2;
-      const uint8_t fl = sl < b ? frow[sl >> 1] : TILE_DROPPED;
+      const int fl = sl < b ? step_flag(frow, sl) : TILE_DROPPED;
       const uint64_t hit = __ballot(!(fl == TILE_DROPPED || (fl == TILE_ZERO && (sl + 1) * BN <= T)));
       if (hit != 0) return base + __builtin_ctzll(hit);
     }
@@ -862,7 +870,7 @@ attn_dense_kernel(const uint16_t* __restrict__ Q, int C, int n_q, const uint16_t
         wait_vm<0>();
       }
       __syncthreads();
-      const uint8_t f = frow[st >> 1];
+      const int f = step_flag(frow, st);
       const uint16_t* kt = lds + buf * TL;
       const uint16_t* vt = lds + (KRK + buf) * TL;
       cx.key0 = st * BN;
@@ -1094,8 +1102,8 @@ DensePlan plan_dense(int C, int T, int n_q, int n_kv, int d) {
   p.hg_log2 = hg_log2_for(n_q, n_kv);
   const int R = 256 >> p.hg_log2;
   p.n_qt = (C + R - 1) / R;
-  p.n_ktile = (T + FLAG_TILE - 1) / FLAG_TILE;
-  p.n_qft = (C + FLAG_TILE - 1) / FLAG_TILE;
+  p.n_ktile = (T + FLAG_KEYS - 1) / FLAG_KEYS;
+  p.n_qft = (C + FLAG_ROWS - 1) / FLAG_ROWS;
   const long wgs = (long)p.n_qt * (n_q >> p.hg_log2);
   const int target = 2 * num_cus();             // two rounds of one resident workgroup per CU
   const int n_steps = (T + BN - 1) / BN;
@@ -1120,7 +1128,7 @@ static hipError_t dense_impl(const uint16_t* Q, int C, int n_q, const uint16_t* 
                              float* part_ml, int causal_q0, hipStream_t stream, bool mask_bits) {
   const float sl2 = scale * LOG2E;
   const int grid = p.n_qt * (n_q >> p.hg_log2) * p.splits;
-  const size_t lds = Geo<D>::LDS_BYTES + ((p.n_ktile + 15) & ~15);   // rings + flag row
+  const size_t lds = Geo<D>::LDS_BYTES + (size_t)((p.n_ktile + 63) / 64) * 16;   // rings + 2-bit flag row
   const bool vec = (mask_ld % 4 == 0) && (reinterpret_cast<uintptr_t>(mask) % 8 == 0);
   const int mask_mode = mask_bits ? MASK_BITS : vec ? MASK_F16_VEC : MASK_F16;
   if (p.splits > 1) {

@@ -13,9 +13,12 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// tile classification of the additive mask (one flag per 128 x 128 tile)
+// tile classification of the additive mask: one flag per tile of 64 rows x 64
+// keys (64 keys = one step of the attention kernels' key loop; 64 rows = the
+// rows of a dense workgroup when it packs four query heads)
 enum : uint8_t { TILE_ZERO = 0, TILE_DROPPED = 1, TILE_MIXED = 2 };
-constexpr int FLAG_TILE = 128;
+constexpr int FLAG_ROWS = 64;
+constexpr int FLAG_KEYS = 64;
 
 // fp16 bit pattern of -30000; an entry is "dropped" when its value is <= -30000
 constexpr uint16_t F16_DROP_MAG = 0x7753;
@@ -75,8 +78,8 @@ hipError_t launch_fold_keep(const int32_t* keep_idx, int64_t keep_ld, const int3
 struct DensePlan {
   int hg_log2;   // log2 of the query heads packed into one workgroup
   int n_qt;      // query tiles of 256 >> hg_log2 rows
-  int n_qft;     // query rows of 128-row mask-flag tiles
-  int n_ktile;   // flag tiles of 128 keys
+  int n_qft;     // rows of mask-flag tiles (64 query rows each)
+  int n_ktile;   // flag tiles along the keys (64 keys each)
   int splits;    // key-range splits per (query tile, head slice)
   size_t flags_bytes, part_o_bytes, part_ml_bytes, total_bytes;
 };

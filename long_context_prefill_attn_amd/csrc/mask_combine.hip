@@ -4,15 +4,15 @@
 namespace pa {
 
 // ---------------------------------------------------------------------------
-// mask_classify: one workgroup per 128 x 128 tile of the fp16 mask.
+// mask_classify: one workgroup per tile of 64 rows x 64 keys of the fp16 mask.
 // ZERO     every entry is +-0      -> the attention kernel never reads the tile
 // DROPPED  every entry <= -30000   -> the attention kernel skips the tile
 // MIXED    anything else           -> the attention kernel reads the tile
 // A dropped entry omits its key ("ANE Prefill Research", What worked, item 2),
 // so a fully dropped tile contributes nothing and needs no arithmetic at all.
-// Each thread reads 8 x 16 bytes (rows tid/16 + 16i, columns (tid%16)*8 ..):
-// 16 lanes cover one 256-byte tile row, so a wave reads 4 rows per instruction.
-// grid = (ceil(T/128), ceil(C/128)), block = 256.
+// Each thread reads 2 x 16 bytes (rows tid/8 + 32i, columns (tid%8)*8 ..):
+// 8 lanes cover one 128-byte tile row, so a wave reads 8 rows per instruction.
+// grid = (ceil(T/64), ceil(C/64)), block = 256.
 // ---------------------------------------------------------------------------
 template <bool VEC>
 __global__ void __launch_bounds__(256) mask_classify_kernel(const uint16_t* __restrict__ mask,
@@ -20,11 +20,11 @@ __global__ void __launch_bounds__(256) mask_classify_kernel(const uint16_t* __re
                                                             uint8_t* __restrict__ flags) {
   const int kt = blockIdx.x, qt = blockIdx.y;
   const int tid = threadIdx.x;
-  const int c0 = kt * FLAG_TILE + (tid % 16) * 8;
+  const int c0 = kt * FLAG_KEYS + (tid % 8) * 8;
   bool all_zero = true, all_drop = true;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = qt * FLAG_TILE + tid / 16 + 16 * i;
+  for (int i = 0; i < FLAG_ROWS / 32; ++i) {
+    const int r = qt * FLAG_ROWS + tid / 8 + 32 * i;
     if (r >= C) break;
     const uint16_t* p = mask + (size_t)r * ld + c0;
     if (VEC && c0 + 8 <= T) {
@@ -108,20 +108,20 @@ hipError_t launch_fold_keep(const int32_t* keep_idx, int64_t keep_ld, const int3
   return hipGetLastError();
 }
 
-// mask_classify for a bit-packed mask: one workgroup per 128 x 128 tile (128 rows x
-// 4 words); only the bits of keys below T count.
+// mask_classify for a bit-packed mask: one workgroup per tile of 64 rows x 64 keys
+// (64 rows x 2 words, one word per thread of the first 128); only the bits of
+// keys below T count.
 __global__ void __launch_bounds__(256) mask_classify_bits_kernel(const uint32_t* __restrict__ bits,
                                                                  int64_t ld, int C, int T,
                                                                  uint8_t* __restrict__ flags) {
   const int kt = blockIdx.x, qt = blockIdx.y;
   bool all_keep = true, all_drop = true;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int p = threadIdx.x + 256 * j;
-    const int r = qt * FLAG_TILE + (p >> 2);
-    const int wi = kt * (FLAG_TILE / 32) + (p & 3);
+  {
+    const int p = threadIdx.x;
+    const int r = qt * FLAG_ROWS + (p >> 1);
+    const int wi = kt * (FLAG_KEYS / 32) + (p & 1);
     const int nvalid = min(max(T - 32 * wi, 0), 32);
-    if (r < C && nvalid > 0) {
+    if (p < 2 * FLAG_ROWS && r < C && nvalid > 0) {
       const uint32_t vmask = nvalid == 32 ? ~0u : ((1u << nvalid) - 1u);
       const uint32_t w = bits[(size_t)r * ld + wi] & vmask;
       all_keep &= w == vmask;
@@ -136,14 +136,14 @@ __global__ void __launch_bounds__(256) mask_classify_bits_kernel(const uint32_t*
 
 hipError_t launch_mask_classify_bits(const uint32_t* bits, int64_t bits_ld, int C, int T,
                                      uint8_t* flags, hipStream_t stream) {
-  const dim3 grid((T + FLAG_TILE - 1) / FLAG_TILE, (C + FLAG_TILE - 1) / FLAG_TILE);
+  const dim3 grid((T + FLAG_KEYS - 1) / FLAG_KEYS, (C + FLAG_ROWS - 1) / FLAG_ROWS);
   hipLaunchKernelGGL(mask_classify_bits_kernel, grid, dim3(256), 0, stream, bits, bits_ld, C, T, flags);
   return hipGetLastError();
 }
 
 hipError_t launch_mask_classify(const uint16_t* mask, int64_t mask_ld, int C, int T,
                                 uint8_t* flags, hipStream_t stream) {
-  dim3 grid((T + FLAG_TILE - 1) / FLAG_TILE, (C + FLAG_TILE - 1) / FLAG_TILE);
+  dim3 grid((T + FLAG_KEYS - 1) / FLAG_KEYS, (C + FLAG_ROWS - 1) / FLAG_ROWS);
   const bool vec = (mask_ld % 8) == 0 && (reinterpret_cast<uintptr_t>(mask) % 16) == 0;
   if (vec)
     hipLaunchKernelGGL(mask_classify_kernel<true>, grid, dim3(256), 0, stream, mask, mask_ld, C, T,
