@@ -969,13 +969,18 @@ attn_blocksparse_kernel(const uint16_t* __restrict__ Q, int C, int q_start, int 
   const int group = n_q / n_kv;
   const int hpw = (group % 2 == 0) ? 2 : 1;   // query heads per workgroup
 
+  // workgroup ids, after the XCD remap, run KV head by KV head, longest query
+  // blocks first, with the head pairs of one (KV head, query block) adjacent:
+  // they share the selection, so the second reads the first's K/V tiles from L2
   const int bid = remap_xcd(blockIdx.x, gridDim.x);
-  const int hp = bid / n_qblk;                  // head pair (or single head)
-  const int jj = n_qblk - 1 - bid % n_qblk;
+  const int hpk = group / hpw;                  // workgroups per (KV head, query block)
+  const int g = bid / (n_qblk * hpk);
+  const int rr = bid % (n_qblk * hpk);
+  const int jj = n_qblk - 1 - rr / hpk;
+  const int hp = g * hpk + rr % hpk;            // head pair (or single head)
   const int j = q_start / BLK + jj;
   const int head = hp * hpw + (hpw == 2 ? (wave >> 2) : 0);
   const bool storer = hpw == 2 || wave < 4;
-  const int g = (hp * hpw) / group;
   const int32_t* sl = sel_idx + ((size_t)g * n_qblk + jj) * nb;
   const int cnt = sel_cnt[(size_t)g * n_qblk + jj];
 
