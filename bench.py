@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="budget for the CPU oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 512 MiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--no-oneshot", action="store_true",
+                    help="skip the one-shot dense comparator (one call over the whole 32K prompt)")
     ap.add_argument("--no-mfma-ceiling", action="store_true",
                     help="skip the register-only MFMA calibration (random vs zero bf16 operands)")
     ap.add_argument("--parts", default="dense,blocksparse",
@@ -233,6 +235,27 @@ def main():
     lp.timing.enable(False)
 
     ms_step = wall * 1e3 / args.steps
+
+    # the one-shot dense comparator for the block-sparse half (one call over the
+    # whole prompt under its causal mask), timed after the step loop
+    oneshot_ms = None
+    if do_sparse and run_dense_part and not chunked_sparse and not args.no_oneshot:
+        r_ = torch.arange(N, device=dev)
+        mask_full = torch.where(r_[None, :] <= r_[:, None], 0.0, -30000.0).to(torch.float16)
+        del r_
+        ws1 = torch.empty(max(lp.prefill_attn_dense_workspace(N, N, Hq, Hkv, d), 256), dtype=torch.uint8,
+                          device=dev)
+        lp.prefill_attn_dense(Q, K, V, mask_full, scale, O=O_dense, workspace=ws1)
+        ts = []
+        for _ in range(3):
+            e0, e1 = ev(), ev()
+            e0.record()
+            lp.prefill_attn_dense(Q, K, V, mask_full, scale, O=O_dense, workspace=ws1)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        oneshot_ms = float(np.median(ts))
+        del mask_full, ws1
     dense_ms = float(np.median([a.elapsed_time(b) for a, b, _ in part_ev]))
     sparse_ms = float(np.median([b.elapsed_time(c) for _, b, c in part_ev])) if do_sparse else 0.0
     kern = {}
@@ -259,6 +282,11 @@ def main():
         visible = nb * (nb + 1) // 2 * Hkv   # chunks cover each query block once (4,096 = 32 B)
         kept = sum(int(sc.sum().item()) for _, sc in sel)
         sparsity = 1.0 - kept / visible
+        # the work the method does: exact keys of the kept blocks (the diagonal
+        # causally) plus one pooled row per skipped visible block, 4 d FLOP per
+        # (query head, row, key or pooled row)
+        exact_flops = 4.0 * d * (Hq // Hkv) * sum(
+            exact_pairs(sc.cpu().numpy(), q0, C, B) for (q0, C), (_, sc) in zip(sparse_calls, sel))
     tflops = (flops_dense + flops_sparse) / (ms_step * 1e-3) / 1e12
 
     # roofline of the dominant kernel: dense attention, algorithmic FLOPs per launch
@@ -288,7 +316,17 @@ def main():
                                                               / PEAK_BF16_TFLOPS, 2),
                                 "tokens_per_s": round(N / (sparse_ms * 1e-3)),
                                 "skipped_block_fraction": round(sparsity, 4),
+                                "exact_work_tflops": round(exact_flops / (sparse_ms * 1e-3) / 1e12, 2),
+                                "exact_work_pct_peak": round(100 * exact_flops / (sparse_ms * 1e-3) / 1e12
+                                                             / PEAK_BF16_TFLOPS, 2),
                                 "speedup_vs_dense": round(dense_ms / sparse_ms, 3) if run_dense_part else None}
+        if oneshot_ms is not None:
+            parts["dense_oneshot"] = {"ms": round(oneshot_ms, 3),
+                                      "tflops": round(flops_sparse / (oneshot_ms * 1e-3) / 1e12, 2),
+                                      "pct_peak": round(100 * flops_sparse / (oneshot_ms * 1e-3) / 1e12
+                                                        / PEAK_BF16_TFLOPS, 2)}
+            parts["blocksparse"]["speedup_vs_oneshot_dense"] = round(oneshot_ms / sparse_ms, 3)
+            parts["blocksparse"]["speedup_vs_faster_dense"] = round(min(oneshot_ms, dense_ms) / sparse_ms, 3)
 
     ceiling = None if args.no_mfma_ceiling else mfma_ceiling(lp, torch, dev, props.multi_processor_count)
     if ceiling:
@@ -319,6 +357,24 @@ def main():
         "device": {"name": props.name, "cus": props.multi_processor_count},
     }
     print(json.dumps(line), flush=True)
+
+
+def exact_pairs(cnt, q0, C, B):
+    """(row, key) pairs one query head computes in a block-sparse call, pooled
+    rows counted as one key each: for query block j with c kept blocks (the
+    diagonal included) and rows [rlo, rhi) of the call, rows x (c - 1) x B exact
+    keys, the diagonal's causal keys, and rows x (j - (c - 1)) pooled rows;
+    summed over the KV heads (cnt is [n_kv][n_qblk])."""
+    total = 0
+    j0 = q0 // B
+    for jj in range(cnt.shape[1]):
+        j = j0 + jj
+        rlo, rhi = max(j * B, q0), min((j + 1) * B, q0 + C)
+        rows = rhi - rlo
+        diag = sum(p - j * B + 1 for p in range(rlo, rhi))
+        c = cnt[:, jj].astype(np.int64)
+        total += int((rows * (c - 1) * B + diag + rows * (j - (c - 1))).sum())
+    return total
 
 
 def mfma_ceiling(lp, torch, dev, cus):
