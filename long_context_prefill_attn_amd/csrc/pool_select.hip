@@ -263,7 +263,9 @@ __device__ __forceinline__ void exact_pairs(SelShared<D>& S, const uint32_t* lis
 }
 
 template <int D>
-__global__ void __launch_bounds__(SEL_THREADS) select_kernel(
+// Four waves per SIMD (at most 128 registers): two workgroups share a CU, so one
+// workgroup's staging and barriers overlap the other's scoring.
+__global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_eu(4))) select_kernel(
     const uint16_t* __restrict__ Q, int C, int q_start, int n_q, int n_kv,
     const float* __restrict__ Kp, int pool_ld, int nb, int block, double theta, float theta_f,
     float theta_slack,
