@@ -214,6 +214,21 @@ def test_dense_planted_32k_sampled_rows(lp):
         assert_close(got[rows], want, f"planted 32K dense chunk {ci}")
 
 
+def test_dense_planted_32k_oneshot_sampled_rows(lp):
+    """The one-shot dense comparator of the benchmark: one call over the whole
+    planted 32K prompt (C = T = 32,768) under its causal mask, sampled rows of
+    every head across the prompt."""
+    w = make_workload("sparse32k")
+    s = w.spec
+    N = s.N
+    mask = causal_mask(0, N)
+    say("planted 32K dense one-shot")
+    got = gpu_dense(lp, w.Q, w.K, w.V, mask, s.scale)
+    rows = np.concatenate([np.arange(0, N, 1021), [N - 1]])
+    want = dense_ref(f64(w.Q[rows]), f64(w.K), f64(w.V), mask[rows], s.scale)
+    assert_close(got[rows], want, "planted 32K dense one-shot")
+
+
 # ---------------------------------------------------------------- dense: edge cases
 def _edge(seed, C, T, n_q, n_kv, d, kind):
     rng = np.random.default_rng(seed)
