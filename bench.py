@@ -390,20 +390,22 @@ def mfma_ceiling(lp, torch, dev, cus):
     iters = 6000
     flops = 4 * cus * 8 * iters * 32 * 32768.0
     out = {}
-    for name, ops in (("random_bf16_tflops", rnd), ("zero_tflops", zero)):
-        lp.mfma_probe(ops, sink, 200)
+    for name, ops, shape in (("random_bf16_tflops", rnd, 32), ("zero_tflops", zero, 32),
+                             ("random_bf16_16x16x32_tflops", rnd, 16)):
+        lp.mfma_probe(ops, sink, 200, shape)
         best = float("inf")
         for _ in range(3):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            lp.mfma_probe(ops, sink, iters)
+            lp.mfma_probe(ops, sink, iters, shape)
             e1.record()
             torch.cuda.synchronize()
             best = min(best, e0.elapsed_time(e1))
         out[name] = round(flops / (best * 1e-3) / 1e12, 1)
     out["random_frac_of_peak"] = round(out["random_bf16_tflops"] / PEAK_BF16_TFLOPS, 4)
-    out["probe"] = (f"{4 * cus} workgroups x 8 waves, {iters} x 32 v_mfma_f32_32x32x16_bf16 per wave "
-                    "from registers, 4 independent accumulators")
+    out["probe"] = (f"{4 * cus} workgroups x 8 waves, {iters} x 32 v_mfma_f32_32x32x16_bf16 (the attention "
+                    "kernels' shape; 4 accumulators) or the same FLOPs as 16x16x32 (8 accumulators) per "
+                    "wave, from registers")
     return out
 
 

@@ -290,15 +290,19 @@ int pa_timing_read(const char* kernel, double* total_ms, int64_t* launches);
  * attention path): the bf16 MFMA rate the part sustains from registers for
  * given operand data. Enqueues `grid` workgroups of 512 threads. Thread t takes
  * the 16 operand slots operands[(16 t + i) mod 65536], i < 16, of 16 bytes each
- * (so `operands` is a device buffer of 1 MiB, filled by the caller), runs
- * `iters` x 32 v_mfma_f32_32x32x16_bf16 from registers on four independent
- * accumulators, and writes one float to sink[t] (`sink`: grid * 512 floats).
- * FLOPs = grid * 8 * iters * 32 * 32768. Random bf16 operands against zeros
- * show how far the operand-dependent power draw of the matrix cores pulls the
- * clock below the one the published peak assumes.
- * Requires 16-byte aligned pointers, grid >= 1, iters >= 1. Errors: PA_EINVAL, PA_EHIP.
+ * (so `operands` is a device buffer of 1 MiB, filled by the caller). It runs
+ * from registers either `iters` x 32 v_mfma_f32_32x32x16_bf16 on four
+ * independent accumulators (shape 32), or `iters` x 64
+ * v_mfma_f32_16x16x32_bf16 on eight (shape 16). It writes one float to sink[t]
+ * (`sink`: grid * 512 floats).
+ * FLOPs = grid * 8 * iters * 32 * 32768 for either shape. Random bf16 operands
+ * against zeros show how far the operand-dependent power draw of the matrix
+ * cores pulls the clock below the one the published peak assumes; the two
+ * shapes differ in register-file traffic per multiply-add.
+ * Requires 16-byte aligned pointers, grid >= 1, iters >= 1, shape 32 or 16.
+ * Errors: PA_EINVAL, PA_EHIP.
  */
-int pa_mfma_probe(const uint16_t* operands, float* sink, int grid, int iters, void* stream);
+int pa_mfma_probe(const uint16_t* operands, float* sink, int grid, int iters, int shape, void* stream);
 
 #ifdef __cplusplus
 }

@@ -290,16 +290,17 @@ def calibrate_alpha(Q, K_pool, q_start: int, block: int, scale: float, target_sk
     return bisect_alpha(skip_of, target_skip, 0.0, 1.0, iters)
 
 
-def mfma_probe(operands, sink, iters: int) -> None:
+def mfma_probe(operands, sink, iters: int, shape: int = 32) -> None:
     """Matrix-core calibration (pa_mfma_probe): operands = 1 MiB device buffer of
     bf16 bits (65,536 slots of 16 bytes), sink = fp32 [grid * 512]; enqueues
-    grid = sink.numel() // 512 workgroups of iters x 32 bf16 MFMAs per wave."""
+    grid = sink.numel() // 512 workgroups of iters x 32 32x32x16 (shape 32) or
+    iters x 64 16x16x32 (shape 16) bf16 MFMAs per wave."""
     if not (operands.is_cuda and sink.is_cuda and sink.dtype == torch.float32):
         raise ValueError("operands and sink must be device tensors (sink fp32)")
     if operands.numel() * operands.element_size() < (1 << 20) or sink.numel() < 512:
         raise ValueError("operands needs 1 MiB, sink at least 512 floats")
     check(lib().pa_mfma_probe(operands.data_ptr(), sink.data_ptr(), sink.numel() // 512, int(iters),
-                              _stream()), "pa_mfma_probe")
+                              int(shape), _stream()), "pa_mfma_probe")
 
 
 class timing:

@@ -328,10 +328,12 @@ int prefill_attn_blocksparse(const uint16_t* Q, int C, int q_start, int n_q, con
                                      stream);
 }
 
-int pa_mfma_probe(const uint16_t* operands, float* sink, int grid, int iters, void* stream) {
+int pa_mfma_probe(const uint16_t* operands, float* sink, int grid, int iters, int shape, void* stream) {
   if (!aligned16(operands) || !aligned16(sink) || grid < 1 || iters < 1) return PA_EINVAL;
+  if (shape != 32 && shape != 16) return PA_EINVAL;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  return hip_status(timed("mfma_probe", s, [&] { return pa::launch_mfma_probe(operands, sink, grid, iters, s); }));
+  return hip_status(
+      timed("mfma_probe", s, [&] { return pa::launch_mfma_probe(operands, sink, grid, iters, shape, s); }));
 }
 
 int pa_timing_enable(int on) {

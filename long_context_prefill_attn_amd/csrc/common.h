@@ -9,6 +9,7 @@ namespace pa {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -102,6 +103,7 @@ hipError_t launch_attn_blocksparse(const uint16_t* Q, int C, int q_start, int n_
                                    const int32_t* sel_idx, const int32_t* sel_cnt,
                                    float scale, float* O, hipStream_t stream);
 
-hipError_t launch_mfma_probe(const uint16_t* operands, float* sink, int grid, int iters, hipStream_t stream);
+hipError_t launch_mfma_probe(const uint16_t* operands, float* sink, int grid, int iters, int shape,
+                             hipStream_t stream);
 
 }  // namespace pa

@@ -171,10 +171,11 @@ def test_timing_api_host_side():
 
 def test_mfma_probe_rejects():
     f = _lib.lib().pa_mfma_probe
-    assert f(FAKE, FAKE, 0, 10, None) == _lib.PA_EINVAL      # no workgroups
-    assert f(FAKE, FAKE, 4, 0, None) == _lib.PA_EINVAL       # no iterations
-    assert f(FAKE + 8, FAKE, 4, 10, None) == _lib.PA_EINVAL  # misaligned operands
-    assert f(FAKE, None, 4, 10, None) == _lib.PA_EINVAL      # no sink
+    assert f(FAKE, FAKE, 0, 10, 32, None) == _lib.PA_EINVAL      # no workgroups
+    assert f(FAKE, FAKE, 4, 0, 32, None) == _lib.PA_EINVAL       # no iterations
+    assert f(FAKE + 8, FAKE, 4, 10, 32, None) == _lib.PA_EINVAL  # misaligned operands
+    assert f(FAKE, None, 4, 10, 32, None) == _lib.PA_EINVAL      # no sink
+    assert f(FAKE, FAKE, 4, 10, 8, None) == _lib.PA_EINVAL       # no such MFMA shape
 
 
 def test_bisect_alpha_host_logic():

@@ -771,15 +771,17 @@ def test_dense_bits(lp, C, T, n_q, n_kv, d, kind, words):
     assert np.array_equal(got.view(np.uint32), same.view(np.uint32))
 
 
-def test_mfma_probe_calibration_kernel(lp):
+@pytest.mark.parametrize("shape", [32, 16])
+def test_mfma_probe_calibration_kernel(lp, shape):
     # the benchmark's matrix-core calibration: zero operands give exactly zero sums;
-    # unit operands add 16 per MFMA to each accumulator element, 8 MFMAs per chain
-    # per iteration, and the 64 elements of a lane's four chains are summed
+    # unit operands add K per MFMA to each accumulator element (K = 16 for 32x32x16,
+    # 32 for 16x16x32), 8 MFMAs per chain per iteration, and a lane sums its chains'
+    # elements (4 x 16 or 8 x 4): 8192 x iters either way
     import torch
     sink = torch.full((2 * 512,), float("nan"), dtype=torch.float32, device="cuda")
-    lp.mfma_probe(torch.zeros(1 << 19, dtype=torch.bfloat16, device="cuda"), sink, 3)
+    lp.mfma_probe(torch.zeros(1 << 19, dtype=torch.bfloat16, device="cuda"), sink, 3, shape)
     torch.cuda.synchronize()
     assert torch.equal(sink, torch.zeros_like(sink))
-    lp.mfma_probe(torch.ones(1 << 19, dtype=torch.bfloat16, device="cuda"), sink, 3)
+    lp.mfma_probe(torch.ones(1 << 19, dtype=torch.bfloat16, device="cuda"), sink, 3, shape)
     torch.cuda.synchronize()
-    assert torch.equal(sink, torch.full_like(sink, 64.0 * 16 * 8 * 3))
+    assert torch.equal(sink, torch.full_like(sink, 8192.0 * 3))
