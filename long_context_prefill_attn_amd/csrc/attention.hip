@@ -879,6 +879,8 @@ attn_dense_kernel(const uint16_t* __restrict__ Q, int C, int n_q, const uint16_t
         attn_step<D, MODE_CAUSAL_K, true>(kt, vt, lo2, qf, o, m, l, cx);
       else if (f == TILE_MIXED && mask_mode == MASK_BITS)
         attn_step<D, MODE_GBITS, true>(kt, vt, lo2, qf, o, m, l, cx);
+      else if (f == TILE_MIXED && cx.kvalid == BN)   // a full step: 8-byte mask loads where aligned
+        attn_step<D, MODE_GMASK, false>(kt, vt, lo2, qf, o, m, l, cx);
       else if (f == TILE_MIXED)
         attn_step<D, MODE_GMASK, true>(kt, vt, lo2, qf, o, m, l, cx);
       else
