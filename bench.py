@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill32k",
-                    choices=["prefill32k", "dense128k", "sparse128k", "fold2k5"])
+                    choices=["prefill32k", "dense128k", "sparse128k", "fold2k5", "gqa4k"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--dense-entry", default="mask", choices=["mask", "causal", "bits"],
                     help="dense part: prefill_attn_dense over a causal fp16 mask (default), "
@@ -138,6 +138,12 @@ def main():
         w = make_workload("sparse128k")
         chunks = w.spec.chunks
         do_sparse = "blocksparse" in args.parts.split(",")
+    elif args.workload == "gqa4k":
+        # the ~4,333-token prompt: chunk 4,096 at history 0, then the 237-row tail
+        # chunk over the 4,096-token history (16 query heads, 4 KV heads)
+        w = make_workload("gqa4k")
+        chunks = w.spec.chunks
+        do_sparse = False
     elif args.workload == "fold2k5":
         # the ~2,500-token narrow-chunk prompt; each step folds the indexer's keep
         # lists into the chunk masks on the device, then runs dense attention
