@@ -263,6 +263,8 @@ def _edge(seed, C, T, n_q, n_kv, d, kind):
     (256, 4096, 4, 2, 128, "band", 4104),
     (100, 100, 6, 2, 64, "causal", None),
     (37, 4100, 4, 4, 128, "random", None),      # split path with a random mask
+    (300, 2000, 8, 1, 128, "random", None),     # eight heads per workgroup: 32 rows, half a flag row
+    (200, 3000, 16, 2, 64, "band", None),       # the same with whole dropped tiles
 ])
 def test_dense_edge_cases(lp, C, T, n_q, n_kv, d, kind, ld):
     q, k, v, mask = _edge(C * 7 + T, C, T, n_q, n_kv, d, kind)
@@ -329,6 +331,8 @@ def _blocksparse_gpu(lp, q, k, v, q_start, block, alpha, scale):
     (1, 1000, 300, 4, 1, 128, 0.2, 1.0),     # chunk starts mid-block, ragged end
     (2, 700, 0, 2, 2, 64, 0.05, 1.0),
     (3, 2048, 1024, 8, 2, 128, 0.5, 0.5),    # small |q|: pooled rows carry real weight
+    (4, 1500, 200, 6, 2, 128, 0.1, 1.0),     # three query heads per KV head: one head per workgroup
+    (5, 1300, 0, 8, 1, 64, 0.1, 1.0),        # eight query heads per KV head: four workgroups per block
 ])
 def test_blocksparse_small(lp, seed, N, q_start, n_q, n_kv, d, alpha, s):
     rng = np.random.default_rng(seed)
