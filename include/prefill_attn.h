@@ -172,7 +172,8 @@ int build_pooled_index(const uint16_t* K, const uint16_t* V, int T, int n_kv, in
  * alpha = 0 keeps every block). The selection of (KV head g, query block j) is
  * the union of the votes of this call's rows in block j over g's query heads,
  * plus j itself. sel_idx lists it in ascending order (so j comes last) and is
- * zero past sel_cnt.
+ * zero past sel_cnt. Until the call completes, sel_idx may also hold partial
+ * votes, so it must not overlap Q or K_pool.
  * Requires alpha finite and >= 0, scale finite and > 0,
  * ceil(T/block) <= 8192.
  * Errors: PA_EINVAL, PA_EUNSUPPORTED, PA_EHIP.
@@ -278,7 +279,8 @@ int prefill_attn_blocksparse_ld(const uint16_t* Q, int C, int q_start, int n_q,
  * recorded on the launch stream. pa_timing_read synchronises those events and
  * returns the summed milliseconds and launch count for `kernel`, one of
  * "attn_dense", "attn_blocksparse", "mask_classify", "attn_combine", "pool", "select", "fold",
- * "mfma_probe".
+ * "mfma_probe". "select" covers the selection kernel and, when the call splits
+ * its voters over several workgroups, the merge kernel after it.
  * pa_timing_reset clears the totals. Returns PA_OK or PA_EINVAL/PA_EHIP.
  */
 int pa_timing_enable(int on);

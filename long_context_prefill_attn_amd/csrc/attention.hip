@@ -1081,7 +1081,7 @@ attn_blocksparse_kernel(const uint16_t* __restrict__ Q, int C, int q_start, int 
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
-static int num_cus() {
+int device_cus() {
   static int cus = 0;
   if (cus == 0) {
     int dev = 0;
@@ -1112,7 +1112,7 @@ DensePlan plan_dense(int C, int T, int n_q, int n_kv, int d) {
   p.n_ktile = (T + FLAG_KEYS - 1) / FLAG_KEYS;
   p.n_qft = (C + FLAG_ROWS - 1) / FLAG_ROWS;
   const long wgs = (long)p.n_qt * (n_q >> p.hg_log2);
-  const int target = 2 * num_cus();             // two rounds of one resident workgroup per CU
+  const int target = 2 * device_cus();             // two rounds of one resident workgroup per CU
   const int n_steps = (T + BN - 1) / BN;
   int splits = 1;
   if (wgs < target) splits = (int)((target + wgs - 1) / wgs);

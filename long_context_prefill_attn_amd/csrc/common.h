@@ -57,6 +57,9 @@ namespace pa {
 
 struct KernelTimer;  // opaque; see api.cpp
 
+// compute units of the current device (256 if the query fails); read once
+int device_cus();
+
 hipError_t launch_pool(const uint16_t* K, const uint16_t* V, int T, int n_kv, int d, int block,
                        int b_first, float* K_pool, float* V_pool, int pool_ld, hipStream_t stream);
 

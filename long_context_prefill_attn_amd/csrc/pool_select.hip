@@ -9,6 +9,7 @@
 //   pooled score = ((0 + q_0 kbar_0) + q_1 kbar_1) + ...            dims in increasing order
 // Every product of a bf16 and an fp32 value is exact in fp64, so fma and
 // mul+add give the same bits.
+#include <algorithm>
 #include <cmath>
 #include <type_traits>
 
@@ -262,6 +263,53 @@ __device__ __forceinline__ void exact_pairs(SelShared<D>& S, const uint32_t* lis
   }
 }
 
+// The end of a selection: flagw holds the voted candidates of query block j
+// (nc = j candidates, nw words). Adds the blocks kept by rule, then writes the
+// ascending list with the diagonal j last, its count, and zeros to nb. Called by
+// every thread of a SEL_THREADS workgroup after a barrier.
+__device__ void finish_selection(uint32_t* flagw, uint32_t* wsum, int nb, int nc, int jj, int j,
+                                 int n_qblk, int sink_blocks, int window_blocks,
+                                 int dense_tail_blocks, int32_t* out, int32_t* cnt_out) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nw = (nc + 31) >> 5;
+  // kept by rule: sink blocks, a local window below the diagonal, and every
+  // visible block for the call's last query blocks
+  if (sink_blocks > 0 || window_blocks > 0 || dense_tail_blocks > 0) {
+    const bool tail = jj > n_qblk - 1 - dense_tail_blocks;
+    const int s_end = tail ? nc : min(sink_blocks, nc);
+    const int w_beg = max(0, nc - window_blocks);
+    for (int i = tid; i < nw; i += SEL_THREADS)
+      flagw[i] |= range_bits(i * 32, 0, s_end) | range_bits(i * 32, w_beg, nc);
+    __syncthreads();
+  }
+  // ascending compaction: thread t owns flag word t (nc <= 8191 -> at most 256 words)
+  const uint32_t word = tid < nw ? flagw[tid] : 0u;
+  const uint32_t cnt = __popc(word);
+  uint32_t incl = cnt;  // inclusive scan over the wave
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t y = __shfl_up(incl, off);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  uint32_t before = 0, total_u = 0;
+#pragma unroll
+  for (int w = 0; w < SEL_WAVES; ++w) {
+    const uint32_t c = wsum[w];
+    before += w < wave ? c : 0u;
+    total_u += c;
+  }
+  int pos = (int)(before + incl - cnt);
+  for (uint32_t w = word; w != 0; w &= w - 1) out[pos++] = tid * 32 + __builtin_ctz(w);
+  const int total = (int)total_u;
+  if (tid == 0) {
+    out[total] = j;  // the local diagonal block is always kept
+    *cnt_out = total + 1;
+  }
+  for (int b = total + 1 + tid; b < nb; b += SEL_THREADS) out[b] = 0;
+}
+
 template <int D>
 // Four waves per SIMD (at most 128 registers): two workgroups share a CU, so one
 // workgroup's staging and barriers overlap the other's scoring.
@@ -270,15 +318,18 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
     const float* __restrict__ Kp, int pool_ld, int nb, int block, double theta, float theta_f,
     float theta_slack,
     int exact_only, int n_qblk, int sink_blocks, int window_blocks, int dense_tail_blocks,
-    int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_cnt) {
+    int n_split, int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_cnt) {
   constexpr int NST = D / 16;   // MFMA k-steps
   constexpr int TPR = SEL_THREADS / SEL_CH;   // staging threads per candidate row
   constexpr int DPT = D / TPR;                // staged dims per thread
   __shared__ __attribute__((aligned(16))) SelShared<D> S;
 
-  // heaviest query blocks first, KV heads interleaved
-  const int jj = n_qblk - 1 - (int)blockIdx.x / n_kv;
+  // heaviest query blocks first, KV heads interleaved; n_split workgroups share a
+  // (KV head, query block), workgroup s taking voter tiles s, s + n_split, ...
+  const int per = n_kv * n_split;
+  const int jj = n_qblk - 1 - (int)blockIdx.x / per;
   const int g = (int)blockIdx.x % n_kv;
+  const int sp = ((int)blockIdx.x % per) / n_kv;
   const int j = q_start / block + jj;
   const int group = n_q / n_kv;
   const int nc = j;  // candidates 0..j-1
@@ -300,7 +351,7 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
       S.flagw[i] = (i < (nc >> 5)) ? 0xFFFFFFFFu : ((1u << (nc & 31)) - 1u);
   } else if (nc > 0) {
     float mnorm = 0.f;  // max_b |kbar_b|_2 over the candidates (set in the first tile's pass 0)
-    for (int vt0 = 0; vt0 < nv; vt0 += SEL_VT) {
+    for (int vt0 = sp * SEL_VT; vt0 < nv; vt0 += n_split * SEL_VT) {
       __syncthreads();  // previous tile's readers of the shared state are done
       for (int i = tid; i < SEL_VT; i += SEL_THREADS) { S.va[i] = 0; S.mxkey[i] = 0; }
       if (tid == 0) { S.amb_cnt = 0; S.job_cnt = 0; S.near_cnt = 0; S.overflow = exact_only; }
@@ -335,7 +386,7 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
       int nidx = -1;                      // this lane's candidate equal to the max, if any
       bool multi = false;
       float mloc = 0.f;
-      const bool first_tile = vt0 == 0;
+      const bool first_tile = vt0 == sp * SEL_VT;   // this workgroup's first voter tile
       for (int pass = 0; pass < 2; ++pass) {
         for (int c0 = 0; c0 < nc; c0 += SEL_CH) {
           __syncthreads();  // readers of the previous chunk are done
@@ -540,43 +591,37 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
     }
   }
   __syncthreads();
-  // kept by rule: sink blocks, a local window below the diagonal, and every
-  // visible block for the call's last query blocks
-  if (sink_blocks > 0 || window_blocks > 0 || dense_tail_blocks > 0) {
-    const bool tail = jj > n_qblk - 1 - dense_tail_blocks;
-    const int s_end = tail ? nc : min(sink_blocks, nc);
-    const int w_beg = max(0, nc - window_blocks);
-    for (int i = tid; i < nw; i += SEL_THREADS)
-      S.flagw[i] |= range_bits(i * 32, 0, s_end) | range_bits(i * 32, w_beg, nc);
-    __syncthreads();
-  }
-  // ascending compaction: thread t owns flag word t (nc <= 8191 -> at most 256 words)
-  const uint32_t word = tid < nw ? S.flagw[tid] : 0u;
-  const uint32_t cnt = __popc(word);
-  uint32_t incl = cnt;  // inclusive scan over the wave
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint32_t y = __shfl_up(incl, off);
-    if (lane >= off) incl += y;
-  }
-  if (lane == 63) S.wsum[wave] = incl;
-  __syncthreads();
-  uint32_t before = 0, total_u = 0;
-#pragma unroll
-  for (int w = 0; w < SEL_WAVES; ++w) {
-    const uint32_t c = S.wsum[w];
-    before += w < wave ? c : 0u;
-    total_u += c;
-  }
   int32_t* out = sel_idx + ((size_t)g * n_qblk + jj) * nb;
-  int pos = (int)(before + incl - cnt);
-  for (uint32_t w = word; w != 0; w &= w - 1) out[pos++] = tid * 32 + __builtin_ctz(w);
-  const int total = (int)total_u;
-  if (tid == 0) {
-    out[total] = j;  // the local diagonal block is always kept
-    sel_cnt[(size_t)g * n_qblk + jj] = total + 1;
+  if (n_split > 1) {
+    // partial votes: this workgroup's flag words go to words [sp nw, (sp + 1) nw)
+    // of the row, where select_merge_kernel ORs them (n_split nw <= nb by the launch)
+    for (int i = tid; i < nw; i += SEL_THREADS) out[sp * nw + i] = (int32_t)S.flagw[i];
+    return;
   }
-  for (int b = total + 1 + tid; b < nb; b += SEL_THREADS) out[b] = 0;
+  finish_selection(S.flagw, S.wsum, nb, nc, jj, j, n_qblk, sink_blocks, window_blocks,
+                   dense_tail_blocks, out, sel_cnt + (size_t)g * n_qblk + jj);
+}
+
+// One workgroup per (KV head, query block) after a split select_kernel: OR the
+// n_split partial flag rows left at the front of the row, then finish as above.
+__global__ void __launch_bounds__(SEL_THREADS) select_merge_kernel(
+    int q_start, int n_kv, int nb, int block, int n_qblk, int sink_blocks, int window_blocks,
+    int dense_tail_blocks, int n_split, int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_cnt) {
+  __shared__ uint32_t flagw[SEL_MAX_NB / 32];
+  __shared__ uint32_t wsum[SEL_WAVES];
+  const int jj = (int)blockIdx.x / n_kv;
+  const int g = (int)blockIdx.x % n_kv;
+  const int j = q_start / block + jj;
+  const int nc = j, nw = (nc + 31) >> 5;
+  int32_t* out = sel_idx + ((size_t)g * n_qblk + jj) * nb;
+  for (int i = threadIdx.x; i < nw; i += SEL_THREADS) {
+    uint32_t w = 0;
+    for (int s = 0; s < n_split; ++s) w |= (uint32_t)out[s * nw + i];
+    flagw[i] = w;
+  }
+  __syncthreads();   // every partial word is read before the row is rewritten
+  finish_selection(flagw, wsum, nb, nc, jj, j, n_qblk, sink_blocks, window_blocks, dense_tail_blocks,
+                   out, sel_cnt + (size_t)g * n_qblk + jj);
 }
 
 hipError_t launch_select(const uint16_t* Q, int C, int q_start, int n_q, int n_kv, int d,
@@ -592,15 +637,34 @@ hipError_t launch_select(const uint16_t* Q, int C, int q_start, int n_q, int n_k
   const int exact_only = (!inf_theta && !(std::fabs(theta) <= 1e30)) ? 1 : 0;
   const float theta_f = inf_theta ? -HUGE_VALF : (exact_only ? 0.f : (float)theta);
   const float theta_slack = inf_theta || exact_only ? 0.f : (float)std::ldexp(std::fabs(theta), -22);
-  dim3 grid(n_qblk * n_kv);
+  // Two select workgroups fit on a CU. When the (KV head, query block) pairs
+  // fill fewer slots than that (a 4,096-row chunk: 32 query blocks), their voter
+  // tiles are spread over n_split workgroups, as far as the tiles go and as the
+  // partial flag rows fit at the front of a selection row (n_split nw <= nb).
+  const int vt_max = (std::min(block, C) * (n_q / n_kv) + SEL_VT - 1) / SEL_VT;
+  const int pairs = n_qblk * n_kv;
+  const int nw_max = (nb - 1 + 31) / 32;
+  int n_split = 1;
+  if (theta_f != -HUGE_VALF) {
+    const int want = (2 * device_cus() + pairs - 1) / pairs;
+    n_split = std::max(1, std::min(std::min(want, vt_max), nw_max > 0 ? nb / nw_max : 1));
+  }
+  dim3 grid(pairs * n_split);
   if (d == 128)
     hipLaunchKernelGGL(select_kernel<128>, grid, dim3(SEL_THREADS), 0, stream, Q, C, q_start, n_q,
                        n_kv, K_pool, pool_ld, nb, block, theta, theta_f, theta_slack, exact_only, n_qblk,
-                       sink_blocks, window_blocks, dense_tail_blocks, sel_idx, sel_cnt);
+                       sink_blocks, window_blocks, dense_tail_blocks, n_split, sel_idx, sel_cnt);
   else
     hipLaunchKernelGGL(select_kernel<64>, grid, dim3(SEL_THREADS), 0, stream, Q, C, q_start, n_q,
                        n_kv, K_pool, pool_ld, nb, block, theta, theta_f, theta_slack, exact_only, n_qblk,
-                       sink_blocks, window_blocks, dense_tail_blocks, sel_idx, sel_cnt);
+                       sink_blocks, window_blocks, dense_tail_blocks, n_split, sel_idx, sel_cnt);
+  if (n_split > 1) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(select_merge_kernel, dim3(pairs), dim3(SEL_THREADS), 0, stream, q_start, n_kv, nb,
+                       block, n_qblk, sink_blocks, window_blocks, dense_tail_blocks, n_split, sel_idx,
+                       sel_cnt);
+  }
   return hipGetLastError();
 }
 

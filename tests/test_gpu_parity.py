@@ -170,6 +170,34 @@ def test_select_huge_theta(lp):
     _select_pooled(lp, q, kp, q_start, block, 1e-30, 1e-32)
 
 
+@pytest.mark.parametrize("C,q_start,n_q,n_kv,d,block,alpha,sink,window,tail,s", [
+    # voter tiles spread over several workgroups per (KV head, query block) when the
+    # pairs are few; the workgroup counts in the comments are those of a 256-CU part
+    (512, 3000, 16, 2, 128, 128, 0.1, 0, 0, 0, 2.0),   # 4 per pair; first block's 4th has no voters
+    (256, 2048, 8, 1, 64, 64, 0.2, 0, 0, 0, 2.0),      # 2 per pair, head dim 64
+    (256, 0, 32, 1, 128, 128, 0.1, 0, 0, 0, 2.0),      # 2 blocks: 2 per pair fills the row exactly
+    (512, 1024, 8, 2, 128, 128, 0.1, 256, 2, 1, 2.0),  # kept by rule after the merge
+    (300, 700, 8, 2, 128, 128, 0.1, 0, 0, 0, 1e17),    # magnitudes decided in fp64 alone, per tile
+])
+def test_select_split_voters_bit_exact(lp, C, q_start, n_q, n_kv, d, block, alpha, sink, window, tail, s):
+    rng = np.random.default_rng(C + q_start + n_q)
+    T = q_start + C
+    q = rand_bits(rng, C, n_q, d, s=s)
+    k = rand_bits(rng, T, n_kv, d, s=s)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    say("select split voters", C, q_start, n_q, n_kv, d, block, alpha, sink, window, tail, s)
+    kp, _ = lp.build_pooled_index(dev_bf16(k), dev_bf16(k), block)
+    idx, cnt = lp.select_blocks(dev_bf16(q), kp, q_start, block, alpha, scale, sink_tokens=sink,
+                                window_blocks=window, dense_tail_blocks=tail)
+    import torch
+    torch.cuda.synchronize()
+    rkp, _ = pooled_index_ref(f64(k), f64(k), block)
+    ridx, rcnt = select_ref(f64(q), rkp, q_start, block, alpha, scale, sink_tokens=sink,
+                            window_blocks=window, dense_tail_blocks=tail)
+    assert np.array_equal(cnt.cpu().numpy(), rcnt)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+
+
 # ---------------------------------------------------------------- dense: configs
 @pytest.mark.parametrize("name", ["tiny", "gqa4k", "fold2k5"])
 def test_dense_configs(lp, name):
