@@ -1112,7 +1112,10 @@ DensePlan plan_dense(int C, int T, int n_q, int n_kv, int d) {
   p.n_ktile = (T + FLAG_KEYS - 1) / FLAG_KEYS;
   p.n_qft = (C + FLAG_ROWS - 1) / FLAG_ROWS;
   const long wgs = (long)p.n_qt * (n_q >> p.hg_log2);
-  const int target = 2 * device_cus();             // two rounds of one resident workgroup per CU
+  // split the key range only to reach one resident workgroup per CU: splitting
+  // further shortens the longest causal tile but adds a combine pass, and was
+  // slower on 1,024- and 4,096-row chunks over 1-5K keys
+  const int target = device_cus();
   const int n_steps = (T + BN - 1) / BN;
   int splits = 1;
   if (wgs < target) splits = (int)((target + wgs - 1) / wgs);

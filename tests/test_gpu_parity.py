@@ -178,6 +178,7 @@ def test_select_huge_theta(lp):
     (256, 0, 32, 1, 128, 128, 0.1, 0, 0, 0, 2.0),      # 2 blocks: 2 per pair fills the row exactly
     (512, 1024, 8, 2, 128, 128, 0.1, 256, 2, 1, 2.0),  # kept by rule after the merge
     (300, 700, 8, 2, 128, 128, 0.1, 0, 0, 0, 1e17),    # magnitudes decided in fp64 alone, per tile
+    (512, 8192, 16, 2, 128, 256, 0.1, 0, 0, 0, 2.0),   # 8 per pair, two partial words each
 ])
 def test_select_split_voters_bit_exact(lp, C, q_start, n_q, n_kv, d, block, alpha, sink, window, tail, s):
     rng = np.random.default_rng(C + q_start + n_q)
