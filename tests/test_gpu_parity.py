@@ -749,6 +749,38 @@ def test_dense_causal_kv_beyond_2gib(lp):
             assert_close(got[r, g:g + 1], want[0], f"row {r} head {g}")
 
 
+@pytest.mark.timeout(900)
+def test_dense_mask_longest_key_range(lp):
+    """The longest key range the mask entry accepts, T = 2^22 - 4096 (the tile-flag
+    row at its largest), 64 rows at the end of the history. The mask has every
+    tile class along the row: a dropped run of a million keys (DROPPED tiles),
+    a +16 bias on four keys and -2 on the next 96 (MIXED), zeros elsewhere
+    (ZERO) and the causal edge. The four keys carry most of the weight, so the
+    outputs are far from zero and a mishandled tile class moves them past the
+    tolerance. Sampled rows of both query heads against the oracle."""
+    import torch
+    T, C, n_q, n_kv, d = (1 << 22) - 4096, 64, 2, 1, 128
+    q0 = T - C
+    rng = np.random.default_rng(91)
+    say("longest key range: drawing inputs", T)
+    k = rand_bits(rng, T, n_kv, d)
+    v = rand_bits(rng, T, n_kv, d)
+    q = rand_bits(rng, C, n_q, d)
+    mask = np.zeros((C, T), dtype=np.float16)
+    mask[:, 1_000_000:2_000_000] = np.float16(-30000.0)
+    mask[:, 3_000_000:3_000_004] = np.float16(16.0)
+    mask[:, 3_000_004:3_000_100] = np.float16(-2.0)
+    mask[np.arange(T)[None, :] > (q0 + np.arange(C))[:, None]] = np.float16(-30000.0)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    say("longest key range: GPU")
+    got = gpu_dense(lp, q, k, v, mask, scale)
+    say("longest key range: oracle")
+    rows = np.array([0, 37, 63])
+    want = dense_ref(f64(q), f64(k), f64(v), mask, scale, rows=rows)
+    assert np.abs(want).max() > 0.1                     # not a near-zero average
+    assert_close(got[rows], want, "longest key range")
+
+
 # ---------------------------------------------------------------- bit-packed masks
 def gpu_dense_bits(lp, q, k, v, bits, scale):
     Bd = torch.from_numpy(np.ascontiguousarray(bits)).cuda()
