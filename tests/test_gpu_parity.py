@@ -722,19 +722,25 @@ def test_dense_causal_kmask(lp, C, q_start, T, n_q, n_kv, d, pad_from):
 @pytest.mark.timeout(900)
 def test_dense_causal_kv_beyond_2gib(lp):
     """K and V of 1.1M tokens x 8 KV heads x d 128 (2.25 GB each): tiles are
-    addressed past 2^31 bytes. Sampled rows of two heads against the oracle."""
+    addressed past 2^31 bytes. Four keys past that boundary (token offsets
+    t x 2 KiB >= 2^31) carry a +16 per-key bias and most of every row's weight,
+    so the outputs depend on reading them right rather than averaging to near
+    zero. Sampled rows of two heads against the oracle."""
     import torch
     T, C, n_kv, d = 1_100_000, 64, 8, 128
     q0 = T - C
+    hot = slice(1_090_000, 1_090_004)
     rng = np.random.default_rng(77)
     say("beyond 2 GiB: drawing K, V")
     k = rand_bits(rng, T, n_kv, d)
     v = rand_bits(rng, T, n_kv, d)
     q = rand_bits(rng, C, n_kv, d)
+    km = np.zeros(T, dtype=np.float16)
+    km[hot] = np.float16(16.0)
     scale = float(np.float32(1 / math.sqrt(d)))
     say("beyond 2 GiB: GPU")
     Kd, Vd = dev_bf16(k), dev_bf16(v)
-    O = lp.prefill_attn_dense_causal(dev_bf16(q), Kd, Vd, q0, scale)
+    O = lp.prefill_attn_dense_causal(dev_bf16(q), Kd, Vd, q0, scale, kmask=dev_f16(km))
     torch.cuda.synchronize()
     got = O.cpu().numpy()
     del Kd, Vd
@@ -745,7 +751,8 @@ def test_dense_causal_kv_beyond_2gib(lp):
         qg = f64(q[rows][:, g:g + 1, :])
         for r_i, r in enumerate(rows):
             p = q0 + r
-            want = dense_ref(qg[r_i:r_i + 1], kg[:p + 1], vg[:p + 1], np.zeros((1, p + 1), np.float16), scale)
+            want = dense_ref(qg[r_i:r_i + 1], kg[:p + 1], vg[:p + 1], km[None, :p + 1], scale)
+            assert np.abs(want).max() > 0.1             # not a near-zero average
             assert_close(got[r, g:g + 1], want[0], f"row {r} head {g}")
 
 
