@@ -86,7 +86,9 @@ hipError_t launch_pool(const uint16_t* K, const uint16_t* V, int T, int n_kv, in
 }
 
 // ---------------------------------------------------------------------------
-// select_blocks: one workgroup of 8 waves per (KV head g, query block j).
+// select_blocks: one workgroup of 8 waves per (KV head g, query block j), or
+// several sharing its voter tiles when the pairs are too few to fill the chip
+// (their votes are merged by select_merge_kernel; see launch_select).
 //
 // Voters are the (row, query head) pairs of block j in this chunk; candidates
 // are the blocks b < j. The result must equal the fixed-order fp64 rule
