@@ -81,11 +81,17 @@ const char* pa_status_string(int status);
  *
  *   O[i][h] = sum_t w_t V[t][g(h)],  w = softmax_t(scale * Q[i][h].K[t][g(h)] + mask[i][t])
  *
+ * Arithmetic: scores from bf16 Q and K with fp32 accumulation; the softmax
+ * weights are rounded to fp16 and multiplied with V staged as fp16 (times a
+ * power of two that keeps max |V| below 2^15; exact for bf16 values in fp16's
+ * normal range after that factor), accumulated in fp32.
+ *
  * Requires C >= 1, 1 <= T <= 2^22 - 4096, mask_ld >= T (K and V may be any size). The mask alone decides visibility; the
  * library assumes nothing about causality. `workspace` must hold at least
- * prefill_attn_dense_workspace(C, T, n_q, n_kv, d) bytes (tile flags and, when
- * the key range is split across workgroups, partial results); it is scratch,
- * needs no initialisation and may be reused after the stream reaches the call's end.
+ * prefill_attn_dense_workspace(C, T, n_q, n_kv, d) bytes (tile flags, the staged
+ * fp16 copy of V[0..T) -- T * n_kv * d * 2 bytes -- and, when the key range is
+ * split across workgroups, partial results); it is scratch, needs no
+ * initialisation and may be reused after the stream reaches the call's end.
  * Errors: PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP.
  */
 int prefill_attn_dense(const uint16_t* Q, int C, int n_q,
@@ -194,15 +200,27 @@ int select_blocks(const uint16_t* Q, int C, int q_start, int n_q, int n_kv, int 
  * block, and, for every unselected block b < j, the pooled pair
  * (K_pool[g][b], V_pool[g][b]) with weight block * exp(scale*Q.K_pool - m):
  * a skipped block stands for its `block` keys. All terms share one softmax.
- * The selection arrays must come from select_blocks for the same chunk.
- * Requires block == 128 (else PA_EUNSUPPORTED).
- * Errors: PA_EINVAL, PA_EUNSUPPORTED, PA_EHIP.
+ * The selection arrays come from select_blocks for the same chunk. A list is
+ * read as a set: entries outside [0, j) and duplicates are ignored, the
+ * diagonal block j is always taken exactly whatever the list holds, and
+ * sel_cnt is clamped to [0, ceil(T/block)].
+ * Arithmetic as prefill_attn_dense (pooled keys enter as bf16, pooled values as
+ * fp16 with the staged values' factor). `workspace` must hold at least
+ * prefill_attn_blocksparse_workspace(T, n_kv, d) bytes (the staged fp16 copy of
+ * V[0..T)); scratch, as for prefill_attn_dense. Every block size select_blocks
+ * takes is supported (tuned for 128; smaller blocks give steps of 64 keys that
+ * rows of different query blocks take differently, run with a per-key test).
+ * Errors: PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP.
  */
 int prefill_attn_blocksparse(const uint16_t* Q, int C, int q_start, int n_q,
                              const uint16_t* K, const uint16_t* V, int T, int n_kv, int d,
                              const float* K_pool, const float* V_pool, int block,
                              const int32_t* sel_idx, const int32_t* sel_cnt,
-                             float scale, float* O, void* stream);
+                             float scale, float* O,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes prefill_attn_blocksparse(_ld) needs for these sizes (0 for invalid sizes). */
+size_t prefill_attn_blocksparse_workspace(int T, int n_kv, int d);
 
 /*
  * fold_keep_mask -- a sparse indexer's compacted selection folded into the
@@ -271,40 +289,23 @@ int prefill_attn_blocksparse_ld(const uint16_t* Q, int C, int q_start, int n_q,
                                 const uint16_t* K, const uint16_t* V, int T, int n_kv, int d,
                                 const float* K_pool, const float* V_pool, int pool_ld, int block,
                                 const int32_t* sel_idx, const int32_t* sel_cnt,
-                                float scale, float* O, void* stream);
+                                float scale, float* O,
+                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Kernel timing (instrumentation for benchmarks; off by default).
  * When enabled, each launch of the named kernels is bracketed by HIP events
  * recorded on the launch stream. pa_timing_read synchronises those events and
  * returns the summed milliseconds and launch count for `kernel`, one of
- * "attn_dense", "attn_blocksparse", "mask_classify", "attn_combine", "pool", "select", "fold",
- * "mfma_probe". "select" covers the selection kernel and, when the call splits
+ * "attn_dense", "attn_blocksparse", "mask_classify", "stage_values", "attn_combine", "pool",
+ * "select", "fold". "stage_values" covers the two passes of the fp16 value staging.
+ * "select" covers the selection kernel and, when the call splits
  * its voters over several workgroups, the merge kernel after it.
  * pa_timing_reset clears the totals. Returns PA_OK or PA_EINVAL/PA_EHIP.
  */
 int pa_timing_enable(int on);
 int pa_timing_reset(void);
 int pa_timing_read(const char* kernel, double* total_ms, int64_t* launches);
-
-/*
- * Matrix-core calibration (instrumentation for benchmarks, not part of the
- * attention path): the bf16 MFMA rate the part sustains from registers for
- * given operand data. Enqueues `grid` workgroups of 512 threads. Thread t takes
- * the 16 operand slots operands[(16 t + i) mod 65536], i < 16, of 16 bytes each
- * (so `operands` is a device buffer of 1 MiB, filled by the caller). It runs
- * from registers either `iters` x 32 v_mfma_f32_32x32x16_bf16 on four
- * independent accumulators (shape 32), or `iters` x 64
- * v_mfma_f32_16x16x32_bf16 on eight (shape 16). It writes one float to sink[t]
- * (`sink`: grid * 512 floats).
- * FLOPs = grid * 8 * iters * 32 * 32768 for either shape. Random bf16 operands
- * against zeros show how far the operand-dependent power draw of the matrix
- * cores pulls the clock below the one the published peak assumes; the two
- * shapes differ in register-file traffic per multiply-add.
- * Requires 16-byte aligned pointers, grid >= 1, iters >= 1, shape 32 or 16.
- * Errors: PA_EINVAL, PA_EHIP.
- */
-int pa_mfma_probe(const uint16_t* operands, float* sink, int grid, int iters, int shape, void* stream);
 
 #ifdef __cplusplus
 }

@@ -23,8 +23,8 @@ import torch
 from ._lib import PrefillAttnError, check, lib  # noqa: F401
 
 __all__ = ["prefill_attn_dense", "prefill_attn_dense_bits", "prefill_attn_dense_causal", "prefill_attn_dense_workspace",
-           "build_pooled_index",
-           "select_blocks", "prefill_attn_blocksparse", "fold_keep_mask", "PrefillAttnError", "timing", "mfma_probe",
+           "prefill_attn_blocksparse_workspace", "build_pooled_index",
+           "select_blocks", "prefill_attn_blocksparse", "fold_keep_mask", "PrefillAttnError", "timing",
            "bisect_alpha", "calibrate_alpha"]
 
 
@@ -211,8 +211,12 @@ def select_blocks(Q, K_pool, q_start: int, block: int, alpha: float, scale: floa
     return sel_idx, sel_cnt
 
 
+def prefill_attn_blocksparse_workspace(T: int, n_kv: int, d: int) -> int:
+    return int(lib().prefill_attn_blocksparse_workspace(T, n_kv, d))
+
+
 def prefill_attn_blocksparse(Q, K, V, K_pool, V_pool, sel_idx, sel_cnt, q_start: int, block: int,
-                             scale: float, O=None):
+                             scale: float, O=None, workspace=None):
     """Causal block-sparse attention -> O fp32 [C][n_q][d]. K_pool/V_pool may have spare capacity."""
     _req(Q, "Q", torch.bfloat16, 3)
     _req(K, "K", torch.bfloat16, 3)
@@ -234,10 +238,14 @@ def prefill_attn_blocksparse(Q, K, V, K_pool, V_pool, sel_idx, sel_cnt, q_start:
     if O is None:
         O = torch.empty((C, n_q, d), dtype=torch.float32, device=Q.device)
     _req(O, "O", torch.float32, 3)
+    need = prefill_attn_blocksparse_workspace(T, n_kv, d)
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=Q.device)
     check(lib().prefill_attn_blocksparse_ld(Q.data_ptr(), C, q_start, n_q, K.data_ptr(), V.data_ptr(),
                                             T, n_kv, d, K_pool.data_ptr(), V_pool.data_ptr(), cap,
                                             block, sel_idx.data_ptr(), sel_cnt.data_ptr(),
-                                            float(scale), O.data_ptr(), _stream()),
+                                            float(scale), O.data_ptr(), workspace.data_ptr(),
+                                            workspace.numel(), _stream()),
           "prefill_attn_blocksparse")
     return O
 
@@ -288,19 +296,6 @@ def calibrate_alpha(Q, K_pool, q_start: int, block: int, scale: float, target_sk
         return 1.0 - kept / visible
 
     return bisect_alpha(skip_of, target_skip, 0.0, 1.0, iters)
-
-
-def mfma_probe(operands, sink, iters: int, shape: int = 32) -> None:
-    """Matrix-core calibration (pa_mfma_probe): operands = 1 MiB device buffer of
-    bf16 bits (65,536 slots of 16 bytes), sink = fp32 [grid * 512]; enqueues
-    grid = sink.numel() // 512 workgroups of iters x 32 32x32x16 (shape 32) or
-    iters x 64 16x16x32 (shape 16) bf16 MFMAs per wave."""
-    if not (operands.is_cuda and sink.is_cuda and sink.dtype == torch.float32):
-        raise ValueError("operands and sink must be device tensors (sink fp32)")
-    if operands.numel() * operands.element_size() < (1 << 20) or sink.numel() < 512:
-        raise ValueError("operands needs 1 MiB, sink at least 512 floats")
-    check(lib().pa_mfma_probe(operands.data_ptr(), sink.data_ptr(), sink.numel() // 512, int(iters),
-                              int(shape), _stream()), "pa_mfma_probe")
 
 
 class timing:

@@ -49,7 +49,9 @@ EXPORTS = {
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int,
         ctypes.c_void_p, ctypes.c_void_p,
-        ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]),
+        ctypes.c_float, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),            # workspace, bytes, stream
+    "prefill_attn_blocksparse_workspace": (ctypes.c_size_t, [ctypes.c_int] * 3),
     "build_pooled_index_ld": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]),
@@ -63,12 +65,11 @@ EXPORTS = {
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
         ctypes.c_void_p, ctypes.c_void_p,
-        ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]),
+        ctypes.c_float, ctypes.c_void_p,
+        ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),            # workspace, bytes, stream
     "fold_keep_mask": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
         ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]),
-    "pa_mfma_probe": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
-                                     ctypes.c_int, ctypes.c_void_p]),
     "pa_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "pa_timing_reset": (ctypes.c_int, []),
     "pa_timing_read": (ctypes.c_int, [ctypes.c_char_p, ctypes.POINTER(ctypes.c_double),

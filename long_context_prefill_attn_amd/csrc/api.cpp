@@ -43,8 +43,8 @@ struct TimedKernel {
 
 std::mutex g_timing_mu;
 bool g_timing_on = false;
-TimedKernel g_timed[] = {{"attn_dense"}, {"attn_blocksparse"}, {"mask_classify"},
-                         {"attn_combine"}, {"pool"}, {"select"}, {"fold"}, {"mfma_probe"}};
+TimedKernel g_timed[] = {{"attn_dense"}, {"attn_blocksparse"}, {"mask_classify"}, {"stage_values"},
+                         {"attn_combine"}, {"pool"}, {"select"}, {"fold"}};
 std::vector<hipEvent_t> g_event_pool;
 
 hipEvent_t take_event() {
@@ -75,9 +75,20 @@ hipError_t timed(const char* name, hipStream_t stream, F&& launch) {
       b = take_event();
     }
   }
+  if ((a != nullptr) != (b != nullptr)) {   // only one event could be had: time nothing
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    if (a) g_event_pool.push_back(a);
+    if (b) g_event_pool.push_back(b);
+    a = b = nullptr;
+  }
   if (a && b) {
     hipError_t e = hipEventRecord(a, stream);
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess) {
+      std::lock_guard<std::mutex> lk(g_timing_mu);
+      g_event_pool.push_back(a);
+      g_event_pool.push_back(b);
+      return e;
+    }
   }
   hipError_t err = launch();
   if (a && b) {
@@ -87,6 +98,61 @@ hipError_t timed(const char* name, hipStream_t stream, F&& launch) {
     else { g_event_pool.push_back(a); g_event_pool.push_back(b); }
   }
   return err;
+}
+
+// The dense entry points after their own argument checks: size limits, the
+// workspace, then mask-tile flags (if any), value staging, attention and (when
+// the key range is split) the combine, all on `s`.
+enum DenseKind { DENSE_F16_MASK, DENSE_BITS, DENSE_CAUSAL };
+
+int enqueue_dense(DenseKind kind, const uint16_t* Q, int C, int n_q, const uint16_t* K, const uint16_t* V,
+                  int T, int n_kv, int d, const void* mask, int64_t mask_ld, int q_start, float scale, float* O,
+                  void* workspace, size_t workspace_bytes, hipStream_t s) {
+  if (d != 64 && d != 128) return PA_EUNSUPPORTED;
+  if (T > PA_MAX_T) return PA_EUNSUPPORTED;   // the per-tile flag row must fit in LDS
+  const pa::DensePlan plan = pa::plan_dense(C, T, n_q, n_kv, d);
+  if ((long long)plan.n_qt * n_q * plan.splits >= (1LL << 31)) return PA_EUNSUPPORTED;
+  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
+      workspace_bytes < plan.total_bytes)
+    return PA_EWORKSPACE;
+  uint8_t* flags = static_cast<uint8_t*>(workspace);
+  float* part_o = plan.splits > 1 ? reinterpret_cast<float*>(flags + plan.flags_bytes) : nullptr;
+  float* part_ml =
+      plan.splits > 1 ? reinterpret_cast<float*>(flags + plan.flags_bytes + plan.part_o_bytes) : nullptr;
+  uint8_t* stage = flags + plan.stage_off;
+  const uint16_t* V16 = reinterpret_cast<const uint16_t*>(stage + plan.stage.v16_off);
+  const float* vscales = reinterpret_cast<const float*>(stage + plan.stage.scales_off);
+  const uint16_t* m16 = static_cast<const uint16_t*>(mask);
+  hipError_t e = hipSuccess;
+  if (kind == DENSE_F16_MASK) {
+    e = timed("mask_classify", s, [&] { return pa::launch_mask_classify(m16, mask_ld, C, T, flags, s); });
+  } else if (kind == DENSE_BITS) {
+    e = timed("mask_classify", s, [&] {
+      return pa::launch_mask_classify_bits(static_cast<const uint32_t*>(mask), mask_ld, C, T, flags, s);
+    });
+  } else if (mask != nullptr) {   // one-row classification of the per-key mask's 64-key tiles
+    e = timed("mask_classify", s, [&] {
+      return pa::launch_mask_classify(m16, ((int64_t)T + 7) / 8 * 8, 1, T, flags, s);
+    });
+  }
+  if (e != hipSuccess) return hip_status(e);
+  e = timed("stage_values", s, [&] { return pa::launch_stage_values(V, T, n_kv, d, stage, s); });
+  if (e != hipSuccess) return hip_status(e);
+  e = timed("attn_dense", s, [&] {
+    if (kind == DENSE_CAUSAL)
+      return pa::launch_attn_dense(Q, C, n_q, K, V16, vscales, T, n_kv, d, m16, T, scale, O, plan,
+                                   mask != nullptr ? flags : nullptr, part_o, part_ml, q_start, s);
+    return pa::launch_attn_dense(Q, C, n_q, K, V16, vscales, T, n_kv, d, m16, mask_ld, scale, O, plan, flags,
+                                 part_o, part_ml, -1, s, kind == DENSE_BITS);
+  });
+  if (e != hipSuccess) return hip_status(e);
+  if (plan.splits > 1) {
+    e = timed("attn_combine", s, [&] {
+      return pa::launch_attn_combine(C, n_q, d, plan.splits, part_o, part_ml, O, s);
+    });
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return PA_OK;
 }
 
 }  // namespace
@@ -120,34 +186,8 @@ int prefill_attn_dense(const uint16_t* Q, int C, int n_q, const uint16_t* K, con
     return PA_EINVAL;
   if (C < 1 || T < 1 || n_q < 1 || n_kv < 1 || n_q % n_kv != 0) return PA_EINVAL;
   if (mask_ld < T || !good_scale(scale)) return PA_EINVAL;
-  if (d != 64 && d != 128) return PA_EUNSUPPORTED;
-  if (T > PA_MAX_T) return PA_EUNSUPPORTED;   // the per-tile flag row must fit in LDS
-  const pa::DensePlan plan = pa::plan_dense(C, T, n_q, n_kv, d);
-  if ((long long)plan.n_qt * n_q * plan.splits >= (1LL << 31)) return PA_EUNSUPPORTED;
-  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
-      workspace_bytes < plan.total_bytes)
-    return PA_EWORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  uint8_t* flags = static_cast<uint8_t*>(workspace);
-  float* part_o = plan.splits > 1 ? reinterpret_cast<float*>(flags + plan.flags_bytes) : nullptr;
-  float* part_ml =
-      plan.splits > 1 ? reinterpret_cast<float*>(flags + plan.flags_bytes + plan.part_o_bytes) : nullptr;
-  hipError_t e = timed("mask_classify", s, [&] {
-    return pa::launch_mask_classify(mask, mask_ld, C, T, flags, s);
-  });
-  if (e != hipSuccess) return hip_status(e);
-  e = timed("attn_dense", s, [&] {
-    return pa::launch_attn_dense(Q, C, n_q, K, V, T, n_kv, d, mask, mask_ld, scale, O, plan, flags,
-                                 part_o, part_ml, -1, s);
-  });
-  if (e != hipSuccess) return hip_status(e);
-  if (plan.splits > 1) {
-    e = timed("attn_combine", s, [&] {
-      return pa::launch_attn_combine(C, n_q, d, plan.splits, part_o, part_ml, O, s);
-    });
-    if (e != hipSuccess) return hip_status(e);
-  }
-  return PA_OK;
+  return enqueue_dense(DENSE_F16_MASK, Q, C, n_q, K, V, T, n_kv, d, mask, mask_ld, -1, scale, O, workspace,
+                       workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 int prefill_attn_dense_bits(const uint16_t* Q, int C, int n_q, const uint16_t* K, const uint16_t* V,
@@ -158,34 +198,8 @@ int prefill_attn_dense_bits(const uint16_t* Q, int C, int n_q, const uint16_t* K
     return PA_EINVAL;
   if (C < 1 || T < 1 || n_q < 1 || n_kv < 1 || n_q % n_kv != 0) return PA_EINVAL;
   if (bits_ld < ((int64_t)T + 31) / 32 || !good_scale(scale)) return PA_EINVAL;
-  if (d != 64 && d != 128) return PA_EUNSUPPORTED;
-  if (T > PA_MAX_T) return PA_EUNSUPPORTED;   // the per-tile flag row must fit in LDS
-  const pa::DensePlan plan = pa::plan_dense(C, T, n_q, n_kv, d);
-  if ((long long)plan.n_qt * n_q * plan.splits >= (1LL << 31)) return PA_EUNSUPPORTED;
-  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
-      workspace_bytes < plan.total_bytes)
-    return PA_EWORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  uint8_t* flags = static_cast<uint8_t*>(workspace);
-  float* part_o = plan.splits > 1 ? reinterpret_cast<float*>(flags + plan.flags_bytes) : nullptr;
-  float* part_ml =
-      plan.splits > 1 ? reinterpret_cast<float*>(flags + plan.flags_bytes + plan.part_o_bytes) : nullptr;
-  hipError_t e = timed("mask_classify", s, [&] {
-    return pa::launch_mask_classify_bits(mask_bits, bits_ld, C, T, flags, s);
-  });
-  if (e != hipSuccess) return hip_status(e);
-  e = timed("attn_dense", s, [&] {
-    return pa::launch_attn_dense(Q, C, n_q, K, V, T, n_kv, d, reinterpret_cast<const uint16_t*>(mask_bits),
-                                 bits_ld, scale, O, plan, flags, part_o, part_ml, -1, s, true);
-  });
-  if (e != hipSuccess) return hip_status(e);
-  if (plan.splits > 1) {
-    e = timed("attn_combine", s, [&] {
-      return pa::launch_attn_combine(C, n_q, d, plan.splits, part_o, part_ml, O, s);
-    });
-    if (e != hipSuccess) return hip_status(e);
-  }
-  return PA_OK;
+  return enqueue_dense(DENSE_BITS, Q, C, n_q, K, V, T, n_kv, d, mask_bits, bits_ld, -1, scale, O, workspace,
+                       workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 int prefill_attn_dense_causal(const uint16_t* Q, int C, int q_start, int n_q, const uint16_t* K,
@@ -196,37 +210,8 @@ int prefill_attn_dense_causal(const uint16_t* Q, int C, int q_start, int n_q, co
   if (kmask != nullptr && !aligned16(kmask)) return PA_EINVAL;
   if (C < 1 || q_start < 0 || n_q < 1 || n_kv < 1 || n_q % n_kv != 0) return PA_EINVAL;
   if ((long long)q_start + C > T || !good_scale(scale)) return PA_EINVAL;
-  if (d != 64 && d != 128) return PA_EUNSUPPORTED;
-  if (T > PA_MAX_T) return PA_EUNSUPPORTED;
-  const pa::DensePlan plan = pa::plan_dense(C, T, n_q, n_kv, d);
-  if ((long long)plan.n_qt * n_q * plan.splits >= (1LL << 31)) return PA_EUNSUPPORTED;
-  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
-      workspace_bytes < plan.total_bytes)
-    return PA_EWORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  uint8_t* flags = static_cast<uint8_t*>(workspace);
-  float* part_o = plan.splits > 1 ? reinterpret_cast<float*>(flags + plan.flags_bytes) : nullptr;
-  float* part_ml =
-      plan.splits > 1 ? reinterpret_cast<float*>(flags + plan.flags_bytes + plan.part_o_bytes) : nullptr;
-  hipError_t e = hipSuccess;
-  if (kmask != nullptr) {   // one-row classification of the per-key mask's 128-key tiles
-    e = timed("mask_classify", s, [&] {
-      return pa::launch_mask_classify(kmask, ((int64_t)T + 7) / 8 * 8, 1, T, flags, s);
-    });
-    if (e != hipSuccess) return hip_status(e);
-  }
-  e = timed("attn_dense", s, [&] {
-    return pa::launch_attn_dense(Q, C, n_q, K, V, T, n_kv, d, kmask, T, scale, O, plan,
-                                 kmask != nullptr ? flags : nullptr, part_o, part_ml, q_start, s);
-  });
-  if (e != hipSuccess) return hip_status(e);
-  if (plan.splits > 1) {
-    e = timed("attn_combine", s, [&] {
-      return pa::launch_attn_combine(C, n_q, d, plan.splits, part_o, part_ml, O, s);
-    });
-    if (e != hipSuccess) return hip_status(e);
-  }
-  return PA_OK;
+  return enqueue_dense(DENSE_CAUSAL, Q, C, n_q, K, V, T, n_kv, d, kmask, T, q_start, scale, O, workspace,
+                       workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 int fold_keep_mask(const int32_t* keep_idx, int64_t keep_ld, const int32_t* keep_cnt, int C,
@@ -297,43 +282,50 @@ int select_blocks(const uint16_t* Q, int C, int q_start, int n_q, int n_kv, int 
                           alpha, scale, 0, 0, 0, sel_idx, sel_cnt, stream);
 }
 
+size_t prefill_attn_blocksparse_workspace(int T, int n_kv, int d) {
+  if (T < 1 || n_kv < 1 || (d != 64 && d != 128)) return 0;
+  return pa::plan_stage(T, n_kv, d).bytes;
+}
+
 int prefill_attn_blocksparse_ld(const uint16_t* Q, int C, int q_start, int n_q, const uint16_t* K,
                                 const uint16_t* V, int T, int n_kv, int d, const float* K_pool,
                                 const float* V_pool, int pool_ld, int block, const int32_t* sel_idx,
-                                const int32_t* sel_cnt, float scale, float* O, void* stream) {
+                                const int32_t* sel_cnt, float scale, float* O, void* workspace,
+                                size_t workspace_bytes, void* stream) {
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(K_pool) || !aligned16(V_pool) ||
       !aligned16(sel_idx) || !aligned16(sel_cnt) || !aligned16(O))
     return PA_EINVAL;
   if (C < 1 || q_start < 0 || n_q < 1 || n_kv < 1 || n_q % n_kv != 0) return PA_EINVAL;
   if ((long long)q_start + C != T || !good_scale(scale)) return PA_EINVAL;
-  if (d != 64 && d != 128) return PA_EUNSUPPORTED;
-  if (block != 128) return PA_EUNSUPPORTED;  // the attention kernel tiles query blocks of 128
+  if ((d != 64 && d != 128) || !pow2_block(block)) return PA_EUNSUPPORTED;
   const int nb = (T + block - 1) / block;
   if (nb > 8192) return PA_EUNSUPPORTED;
   if (pool_ld < nb) return PA_EINVAL;
+  const pa::StagePlan sp = pa::plan_stage(T, n_kv, d);
+  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
+      workspace_bytes < sp.bytes)
+    return PA_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* stage = static_cast<uint8_t*>(workspace);
+  hipError_t e = timed("stage_values", s, [&] { return pa::launch_stage_values(V, T, n_kv, d, stage, s); });
+  if (e != hipSuccess) return hip_status(e);
+  const uint16_t* V16 = reinterpret_cast<const uint16_t*>(stage + sp.v16_off);
+  const float* vscales = reinterpret_cast<const float*>(stage + sp.scales_off);
   return hip_status(timed("attn_blocksparse", s, [&] {
-    return pa::launch_attn_blocksparse(Q, C, q_start, n_q, K, V, T, n_kv, d, K_pool, V_pool, pool_ld,
-                                       block, sel_idx, sel_cnt, scale, O, s);
+    return pa::launch_attn_blocksparse(Q, C, q_start, n_q, K, V16, vscales, T, n_kv, d, K_pool, V_pool,
+                                       pool_ld, block, sel_idx, sel_cnt, scale, O, s);
   }));
 }
 
 int prefill_attn_blocksparse(const uint16_t* Q, int C, int q_start, int n_q, const uint16_t* K,
                              const uint16_t* V, int T, int n_kv, int d, const float* K_pool,
                              const float* V_pool, int block, const int32_t* sel_idx,
-                             const int32_t* sel_cnt, float scale, float* O, void* stream) {
+                             const int32_t* sel_cnt, float scale, float* O, void* workspace,
+                             size_t workspace_bytes, void* stream) {
   if (T < 1 || block < 1) return PA_EINVAL;
   return prefill_attn_blocksparse_ld(Q, C, q_start, n_q, K, V, T, n_kv, d, K_pool, V_pool,
                                      (T + block - 1) / block, block, sel_idx, sel_cnt, scale, O,
-                                     stream);
-}
-
-int pa_mfma_probe(const uint16_t* operands, float* sink, int grid, int iters, int shape, void* stream) {
-  if (!aligned16(operands) || !aligned16(sink) || grid < 1 || iters < 1) return PA_EINVAL;
-  if (shape != 32 && shape != 16) return PA_EINVAL;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  return hip_status(
-      timed("mfma_probe", s, [&] { return pa::launch_mfma_probe(operands, sink, grid, iters, shape, s); }));
+                                     workspace, workspace_bytes, stream);
 }
 
 int pa_timing_enable(int on) {
@@ -362,17 +354,23 @@ int pa_timing_read(const char* kernel, double* total_ms, int64_t* launches) {
   std::lock_guard<std::mutex> lk(g_timing_mu);
   TimedKernel* t = find_timed(kernel);
   if (t == nullptr) return PA_EINVAL;
-  for (auto& pr : t->pending) {
+  // pairs are taken off the pending list as they are read, so an error leaves
+  // only the unread ones pending and no event is both pooled and pending
+  size_t done = 0;
+  hipError_t err = hipSuccess;
+  for (; done < t->pending.size(); ++done) {
+    const auto& pr = t->pending[done];
     hipError_t e = hipEventSynchronize(pr.second);
     float ms = 0.f;
     if (e == hipSuccess) e = hipEventElapsedTime(&ms, pr.first, pr.second);
-    if (e != hipSuccess) return hip_status(e);
+    if (e != hipSuccess) { err = e; break; }
     t->total_ms += ms;
     t->launches += 1;
     g_event_pool.push_back(pr.first);
     g_event_pool.push_back(pr.second);
   }
-  t->pending.clear();
+  t->pending.erase(t->pending.begin(), t->pending.begin() + done);
+  if (err != hipSuccess) return hip_status(err);
   *total_ms = t->total_ms;
   *launches = t->launches;
   return PA_OK;

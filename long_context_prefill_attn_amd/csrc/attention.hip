@@ -53,7 +53,7 @@ constexpr float SLACK = 8.0f;   // lazy-rescale threshold in log2 units
 #define LDS_AS __attribute__((address_space(3)))
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 
-enum { MODE_PLAIN = 0, MODE_GMASK = 1, MODE_CAUSAL = 2, MODE_POOLED = 3, MODE_CAUSAL_K = 4, MODE_GBITS = 5 };
+enum { MODE_PLAIN = 0, MODE_GMASK = 1, MODE_BSEL = 2, MODE_POOLED = 3, MODE_CAUSAL_K = 4, MODE_GBITS = 5 };
 // how the dense kernel reads its mask: fp16 (8-byte loads when aligned) or bit-packed
 enum { MASK_F16 = 0, MASK_F16_VEC = 1, MASK_BITS = 2 };
 
@@ -204,12 +204,19 @@ __device__ __forceinline__ LaneOffs<D> lane_offsets() {
   return o;
 }
 
-// acc + lo + hi of a packed bf16 pair (v_dot2_f32_bf16 against (1, 1), fp32
+// acc + lo + hi of a packed fp16 pair (v_dot2_f32_f16 against (1, 1), fp32
 // accumulate): the row sum is taken over the same rounded weights that enter
 // the PV product, so the normalised weights sum to one.
 __device__ __forceinline__ float row_sum_add(uint32_t packed, float acc) {
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed), ones, acc, false);
+  const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, packed), ones, acc, false);
+}
+
+// O^T += V^T P^T on the fp16 matrix cores: A = four V rows x 8 dims gathered by two
+// transposed LDS reads, B = a fragment of packed fp16 weights
+__device__ __forceinline__ f32x16 pv_mfma(v4i16 a0, v4i16 a1, const u32x4& p, f32x16 acc) {
+  const f16x8 a = __builtin_bit_cast(f16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, __builtin_bit_cast(f16x8, p), acc, 0, 0, 0);
 }
 
 struct StepCtx {
@@ -219,9 +226,10 @@ struct StepCtx {
   const uint32_t* __restrict__ brow; // MODE_GBITS: bit-mask row of this lane's query (may be null)
   bool mask_vec;                     // MODE_GMASK: 8-byte aligned mask rows
   int key0;                          // absolute key (or pooled block) index of the step's first key
-  int qpos;                          // MODE_CAUSAL: absolute position of this lane's query
-  const uint32_t* selbits;           // MODE_POOLED: selected-block bitmap (LDS)
-  int jlimit;                        // MODE_POOLED: pooled rows exist only for blocks < jlimit
+  int qpos;                          // MODE_CAUSAL_K, MODE_BSEL: absolute position of this lane's query
+  const uint32_t* selrow;            // MODE_BSEL, MODE_POOLED: selected-block bitmap of the row's query block (LDS)
+  int jrow;                          // MODE_BSEL, MODE_POOLED: the row's query block (-1: no row)
+  int blog2;                         // MODE_BSEL: log2(block)
   float pool_bias;                   // MODE_POOLED: log2(block)
 };
 
@@ -254,6 +262,18 @@ __device__ __forceinline__ void attn_step(const uint16_t* __restrict__ kt, const
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
     s[kb] = qk_slice<D>(kt + kb * 32 * D, lo, qf, f32x16{});
+  }
+  // MODE_BSEL: the row's selection bits of the step's blocks, from block b0 (a
+  // step spans at most four blocks, all in one word); MODE_POOLED: the bits of
+  // the step's 64 pooled rows (blocks key0 .. key0 + 63)
+  uint32_t sw0 = 0, sw1 = 0;
+  int b0 = 0;
+  if (MODE == MODE_BSEL) {
+    b0 = cx.key0 >> cx.blog2;
+    if (b0 < cx.jrow) sw0 = cx.selrow[b0 >> 5] >> (b0 & 31);
+  } else if (MODE == MODE_POOLED) {
+    if (cx.key0 < cx.jrow) sw0 = cx.selrow[cx.key0 >> 5];
+    if (cx.key0 + 32 < cx.jrow) sw1 = cx.selrow[(cx.key0 >> 5) + 1];
   }
 
   float x[2][16];
@@ -288,8 +308,12 @@ __device__ __forceinline__ void attn_step(const uint16_t* __restrict__ kt, const
                                : __builtin_fmaf((float)__builtin_bit_cast(_Float16, mv[i]), LOG2E, v);
       } else if (MODE == MODE_GBITS) {
         if (!((mw >> (kk - 32 * kb)) & 1u)) v = -__builtin_inff();
-      } else if (MODE == MODE_CAUSAL) {
-        if (cx.key0 + kk > cx.qpos) v = -__builtin_inff();
+      } else if (MODE == MODE_BSEL) {
+        // exact keys of a row: every key of a selected block below its own, and
+        // the keys of its own block up to its position
+        const int key = cx.key0 + kk, b = key >> cx.blog2;
+        const bool vis = b < cx.jrow ? ((sw0 >> (b - b0)) & 1u) != 0 : (b == cx.jrow && key <= cx.qpos);
+        if (!vis) v = -__builtin_inff();
       } else if (MODE == MODE_CAUSAL_K) {
         // causal by position, plus the per-key mask (cx.mrow, shared by all rows) if any
         const int key = cx.key0 + kk;
@@ -301,9 +325,9 @@ __device__ __forceinline__ void attn_step(const uint16_t* __restrict__ kt, const
                               : __builtin_fmaf((float)__builtin_bit_cast(_Float16, hv), LOG2E, v);
         }
       } else if (MODE == MODE_POOLED) {
+        // a pooled row stands for an unselected block below the row's own
         const int b = cx.key0 + kk;
-        bool live = false;
-        if (b < cx.jlimit) live = !((cx.selbits[b >> 5] >> (b & 31)) & 1u);
+        const bool live = b < cx.jrow && !(((kb == 0 ? sw0 : sw1) >> (kk & 31)) & 1u);
         v = live ? v + cx.pool_bias : -__builtin_inff();
       }
       if (TAIL && kk >= cx.kvalid) v = -__builtin_inff();
@@ -332,7 +356,7 @@ __device__ __forceinline__ void attn_step(const uint16_t* __restrict__ kt, const
       for (int w = 0; w < 4; ++w) {
         const float p0 = __builtin_amdgcn_exp2f(x[kb][8 * c + 2 * w] - mu);
         const float p1 = __builtin_amdgcn_exp2f(x[kb][8 * c + 2 * w + 1] - mu);
-        P[kb][c][w] = pack_bf16x2(p0, p1);
+        P[kb][c][w] = pack_f16x2(p0, p1);
         psum = row_sum_add(P[kb][c][w], psum);
       }
     }
@@ -346,13 +370,9 @@ __device__ __forceinline__ void attn_step(const uint16_t* __restrict__ kt, const
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const int off = lo.vofs(nb) + (kb * 32 + 16 * c) * D;
-        const bf16x8 b = __builtin_bit_cast(bf16x8, P[kb][c]);
-        {
-          const v4i16 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt + off));
-          const v4i16 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt + off + 8 * D));
-          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, o[nb], 0, 0, 0);
-        }
+        const v4i16 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt + off));
+        const v4i16 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt + off + 8 * D));
+        o[nb] = pv_mfma(a0, a1, P[kb][c], o[nb]);
       }
     }
   }
@@ -396,7 +416,7 @@ __device__ __forceinline__ float row_max(const f32x16 (&s)[2]) {
   return __builtin_fmaxf(mx, partner32(mx));
 }
 
-// P = 2^(S*scale_log2 - m) packed to bf16 in PV-operand order; l += sum of the packed values
+// P = 2^(S*scale_log2 - m) packed to fp16 in PV-operand order; l += sum of the packed values
 __device__ __forceinline__ void exp_pack(const f32x16 (&s)[2], float m, float scale_log2, u32x4 (&P)[2][2],
                                          float& l) {
   const float nmu = (m == -__builtin_inff()) ? 0.f : -m;
@@ -408,7 +428,7 @@ __device__ __forceinline__ void exp_pack(const f32x16 (&s)[2], float m, float sc
       for (int w = 0; w < 4; ++w) {
         const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * c + 2 * w], scale_log2, nmu));
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * c + 2 * w + 1], scale_log2, nmu));
-        P[kb][c][w] = pack_bf16x2(p0, p1);
+        P[kb][c][w] = pack_f16x2(p0, p1);
         l = row_sum_add(P[kb][c][w], l);
       }
     }
@@ -469,16 +489,14 @@ __device__ __forceinline__ float pipe_step(const uint16_t* __restrict__ kt_next,
     if (PV) {
       const int f = k / NB;
       const v4i16 (&v)[2] = vf[k % (VA + 1)];
-      const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v[0], v[1], 0, 1, 2, 3, 4, 5, 6, 7));
-      o[k % NB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, __builtin_bit_cast(bf16x8, pp[f >> 1][f & 1]),
-                                                          o[k % NB], 0, 0, 0);
+      o[k % NB] = pv_mfma(v[0], v[1], pp[f >> 1][f & 1], o[k % NB]);
     }
 #pragma unroll
     for (int pi = k * 16 / NS; pi < (k + 1) * 16 / NS; ++pi) {
       const int kb = pi >> 3, c = (pi >> 2) & 1, w = pi & 3;
       const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][8 * c + 2 * w], scale_log2, nmu));
       const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][8 * c + 2 * w + 1], scale_log2, nmu));
-      pc[kb][c][w] = pack_bf16x2(p0, p1);
+      pc[kb][c][w] = pack_f16x2(p0, p1);
       psum = row_sum_add(pc[kb][c][w], psum);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -497,8 +515,7 @@ __device__ __forceinline__ void pv_only(const uint16_t* __restrict__ vt, const L
     const int off = lo.vofs(nb) + ((f >> 1) * 32 + 16 * (f & 1)) * D;
     const v4i16 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt + off));
     const v4i16 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt + off + 8 * D));
-    const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-    o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, __builtin_bit_cast(bf16x8, P[f >> 1][f & 1]), o[nb], 0, 0, 0);
+    o[nb] = pv_mfma(v0, v1, P[f >> 1][f & 1], o[nb]);
   }
 }
 
@@ -680,14 +697,47 @@ struct DenseSrc {
   __device__ int kbase(int st) const { return st * BN; }
 };
 
-// Block-sparse: the two 64-key halves of each selected block below the diagonal.
-struct SparseSrc {
-  const int32_t* __restrict__ sl;   // selected block ids (global; uniform index, so scalar loads)
-  int n;
-  __device__ int first() const { return n > 0 ? 0 : -1; }
-  __device__ int next(int e) const { return e + 1 < n ? e + 1 : -1; }
-  __device__ int kbase(int e) const { return sl[e >> 1] * 128 + (e & 1) * BN; }
-};
+// The steps that are neither plain nor skipped (flag MIXED, or a ragged last
+// step) in [a, b): found 64 steps at a time by a wave-wide ballot over the LDS
+// flag row (every wave forms the same mask, so the barriers inside stay
+// uniform), their K and V tiles double buffered in the first two ring slots
+// (the next such step's tiles load while this one computes). run(st, kt, vt)
+// computes step st from the K and V tiles kt, vt.
+template <int D, class Run>
+__device__ __forceinline__ void special_steps(const TileLoader<D>& tl, uint16_t* lds, const uint32_t* frow,
+                                              int a, int b, int T, Run&& run) {
+  constexpr int TL = Geo<D>::TILE, NIW = Geo<D>::NIW;
+  const int lane = fresh_lane_id();
+  auto next_special = [&](int st) -> int {
+    for (int base = st; base < b; base += 64) {
+      const int sl = base + lane;
+      const int fl = sl < b ? step_flag(frow, sl) : TILE_DROPPED;
+      const uint64_t hit = __ballot(!(fl == TILE_DROPPED || (fl == TILE_ZERO && (sl + 1) * BN <= T)));
+      if (hit != 0) return base + __builtin_ctzll(hit);
+    }
+    return b;
+  };
+  int st = next_special(a), buf = 0;
+  if (st < b) {
+    tl.issue(false, st * BN, lds);
+    tl.issue(true, st * BN, lds + KRK * TL);
+  }
+  while (st < b) {
+    const int nx = next_special(st + 1);
+    if (nx < b) {
+      tl.issue(false, nx * BN, lds + (buf ^ 1) * TL);
+      tl.issue(true, nx * BN, lds + (KRK + (buf ^ 1)) * TL);
+      wait_vm<2 * NIW>();   // this step's tiles landed
+    } else {
+      wait_vm<0>();
+    }
+    __syncthreads();
+    run(st, lds + buf * TL, lds + (KRK + buf) * TL);
+    __syncthreads();
+    st = nx;
+    buf ^= 1;
+  }
+}
 
 // load this wave's 32 query rows as the B operand: lane holds Q[row n][dims 16st+8h .. +7]
 template <int D>
@@ -733,7 +783,8 @@ __device__ __forceinline__ int remap_xcd(int bid, int nblk) {
 template <int D, bool SPLIT>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
 attn_dense_kernel(const uint16_t* __restrict__ Q, int C, int n_q, const uint16_t* __restrict__ K,
-                  const uint16_t* __restrict__ V, int T, int n_kv, const uint16_t* __restrict__ mask,
+                  const uint16_t* __restrict__ V, const float* __restrict__ vscales, int T, int n_kv,
+                  const uint16_t* __restrict__ mask,
                   int64_t mask_ld, float scale_log2, float* __restrict__ O,
                   const uint8_t* __restrict__ flags, int n_qt, int n_ktile, int splits,
                   float* __restrict__ part_o, float* __restrict__ part_ml, int mask_mode, int hg_log2,
@@ -836,88 +887,59 @@ attn_dense_kernel(const uint16_t* __restrict__ Q, int C, int n_q, const uint16_t
     cx.qpos = 0;
   }
   cx.mask_vec = mask_mode == MASK_F16_VEC;
-  cx.selbits = nullptr; cx.jlimit = 0; cx.pool_bias = 0.f;
+  cx.selrow = nullptr; cx.jrow = -1; cx.blog2 = 0; cx.pool_bias = 0.f;
 
-  // 2) the remaining steps: mask tiles (MIXED) and a ragged last step. The next
-  // one is found 64 steps at a time by a wave-wide ballot over the LDS flags
-  // (every wave forms the same mask, so the barriers inside the steps stay
-  // uniform); the walk between them carries nothing but the step index.
-  auto next_special = [&](int st) -> int {
-    for (int base = st; base < b; base += 64) {
-      const int sl = base + lane2;
-      const int fl = sl < b ? step_flag(frow, sl) : TILE_DROPPED;
-      const uint64_t hit = __ballot(!(fl == TILE_DROPPED || (fl == TILE_ZERO && (sl + 1) * BN <= T)));
-      if (hit != 0) return base + __builtin_ctzll(hit);
-    }
-    return b;
-  };
-  // Two buffers (the first two K and V ring slots): the next such step's tiles
-  // load while this one computes.
-  {
-    constexpr int TL = Geo<D>::TILE, NIW = Geo<D>::NIW;
-    int st = next_special(a), buf = 0;
-    if (st < b) {
-      tl.issue(false, st * BN, lds);
-      tl.issue(true, st * BN, lds + KRK * TL);
-    }
-    while (st < b) {
-      const int nx = next_special(st + 1);
-      if (nx < b) {
-        tl.issue(false, nx * BN, lds + (buf ^ 1) * TL);
-        tl.issue(true, nx * BN, lds + (KRK + (buf ^ 1)) * TL);
-        wait_vm<2 * NIW>();   // this step's tiles landed
-      } else {
-        wait_vm<0>();
-      }
-      __syncthreads();
-      const int f = step_flag(frow, st);
-      const uint16_t* kt = lds + buf * TL;
-      const uint16_t* vt = lds + (KRK + buf) * TL;
-      cx.key0 = st * BN;
-      cx.kvalid = min(BN, T - st * BN);
-      if (f == TILE_MIXED && causal_q0 >= 0)
-        attn_step<D, MODE_CAUSAL_K, true>(kt, vt, lo2, qf, o, m, l, cx);
-      else if (f == TILE_MIXED && mask_mode == MASK_BITS)
-        attn_step<D, MODE_GBITS, true>(kt, vt, lo2, qf, o, m, l, cx);
-      else if (f == TILE_MIXED && cx.kvalid == BN)   // a full step: 8-byte mask loads where aligned
-        attn_step<D, MODE_GMASK, false>(kt, vt, lo2, qf, o, m, l, cx);
-      else if (f == TILE_MIXED)
-        attn_step<D, MODE_GMASK, true>(kt, vt, lo2, qf, o, m, l, cx);
-      else
-        attn_step<D, MODE_PLAIN, true>(kt, vt, lo2, qf, o, m, l, cx);
-      __syncthreads();
-      st = nx;
-      buf ^= 1;
-    }
-  }
+  // 2) the remaining steps: mask tiles (MIXED) and a ragged last step
+  special_steps<D>(tl, lds, frow, a, b, T, [&](int st, const uint16_t* kt, const uint16_t* vt) {
+    const int f = step_flag(frow, st);
+    cx.key0 = st * BN;
+    cx.kvalid = min(BN, T - st * BN);
+    if (f == TILE_MIXED && causal_q0 >= 0)
+      attn_step<D, MODE_CAUSAL_K, true>(kt, vt, lo2, qf, o, m, l, cx);
+    else if (f == TILE_MIXED && mask_mode == MASK_BITS)
+      attn_step<D, MODE_GBITS, true>(kt, vt, lo2, qf, o, m, l, cx);
+    else if (f == TILE_MIXED && cx.kvalid == BN)   // a full step: 8-byte mask loads where aligned
+      attn_step<D, MODE_GMASK, false>(kt, vt, lo2, qf, o, m, l, cx);
+    else if (f == TILE_MIXED)
+      attn_step<D, MODE_GMASK, true>(kt, vt, lo2, qf, o, m, l, cx);
+    else
+      attn_step<D, MODE_PLAIN, true>(kt, vt, lo2, qf, o, m, l, cx);
+  });
 
   const float lt = l + partner32(l);
   if (!qvalid2) return;
+  const float vup = vscales[1];   // the staged values were scaled by 1 / vup
   const size_t row = (size_t)qrow2 * n_q + head;
   if (SPLIT) {
     const size_t rows = (size_t)C * n_q;
-    store_rows<D>(part_o + ((size_t)split * rows + row) * D, o, 1.f);
+    store_rows<D>(part_o + ((size_t)split * rows + row) * D, o, vup);
     if (lane2 < 32) {
       float2* ml = reinterpret_cast<float2*>(part_ml + ((size_t)split * rows + row) * 2);
       *ml = make_float2(m == -__builtin_inff() ? 0.f : m, lt);
     }
   } else {
-    store_rows<D>(O + row * D, o, lt > 0.f ? 1.f / lt : 0.f);
+    store_rows<D>(O + row * D, o, lt > 0.f ? vup / lt : 0.f);
   }
 }
 
 // ---------------------------------------------------------------------------
-// block-sparse prefill attention: one workgroup per (query block of 128
-// positions, pair of query heads of one KV group). The diagonal block first
-// (causally by position; its tiles load while the selection bitmap is built and
-// Q is read), then exact steps over the other selected key blocks, then the
-// pooled rows of the unselected visible blocks with multiplicity `block`
-// ("Porting FlashPrefill V2 to Apple silicon", Compute the peaks, summarize the
-// rest). Pooled keys/values are fp32 in memory and enter the bf16 MFMA rounded
-// to bf16 (as the keys and values themselves are); the next pooled tile's
-// global loads are in flight while the current one is computed. With an odd
-// number of query heads per KV head, the second half of the workgroup repeats
-// the first head and does not store.
+// block-sparse prefill attention ("Porting FlashPrefill V2 to Apple silicon",
+// Compute the peaks, summarize the rest): one workgroup per (128 aligned query
+// positions, pair of query heads of one KV group). With block size B, those
+// positions lie in one query block (B >= 128) or span 128/B of them (B < 128).
+// A row of query block j takes exact attention over every key of each selected
+// block below j and the keys of block j up to its own position, and one pooled
+// row (mean key, mean value) of multiplicity B for every unselected block below
+// j. The selections enter as bitmaps in LDS (list entries outside [0, j) and
+// duplicates are ignored), and each 64-key step is classified for the
+// workgroup's rows as in the dense kernel: plain (every row takes all 64 keys
+// exactly: the pipelined loop), skipped (no row takes any), or masked (a per-key
+// test against the row's own selection and position). Then the pooled rows, 64
+// per step: pooled keys/values are fp32 in memory and enter the MFMAs rounded
+// (keys to bf16, values to fp16 with the staged values' factor); the next
+// pooled tile's global loads are in flight while the current one is computed.
+// With an odd number of query heads per KV head, the second half of the
+// workgroup repeats the first head and does not store.
 // ---------------------------------------------------------------------------
 template <int D>
 struct PooledFetch {
@@ -941,15 +963,23 @@ struct PooledFetch {
     }
   }
 
-  // the same chunks rounded to bf16 (nearest even) into a swizzled LDS tile
-  __device__ __forceinline__ void store(uint16_t* tile) const {
+  // the same chunks rounded (nearest even) into a swizzled LDS tile: to bf16 for
+  // pooled keys (F16 false), or times vs to fp16 for pooled values (F16 true)
+  template <bool F16>
+  __device__ __forceinline__ void store(uint16_t* tile, float vs = 1.f) const {
     constexpr int CPR = Geo<D>::CPR;
 #pragma unroll
     for (int i = 0; i < Geo<D>::KCH; ++i) {
       const int c = threadIdx.x + NT * i;
       const int row = c / CPR, lc = c % CPR;
-      const u32x4 h = {pack_bf16x2(f[i][0].x, f[i][0].y), pack_bf16x2(f[i][0].z, f[i][0].w),
-                       pack_bf16x2(f[i][1].x, f[i][1].y), pack_bf16x2(f[i][1].z, f[i][1].w)};
+      u32x4 h;
+      if (F16) {
+        h = u32x4{pack_f16x2(f[i][0].x * vs, f[i][0].y * vs), pack_f16x2(f[i][0].z * vs, f[i][0].w * vs),
+                  pack_f16x2(f[i][1].x * vs, f[i][1].y * vs), pack_f16x2(f[i][1].z * vs, f[i][1].w * vs)};
+      } else {
+        h = u32x4{pack_bf16x2(f[i][0].x, f[i][0].y), pack_bf16x2(f[i][0].z, f[i][0].w),
+                  pack_bf16x2(f[i][1].x, f[i][1].y), pack_bf16x2(f[i][1].z, f[i][1].w)};
+      }
       *reinterpret_cast<u32x4*>(tile + row * D + ((lc ^ swz(row)) * 8)) = h;
     }
   }
@@ -958,60 +988,85 @@ struct PooledFetch {
 template <int D>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
 attn_blocksparse_kernel(const uint16_t* __restrict__ Q, int C, int q_start, int n_q,
-                        const uint16_t* __restrict__ K, const uint16_t* __restrict__ V, int T,
-                        int n_kv, const float* __restrict__ Kp, const float* __restrict__ Vp,
-                        int pool_ld, int nb, int n_qblk, const int32_t* __restrict__ sel_idx,
+                        const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+                        const float* __restrict__ vscales, int T, int n_kv,
+                        const float* __restrict__ Kp, const float* __restrict__ Vp, int pool_ld, int nb,
+                        int blog2, int n_qblk, int n_wrb, const int32_t* __restrict__ sel_idx,
                         const int32_t* __restrict__ sel_cnt, float scale_log2, float* __restrict__ O) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-  __shared__ uint32_t selbits[256];  // up to 8192 blocks
-  constexpr int TL = Geo<D>::TILE;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, n = lane & 31;
-  constexpr int BLK = 128;
   const int group = n_q / n_kv;
   const int hpw = (group % 2 == 0) ? 2 : 1;   // query heads per workgroup
 
-  // workgroup ids, after the XCD remap, run KV head by KV head, longest query
-  // blocks first, with the head pairs of one (KV head, query block) adjacent:
-  // they share the selection, so the second reads the first's K/V tiles from L2
+  // workgroup ids, after the XCD remap, run KV head by KV head, longest row
+  // blocks first, with the head pairs of one (KV head, row block) adjacent: they
+  // share the selections, so the second reads the first's K/V tiles from L2
   const int bid = remap_xcd(blockIdx.x, gridDim.x);
-  const int hpk = group / hpw;                  // workgroups per (KV head, query block)
-  const int g = bid / (n_qblk * hpk);
-  const int rr = bid % (n_qblk * hpk);
-  const int jj = n_qblk - 1 - rr / hpk;
+  const int hpk = group / hpw;                  // workgroups per (KV head, row block)
+  const int g = bid / (n_wrb * hpk);
+  const int rr = bid % (n_wrb * hpk);
+  const int wrb = n_wrb - 1 - rr / hpk;
   const int hp = g * hpk + rr % hpk;            // head pair (or single head)
-  const int j = q_start / BLK + jj;
   const int head = hp * hpw + (hpw == 2 ? (wave >> 2) : 0);
   const bool storer = hpw == 2 || wave < 4;
-  const int32_t* sl = sel_idx + ((size_t)g * n_qblk + jj) * nb;
-  const int cnt = sel_cnt[(size_t)g * n_qblk + jj];
 
-  // the diagonal block's tiles (its keys may end before 128: ragged T; its
-  // first key j*128 <= the chunk's last position < T)
-  TileLoader<D> tl;
-  tl.init(K, V, T, n_kv, g);
-  const int n_diag = (j * BLK + BN < T) ? 2 : 1;
-  tl.issue(false, j * BLK, lds);
-  tl.issue(true, j * BLK, lds + KRK * TL);
-  if (n_diag == 2) {
-    tl.issue(false, j * BLK + BN, lds + TL);
-    tl.issue(true, j * BLK + BN, lds + (KRK + 1) * TL);
-  }
+  // this workgroup's rows: positions [r_lo, r_hi) of the aligned block of 128
+  const int P0 = (q_start / 128 + wrb) * 128;
+  const int r_lo = max(P0, q_start), r_hi = min(P0 + 128, q_start + C);
+  const int j_lo = r_lo >> blog2, j_hi = (r_hi - 1) >> blog2;
+  const int nq = j_hi - j_lo + 1;               // query blocks among the rows (<= 8)
+  const int jj0 = j_lo - (q_start >> blog2);    // their index in the selection arrays
+  const int sw = (j_hi + 31) >> 5;              // bitmap words per query block (blocks < j_hi)
+  const int n_steps = (r_hi + BN - 1) / BN;     // keys at or past r_hi are in every row's future
 
-  const int nwords = (nb + 31) / 32;
-  for (int w = tid; w < nwords; w += NT) selbits[w] = 0;
+  // LDS after the rings: the step flag row (2 bits per step), then the bitmaps
+  uint32_t* frow = reinterpret_cast<uint32_t*>(lds + Geo<D>::RING);
+  const int fwords = (n_steps + 15) / 16;
+  uint32_t* selw = frow + fwords;
+  for (int i = tid; i < fwords + nq * sw; i += NT) frow[i] = 0u;
   __syncthreads();
-  // the selected blocks as a bitmap (the pooled steps skip them)
-  for (int e = tid; e < cnt; e += NT) {
-    const int bb = sl[e];
-    atomicOr(&selbits[bb >> 5], 1u << (bb & 31));
+  for (int qi = 0; qi < nq; ++qi) {
+    const size_t srow = (size_t)g * n_qblk + jj0 + qi;
+    const int cnt = min(max(sel_cnt[srow], 0), nb);
+    const int jq = j_lo + qi;
+    const int32_t* sl = sel_idx + srow * nb;
+    for (int e = tid; e < cnt; e += NT) {
+      const int b = sl[e];
+      if (b >= 0 && b < jq) atomicOr(&selw[qi * sw + (b >> 5)], 1u << (b & 31));
+    }
+  }
+  __syncthreads();
+  // step flags over the workgroup's rows: ZERO = every row takes all 64 keys
+  // exactly, DROPPED = no row takes any key exactly, MIXED = otherwise
+  for (int st = tid; st < n_steps; st += NT) {
+    const int k0 = st * BN;
+    const int bA = k0 >> blog2, bZ = (k0 + BN - 1) >> blog2;
+    bool all = true, any = false;
+    for (int qi = 0; qi < nq; ++qi) {
+      const int jq = j_lo + qi;
+      const int plo = max(jq << blog2, r_lo), phi = min((jq + 1) << blog2, r_hi) - 1;  // its rows here
+      for (int b = bA; b <= bZ; ++b) {
+        bool a_ = false, y_ = false;   // every row of jq takes all the step's keys of b / some row takes some
+        if (b < jq) {
+          a_ = y_ = ((selw[qi * sw + (b >> 5)] >> (b & 31)) & 1u) != 0;
+        } else if (b == jq) {
+          const int t0 = max(k0, b << blog2), t1 = min(k0 + BN, (b + 1) << blog2) - 1;
+          a_ = t1 <= plo;
+          y_ = t0 <= phi;
+        }
+        all = all && a_;
+        any = any || y_;
+      }
+    }
+    const uint32_t f = all ? TILE_ZERO : (any ? TILE_MIXED : TILE_DROPPED);
+    if (f != TILE_ZERO) atomicOr(&frow[st >> 4], f << (2 * (st & 15)));
   }
 
-  const int qpos = j * BLK + (wave & 3) * 32 + n;
-  const bool qvalid = qpos >= q_start && qpos < q_start + C;
-  const int qrow = qpos - q_start;
+  const int qpos = P0 + (wave & 3) * 32 + n;
+  const bool qvalid = qpos >= r_lo && qpos < r_hi;
   bf16x8 qf[D / 16];
-  load_q<D>(Q, n_q, head, qrow, qvalid, qf);
+  load_q<D>(Q, n_q, head, qpos - q_start, qvalid, qf);
 
   f32x16 o[D / 32];
 #pragma unroll
@@ -1019,63 +1074,67 @@ attn_blocksparse_kernel(const uint16_t* __restrict__ Q, int C, int q_start, int 
   float m = -__builtin_inff(), l = 0.f;
 
   const LaneOffs<D> lo = lane_offsets<D>();
+  TileLoader<D> tl;
+  tl.init(K, V, T, n_kv, g);
+  __syncthreads();
+
+  // 1) plain steps: the pipelined loop
+  DenseSrc dsrc{0, n_steps, T, frow, -64, 0};
+  plain_steps<D>(tl, lds, dsrc, lo, qf, o, m, l, scale_log2);
+
+  // lane-derived values for what follows, formed afresh (see fresh_lane_id)
+  const int qpos2 = P0 + (wave & 3) * 32 + (fresh_lane_id() & 31);
+  const bool qvalid2 = qpos2 >= r_lo && qpos2 < r_hi;
+  const int jrow = qvalid2 ? (qpos2 >> blog2) : -1;
+  const LaneOffs<D> lo2 = lane_offsets<D>();
   StepCtx cx;
   cx.scale_log2 = scale_log2;
   cx.mrow = nullptr;
   cx.brow = nullptr;
   cx.mask_vec = false;
-  cx.qpos = qpos;
-  cx.selbits = selbits;
-  cx.jlimit = j;
-  cx.pool_bias = __builtin_log2f((float)BLK);
-  wait_vm<0>();
-  __syncthreads();
-  for (int e = 0; e < n_diag; ++e) {
-    cx.key0 = j * BLK + e * BN;
-    cx.kvalid = min(BN, T - cx.key0);
-    attn_step<D, MODE_CAUSAL, true>(lds + e * TL, lds + (KRK + e) * TL, lo, qf, o, m, l, cx);
-  }
-  __syncthreads();
+  cx.qpos = qpos2;
+  cx.jrow = jrow;
+  cx.selrow = selw + (qvalid2 ? (jrow - j_lo) * sw : 0);
+  cx.blog2 = blog2;
+  cx.pool_bias = (float)blog2;
 
-  // exact steps: the two 64-key halves of every selected block but the last
-  // (the diagonal), which lie fully below the query block
-  SparseSrc ssrc{sl, 2 * (cnt - 1)};
-  plain_steps<D>(tl, lds, ssrc, lo, qf, o, m, l, scale_log2);
+  // 2) masked steps: the diagonal blocks and partly selected steps
+  special_steps<D>(tl, lds, frow, 0, n_steps, T, [&](int st, const uint16_t* kt, const uint16_t* vt) {
+    cx.key0 = st * BN;
+    cx.kvalid = min(BN, T - st * BN);
+    attn_step<D, MODE_BSEL, true>(kt, vt, lo2, qf, o, m, l, cx);
+  });
 
-  // lane-derived values for what follows, formed afresh (see fresh_lane_id)
-  const int qpos2 = j * BLK + (wave & 3) * 32 + (fresh_lane_id() & 31);
-  const bool qvalid2 = qpos2 >= q_start && qpos2 < q_start + C;
-  const LaneOffs<D> lo2 = lane_offsets<D>();
-
-  // pooled rows of the unselected visible blocks b < j, 64 per step, in two
-  // alternating LDS buffers (one barrier per step)
+  // 3) pooled rows of blocks 0 .. j_hi - 1, 64 per step, in two alternating LDS
+  // buffers (one barrier per step); each row keeps those of its unselected
+  // blocks below its own
   const float* kpg = Kp + (size_t)g * pool_ld * D;
   const float* vpg = Vp + (size_t)g * pool_ld * D;
-  const int n_pool = (j + BN - 1) / BN;
+  const int n_pool = (j_hi + BN - 1) / BN;
+  const float vdn = vscales[0];   // pooled values enter scaled like the staged values
   PooledFetch<D> fk, fv;
   if (n_pool > 0) {
-    fk.load(kpg, 0, j);
-    fv.load(vpg, 0, j);
+    fk.load(kpg, 0, j_hi);
+    fv.load(vpg, 0, j_hi);
   }
   for (int p = 0; p < n_pool; ++p) {
-    uint16_t* kt = lds + (p & 1) * TL;
-    uint16_t* vt = lds + (KRK + (p & 1)) * TL;
-    fk.store(kt);
-    fv.store(vt);
+    uint16_t* kt = lds + (p & 1) * Geo<D>::TILE;
+    uint16_t* vt = lds + (KRK + (p & 1)) * Geo<D>::TILE;
+    fk.template store<false>(kt);
+    fv.template store<true>(vt, vdn);
     __syncthreads();
     if (p + 1 < n_pool) {
-      fk.load(kpg, (p + 1) * BN, j);
-      fv.load(vpg, (p + 1) * BN, j);
+      fk.load(kpg, (p + 1) * BN, j_hi);
+      fv.load(vpg, (p + 1) * BN, j_hi);
     }
     cx.key0 = p * BN;
-    cx.kvalid = min(BN, j - p * BN);
-    cx.qpos = qpos2;
-    attn_step<D, MODE_POOLED, true>(kt, vt, lo2, qf, o, m, l, cx);
+    cx.kvalid = BN;
+    attn_step<D, MODE_POOLED, false>(kt, vt, lo2, qf, o, m, l, cx);
   }
 
   const float lt = l + partner32(l);
   if (!qvalid2 || !storer) return;
-  store_rows<D>(O + ((size_t)(qpos2 - q_start) * n_q + head) * D, o, lt > 0.f ? 1.f / lt : 0.f);
+  store_rows<D>(O + ((size_t)(qpos2 - q_start) * n_q + head) * D, o, lt > 0.f ? vscales[1] / lt : 0.f);
 }
 
 // ---------------------------------------------------------------------------
@@ -1127,13 +1186,16 @@ DensePlan plan_dense(int C, int T, int n_q, int n_kv, int d) {
     p.part_o_bytes = align256((size_t)splits * C * n_q * d * sizeof(float));
     p.part_ml_bytes = align256((size_t)splits * C * n_q * 2 * sizeof(float));
   }
-  p.total_bytes = p.flags_bytes + p.part_o_bytes + p.part_ml_bytes;
+  p.stage_off = p.flags_bytes + p.part_o_bytes + p.part_ml_bytes;
+  p.stage = plan_stage(T, n_kv, d);
+  p.total_bytes = p.stage_off + p.stage.bytes;
   return p;
 }
 
 template <int D>
 static hipError_t dense_impl(const uint16_t* Q, int C, int n_q, const uint16_t* K, const uint16_t* V,
-                             int T, int n_kv, const uint16_t* mask, int64_t mask_ld, float scale,
+                             const float* vscales, int T, int n_kv, const uint16_t* mask, int64_t mask_ld,
+                             float scale,
                              float* O, const DensePlan& p, const uint8_t* flags, float* part_o,
                              float* part_ml, int causal_q0, hipStream_t stream, bool mask_bits) {
   const float sl2 = scale * LOG2E;
@@ -1145,56 +1207,63 @@ static hipError_t dense_impl(const uint16_t* Q, int C, int n_q, const uint16_t* 
     hipFuncSetAttribute((const void*)attn_dense_kernel<D, true>,
                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     hipLaunchKernelGGL((attn_dense_kernel<D, true>), dim3(grid), dim3(NT), lds, stream, Q, C, n_q, K, V,
-                       T, n_kv, mask, mask_ld, sl2, O, flags, p.n_qt, p.n_ktile, p.splits, part_o,
+                       vscales, T, n_kv, mask, mask_ld, sl2, O, flags, p.n_qt, p.n_ktile, p.splits, part_o,
                        part_ml, mask_mode, p.hg_log2, causal_q0);
   } else {
     hipFuncSetAttribute((const void*)attn_dense_kernel<D, false>,
                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     hipLaunchKernelGGL((attn_dense_kernel<D, false>), dim3(grid), dim3(NT), lds, stream, Q, C, n_q, K,
-                       V, T, n_kv, mask, mask_ld, sl2, O, flags, p.n_qt, p.n_ktile, 1, part_o,
+                       V, vscales, T, n_kv, mask, mask_ld, sl2, O, flags, p.n_qt, p.n_ktile, 1, part_o,
                        part_ml, mask_mode, p.hg_log2, causal_q0);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_attn_dense(const uint16_t* Q, int C, int n_q, const uint16_t* K, const uint16_t* V,
-                             int T, int n_kv, int d, const uint16_t* mask, int64_t mask_ld,
-                             float scale, float* O, const DensePlan& plan, const uint8_t* flags,
-                             float* part_o, float* part_ml, int causal_q0, hipStream_t stream,
-                             bool mask_bits) {
+hipError_t launch_attn_dense(const uint16_t* Q, int C, int n_q, const uint16_t* K, const uint16_t* V16,
+                             const float* vscales, int T, int n_kv, int d, const uint16_t* mask,
+                             int64_t mask_ld, float scale, float* O, const DensePlan& plan,
+                             const uint8_t* flags, float* part_o, float* part_ml, int causal_q0,
+                             hipStream_t stream, bool mask_bits) {
   if (d == 128)
-    return dense_impl<128>(Q, C, n_q, K, V, T, n_kv, mask, mask_ld, scale, O, plan, flags, part_o,
-                           part_ml, causal_q0, stream, mask_bits);
-  return dense_impl<64>(Q, C, n_q, K, V, T, n_kv, mask, mask_ld, scale, O, plan, flags, part_o,
+    return dense_impl<128>(Q, C, n_q, K, V16, vscales, T, n_kv, mask, mask_ld, scale, O, plan, flags,
+                           part_o, part_ml, causal_q0, stream, mask_bits);
+  return dense_impl<64>(Q, C, n_q, K, V16, vscales, T, n_kv, mask, mask_ld, scale, O, plan, flags, part_o,
                         part_ml, causal_q0, stream, mask_bits);
 }
 
 template <int D>
 static hipError_t blocksparse_impl(const uint16_t* Q, int C, int q_start, int n_q, const uint16_t* K,
-                                   const uint16_t* V, int T, int n_kv, const float* Kp,
+                                   const uint16_t* V, const float* vscales, int T, int n_kv, const float* Kp,
                                    const float* Vp, int pool_ld, int block, const int32_t* sel_idx,
                                    const int32_t* sel_cnt, float scale, float* O, hipStream_t stream) {
   const int nb = (T + block - 1) / block;
+  const int blog2 = __builtin_ctz((unsigned)block);
   const int n_qblk = (q_start + C - 1) / block - q_start / block + 1;
+  const int n_wrb = (q_start + C - 1) / 128 - q_start / 128 + 1;   // aligned blocks of 128 rows
   const int hpw = ((n_q / n_kv) % 2 == 0) ? 2 : 1;
-  const size_t lds = Geo<D>::LDS_BYTES;   // the rings
+  // LDS: the rings, the step flag row of the longest key range and the bitmaps
+  const int max_steps = (q_start + C + BN - 1) / BN;
+  const int max_nq = block >= 128 ? 1 : 128 / block;
+  const size_t lds = Geo<D>::LDS_BYTES + (size_t)((max_steps + 15) / 16) * 4 +
+                     (size_t)max_nq * ((nb + 31) / 32) * 4;
   hipFuncSetAttribute((const void*)attn_blocksparse_kernel<D>,
                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  hipLaunchKernelGGL(attn_blocksparse_kernel<D>, dim3(n_qblk * (n_q / hpw)), dim3(NT), lds, stream, Q, C,
-                     q_start, n_q, K, V, T, n_kv, Kp, Vp, pool_ld, nb, n_qblk, sel_idx, sel_cnt,
-                     scale * LOG2E, O);
+  hipLaunchKernelGGL(attn_blocksparse_kernel<D>, dim3(n_wrb * (n_q / hpw)), dim3(NT), lds, stream, Q, C,
+                     q_start, n_q, K, V, vscales, T, n_kv, Kp, Vp, pool_ld, nb, blog2, n_qblk, n_wrb, sel_idx,
+                     sel_cnt, scale * LOG2E, O);
   return hipGetLastError();
 }
 
 hipError_t launch_attn_blocksparse(const uint16_t* Q, int C, int q_start, int n_q,
-                                   const uint16_t* K, const uint16_t* V, int T, int n_kv, int d,
+                                   const uint16_t* K, const uint16_t* V16, const float* vscales,
+                                   int T, int n_kv, int d,
                                    const float* K_pool, const float* V_pool, int pool_ld, int block,
                                    const int32_t* sel_idx, const int32_t* sel_cnt, float scale,
                                    float* O, hipStream_t stream) {
   if (d == 128)
-    return blocksparse_impl<128>(Q, C, q_start, n_q, K, V, T, n_kv, K_pool, V_pool, pool_ld, block,
+    return blocksparse_impl<128>(Q, C, q_start, n_q, K, V16, vscales, T, n_kv, K_pool, V_pool, pool_ld, block,
                                  sel_idx, sel_cnt, scale, O, stream);
-  return blocksparse_impl<64>(Q, C, q_start, n_q, K, V, T, n_kv, K_pool, V_pool, pool_ld, block,
+  return blocksparse_impl<64>(Q, C, q_start, n_q, K, V16, vscales, T, n_kv, K_pool, V_pool, pool_ld, block,
                               sel_idx, sel_cnt, scale, O, stream);
 }
 

@@ -8,6 +8,8 @@ namespace pa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -48,6 +50,12 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, b);
 }
 
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  f32x2 f = {lo, hi};
+  f16x2 h = __builtin_convertvector(f, f16x2);   // v_cvt_pk_f16_f32, round to nearest even
+  return __builtin_bit_cast(uint32_t, h);
+}
+
 }  // namespace pa
 
 // ---------------------------------------------------------------------------
@@ -79,34 +87,48 @@ hipError_t launch_fold_keep(const int32_t* keep_idx, int64_t keep_ld, const int3
                             int q_start, int T, int width, int recent, uint16_t* mask, int64_t mask_ld,
                             hipStream_t stream);
 
+// Value staging: the attention kernels take V as fp16 (the PV product runs on
+// fp16 MFMAs so the softmax weights keep 11 significant bits), scaled by a
+// power of two 2^-k that maps max |V| into [2^14, 2^15). Two passes over V[0..T):
+// partial maxima of |V| per workgroup, then every workgroup reduces the
+// partials, converts its share of V and (workgroup 0) writes
+// scales = {2^-k, 2^k} for the kernels that use the staged copy.
+constexpr int STAGE_PARTS = 512;   // workgroups of the range pass
+struct StagePlan {
+  size_t v16_off, part_off, scales_off, bytes;   // byte offsets inside the stage region
+};
+StagePlan plan_stage(int T, int n_kv, int d);
+hipError_t launch_stage_values(const uint16_t* V, int T, int n_kv, int d, void* stage, hipStream_t stream);
+
 struct DensePlan {
   int hg_log2;   // log2 of the query heads packed into one workgroup
   int n_qt;      // query tiles of 256 >> hg_log2 rows
   int n_qft;     // rows of mask-flag tiles (64 query rows each)
   int n_ktile;   // flag tiles along the keys (64 keys each)
   int splits;    // key-range splits per (query tile, head slice)
-  size_t flags_bytes, part_o_bytes, part_ml_bytes, total_bytes;
+  size_t flags_bytes, part_o_bytes, part_ml_bytes, stage_off, total_bytes;
+  StagePlan stage;
 };
 DensePlan plan_dense(int C, int T, int n_q, int n_kv, int d);
 
 // mask: fp16 [C][mask_ld] (mask_bits false) or, with mask_bits true, uint32 words
 // [C][mask_ld] of a bit-packed mask (the pointer is reinterpreted).
-hipError_t launch_attn_dense(const uint16_t* Q, int C, int n_q, const uint16_t* K, const uint16_t* V,
-                             int T, int n_kv, int d, const uint16_t* mask, int64_t mask_ld,
-                             float scale, float* O, const DensePlan& plan, const uint8_t* flags,
-                             float* part_o, float* part_ml, int causal_q0, hipStream_t stream,
-                             bool mask_bits = false);
+// V16: the staged fp16 values, vscales: {2^-k, 2^k} (see launch_stage_values)
+hipError_t launch_attn_dense(const uint16_t* Q, int C, int n_q, const uint16_t* K, const uint16_t* V16,
+                             const float* vscales, int T, int n_kv, int d, const uint16_t* mask,
+                             int64_t mask_ld, float scale, float* O, const DensePlan& plan,
+                             const uint8_t* flags, float* part_o, float* part_ml, int causal_q0,
+                             hipStream_t stream, bool mask_bits = false);
 
 hipError_t launch_attn_combine(int C, int n_q, int d, int splits, const float* part_o,
                                const float* part_ml, float* O, hipStream_t stream);
 
 hipError_t launch_attn_blocksparse(const uint16_t* Q, int C, int q_start, int n_q,
-                                   const uint16_t* K, const uint16_t* V, int T, int n_kv, int d,
+                                   const uint16_t* K, const uint16_t* V16, const float* vscales,
+                                   int T, int n_kv, int d,
                                    const float* K_pool, const float* V_pool, int pool_ld, int block,
                                    const int32_t* sel_idx, const int32_t* sel_cnt,
                                    float scale, float* O, hipStream_t stream);
 
-hipError_t launch_mfma_probe(const uint16_t* operands, float* sink, int grid, int iters, int shape,
-                             hipStream_t stream);
 
 }  // namespace pa

@@ -239,4 +239,111 @@ hipError_t launch_attn_combine(int C, int n_q, int d, int splits, const float* p
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Value staging (see StagePlan): the PV products of the attention kernels run
+// on fp16 MFMAs, so the softmax weights are rounded to fp16 (11 significant
+// bits) rather than bf16 (8). Values are converted once per call, times a
+// power of two 2^-k (k may be negative) chosen from max |V| so that the scaled
+// maximum lies in [2^14, 2^15): bf16 -> fp16 is then exact for every value
+// within 2^-28 of the maximum, and smaller ones lose at most 2^-25 absolutely in
+// scaled units, 2^-39 of the maximum. The attention kernels multiply their
+// outputs by 2^k.
+//   stage_range_kernel: STAGE_PARTS workgroups, partial max of the bf16
+//     magnitude bits (monotone in |v|) over a grid-strided share of V.
+//   stage_convert_kernel: each workgroup reduces the partials to k, converts
+//     its share; workgroup 0 writes scales = {2^-k, 2^k}.
+// ---------------------------------------------------------------------------
+constexpr int STAGE_THREADS = 256;
+constexpr int STAGE_CONVERT_WG = 1024;
+
+__device__ __forceinline__ uint32_t mag_max8(u32x4 v, uint32_t m) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) m = max(m, max(v[w] & 0x7FFFu, (v[w] >> 16) & 0x7FFFu));
+  return m;
+}
+
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t m, uint32_t* red) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off));
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[wave] = m;
+  __syncthreads();
+  m = red[0];
+#pragma unroll
+  for (int w = 1; w < STAGE_THREADS / 64; ++w) m = max(m, red[w]);
+  return m;
+}
+
+__global__ void __launch_bounds__(STAGE_THREADS) stage_range_kernel(const u32x4* __restrict__ V, size_t n8,
+                                                                     uint32_t* __restrict__ part) {
+  __shared__ uint32_t red[STAGE_THREADS / 64];
+  const size_t stride = (size_t)gridDim.x * STAGE_THREADS;
+  size_t c = (size_t)blockIdx.x * STAGE_THREADS + threadIdx.x;
+  uint32_t m = 0;
+  for (; c + 3 * stride < n8; c += 4 * stride) {
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = V[c + u * stride];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) m = mag_max8(v[u], m);
+  }
+  for (; c < n8; c += stride) m = mag_max8(V[c], m);
+  m = block_max_u32(m, red);
+  if (threadIdx.x == 0) part[blockIdx.x] = m;
+}
+
+__global__ void __launch_bounds__(STAGE_THREADS) stage_convert_kernel(const u32x4* __restrict__ V, size_t n8,
+                                                                       const uint32_t* __restrict__ part,
+                                                                       u32x4* __restrict__ V16,
+                                                                       float* __restrict__ scales) {
+  __shared__ uint32_t red[STAGE_THREADS / 64];
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < STAGE_PARTS; i += STAGE_THREADS) m = max(m, part[i]);
+  m = block_max_u32(m, red);
+  // bf16 exponent field e of max |v| (max in [2^(e-127), 2^(e-126))): k = e - 141
+  // puts the scaled max in [2^14, 2^15); clamped so both factors stay normal fp32
+  // (an all-zero V takes the lower clamp, non-finite values the upper)
+  const int e = (int)(m >> 7);
+  const int k = min(max(e - 141, -100), 114);
+  const float dn = __builtin_ldexpf(1.0f, -k);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    scales[0] = dn;
+    scales[1] = __builtin_ldexpf(1.0f, k);
+  }
+  const size_t stride = (size_t)gridDim.x * STAGE_THREADS;
+  for (size_t c = (size_t)blockIdx.x * STAGE_THREADS + threadIdx.x; c < n8; c += stride) {
+    const u32x4 v = V[c];
+    u32x4 h;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      h[w] = pack_f16x2(__uint_as_float(v[w] << 16) * dn, __uint_as_float(v[w] & 0xFFFF0000u) * dn);
+    V16[c] = h;
+  }
+}
+
+static size_t align256_s(size_t x) { return (x + 255) & ~(size_t)255; }
+
+StagePlan plan_stage(int T, int n_kv, int d) {
+  StagePlan p{};
+  p.v16_off = 0;
+  p.part_off = align256_s((size_t)T * n_kv * d * 2);
+  p.scales_off = p.part_off + align256_s(STAGE_PARTS * sizeof(uint32_t));
+  p.bytes = p.scales_off + 256;
+  return p;
+}
+
+hipError_t launch_stage_values(const uint16_t* V, int T, int n_kv, int d, void* stage, hipStream_t stream) {
+  const StagePlan p = plan_stage(T, n_kv, d);
+  uint8_t* base = static_cast<uint8_t*>(stage);
+  const size_t n8 = (size_t)T * n_kv * d / 8;
+  const u32x4* src = reinterpret_cast<const u32x4*>(V);
+  uint32_t* part = reinterpret_cast<uint32_t*>(base + p.part_off);
+  hipLaunchKernelGGL(stage_range_kernel, dim3(STAGE_PARTS), dim3(STAGE_THREADS), 0, stream, src, n8, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(stage_convert_kernel, dim3(STAGE_CONVERT_WG), dim3(STAGE_THREADS), 0, stream, src, n8, part,
+                     reinterpret_cast<u32x4*>(base + p.v16_off), reinterpret_cast<float*>(base + p.scales_off));
+  return hipGetLastError();
+}
+
 }  // namespace pa

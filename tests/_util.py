@@ -31,3 +31,12 @@ def assert_close(got, want, what=""):
     assert worst <= 1.0, (f"{what}: max err/bound {worst:.3f}, max abs err {err.max():.3e}, "
                           f"rel fro {np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-300):.3e}")
     return worst
+
+
+# Rows of the planted 32K prompt that the block-sparse GPU test checks (all
+# heads) and on which the negative controls run: three rows of eight spread
+# query blocks, plus rows where an oracle-only scan found dropping the pooled
+# correction to move the output most (one or more per KV head).
+PLANTED32K_QBLOCKS = (0, 1, 17, 20, 64, 127, 200, 255)
+PLANTED32K_ROWS = tuple(sorted({j * 128 + o for j in PLANTED32K_QBLOCKS for o in (0, 63, 127)} |
+                               {20543, 24383, 24576, 28672, 31071, 31615, 31807, 32543, 32607, 32767}))

@@ -81,7 +81,7 @@ def test_dense_bits_rejects(kw, code):
 
 def test_dense_workspace_size():
     lib = _lib.lib()
-    assert lib.prefill_attn_dense_workspace(64, 256, 4, 2, 128) >= 256
+    assert lib.prefill_attn_dense_workspace(64, 256, 4, 2, 128) >= 256 * 2 * 128 * 2   # staged fp16 values
     assert lib.prefill_attn_dense_workspace(0, 256, 4, 2, 128) == 0
     assert lib.prefill_attn_dense_workspace(64, 256, 4, 2, 96) == 0
 
@@ -118,12 +118,23 @@ def test_pool_and_blocksparse_reject():
     assert lib.build_pooled_index(FAKE, FAKE, 10, 1, 128, 48, FAKE, FAKE, None) == _lib.PA_EUNSUPPORTED
     bs = lambda **kw: lib.prefill_attn_blocksparse(
         kw.get("Q", FAKE), 256, 0, 4, FAKE, FAKE, kw.get("T", 256), 2, kw.get("d", 128), FAKE, FAKE,
-        kw.get("block", 128), FAKE, FAKE, kw.get("scale", 0.1), FAKE, None)
+        kw.get("block", 128), FAKE, FAKE, kw.get("scale", 0.1), FAKE, kw.get("ws", FAKE),
+        kw.get("ws_bytes", 0), None)
     assert bs(Q=None) == _lib.PA_EINVAL
     assert bs(T=255) == _lib.PA_EINVAL
     assert bs(scale=float("nan")) == _lib.PA_EINVAL
-    assert bs(block=64) == _lib.PA_EUNSUPPORTED
+    assert bs(block=48) == _lib.PA_EUNSUPPORTED
+    assert bs(block=512) == _lib.PA_EUNSUPPORTED
     assert bs(d=256) == _lib.PA_EUNSUPPORTED
+    for block in (16, 32, 64, 128, 256):                  # every block size is taken: the workspace is next
+        assert bs(block=block) == _lib.PA_EWORKSPACE
+    assert bs(ws=None, ws_bytes=1 << 30) == _lib.PA_EWORKSPACE
+    assert bs(ws=FAKE + 16, ws_bytes=1 << 30) == _lib.PA_EWORKSPACE   # not 256-aligned
+    need = lib.prefill_attn_blocksparse_workspace(256, 2, 128)
+    assert need >= 256 * 2 * 128 * 2                     # holds the staged fp16 values
+    assert bs(ws_bytes=need - 1) == _lib.PA_EWORKSPACE
+    assert lib.prefill_attn_blocksparse_workspace(0, 2, 128) == 0
+    assert lib.prefill_attn_blocksparse_workspace(256, 2, 96) == 0
 
 
 def test_ld_forms_reject():
@@ -140,9 +151,11 @@ def test_ld_forms_reject():
         assert lib.select_blocks_ld(FAKE, 256, 744, 4, 2, 128, FAKE, 8, 1000, 128, 0.1, 0.125, *rules,
                                     FAKE, FAKE, None) == _lib.PA_EINVAL
     assert lib.prefill_attn_blocksparse_ld(FAKE, 256, 744, 4, FAKE, FAKE, 1000, 2, 128, FAKE, FAKE, 7,
-                                           128, FAKE, FAKE, 0.1, FAKE, None) == _lib.PA_EINVAL
+                                           128, FAKE, FAKE, 0.1, FAKE, FAKE, 1 << 30, None) == _lib.PA_EINVAL
     assert lib.prefill_attn_blocksparse_ld(FAKE, 256, 744, 4, FAKE, FAKE, 1000, 2, 128, FAKE, FAKE, 8,
-                                           64, FAKE, FAKE, 0.1, FAKE, None) == _lib.PA_EUNSUPPORTED
+                                           96, FAKE, FAKE, 0.1, FAKE, FAKE, 1 << 30, None) == _lib.PA_EUNSUPPORTED
+    assert lib.prefill_attn_blocksparse_ld(FAKE, 256, 744, 4, FAKE, FAKE, 1000, 2, 128, FAKE, FAKE, 16,
+                                           64, FAKE, FAKE, 0.1, FAKE, FAKE, 0, None) == _lib.PA_EWORKSPACE
 
 
 def test_fold_rejects():
@@ -167,15 +180,6 @@ def test_timing_api_host_side():
     assert lib.pa_timing_reset() == 0
     assert lib.pa_timing_read(b"attn_dense", ctypes.byref(ms), ctypes.byref(n)) == 0
     assert n.value == 0
-
-
-def test_mfma_probe_rejects():
-    f = _lib.lib().pa_mfma_probe
-    assert f(FAKE, FAKE, 0, 10, 32, None) == _lib.PA_EINVAL      # no workgroups
-    assert f(FAKE, FAKE, 4, 0, 32, None) == _lib.PA_EINVAL       # no iterations
-    assert f(FAKE + 8, FAKE, 4, 10, 32, None) == _lib.PA_EINVAL  # misaligned operands
-    assert f(FAKE, None, 4, 10, 32, None) == _lib.PA_EINVAL      # no sink
-    assert f(FAKE, FAKE, 4, 10, 8, None) == _lib.PA_EINVAL       # no such MFMA shape
 
 
 def test_bisect_alpha_host_logic():

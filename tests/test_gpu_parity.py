@@ -14,7 +14,7 @@ import pytest
 from oracle import (bits_mask_ref, blocksparse_ref, causal_kmask_ref, dense_ref, fold_mask_ref,
                     pooled_index_ref, select_ref, selection_sets)
 from workloads import CONFIGS, bf16_bits, causal_mask, make_workload, pack_keep_bits
-from _util import assert_close, dev_bf16, dev_f16, f64
+from _util import PLANTED32K_ROWS, assert_close, dev_bf16, dev_f16, f64
 
 pytestmark = pytest.mark.gpu
 
@@ -393,34 +393,64 @@ def test_blocksparse_alpha_zero_equals_dense(lp):
     assert_close(got, want, "alpha 0")
 
 
-def test_blocksparse_32k_sampled(lp):
-    """Full planted 32K workload as the bench runs it: pooled index bit-exact in
-    full, selection bit-exact on sampled query blocks of every KV head, and the
-    output on sampled rows of every head."""
+def near_threshold_pairs(Q, K_pool, q_start, C, block, alpha, scale, band=1e-4):
+    """Voter pairs (row, query head, candidate block) whose exact pooled-score gap
+    r - M lies within band * |q| * max|kbar| of ln(alpha)/scale: the selection
+    kernel's fp32 filter cannot decide these (its error bound is below that band),
+    so each one must have been settled by the exact fp64 re-evaluation."""
+    from oracle.blocksparse import threshold
+    Hq, d = Q.shape[1], Q.shape[2]
+    Hkv = K_pool.shape[0]
+    grp = Hq // Hkv
+    th = threshold(alpha, scale)
+    n = 0
+    for g in range(Hkv):
+        kb = K_pool[g].astype(np.float64)
+        for j in range(q_start // block, (q_start + C - 1) // block + 1):
+            if j == 0:
+                continue
+            r0, r1 = max(j * block, q_start) - q_start, min((j + 1) * block, q_start + C) - q_start
+            q = Q[r0:r1, g * grp:(g + 1) * grp].reshape(-1, d)
+            r = q @ kb[:j].T
+            gap = r - r.max(axis=1, keepdims=True) - th
+            e = band * np.linalg.norm(q, axis=1, keepdims=True) * np.linalg.norm(kb[:j], axis=1).max()
+            n += int(np.sum(np.abs(gap) <= e))
+    return n
+
+
+@pytest.mark.timeout(900)
+def test_blocksparse_32k(lp):
+    """Full planted 32K workload as the bench runs it: pooled index and the whole
+    selection arrays (every KV head, every query block) bit-exact, and the output
+    on the checked rows of every head. Pairs whose gap to the threshold lies
+    inside the filter's error band exist at this size, so the exact fp64 path of
+    the selection is exercised and compared."""
     w = make_workload("sparse32k")
     s = w.spec
     B = s.block
-    say("blocksparse 32K")
+    say("blocksparse 32K: GPU")
     kp, vp, idx, cnt, got = _blocksparse_gpu(lp, w.Q, w.K, w.V, 0, B, s.alpha, s.scale)
     Q64, K64, V64 = f64(w.Q), f64(w.K), f64(w.V)
     rkp, rvp = pooled_index_ref(K64, V64, B)
     assert np.array_equal(kp.view(np.uint32), rkp.view(np.uint32))
     assert np.array_equal(vp.view(np.uint32), rvp.view(np.uint32))
-    qblocks = [0, 1, 17, 20, 64, 127, 200, 255]
-    sets = selection_sets(Q64, rkp, 0, B, s.alpha, s.scale, qblocks=qblocks)
+    say("blocksparse 32K: oracle selection (whole arrays)")
+    ridx, rcnt = select_ref(Q64, rkp, 0, B, s.alpha, s.scale)
+    assert np.array_equal(cnt, rcnt)
+    assert np.array_equal(idx, ridx)
     nb = s.N // B
-    ridx = np.zeros((s.n_kv, nb, nb), dtype=np.int32)
-    rcnt = np.zeros((s.n_kv, nb), dtype=np.int32)
-    for (g, j), kept in sets.items():
-        ridx[g, j, :len(kept)] = kept
-        rcnt[g, j] = len(kept)
-        assert np.array_equal(idx[g, j], ridx[g, j]), (g, j)
-        assert cnt[g, j] == rcnt[g, j], (g, j)
-    visible = sum(j + 1 for j in range(nb)) * s.n_kv
-    say("sparsity", 1.0 - cnt.sum() / visible)
-    rows = np.array([j * B + o for j in qblocks for o in (0, 63, 127)])
+    say("sparsity", 1.0 - cnt.sum() / (sum(j + 1 for j in range(nb)) * s.n_kv))
+    amb = near_threshold_pairs(Q64, rkp, 0, s.N, B, s.alpha, s.scale)
+    say("pairs inside the filter band", amb)
+    assert amb > 0
+    rows = np.array(PLANTED32K_ROWS)
     want = blocksparse_ref(Q64, K64, V64, rkp, rvp, ridx, rcnt, 0, B, s.scale, rows=rows)
     assert_close(got[rows], want, "sparse32k")
+    # the same call again: every output bit for bit the same (no atomics decide a value)
+    say("blocksparse 32K: second run")
+    kp2, vp2, idx2, cnt2, got2 = _blocksparse_gpu(lp, w.Q, w.K, w.V, 0, B, s.alpha, s.scale)
+    for a, b in ((kp, kp2), (vp, vp2), (idx, idx2), (cnt, cnt2), (got, got2)):
+        assert np.array_equal(np.ascontiguousarray(a).view(np.uint32), np.ascontiguousarray(b).view(np.uint32))
 
 
 def test_calibrate_alpha_planted_32k(lp):
@@ -521,11 +551,11 @@ def test_blocksparse_chunked_unaligned(lp):
         assert pk.shape[1] == nbT
 
 
-@pytest.mark.timeout(600)
-def test_blocksparse_128k_chunked_sampled(lp):
+@pytest.mark.timeout(900)
+def test_blocksparse_128k_chunked(lp):
     """The planted 128K prompt in 32 chunks of 4,096 over the growing history, as
-    the bench runs it: full pooled index bit-exact, selection bit-exact on sampled
-    query blocks of sampled chunks, outputs on sampled rows."""
+    the bench runs it: full pooled index bit-exact, the whole selection arrays of
+    chunks 0, 15 and 31 bit-exact, outputs on sampled rows of those chunks."""
     say("blocksparse 128K chunked: generating inputs")
     w = make_workload("sparse128k")
     s = w.spec
@@ -540,22 +570,18 @@ def test_blocksparse_128k_chunked_sampled(lp):
     assert np.array_equal(vp.view(np.uint32), rvp.view(np.uint32))
     kept = sum(int(c.sum()) for _, c in sels)
     say("sparsity", 1.0 - kept / (nb * (nb + 1) // 2 * s.n_kv))
-    for ci in (0, 9, 31):
+    for ci in (0, 15, 31):
         q0, C = s.chunks[ci]
         T = q0 + C
         idx, cnt = sels[ci]
         j0 = q0 // B
-        qblocks = [j0, j0 + 13, j0 + 31]
-        Qc = f64(w.Q[q0:T])
-        sets = selection_sets(Qc, rkp, q0, B, s.alpha, s.scale, qblocks=qblocks)
         nbT = T // B
-        ridx = np.zeros((s.n_kv, C // B, nbT), dtype=np.int32)
-        rcnt = np.zeros((s.n_kv, C // B), dtype=np.int32)
-        for (g, j), keep in sets.items():
-            ridx[g, j - j0, :len(keep)] = keep
-            rcnt[g, j - j0] = len(keep)
-            assert np.array_equal(idx[g, j - j0], ridx[g, j - j0]), (ci, g, j)
-            assert cnt[g, j - j0] == rcnt[g, j - j0], (ci, g, j)
+        Qc = f64(w.Q[q0:T])
+        say("blocksparse 128K chunked: oracle selection of chunk", ci)
+        ridx, rcnt = select_ref(Qc, rkp[:, :nbT], q0, B, s.alpha, s.scale)
+        assert np.array_equal(cnt, rcnt), ci
+        assert np.array_equal(idx, ridx), ci
+        qblocks = [j0, j0 + 13, j0 + 31]
         rows = np.array([(j - j0) * B + o for j in qblocks for o in (0, 77, 127)])
         want = blocksparse_ref(Qc, K64[:T], V64[:T], rkp[:, :nbT], rvp[:, :nbT], ridx, rcnt, q0, B,
                                s.scale, rows=rows)
@@ -843,17 +869,210 @@ def test_dense_bits(lp, C, T, n_q, n_kv, d, kind, words):
     assert np.array_equal(got.view(np.uint32), same.view(np.uint32))
 
 
-@pytest.mark.parametrize("shape", [32, 16])
-def test_mfma_probe_calibration_kernel(lp, shape):
-    # the benchmark's matrix-core calibration: zero operands give exactly zero sums;
-    # unit operands add K per MFMA to each accumulator element (K = 16 for 32x32x16,
-    # 32 for 16x16x32), 8 MFMAs per chain per iteration, and a lane sums its chains'
-    # elements (4 x 16 or 8 x 4): 8192 x iters either way
-    import torch
-    sink = torch.full((2 * 512,), float("nan"), dtype=torch.float32, device="cuda")
-    lp.mfma_probe(torch.zeros(1 << 19, dtype=torch.bfloat16, device="cuda"), sink, 3, shape)
+# ---------------------------------------------------------------- block sizes other than 128
+@pytest.mark.parametrize("B,N,q_start,n_q,n_kv,d,alpha", [
+    (16, 700, 300, 4, 2, 128, 0.2),      # four blocks per 64-key step, eight query blocks per workgroup
+    (32, 1000, 0, 4, 1, 64, 0.3),
+    (64, 1536, 512, 8, 2, 128, 0.3),     # two query blocks per workgroup
+    (256, 2048, 300, 4, 2, 128, 0.5),    # two workgroups per query block, chunk starts mid-block
+    (256, 2600, 0, 6, 2, 128, 0.7),      # three query heads per KV head
+    (16, 2100, 2000, 2, 2, 128, 0.5),    # 100 rows over 132 blocks
+])
+def test_blocksparse_block_sizes(lp, B, N, q_start, n_q, n_kv, d, alpha):
+    rng = np.random.default_rng(B + N + q_start)
+    # queries share an N(0,1) direction per query block (plus N(0, 1/4) noise) and
+    # keys carry an N(0,1) offset per key block: the rows of a query block vote
+    # alike, so the union keeps some blocks and skips others
+    nbk = -(-N // B)
+    u = rng.standard_normal((nbk, 1, d)).astype(np.float32)
+    q = bf16_bits((0.5 * rng.standard_normal((N, n_q, d)).astype(np.float32) + np.repeat(u, B, axis=0)[:N])[q_start:])
+    off = rng.standard_normal((nbk, n_kv, d)).astype(np.float32)
+    k = bf16_bits(rng.standard_normal((N, n_kv, d)).astype(np.float32) + np.repeat(off, B, axis=0)[:N])
+    v = rand_bits(rng, N, n_kv, d)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    say("blocksparse block size", B, N, q_start, n_q, n_kv, d, alpha)
+    kp, vp, idx, cnt, got = _blocksparse_gpu(lp, q, k, v, q_start, B, alpha, scale)
+    rkp, rvp = pooled_index_ref(f64(k), f64(v), B)
+    assert np.array_equal(kp.view(np.uint32), rkp.view(np.uint32))
+    assert np.array_equal(vp.view(np.uint32), rvp.view(np.uint32))
+    ridx, rcnt = select_ref(f64(q), rkp, q_start, B, alpha, scale)
+    assert np.array_equal(cnt, rcnt) and np.array_equal(idx, ridx)
+    visible = q_start // B + 1 + np.arange(rcnt.shape[1])[None, :]
+    assert (rcnt > 1).any() and (rcnt < visible).any()   # some blocks kept below the diagonal, some skipped
+    want = blocksparse_ref(f64(q), f64(k), f64(v), rkp, rvp, ridx, rcnt, q_start, B, scale)
+    assert_close(got, want, f"blocksparse B={B}")
+
+
+def test_blocksparse_plain_entry_points(lp):
+    """build_pooled_index, select_blocks and prefill_attn_blocksparse called
+    through the C ABI directly (not the *_ld forms), block 64, against the oracle."""
+    import ctypes
+    lib = lp.lib()
+    rng = np.random.default_rng(55)
+    N, q_start, n_q, n_kv, d, B, alpha = 1200, 400, 4, 2, 128, 64, 0.1
+    C, T = N - q_start, N
+    q, k, v = rand_bits(rng, C, n_q, d), rand_bits(rng, T, n_kv, d), rand_bits(rng, T, n_kv, d)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    nb = -(-T // B)
+    n_qblk = (q_start + C - 1) // B - q_start // B + 1
+    Qd, Kd, Vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    kp = torch.empty((n_kv, nb, d), dtype=torch.float32, device="cuda")
+    vp = torch.empty_like(kp)
+    idx = torch.empty((n_kv, n_qblk, nb), dtype=torch.int32, device="cuda")
+    cnt = torch.empty((n_kv, n_qblk), dtype=torch.int32, device="cuda")
+    O = torch.empty((C, n_q, d), dtype=torch.float32, device="cuda")
+    need = lib.prefill_attn_blocksparse_workspace(T, n_kv, d)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    say("blocksparse plain entry points")
+    assert lib.build_pooled_index(Kd.data_ptr(), Vd.data_ptr(), T, n_kv, d, B, kp.data_ptr(), vp.data_ptr(),
+                                  st) == 0
+    assert lib.select_blocks(Qd.data_ptr(), C, q_start, n_q, n_kv, d, kp.data_ptr(), T, B, alpha, scale,
+                             idx.data_ptr(), cnt.data_ptr(), st) == 0
+    assert lib.prefill_attn_blocksparse(Qd.data_ptr(), C, q_start, n_q, Kd.data_ptr(), Vd.data_ptr(), T, n_kv, d,
+                                        kp.data_ptr(), vp.data_ptr(), B, idx.data_ptr(), cnt.data_ptr(), scale,
+                                        O.data_ptr(), ws.data_ptr(), need, st) == 0
     torch.cuda.synchronize()
-    assert torch.equal(sink, torch.zeros_like(sink))
-    lp.mfma_probe(torch.ones(1 << 19, dtype=torch.bfloat16, device="cuda"), sink, 3, shape)
+    rkp, rvp = pooled_index_ref(f64(k), f64(v), B)
+    assert np.array_equal(kp.cpu().numpy().view(np.uint32), rkp.view(np.uint32))
+    ridx, rcnt = select_ref(f64(q), rkp, q_start, B, alpha, scale)
+    assert np.array_equal(cnt.cpu().numpy(), rcnt) and np.array_equal(idx.cpu().numpy(), ridx)
+    want = blocksparse_ref(f64(q), f64(k), f64(v), rkp, rvp, ridx, rcnt, q_start, B, scale)
+    assert_close(O.cpu().numpy(), want, "plain entry points")
+
+
+@pytest.mark.parametrize("B", [128, 64])
+def test_blocksparse_malformed_lists(lp, B):
+    """Selection lists as a caller might corrupt them: ids outside [0, j),
+    duplicates, any order, counts below zero or past the row. The entry point
+    reads each list as the set of its valid ids plus the diagonal; the result
+    equals the oracle on those cleaned lists."""
+    rng = np.random.default_rng(B)
+    N, q_start, n_q, n_kv, d = 1500, 200, 4, 2, 128
+    C = N - q_start
+    q, k, v = rand_bits(rng, C, n_q, d), rand_bits(rng, N, n_kv, d), rand_bits(rng, N, n_kv, d)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    nb = -(-N // B)
+    j0 = q_start // B
+    n_qblk = (N - 1) // B - j0 + 1
+    idx = rng.integers(-3, nb + 4, size=(n_kv, n_qblk, nb)).astype(np.int32)
+    idx[:, :, 1] = idx[:, :, 0]                                 # duplicates
+    cnt = rng.integers(-2, nb + 3, size=(n_kv, n_qblk)).astype(np.int32)
+    clean_idx = np.zeros_like(idx)
+    clean_cnt = np.zeros_like(cnt)
+    for g in range(n_kv):
+        for jj in range(n_qblk):
+            j = j0 + jj
+            c = min(max(int(cnt[g, jj]), 0), nb)
+            kept = sorted({int(b) for b in idx[g, jj, :c] if 0 <= b < j}) + [j]
+            clean_idx[g, jj, :len(kept)] = kept
+            clean_cnt[g, jj] = len(kept)
+    Qd, Kd, Vd = dev_bf16(q), dev_bf16(k), dev_bf16(v)
+    say("blocksparse malformed lists", B)
+    kp, vp = lp.build_pooled_index(Kd, Vd, B)
+    O = lp.prefill_attn_blocksparse(Qd, Kd, Vd, kp, vp, torch.from_numpy(idx).cuda(),
+                                    torch.from_numpy(cnt).cuda(), q_start, B, scale)
     torch.cuda.synchronize()
-    assert torch.equal(sink, torch.full_like(sink, 8192.0 * 3))
+    rkp, rvp = pooled_index_ref(f64(k), f64(v), B)
+    want = blocksparse_ref(f64(q), f64(k), f64(v), rkp, rvp, clean_idx, clean_cnt, q_start, B, scale)
+    assert_close(O.cpu().numpy(), want, f"malformed lists B={B}")
+
+
+def test_chunked_pipeline_is_deterministic(lp):
+    """Pool, select and block-sparse attention over 1,000-row chunks, run twice:
+    every output bit for bit the same."""
+    rng = np.random.default_rng(23)
+    N, n_q, n_kv, d, B = 3000, 8, 2, 128, 64
+    q, k, v = rand_bits(rng, N, n_q, d), rand_bits(rng, N, n_kv, d), rand_bits(rng, N, n_kv, d)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    chunks = ((0, 1000), (1000, 1000), (2000, 1000))
+    say("chunked pipeline determinism")
+    a = _chunked_sparse_gpu(lp, q, k, v, chunks, B, 0.1, scale, cap=-(-N // B))
+    b = _chunked_sparse_gpu(lp, q, k, v, chunks, B, 0.1, scale, cap=-(-N // B))
+    assert np.array_equal(a[0].view(np.uint32), b[0].view(np.uint32))
+    assert np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+    for (i1, c1), (i2, c2) in zip(a[2], b[2]):
+        assert np.array_equal(i1, i2) and np.array_equal(c1, c2)
+    assert np.array_equal(a[3].view(np.uint32), b[3].view(np.uint32))
+
+
+# ---------------------------------------------------------------- sharp scores, few keys, value range
+@pytest.mark.parametrize("q_start,C,T,n_q,n_kv,sq", [
+    (0, 1024, 1024, 8, 2, 1.5),       # causal from position 0: rows 0.. see 1.. keys
+    (1024, 1024, 2048, 8, 2, 1.5),
+    (0, 512, 512, 4, 4, 2.0),
+])
+def test_dense_sharp_scores(lp, q_start, C, T, n_q, n_kv, sq):
+    """Q and K drawn N(0, sq^2): scores sq^2 times sharper than the workloads',
+    so a few keys carry most of a row's weight."""
+    rng = np.random.default_rng(C + T)
+    d = 128
+    q, k, v = rand_bits(rng, C, n_q, d, s=sq), rand_bits(rng, T, n_kv, d, s=sq), rand_bits(rng, T, n_kv, d)
+    mask = causal_mask(q_start, C, T)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    say("dense sharp scores", q_start, C, T, sq)
+    got = gpu_dense(lp, q, k, v, mask, scale)
+    want = dense_ref(f64(q), f64(k), f64(v), mask, scale)
+    worst = assert_close(got, want, f"sharp x{sq}")
+    say("worst err/bound", worst)
+
+
+@pytest.mark.parametrize("kept,sq", [(10, 1.0), (10, 1.5), (3, 1.0)])
+def test_dense_few_keys(lp, kept, sq):
+    """About `kept` keys per row in a random mask over 2,048 keys, and rows with
+    exactly 2 to 5 keys: a handful of comparable weights, where their rounding
+    matters most."""
+    rng = np.random.default_rng(kept * 10 + int(sq * 10))
+    C, T, n_q, n_kv, d = 512, 2048, 4, 2, 128
+    q, k, v = rand_bits(rng, C, n_q, d, s=sq), rand_bits(rng, T, n_kv, d, s=sq), rand_bits(rng, T, n_kv, d)
+    keep = rng.random((C, T)) < kept / T
+    keep[:, 5] = True
+    for r in range(8):                         # rows with exactly 2..5 keys
+        keep[r] = False
+        keep[r, rng.choice(T, size=2 + r % 4, replace=False)] = True
+    mask = np.where(keep, np.float16(0), np.float16(-30000)).astype(np.float16)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    say("dense few keys", kept, sq)
+    got = gpu_dense(lp, q, k, v, mask, scale)
+    want = dense_ref(f64(q), f64(k), f64(v), mask, scale)
+    worst = assert_close(got, want, f"{kept} keys x{sq}")
+    say("worst err/bound", worst)
+
+
+def test_blocksparse_sharp_scores(lp):
+    rng = np.random.default_rng(61)
+    N, n_q, n_kv, d, B = 2048, 8, 2, 128, 128
+    q, k, v = rand_bits(rng, N, n_q, d, s=1.5), rand_bits(rng, N, n_kv, d, s=1.5), rand_bits(rng, N, n_kv, d)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    say("blocksparse sharp scores")
+    kp, vp, idx, cnt, got = _blocksparse_gpu(lp, q, k, v, 0, B, 0.1, scale)
+    rkp, rvp = pooled_index_ref(f64(k), f64(v), B)
+    ridx, rcnt = select_ref(f64(q), rkp, 0, B, 0.1, scale)
+    assert np.array_equal(cnt, rcnt) and np.array_equal(idx, ridx)
+    want = blocksparse_ref(f64(q), f64(k), f64(v), rkp, rvp, ridx, rcnt, 0, B, scale)
+    worst = assert_close(got, want, "blocksparse sharp")
+    say("worst err/bound", worst)
+
+
+@pytest.mark.parametrize("vs", [3.0e5, 1.0e30, 2.0e-6])
+def test_value_range_staging(lp, vs):
+    """Values far outside fp16's range (the staging factor 2^-k brings them in and
+    the output is scaled back) and tiny values, through the dense and the
+    block-sparse entry points."""
+    rng = np.random.default_rng(71)
+    N, q_start, n_q, n_kv, d, B = 1024, 512, 4, 2, 128, 128
+    C = N - q_start
+    q, k = rand_bits(rng, C, n_q, d), rand_bits(rng, N, n_kv, d)
+    v = rand_bits(rng, N, n_kv, d, s=vs)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    mask = causal_mask(q_start, C, N)
+    say("value range", vs)
+    got = gpu_dense(lp, q, k, v, mask, scale)
+    want = dense_ref(f64(q), f64(k), f64(v), mask, scale)
+    assert_close(got / vs, want / vs, f"dense values x{vs:g}")
+    kp, vp, idx, cnt, gs = _blocksparse_gpu(lp, q, k, v, q_start, B, 0.1, scale)
+    rkp, rvp = pooled_index_ref(f64(k), f64(v), B)
+    ridx, rcnt = select_ref(f64(q), rkp, q_start, B, 0.1, scale)
+    want = blocksparse_ref(f64(q), f64(k), f64(v), rkp, rvp, ridx, rcnt, q_start, B, scale)
+    assert_close(gs / vs, want / vs, f"blocksparse values x{vs:g}")
+

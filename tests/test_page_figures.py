@@ -39,10 +39,24 @@ def test_masked_vs_gathered_and_gather_sizing():
 
 
 def test_pruned_block_cost_ratio():
+    """The page's "128x cheaper per pruned block", through the benchmark's work
+    accounting: pruning one visible block of a query block removes B exact keys
+    per row and adds one pooled row, so the block costs rows x B when kept and
+    rows x 1 when pruned."""
+    import bench
     g = GOLD["pruned_block_cost"]
-    # exact: one dot product per key of the block; pooled: one per block
-    assert CONFIGS["sparse32k"].block == g["block"]
-    assert g["block"] // 1 == g["ratio"]
+    B = CONFIGS["sparse32k"].block
+    assert B == g["block"]
+    q0, C = 0, 4 * B                                   # query blocks 0..3, block 3 sees 4 blocks
+    kept_all = np.array([[1, 2, 3, 4]], dtype=np.int32)
+    pruned = kept_all.copy()
+    pruned[0, 3] -= 1                                  # one of block 3's visible blocks pruned
+    rows = B
+    removed = bench.exact_pairs(kept_all, q0, C, B) - bench.exact_pairs(pruned, q0, C, B)
+    kept_cost = rows * B
+    pruned_cost = kept_cost - removed
+    assert pruned_cost == rows
+    assert kept_cost // pruned_cost == g["ratio"]
 
 
 def test_alpha_toy_selection():
