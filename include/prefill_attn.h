@@ -59,7 +59,8 @@ enum {
   PA_EINVAL = -1,        /* a bad argument: null/misaligned pointer, inconsistent sizes, bad scalar */
   PA_EUNSUPPORTED = -2,  /* valid but outside what the kernels implement (d, block, sizes) */
   PA_EHIP = -3,          /* the HIP runtime reported an error while enqueueing */
-  PA_EWORKSPACE = -4     /* workspace missing or smaller than the size helper returned */
+  PA_EWORKSPACE = -4,    /* workspace missing or smaller than the size helper returned */
+  PA_ESCRATCH = -5       /* prefill_attn_dense_noalloc: the sizes need more than its static scratch */
 };
 
 /* Human-readable text for a status; for PA_EHIP it includes the runtime's message
@@ -102,6 +103,30 @@ int prefill_attn_dense(const uint16_t* Q, int C, int n_q,
 
 /* Workspace bytes prefill_attn_dense needs for these sizes (0 for invalid sizes). */
 size_t prefill_attn_dense_workspace(int C, int T, int n_q, int n_kv, int d);
+
+/*
+ * prefill_attn_dense_noalloc -- prefill_attn_dense for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same computation and arguments without
+ * `workspace`. Its scratch is a static device array inside the library of
+ * PA_NOALLOC_SCRATCH_BYTES (80 MiB), one copy per GPU, held until the process
+ * ends. The call allocates nothing (no hipMalloc, no events: the kernel timing
+ * hooks do not see it) and needs no initialised scratch.
+ * Sizes whose prefill_attn_dense_workspace(C, T, n_q, n_kv, d) exceeds the
+ * array return PA_ESCRATCH with nothing enqueued; the largest such size is
+ * prefill_attn_dense_noalloc_limit(). The staged values take T * n_kv * d * 2
+ * bytes of it, so, for example, 32,768 keys of 8 KV heads at d = 128 fit.
+ * Every call on one GPU uses that GPU's one array: calls that may overlap on a
+ * GPU (other streams, other host threads) race and must be serialised by the
+ * caller; calls in order on one stream are safe.
+ * Errors: PA_EINVAL, PA_EUNSUPPORTED, PA_ESCRATCH, PA_EHIP.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)80 << 20)
+int prefill_attn_dense_noalloc(const uint16_t* Q, int C, int n_q,
+                               const uint16_t* K, const uint16_t* V, int T, int n_kv, int d,
+                               const uint16_t* mask, int64_t mask_ld,
+                               float scale, float* O, void* stream);
+size_t prefill_attn_dense_noalloc_limit(void);
 
 /*
  * prefill_attn_dense_bits -- prefill_attn_dense with a keep/drop mask packed one

@@ -12,7 +12,7 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libprefill_attn.so")
 
-PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EHIP, PA_EWORKSPACE = 0, -1, -2, -3, -4
+PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EHIP, PA_EWORKSPACE, PA_ESCRATCH = 0, -1, -2, -3, -4, -5
 
 EXPORTS = {
     # name: (restype, argtypes)
@@ -25,6 +25,13 @@ EXPORTS = {
         ctypes.c_float, ctypes.c_void_p,                                # scale, O
         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),            # workspace, bytes, stream
     "prefill_attn_dense_workspace": (ctypes.c_size_t, [ctypes.c_int] * 5),
+    "prefill_attn_dense_noalloc": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_int, ctypes.c_int,                    # Q, C, n_q
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,   # K, V, T, n_kv
+        ctypes.c_int,                                                   # d
+        ctypes.c_void_p, ctypes.c_int64,                                # mask, mask_ld
+        ctypes.c_float, ctypes.c_void_p, ctypes.c_void_p]),             # scale, O, stream
+    "prefill_attn_dense_noalloc_limit": (ctypes.c_size_t, []),
     "prefill_attn_dense_bits": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_int, ctypes.c_int,                    # Q, C, n_q
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,   # K, V, T, n_kv

@@ -64,13 +64,14 @@ TimedKernel* find_timed(const char* name) {
   return nullptr;
 }
 
-// Runs `launch` on `stream`, bracketed by events when timing is on.
+// Runs `launch` on `stream`, bracketed by events when timing is on (and the
+// caller allows it: the allocation-free entry point never creates events).
 template <class F>
-hipError_t timed(const char* name, hipStream_t stream, F&& launch) {
+hipError_t timed(const char* name, hipStream_t stream, F&& launch, bool allow = true) {
   hipEvent_t a = nullptr, b = nullptr;
   {
     std::lock_guard<std::mutex> lk(g_timing_mu);
-    if (g_timing_on) {
+    if (g_timing_on && allow) {
       a = take_event();
       b = take_event();
     }
@@ -107,7 +108,10 @@ enum DenseKind { DENSE_F16_MASK, DENSE_BITS, DENSE_CAUSAL };
 
 int enqueue_dense(DenseKind kind, const uint16_t* Q, int C, int n_q, const uint16_t* K, const uint16_t* V,
                   int T, int n_kv, int d, const void* mask, int64_t mask_ld, int q_start, float scale, float* O,
-                  void* workspace, size_t workspace_bytes, hipStream_t s) {
+                  void* workspace, size_t workspace_bytes, hipStream_t s, bool allow_timing = true) {
+  auto timed = [&](const char* name, hipStream_t st, auto&& launch) {
+    return ::timed(name, st, launch, allow_timing);
+  };
   if (d != 64 && d != 128) return PA_EUNSUPPORTED;
   if (T > PA_MAX_T) return PA_EUNSUPPORTED;   // the per-tile flag row must fit in LDS
   const pa::DensePlan plan = pa::plan_dense(C, T, n_q, n_kv, d);
@@ -155,6 +159,34 @@ int enqueue_dense(DenseKind kind, const uint16_t* Q, int C, int n_q, const uint1
   return PA_OK;
 }
 
+// ---------------------------------------------------------------- allocation-free scratch
+// Device memory for prefill_attn_dense_noalloc: what prefill_attn_dense takes as
+// its workspace (tile flags, split partials, staged fp16 values). Each GPU the
+// library runs on holds its own copy for the life of the process. In host code
+// `scratch` names a host-side stand-in, not device memory: only the address
+// hipGetSymbolAddress returns for the current device is ever used.
+static __device__ __align__(256) uint8_t scratch[PA_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;   // per device id; null until looked up
+
+// The current device's copy of `scratch`, looked up once per device with that
+// device current (nullptr and the HIP error on failure).
+void* device_scratch(hipError_t* err) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) { *err = e; return nullptr; }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if ((size_t)dev >= g_scratch_ptr.size()) g_scratch_ptr.resize(dev + 1, nullptr);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) { *err = e != hipSuccess ? e : hipErrorInvalidSymbol; return nullptr; }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -165,6 +197,7 @@ const char* pa_status_string(int status) {
     case PA_EINVAL: return "invalid argument";
     case PA_EUNSUPPORTED: return "unsupported size or parameter";
     case PA_EWORKSPACE: return "workspace missing or too small";
+    case PA_ESCRATCH: return "sizes need more scratch than the allocation-free entry point's static array holds";
     case PA_EHIP: {
       thread_local std::string msg;
       msg = "HIP runtime error: " + g_last_hip_error;
@@ -189,6 +222,25 @@ int prefill_attn_dense(const uint16_t* Q, int C, int n_q, const uint16_t* K, con
   return enqueue_dense(DENSE_F16_MASK, Q, C, n_q, K, V, T, n_kv, d, mask, mask_ld, -1, scale, O, workspace,
                        workspace_bytes, static_cast<hipStream_t>(stream));
 }
+
+int prefill_attn_dense_noalloc(const uint16_t* Q, int C, int n_q, const uint16_t* K, const uint16_t* V,
+                               int T, int n_kv, int d, const uint16_t* mask, int64_t mask_ld, float scale,
+                               float* O, void* stream) {
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(mask) || !aligned16(O))
+    return PA_EINVAL;
+  if (C < 1 || T < 1 || n_q < 1 || n_kv < 1 || n_q % n_kv != 0) return PA_EINVAL;
+  if (mask_ld < T || !good_scale(scale)) return PA_EINVAL;
+  if (d != 64 && d != 128) return PA_EUNSUPPORTED;
+  if (T > PA_MAX_T) return PA_EUNSUPPORTED;
+  if (pa::plan_dense(C, T, n_q, n_kv, d).total_bytes > PA_NOALLOC_SCRATCH_BYTES) return PA_ESCRATCH;
+  hipError_t e = hipSuccess;
+  void* ws = device_scratch(&e);
+  if (ws == nullptr) return hip_status(e);
+  return enqueue_dense(DENSE_F16_MASK, Q, C, n_q, K, V, T, n_kv, d, mask, mask_ld, -1, scale, O, ws,
+                       PA_NOALLOC_SCRATCH_BYTES, static_cast<hipStream_t>(stream), false);
+}
+
+size_t prefill_attn_dense_noalloc_limit(void) { return PA_NOALLOC_SCRATCH_BYTES; }
 
 int prefill_attn_dense_bits(const uint16_t* Q, int C, int n_q, const uint16_t* K, const uint16_t* V,
                             int T, int n_kv, int d, const uint32_t* mask_bits, int64_t bits_ld,

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = _lib.lib()
-    for code in (0, -1, -2, -3, -4, 7):
+    for code in (0, -1, -2, -3, -4, -5, 7):
         assert lib.pa_status_string(code)
 
 
@@ -77,6 +77,26 @@ def test_dense_bits_rejects(kw, code):
     assert _lib.lib().prefill_attn_dense_bits(a["Q"], a["C"], a["n_q"], a["K"], a["V"], a["T"], a["n_kv"],
                                               a["d"], a["mask"], a["ld"], a["scale"], a["O"], a["ws"],
                                               a["ws_bytes"], a["stream"]) == code
+
+
+def test_dense_noalloc_rejects():
+    """The allocation-free entry: bad arguments as prefill_attn_dense, and sizes whose
+    workspace exceeds its static scratch refused with PA_ESCRATCH (before any launch)."""
+    lib = _lib.lib()
+    f = lambda **kw: lib.prefill_attn_dense_noalloc(
+        kw.get("Q", FAKE), kw.get("C", 64), 4, FAKE, FAKE, kw.get("T", 256), kw.get("n_kv", 2), kw.get("d", 128),
+        FAKE, kw.get("ld", kw.get("T", 256)), kw.get("scale", 0.125), FAKE, None)
+    limit = lib.prefill_attn_dense_noalloc_limit()
+    assert limit == 80 << 20
+    assert f(Q=None) == _lib.PA_EINVAL
+    assert f(ld=100) == _lib.PA_EINVAL
+    assert f(scale=0.0) == _lib.PA_EINVAL
+    assert f(d=96) == _lib.PA_EUNSUPPORTED
+    T = 200_000                                    # staged values alone: 200,000 x 4 x 128 x 2 bytes > 80 MiB
+    assert lib.prefill_attn_dense_workspace(64, T, 4, 4, 128) > limit
+    assert f(T=T, n_kv=4) == _lib.PA_ESCRATCH
+    assert lib.prefill_attn_dense_workspace(64, 32768, 4, 2, 128) <= limit
+    assert b"static" in lib.pa_status_string(_lib.PA_ESCRATCH)
 
 
 def test_dense_workspace_size():
