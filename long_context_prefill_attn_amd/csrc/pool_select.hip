@@ -88,7 +88,11 @@ hipError_t launch_pool(const uint16_t* K, const uint16_t* V, int T, int n_kv, in
 // ---------------------------------------------------------------------------
 // select_blocks: one workgroup of 8 waves per (KV head g, query block j), or
 // several sharing its voter tiles when the pairs are too few to fill the chip
-// (their votes are merged by select_merge_kernel; see launch_select).
+// (their votes are merged by select_merge_kernel; see launch_select). A voter
+// tile is 512 voters (64 per wave): the 128 rows x 4 query heads of a block at
+// B = 128 in one tile. Candidates are staged into LDS as bf16 hi/lo in chunks
+// of 256 (head dim 128) or 512 (64); when all of a block's candidates fit in
+// one chunk they are staged once and serve both passes of every voter tile.
 //
 // Voters are the (row, query head) pairs of block j in this chunk; candidates
 // are the blocks b < j. The result must equal the fixed-order fp64 rule
@@ -110,16 +114,13 @@ hipError_t launch_pool(const uint16_t* K, const uint16_t* V, int T, int n_kv, in
 //     also absorbs the fp32 norms and comparisons) plus 1e-30 per unit for
 //     flushed denormals. Then |(r' - M') - (r - M)| <= 2E, so a pair whose
 //     filtered gap lies more than 2E (+ 2^-22 |theta|) from theta is decided;
-//  2. lists the other pairs as ambiguous. The exact argmax of voter i is the
-//     filter's argmax unless another candidate came within 2E of the filtered
-//     max; such voters are flagged and their near-max pairs listed;
-//  3. re-evaluates the listed pairs in fp64 in the reference order: M_i
-//     exactly (the filter's argmax, or the max over a flagged voter's near-max
-//     pairs),
-//     then each ambiguous pair against theta. Each exact dot product is done
-//     by a wave: one coalesced load of the two rows, the exact fp64 products
-//     staged in LDS, one lane summing them in order (4 pairs per wave at a
-//     time).
+//  2. lists the other pairs as ambiguous, and every pair whose filtered score
+//     lies within 2E of its voter's filtered max (near-max pairs): the exact
+//     max M_i is attained at one of those;
+//  3. re-evaluates in fp64 in the reference order the near-max pairs of the
+//     voters with ambiguous pairs (their max gives M_i exactly) and the
+//     ambiguous pairs, in one round, one pair per thread as a sequential fp64
+//     fma chain over d; then each ambiguous pair is tested against theta.
 // If a list overflows, or magnitudes leave the range where the bound holds
 // (|q|, |kbar| or their product above 1e30), the voter tile is redone exactly
 // in fp64 for all pairs. alpha = 0 (theta = -inf) keeps every visible block.
@@ -128,24 +129,52 @@ hipError_t launch_pool(const uint16_t* K, const uint16_t* V, int T, int n_kv, in
 //
 // MFMA orientation: A = kbar (32 candidates x 16 dims, LDS), B = Q^T (16 dims x
 // 32 voters, registers). Accumulator element i of lane l is candidate
-// 8(i/4) + 4(l/32) + i%4 against voter l%32, so a voter's max, near-max count
-// and argmax live in lanes l and l^32; "some voter votes for candidate c" is one
-// ballot per accumulator element, consumed on the scalar unit.
+// 8(i/4) + 4(l/32) + i%4 against voter l%32, so a voter's max lives in lanes l
+// and l^32; a lane's vote bits for its 16 candidates are ORed over the 32
+// voters of each half-wave with DPP row operations.
 // ---------------------------------------------------------------------------
 constexpr int SEL_WAVES = 8;
 constexpr int SEL_THREADS = SEL_WAVES * 64;
-constexpr int SEL_VT = SEL_WAVES * 32;   // voters per tile: 32 per wave
-constexpr int SEL_CH = 64;               // candidates staged per chunk
+constexpr int SEL_VT = SEL_WAVES * 64;   // voters per tile: 64 per wave
 constexpr int SEL_MAX_NB = 8192;
-constexpr int SEL_AMB_CAP = 2048;        // ambiguous pairs per voter tile
-constexpr int SEL_JOB_CAP = 2048;        // exact max evaluations per voter tile
-constexpr int SEL_NEAR_CAP = 1024;       // near-max pairs of flagged voters per voter tile
-constexpr int SEL_JOBS = 4;              // exact dot products per wave at a time
+constexpr int SEL_AMB_CAP = 1024;        // ambiguous pairs per voter tile
+constexpr int SEL_JOB_CAP = 1024;        // exact max evaluations per voter tile
+constexpr int SEL_NEAR_W = 128;          // near-max pairs per wave and voter tile (at least one per voter)
+// candidates per LDS chunk: 128 KB of bf16 hi + lo rows
+template <int D> struct SelGeo { static constexpr int CH = 32768 / D; };
 constexpr float SEL_ERR = 1.0e-4f;
 constexpr float SEL_ABS = 1.0e-30f;
 constexpr float SEL_MAG = 1.0e30f;
 
 __device__ __forceinline__ int sel_swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+
+// Workgroup barrier after this wave's LDS writes have completed, leaving its
+// global loads in flight (the query loads of the voter tile keep arriving while
+// the staged candidates are published).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt at their maxima
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// A 16-byte load through a buffer resource over base[0 .. range): offsets at or
+// past the range read as zeros without touching memory. (Kept outside the
+// templates: hipcc's host pass drops kernel stubs when the buffer-resource type
+// appears inside templated device code.)
+__device__ __forceinline__ u32x4 buffer_load16(const void* base, uint32_t range, uint32_t voff) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, range, 0x00020000);
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, 0));
+}
+
+// The thread id, opaque to the optimiser: addresses derived from it where the
+// scoring loops are not are formed afresh there rather than held in registers
+// through those loops.
+__device__ __forceinline__ int fresh_tid() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
 
 // All ones if the wave-uniform x is non-zero, else 0, on the scalar unit (a
 // plain C++ test of the upper half of a 64-bit ballot becomes a 64-bit vector
@@ -200,69 +229,93 @@ __device__ __forceinline__ double dval(unsigned long long k) {
 
 template <int D>
 struct SelShared {
-  union {
-    struct {
-      uint16_t khi[SEL_CH * D];   // bf16 hi parts, row-major [candidate][d], 16-byte chunks swizzled
-      uint16_t klo[SEL_CH * D];   // bf16 lo parts, same layout
-    } k;
-    double prod[SEL_WAVES][SEL_JOBS][D];   // exact products of the re-evaluated pairs
-  } u;
+  struct {
+    uint16_t khi[SelGeo<D>::CH * D];   // bf16 hi parts, row-major [candidate][d], 16-byte chunks swizzled
+    uint16_t klo[SelGeo<D>::CH * D];   // bf16 lo parts, same layout
+  } k;
   unsigned long long mxkey[SEL_VT];        // exact max (as dkey) of voters with ambiguous pairs
+  double ambval[SEL_AMB_CAP];              // exact scores of the ambiguous pairs
   uint32_t amb[SEL_AMB_CAP];               // (voter << 16) | block
   uint32_t jobs[SEL_JOB_CAP];              // pairs whose exact score enters a max
-  uint32_t nearl[SEL_NEAR_CAP];            // near-max pairs of flagged voters: (voter << 16) | block
+  uint32_t nearl[SEL_WAVES * SEL_NEAR_W];  // near-max pairs, (voter << 16) | block, a part per wave
+  uint32_t ncnt[SEL_WAVES];                // entries in each wave's part
   uint32_t flagw[SEL_MAX_NB / 32];
   uint32_t wsum[SEL_WAVES];
-  uint16_t argb[SEL_VT];                   // the filter's argmax per voter
   uint8_t va[SEL_VT];                      // voter has ambiguous pairs
-  uint8_t multi[SEL_VT];                   // several candidates came within 2E of the max
   float red[SEL_WAVES];
-  uint32_t amb_cnt, job_cnt, near_cnt;
+  uint32_t amb_cnt, job_cnt;
   uint32_t overflow;
 };
 
-// Exact fp64 scores of the listed (voter, block) pairs, SEL_JOBS pairs per wave
-// at a time. MODE 0: raise the voter's exact max; MODE 1: vote if the pair clears
-// theta against that max.
-template <int D, int MODE>
-__device__ __forceinline__ void exact_pairs(SelShared<D>& S, const uint32_t* list, int n,
-                                            const uint16_t* qg, int group, int n_q, int vt0,
-                                            const float* kg, double theta, int wave, int lane) {
-  for (int base = wave * SEL_JOBS; base < n; base += SEL_WAVES * SEL_JOBS) {
+// r = q.kbar in fp64, dims in increasing order, with each half of both rows
+// loaded before its 64 fmas (two rounds of loads in flight instead of sixteen)
+template <int D>
+__device__ __forceinline__ double dot_exact_prefetched(const uint16_t* __restrict__ q,
+                                                       const float* __restrict__ kb) {
+  constexpr int H = D / 2;
+  double acc = 0.0;
+#pragma unroll 1
+  for (int h = 0; h < 2; ++h) {
+    u32x4 qv[H / 8];
+    float4 kv[H / 4];
 #pragma unroll
-    for (int k = 0; k < SEL_JOBS; ++k) {
-      if (base + k >= n) break;  // wave-uniform
-      const uint32_t job = list[base + k];
-      const int v = vt0 + (int)(job >> 16), b = (int)(job & 0xFFFFu);
-      const uint16_t* qp = qg + ((size_t)(v / group) * n_q + (v % group)) * D;
-      const float* kb = kg + (size_t)b * D;
-      double* pr = S.u.prod[wave][k];
-      if (D == 128) {
-        const uint32_t qq = reinterpret_cast<const uint32_t*>(qp)[lane];
-        const float2 kk = reinterpret_cast<const float2*>(kb)[lane];
-        pr[2 * lane] = (double)__uint_as_float(qq << 16) * (double)kk.x;
-        pr[2 * lane + 1] = (double)__uint_as_float(qq & 0xFFFF0000u) * (double)kk.y;
-      } else {
-        pr[lane] = (double)bf16_to_f32(qp[lane]) * (double)kb[lane];
+    for (int c = 0; c < H / 8; ++c) qv[c] = *reinterpret_cast<const u32x4*>(q + h * H + 8 * c);
+#pragma unroll
+    for (int c = 0; c < H / 4; ++c) kv[c] = *reinterpret_cast<const float4*>(kb + h * H + 4 * c);
+#pragma unroll
+    for (int c = 0; c < H / 8; ++c) {
+      const float k8[8] = {kv[2 * c].x, kv[2 * c].y, kv[2 * c].z, kv[2 * c].w,
+                           kv[2 * c + 1].x, kv[2 * c + 1].y, kv[2 * c + 1].z, kv[2 * c + 1].w};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        acc = __builtin_fma((double)__uint_as_float(qv[c][w] << 16), (double)k8[2 * w], acc);
+        acc = __builtin_fma((double)__uint_as_float(qv[c][w] & 0xFFFF0000u), (double)k8[2 * w + 1], acc);
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (lane < SEL_JOBS && base + lane < n) {
-      const double* pr = S.u.prod[wave][lane];
-      double acc = 0.0;
-#pragma unroll 8
-      for (int d = 0; d < D; ++d) acc = acc + pr[d];   // increasing d, as the reference sums
-      const uint32_t job = list[base + lane];
-      const int vl = (int)(job >> 16), b = (int)(job & 0xFFFFu);
-      if (MODE == 0) atomicMax(&S.mxkey[vl], dkey(acc));
-      else if (acc - dval(S.mxkey[vl]) > theta) atomicOr(&S.flagw[b >> 5], 1u << (b & 31));
-    }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
+  return acc;
+}
+
+// Exact fp64 scores of the listed pairs in one round, one pair per thread: the
+// max jobs (jobs[0 .. njob), whose results raise their voters' exact max) and the
+// ambiguous pairs (amb[0 .. namb), whose results are kept); then, after a
+// barrier, each ambiguous pair votes if it clears theta against its voter's max.
+template <int D>
+__device__ __forceinline__ void exact_pairs(SelShared<D>& S, int njob, int namb, const uint16_t* qg,
+                                            int group, int n_q, int vt0, const float* kg, double theta) {
+  for (int e = fresh_tid(); e < njob + namb; e += SEL_THREADS) {
+    const uint32_t pr = e < njob ? S.jobs[e] : S.amb[e - njob];
+    const int vl = (int)(pr >> 16), b = (int)(pr & 0xFFFFu);
+    const int v = vt0 + vl;
+    const double r = dot_exact_prefetched<D>(qg + ((size_t)(v / group) * n_q + (v % group)) * D, kg + (size_t)b * D);
+    if (e < njob) atomicMax(&S.mxkey[vl], dkey(r));
+    else S.ambval[e - njob] = r;
+  }
+  __syncthreads();
+  for (int e = fresh_tid(); e < namb; e += SEL_THREADS) {
+    const uint32_t pr = S.amb[e];
+    const int vl = (int)(pr >> 16), b = (int)(pr & 0xFFFFu);
+    if (S.ambval[e] - dval(S.mxkey[vl]) > theta) atomicOr(&S.flagw[b >> 5], 1u << (b & 31));
+  }
+}
+
+// max(m, x[0..15])
+__device__ __forceinline__ float slice_max(float m, const float (&x)[16]) {
+#pragma unroll
+  for (int i = 0; i < 16; i += 2) m = __builtin_fmaxf(m, __builtin_fmaxf(x[i], x[i + 1]));
+  return m;
+}
+
+// OR of x over each half-wave: lane 31 returns the OR of lanes 0..31, lane 63 that
+// of lanes 32..63 (prefix ORs within rows of 16 by row shifts, then row 0's and
+// row 2's totals broadcast into rows 1 and 3)
+__device__ __forceinline__ uint32_t or_half_waves(uint32_t x) {
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);   // row_shr:1
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);   // row_shr:2
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);   // row_shr:4
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);   // row_shr:8
+  x |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  return x;
 }
 
 // The end of a selection: flagw holds the voted candidates of query block j
@@ -313,16 +366,18 @@ __device__ void finish_selection(uint32_t* flagw, uint32_t* wsum, int nb, int nc
 }
 
 template <int D>
-// Four waves per SIMD (at most 128 registers): two workgroups share a CU, so one
-// workgroup's staging and barriers overlap the other's scoring.
-__global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_eu(4))) select_kernel(
+// 8 waves, two per SIMD (up to 256 registers), one workgroup per CU (the LDS
+// holds a 128 KB candidate chunk). Each wave scores 64 voters: two groups of 32,
+// so every candidate fragment read from LDS feeds two MFMA chains.
+__global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_eu(1, 2))) select_kernel(
     const uint16_t* __restrict__ Q, int C, int q_start, int n_q, int n_kv,
     const float* __restrict__ Kp, int pool_ld, int nb, int block, double theta, float theta_f,
     float theta_slack,
     int exact_only, int n_qblk, int sink_blocks, int window_blocks, int dense_tail_blocks,
     int n_split, int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_cnt) {
-  constexpr int NST = D / 16;   // MFMA k-steps
-  constexpr int TPR = SEL_THREADS / SEL_CH;   // staging threads per candidate row
+  constexpr int NST = D / 16;                 // MFMA k-steps
+  constexpr int CH = SelGeo<D>::CH;           // candidates per LDS chunk
+  constexpr int TPR = SEL_THREADS / CH;       // staging threads per candidate row
   constexpr int DPT = D / TPR;                // staged dims per thread
   __shared__ __attribute__((aligned(16))) SelShared<D> S;
 
@@ -353,161 +408,213 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
       S.flagw[i] = (i < (nc >> 5)) ? 0xFFFFFFFFu : ((1u << (nc & 31)) - 1u);
   } else if (nc > 0) {
     float mnorm = 0.f;  // max_b |kbar_b|_2 over the candidates (set in the first tile's pass 0)
+    const bool resident = nc <= CH;   // every candidate fits in one chunk: stage once
+    bool staged = false;              // the LDS chunk holds candidates 0 .. nc-1
     for (int vt0 = sp * SEL_VT; vt0 < nv; vt0 += n_split * SEL_VT) {
       __syncthreads();  // previous tile's readers of the shared state are done
-      for (int i = tid; i < SEL_VT; i += SEL_THREADS) { S.va[i] = 0; S.mxkey[i] = 0; }
-      if (tid == 0) { S.amb_cnt = 0; S.job_cnt = 0; S.near_cnt = 0; S.overflow = exact_only; }
+      for (int i = fresh_tid(); i < SEL_VT; i += SEL_THREADS) { S.va[i] = 0; S.mxkey[i] = 0; }
+      if (tid == 0) { S.amb_cnt = 0; S.job_cnt = 0; S.overflow = exact_only; }
 
-      // B operand: q of the wave's 32 voters (voter = lane % 32), held for the whole tile
-      const int vl = wave * 32 + col;  // voter within the tile
-      const bool vok = vt0 + vl < nv;
-      bf16x8 qf[NST];
-      float qn;
-      {
-        const uint16_t* qp = vok ? qptr(vt0 + vl) : Q;
-        float ss = 0.f;
+      // B operands: q of the wave's two groups of 32 voters (voter = lane % 32),
+      // held for the whole tile; voter index in the tile vl = 64 wave + 32 gi + col
+      // (the norms |q| are formed at the end of pass 0, where the error bound needs them)
+      bf16x8 qf[2][NST];
+      bool vok[2];
+      auto load_q = [&]() {
 #pragma unroll
-        for (int st = 0; st < NST; ++st) {
-          u32x4 raw = {0u, 0u, 0u, 0u};
-          if (vok) raw = *reinterpret_cast<const u32x4*>(qp + 16 * st + 8 * half);
+        for (int gi = 0; gi < 2; ++gi) {
+          const int vl = wave * 64 + gi * 32 + col;
+          vok[gi] = vt0 + vl < nv;
+          const uint16_t* qp = vok[gi] ? qptr(vt0 + vl) : Q;
 #pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const float a = __uint_as_float(raw[w] << 16), b = __uint_as_float(raw[w] & 0xFFFF0000u);
-            ss = __builtin_fmaf(a, a, ss);
-            ss = __builtin_fmaf(b, b, ss);
+          for (int st = 0; st < NST; ++st) {
+            // loaded unconditionally (a missing voter reads row 0) and zeroed by a
+            // select: no branch, so the loads queue without forcing waits
+            u32x4 raw = *reinterpret_cast<const u32x4*>(qp + 16 * st + 8 * half);
+            if (!vok[gi]) raw = u32x4{0u, 0u, 0u, 0u};
+            qf[gi][st] = __builtin_bit_cast(bf16x8, raw);
           }
-          qf[st] = __builtin_bit_cast(bf16x8, raw);
         }
-        qn = __builtin_sqrtf(ss + partner32(ss));
-      }
+      };
 
-      // the voter's running max and second max over this lane's candidates
-      float m1 = -__builtin_inff(), m2 = -__builtin_inff();
-      float M = 0.f, tY = 0.f, tA = 0.f;  // the voter's max; yes above tY; ambiguous from tA
-      float tN = 0.f;                     // near-max from tN (recorded for flagged voters)
-      int nidx = -1;                      // this lane's candidate equal to the max, if any
-      bool multi = false;
+      // per voter: running max over this lane's candidates (pass 0); then the
+      // thresholds yes-above tY, ambiguous-from tA and near-max-from tN (pass 1)
+      float m1[2] = {-__builtin_inff(), -__builtin_inff()};
+      float tY[2] = {0.f, 0.f}, tA[2] = {0.f, 0.f}, tN[2] = {0.f, 0.f};
       float mloc = 0.f;
+      uint32_t nbase = 0;   // entries in this wave's part of the near list (wave-uniform)
       const bool first_tile = vt0 == sp * SEL_VT;   // this workgroup's first voter tile
-      for (int pass = 0; pass < 2; ++pass) {
-        for (int c0 = 0; c0 < nc; c0 += SEL_CH) {
-          __syncthreads();  // readers of the previous chunk are done
-          {  // stage candidates c0 .. c0+63 as bf16 hi/lo
-            const int row = tid / TPR, part = tid % TPR;
-            const int b = c0 + row;
-            float x[DPT];
-            if (b < nc) {
-              const float4* src = reinterpret_cast<const float4*>(kg + (size_t)b * D + part * DPT);
+      // Stage candidates c0 .. min(c0 + CH, nc) - 1 as bf16 hi/lo: TPR threads per
+      // candidate row, in two rounds of loads (half of the thread's dims each).
+      // Rows past the last candidate are left as they are: the tiles mask them.
+      // WithQ: the voter tile's q loads are issued behind the first round, so the
+      // candidates' loads do not queue behind them.
+      auto stage = [&](int c0, bool norms, auto with_q) {
+        constexpr bool WithQ = decltype(with_q)::value;
+        const int t = fresh_tid();   // recomputed here, not held through the passes
+        const int row = t / TPR, part = t % TPR;
+        const int b = c0 + row;
+        const bool live = b < nc;
+        // loads through a buffer resource over the candidates: a row past the
+        // last one reads nothing, and the loads need no branch, so the q loads
+        // behind them are not waited for with them
+        const uint32_t range = (uint32_t)(nc * D * 4);
+        const uint32_t voff = (uint32_t)((b * D + part * DPT) * 4);
+        float ss = 0.f;
+        auto convert = [&](const float4* fv, int hh) {
 #pragma unroll
-              for (int e = 0; e < DPT / 4; ++e) {
-                const float4 f = src[e];
-                x[4 * e] = f.x; x[4 * e + 1] = f.y; x[4 * e + 2] = f.z; x[4 * e + 3] = f.w;
-              }
-            } else {
+          for (int cc = 0; cc < DPT / 16; ++cc) {
+            const int c = hh * (DPT / 16) + cc;
+            const float x[8] = {fv[2 * cc].x, fv[2 * cc].y, fv[2 * cc].z, fv[2 * cc].w,
+                                fv[2 * cc + 1].x, fv[2 * cc + 1].y, fv[2 * cc + 1].z, fv[2 * cc + 1].w};
+            u32x4 h, l;
 #pragma unroll
-              for (int e = 0; e < DPT; ++e) x[e] = 0.f;
+            for (int w = 0; w < 4; ++w) {
+              const float a = x[2 * w], bb = x[2 * w + 1];
+              const uint32_t hp = pack_bf16x2(a, bb);
+              h[w] = hp;
+              l[w] = pack_bf16x2(a - __uint_as_float(hp << 16), bb - __uint_as_float(hp & 0xFFFF0000u));
+              ss = __builtin_fmaf(a, a, ss);
+              ss = __builtin_fmaf(bb, bb, ss);
             }
-#pragma unroll
-            for (int c = 0; c < DPT / 8; ++c) {
-              u32x4 h, l;
-#pragma unroll
-              for (int w = 0; w < 4; ++w) {
-                const float a = x[8 * c + 2 * w], bb = x[8 * c + 2 * w + 1];
-                const uint32_t hp = pack_bf16x2(a, bb);
-                h[w] = hp;
-                l[w] = pack_bf16x2(a - __uint_as_float(hp << 16), bb - __uint_as_float(hp & 0xFFFF0000u));
-              }
-              const int off = row * D + (((part * (DPT / 8) + c) ^ sel_swz(row)) * 8);
-              *reinterpret_cast<u32x4*>(&S.u.k.khi[off]) = h;
-              *reinterpret_cast<u32x4*>(&S.u.k.klo[off]) = l;
-            }
-            if (pass == 0 && first_tile) {
-              float ss = 0.f;
-#pragma unroll
-              for (int e = 0; e < DPT; ++e) ss = __builtin_fmaf(x[e], x[e], ss);
-#pragma unroll
-              for (int off = 1; off < TPR; off <<= 1) ss += __shfl_xor(ss, off);
-              if (b < nc) mloc = fmaxf(mloc, __builtin_sqrtf(ss));
-            }
+            const int off = row * D + (((part * (DPT / 8) + c) ^ sel_swz(row)) * 8);
+            *reinterpret_cast<u32x4*>(&S.k.khi[off]) = h;
+            *reinterpret_cast<u32x4*>(&S.k.klo[off]) = l;
           }
-          __syncthreads();
+        };
+        float4 f0[DPT / 8], f1[DPT / 8];
+#pragma unroll
+        for (int c = 0; c < DPT / 8; ++c)
+          f0[c] = __builtin_bit_cast(float4, buffer_load16(kg, range, voff + 16 * c));
+#pragma unroll
+        for (int c = 0; c < DPT / 8; ++c)
+          f1[c] = __builtin_bit_cast(float4, buffer_load16(kg, range, voff + 16 * (DPT / 8 + c)));
+        if constexpr (WithQ) load_q();
+        if (live) {
+          convert(f0, 0);
+          convert(f1, 1);
+        }
+        if (norms) {
+#pragma unroll
+          for (int off = 1; off < TPR; off <<= 1) ss += __shfl_xor(ss, off);
+          if (live) mloc = fmaxf(mloc, __builtin_sqrtf(ss));
+        }
+        staged = resident;
+        lds_barrier();
+      };
+      if (!(resident && staged)) stage(0, first_tile, std::true_type{});
+      else load_q();
+      for (int pass = 0; pass < 2; ++pass) {
+        for (int c0 = 0; c0 < nc; c0 += CH) {
+          if ((pass > 0 || c0 > 0) && !(resident && staged)) {
+            __syncthreads();  // readers of the previous chunk are done
+            stage(c0, pass == 0 && first_tile, std::false_type{});
+          }
+          const int nch = min(CH, nc - c0);
 #pragma unroll 1
-          for (int t = 0; t < SEL_CH / 32; ++t) {
+          for (int t = 0; t < (nch + 31) / 32; ++t) {
             const int cb = c0 + 32 * t;
-            if (cb >= nc) break;
-            f32x16 acc = {};
+            f32x16 acc[2] = {f32x16{}, f32x16{}};
             const int arow = 32 * t + col;
 #pragma unroll
             for (int st = 0; st < NST; ++st) {
               const int off = arow * D + (((2 * st + half) ^ sel_swz(arow)) * 8);
-              const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&S.u.k.khi[off]);
-              const bf16x8 al = *reinterpret_cast<const bf16x8*>(&S.u.k.klo[off]);
-              acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, qf[st], acc, 0, 0, 0);
-              acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, qf[st], acc, 0, 0, 0);
+              const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&S.k.khi[off]);
+              const bf16x8 al = *reinterpret_cast<const bf16x8*>(&S.k.klo[off]);
+              acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, qf[0][st], acc[0], 0, 0, 0);
+              acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, qf[1][st], acc[1], 0, 0, 0);
+              acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, qf[0][st], acc[0], 0, 0, 0);
+              acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, qf[1][st], acc[1], 0, 0, 0);
             }
-            // element i: candidate cb + 4 half + 8(i/4) + i%4, voter col
+            // element i of acc[gi]: candidate cb + 4 half + 8(i/4) + i%4 against voter
+            // 64 wave + 32 gi + col
             const int cbase = cb + 4 * half;
             // RG: the tile runs past the last candidate (the final tile only)
             auto tile = [&](auto rg) {
               constexpr bool RG = decltype(rg)::value;
-              if (pass == 0) {
+              if (pass == 0) {   // running max
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                  const float x = (!RG || cbase + 8 * (i >> 2) + (i & 3) < nc) ? acc[i] : -__builtin_inff();
-                  m2 = __builtin_amdgcn_fmed3f(m1, x, m2);
-                  m1 = fmaxf(m1, x);
+                for (int gi = 0; gi < 2; ++gi) {
+                  float x[16];
+#pragma unroll
+                  for (int i = 0; i < 16; ++i)
+                    x[i] = (!RG || cbase + 8 * (i >> 2) + (i & 3) < nc) ? acc[gi][i] : -__builtin_inff();
+                  m1[gi] = slice_max(m1[gi], x);
                 }
                 return;
               }
-              // one ballot per comparison: yes masks become the candidates' vote
-              // bits, (>= tA) & !(> tY) marks ambiguous pairs
-              uint32_t word = 0;
-              uint64_t rare_m = 0;
+              // vote bits: bit 8(i/4) + i%4 of a lane's mask set when its voter clears
+              // tY on element i (either group); then the OR over the 32 voters of each
+              // half-wave gives the slice's vote word (the second half's candidates
+              // sit 4 positions up)
+              uint32_t ymask = 0;
+              float dmin[2] = {__builtin_inff(), __builtin_inff()};
+              float smax[2] = {-__builtin_inff(), -__builtin_inff()};
+              // threshold centre and the trigger band, formed here (from tA and tY) rather
+              // than held through the loops
+              float ctr[2], band[2];
 #pragma unroll
-              for (int i = 0; i < 16; ++i) {
-                const int c = cbase + 8 * (i >> 2) + (i & 3);
-                const float a = acc[i];
-                bool yv = a > tY, av = a >= tA, ev = a == M;
-                if (RG) {
-                  const bool ok = c < nc;
-                  yv = yv && ok;
-                  av = av && ok;
-                  ev = ev && ok;
-                }
-                const uint64_t ym = __builtin_amdgcn_ballot_w64(yv);
-                const uint64_t am = __builtin_amdgcn_ballot_w64(av);
-                rare_m |= am & ~ym;
-                word |= ones_if_nonzero((uint32_t)ym) & (1u << (8 * (i >> 2) + (i & 3)));
-                word |= ones_if_nonzero((uint32_t)(ym >> 32)) & (1u << (8 * (i >> 2) + 4 + (i & 3)));
-                nidx = ev ? c : nidx;
+              for (int gi = 0; gi < 2; ++gi) {
+                float ya = tY[gi], aa = tA[gi];
+                asm volatile("" : "+v"(ya), "+v"(aa));
+                ctr[gi] = 0.5f * ya + 0.5f * aa;   // inf for a missing voter: |a - inf| = inf
+                band[gi] = (ya - aa) + 0x1p-20f * __builtin_fabsf(ctr[gi]);
               }
-              if (rare_m != 0) {
-                if ((rare_m >> lane) & 1) {
+#pragma unroll
+              for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                  const float a =
+                      (!RG || cbase + 8 * (i >> 2) + (i & 3) < nc) ? acc[gi][i] : -__builtin_inff();
+                  ymask |= (uint32_t)(a > tY[gi]) << (8 * (i >> 2) + (i & 3));
+                  dmin[gi] = fminf(dmin[gi], __builtin_fabsf(a - ctr[gi]));
+                  smax[gi] = __builtin_fmaxf(smax[gi], a);
+                }
+#pragma unroll
+              for (int gi = 0; gi < 2; ++gi) {
+                const int vl = wave * 64 + gi * 32 + col;
+                // ambiguous pairs lie within w of the threshold; dmin <= band is a
+                // conservative trigger for them (band covers w and the roundings of
+                // tA, tY and ctr), re-tested exactly below
+                const bool near_th = dmin[gi] <= band[gi];
+                if (__builtin_amdgcn_ballot_w64(near_th)) {
+                  if (near_th) {
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                      const int c = cbase + 8 * (i >> 2) + (i & 3);
+                      if ((!RG || c < nc) & (acc[gi][i] >= tA[gi]) & !(acc[gi][i] > tY[gi])) {
+                        const uint32_t k = atomicAdd(&S.amb_cnt, 1u);
+                        if (k < SEL_AMB_CAP) S.amb[k] = ((uint32_t)vl << 16) | (uint32_t)c;
+                        else S.overflow = 1u;
+                        S.va[vl] = 1;
+                      }
+                    }
+                  }
+                }
+                // near-max pairs (within 2E of the voter's filtered max), listed in
+                // the wave's own part of the near list at a wave-uniform position
+                // (no atomics: the wave's count stays in a scalar register)
+                const bool near_max = smax[gi] >= tN[gi];
+                if (__builtin_amdgcn_ballot_w64(near_max)) {
 #pragma unroll
                   for (int i = 0; i < 16; ++i) {
                     const int c = cbase + 8 * (i >> 2) + (i & 3);
-                    if ((!RG || c < nc) & (acc[i] >= tA) & !(acc[i] > tY)) {
-                      const uint32_t k = atomicAdd(&S.amb_cnt, 1u);
-                      if (k < SEL_AMB_CAP) S.amb[k] = ((uint32_t)vl << 16) | (uint32_t)c;
-                      else S.overflow = 1u;
-                      S.va[vl] = 1;
+                    const bool hit = (!RG || c < nc) & (acc[gi][i] >= tN[gi]);
+                    const uint64_t m = __builtin_amdgcn_ballot_w64(hit);
+                    if (m) {
+                      if (hit) {
+                        const uint32_t pos = nbase + __builtin_amdgcn_mbcnt_hi(
+                            (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                        if (pos < (uint32_t)SEL_NEAR_W)
+                          S.nearl[wave * SEL_NEAR_W + pos] = ((uint32_t)vl << 16) | (uint32_t)c;
+                      }
+                      nbase += (uint32_t)__builtin_popcountll(m);
                     }
                   }
                 }
               }
-              if (__builtin_amdgcn_ballot_w64(multi)) {
-                if (multi) {   // the exact max of a flagged voter is among these
-#pragma unroll
-                  for (int i = 0; i < 16; ++i) {
-                    const int c = cbase + 8 * (i >> 2) + (i & 3);
-                    if ((!RG || c < nc) & (acc[i] >= tN)) {
-                      const uint32_t k = atomicAdd(&S.near_cnt, 1u);
-                      if (k < SEL_NEAR_CAP) S.nearl[k] = ((uint32_t)vl << 16) | (uint32_t)c;
-                      else S.overflow = 1u;
-                    }
-                  }
-                }
-              }
+              const uint32_t r = or_half_waves(ymask);
+              const uint32_t word = __builtin_amdgcn_readlane(r, 31) | (__builtin_amdgcn_readlane(r, 63) << 4);
               if (word != 0 && lane == 0) atomicOr(&S.flagw[cb >> 5], word);
             };
             if (cb + 32 > nc) tile(std::true_type{});
@@ -525,43 +632,48 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
 #pragma unroll
             for (int w = 1; w < SEL_WAVES; ++w) mnorm = fmaxf(mnorm, S.red[w]);
           }
-          const float p1 = partner32(m1), p2 = partner32(m2);
-          M = fmaxf(m1, p1);
-          const float second = fmaxf(fmaxf(m2, p2), fminf(m1, p1));
-          const float nm = qn * mnorm;
-          const bool bad = vok && !(qn <= SEL_MAG && mnorm <= SEL_MAG && nm <= SEL_MAG);
-          const float e2 = 2.f * (SEL_ERR * nm + SEL_ABS * (qn + mnorm + 1.f));
-          tN = M - e2;
-          multi = vok && second >= tN;  // another candidate may hold the exact max
-          tY = M + (theta_f + (e2 + theta_slack));
-          tA = M + (theta_f - (e2 + theta_slack));
-          if (!vok) M = tY = tA = __builtin_inff();  // no voter: nothing passes any test
+          bool bad = false;
+#pragma unroll
+          for (int gi = 0; gi < 2; ++gi) {
+            float ss = 0.f;
+#pragma unroll
+            for (int st = 0; st < NST; ++st) {
+              const u32x4 raw = __builtin_bit_cast(u32x4, qf[gi][st]);
+#pragma unroll
+              for (int w = 0; w < 4; ++w) {
+                const float a = __uint_as_float(raw[w] << 16), b = __uint_as_float(raw[w] & 0xFFFF0000u);
+                ss = __builtin_fmaf(a, a, ss);
+                ss = __builtin_fmaf(b, b, ss);
+              }
+            }
+            const float qn = __builtin_sqrtf(ss + partner32(ss));
+            const float M = fmaxf(m1[gi], partner32(m1[gi]));
+            const float nm = qn * mnorm;
+            bad = bad || (vok[gi] && !(qn <= SEL_MAG && mnorm <= SEL_MAG && nm <= SEL_MAG));
+            const float e2 = 2.f * (SEL_ERR * nm + SEL_ABS * (qn + mnorm + 1.f));
+            tN[gi] = M - e2;
+            tY[gi] = M + (theta_f + (e2 + theta_slack));
+            tA[gi] = M + (theta_f - (e2 + theta_slack));
+            if (!vok[gi]) tN[gi] = tY[gi] = tA[gi] = __builtin_inff();  // no voter: nothing passes any test
+          }
           if (__ballot(bad) && lane == 0) S.overflow = 1u;
           __syncthreads();
           if (S.overflow) break;  // uniform: redo this voter tile exactly
         }
       }
-      {  // the filter's argmax, and whether another candidate came within 2E of it
-        const int pidx = __float_as_int(partner32(__int_as_float(nidx)));
-        if (half == 0 && vok) {
-          S.argb[vl] = (uint16_t)(nidx >= 0 ? nidx : max(pidx, 0));
-          S.multi[vl] = multi;
-        }
+      if (lane == 0) {
+        S.ncnt[wave] = nbase;
+        if (nbase > (uint32_t)SEL_NEAR_W) S.overflow = 1u;
       }
       __syncthreads();
       const bool go = !S.overflow && S.amb_cnt > 0;
       __syncthreads();  // every thread has read the flags before they change again
       if (go) {
         // pairs whose exact score may be the max of a voter with ambiguous pairs:
-        // its argmax, or its recorded near-max pairs when several came within 2E
-        for (int v = tid; v < SEL_VT; v += SEL_THREADS) {
-          if (!S.va[v] || S.multi[v]) continue;
-          const uint32_t k = atomicAdd(&S.job_cnt, 1u);
-          if (k < SEL_JOB_CAP) S.jobs[k] = ((uint32_t)v << 16) | S.argb[v];
-          else S.overflow = 1u;
-        }
-        const int nn = (int)min(S.near_cnt, (uint32_t)SEL_NEAR_CAP);
-        for (int e = tid; e < nn; e += SEL_THREADS) {
+        // its near-max pairs
+        for (int e = fresh_tid(); e < SEL_WAVES * SEL_NEAR_W; e += SEL_THREADS) {
+          const int w = e / SEL_NEAR_W;
+          if (e - w * SEL_NEAR_W >= (int)S.ncnt[w]) continue;
           const uint32_t pr = S.nearl[e];
           if (!S.va[pr >> 16]) continue;
           const uint32_t k = atomicAdd(&S.job_cnt, 1u);
@@ -569,11 +681,7 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
           else S.overflow = 1u;
         }
         __syncthreads();
-        if (!S.overflow) {
-          exact_pairs<D, 0>(S, S.jobs, (int)S.job_cnt, qg, group, n_q, vt0, kg, theta, wave, lane);
-          __syncthreads();
-          exact_pairs<D, 1>(S, S.amb, (int)S.amb_cnt, qg, group, n_q, vt0, kg, theta, wave, lane);
-        }
+        if (!S.overflow) exact_pairs<D>(S, (int)S.job_cnt, (int)S.amb_cnt, qg, group, n_q, vt0, kg, theta);
       }
       __syncthreads();
       if (S.overflow) {
@@ -639,16 +747,16 @@ hipError_t launch_select(const uint16_t* Q, int C, int q_start, int n_q, int n_k
   const int exact_only = (!inf_theta && !(std::fabs(theta) <= 1e30)) ? 1 : 0;
   const float theta_f = inf_theta ? -HUGE_VALF : (exact_only ? 0.f : (float)theta);
   const float theta_slack = inf_theta || exact_only ? 0.f : (float)std::ldexp(std::fabs(theta), -22);
-  // Two select workgroups fit on a CU. When the (KV head, query block) pairs
-  // fill fewer slots than that (a 4,096-row chunk: 32 query blocks), their voter
-  // tiles are spread over n_split workgroups, as far as the tiles go and as the
-  // partial flag rows fit at the front of a selection row (n_split nw <= nb).
+  // One select workgroup fits on a CU. When the (KV head, query block) pairs
+  // are fewer than the CUs, their voter tiles are spread over n_split
+  // workgroups, as far as the tiles go and as the partial flag rows fit at the
+  // front of a selection row (n_split nw <= nb).
   const int vt_max = (std::min(block, C) * (n_q / n_kv) + SEL_VT - 1) / SEL_VT;
   const int pairs = n_qblk * n_kv;
   const int nw_max = (nb - 1 + 31) / 32;
   int n_split = 1;
   if (theta_f != -HUGE_VALF) {
-    const int want = (2 * device_cus() + pairs - 1) / pairs;
+    const int want = (device_cus() + pairs - 1) / pairs;
     n_split = std::max(1, std::min(std::min(want, vt_max), nw_max > 0 ? nb / nw_max : 1));
   }
   dim3 grid(pairs * n_split);
