@@ -57,20 +57,34 @@ enum { MODE_PLAIN = 0, MODE_GMASK = 1, MODE_BSEL = 2, MODE_POOLED = 3, MODE_CAUS
 // how the dense kernel reads its mask: fp16 (8-byte loads when aligned) or bit-packed
 enum { MASK_F16 = 0, MASK_F16_VEC = 1, MASK_BITS = 2 };
 
-// LDS tiles are row-major [64 keys][D] bf16 with no padding; the 16-byte chunk c
-// of row r sits at chunk position c ^ swz(r). The swizzle spreads the 8 rows a
-// K-operand read touches, and the 4 rows a transposed V read touches, over
-// distinct bank groups.
+// LDS tiles: a tile of 64 keys x D is D/64 half-tiles, each [64 keys][64 dims]
+// with rows of 128 bytes and no padding; dims 64h .. 64h+63 live in half-tile h.
+// Within a half-tile, the 16-byte chunk c of row r sits at chunk position
+// c ^ kswz(r) in K tiles and c ^ vswz(r) in V tiles. gfx950's LDS serves 256 bytes
+// per clock from 64 banks, so a read is conflict-free when each 256-byte group of
+// lanes touches 16 distinct 16-byte bank groups:
+//   * a K-operand read (ds_read_b128): lanes 0..15 take rows n .. n+15 at one
+//     chunk; kswz gives the 8 even and the 8 odd rows 8 distinct positions
+//     (two rows share a 256-byte bank line);
+//   * a transposed V read (ds_read_b64_tr_b16): 32 lanes take 4 rows x 4 chunks;
+//     vswz moves the 4 rows into distinct 4-chunk groups, and repeats every 8
+//     rows so that the read 8 rows further on keeps the same lane offsets.
+// Splitting the rows in halves keeps the swizzle inside the low 3 bits of the
+// chunk index, so dims 64.. of a row sit a fixed HT halves after dims 0..
+// (immediate offsets instead of per-lane registers).
 template <int D>
 struct Geo {
   static constexpr int CPR = D / 8;              // 16-byte chunks per row
+  static constexpr int NH = D / 64;              // half-tiles per tile
+  static constexpr int HT = BN * 64;             // halves of one half-tile
   static constexpr int TILE = BN * D;            // halves of one K or V tile
   static constexpr int RING = (KRK + KRV) * TILE;  // K ring then V ring (halves)
   static constexpr size_t LDS_BYTES = RING * sizeof(uint16_t);
-  static constexpr int RPI = 64 / CPR;           // rows written by one wave-wide 16-byte load
-  static constexpr int NIW = BN / RPI / NW;      // such loads per wave per tile
+  static constexpr int RPI = 8;                  // half-rows written by one wave-wide 16-byte load
+  static constexpr int NIW = NH;                 // such loads per wave per tile
   static constexpr int KCH = BN * D / 8 / NT;    // 16-byte chunks per thread per tile
 };
+constexpr int RS = 64;   // halves between consecutive rows of a half-tile
 
 // The lane id, opaque to the optimiser: what is derived from it after the long
 // step loop is recomputed there instead of being held in registers through it.
@@ -80,7 +94,15 @@ __device__ __forceinline__ int fresh_lane_id() {
   return l;
 }
 
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+__device__ __forceinline__ int kswz(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int vswz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+
+// halves offset of chunk c (16 bytes, dims 8c .. 8c+7) of row r inside a K (V false)
+// or V (V true) tile
+template <int D, bool V>
+__device__ __forceinline__ int tile_pos(int r, int c) {
+  return (c >> 3) * Geo<D>::HT + r * RS + (((c & 7) ^ (V ? vswz(r) : kswz(r))) * 8);
+}
 
 static_assert(FLAG_KEYS == BN, "one mask-flag tile per key step");
 
@@ -100,9 +122,10 @@ __device__ __forceinline__ void buffer_load_lds16(const void* base, uint32_t ran
 
 // Direct HBM -> LDS loads of 64-key tiles of K or V for KV head g, through a
 // buffer resource per tile whose range ends at row T: rows past T read as zeros
-// (their scores are masked). Lane l of a wave-wide 16-byte load lands at byte 16*l of
-// the 1 KB it writes, so each lane fetches the global chunk that belongs at
-// that swizzled position. Each of the 8 waves issues NIW such loads per tile.
+// (their scores are masked). Load j of a tile writes 8 half-rows (1 KB) of half-tile
+// j / 8; lane l lands at byte 16*l, so each lane fetches the global chunk that
+// belongs at that swizzled position (K and V tiles swizzle differently, hence two
+// offset sets). Each of the 8 waves issues NIW such loads per tile.
 template <int D>
 struct TileLoader {
   const uint16_t* kptr;   // K + g*D
@@ -112,10 +135,11 @@ struct TileLoader {
   uint32_t range;         // whole-tensor range (bytes readable from kptr / vptr, rows 0..T-1)
   int T;
   bool rebase;            // K/V too large for 32-bit offsets: one buffer resource per tile
-  uint32_t voff[Geo<D>::NIW];   // per-lane byte offsets inside a tile
+  uint32_t koff[Geo<D>::NIW];   // per-lane byte offsets inside a K tile
+  uint32_t voff[Geo<D>::NIW];   // and inside a V tile
 
   __device__ __forceinline__ void init(const uint16_t* K, const uint16_t* V, int T_, int n_kv, int g) {
-    constexpr int CPR = Geo<D>::CPR, RPI = Geo<D>::RPI, NIW = Geo<D>::NIW;
+    constexpr int RPI = Geo<D>::RPI, NIW = Geo<D>::NIW;
     row_elems = (size_t)n_kv * D;
     row_bytes = (uint32_t)n_kv * D * 2;
     T = T_;
@@ -125,11 +149,14 @@ struct TileLoader {
     kptr = K + (size_t)g * D;
     vptr = V + (size_t)g * D;
     const int lane = __lane_id(), wave = threadIdx.x >> 6;
-    const int r_in = lane / CPR, pc = lane % CPR;
+    const int r_in = lane / 8, pc = lane % 8;
 #pragma unroll
     for (int i = 0; i < NIW; ++i) {
-      const int row = (wave * NIW + i) * RPI + r_in;
-      voff[i] = (uint32_t)row * row_bytes + (uint32_t)((pc ^ swz(row)) * 16);
+      const int j = wave * NIW + i;
+      const int row = (j % 8) * RPI + r_in;
+      const uint32_t rb = (uint32_t)row * row_bytes + (uint32_t)(j / 8) * 128;
+      koff[i] = rb + (uint32_t)((pc ^ kswz(row)) * 16);
+      voff[i] = rb + (uint32_t)((pc ^ vswz(row)) * 16);
     }
   }
 
@@ -138,7 +165,7 @@ struct TileLoader {
   // tile's first row (64-bit address) and its range ends with this head's slice
   // of the tile's last valid row. Either way rows at or past T read as zeros.
   __device__ __forceinline__ void issue(bool is_v, int kbase, uint16_t* tile) const {
-    constexpr int RPI = Geo<D>::RPI, NIW = Geo<D>::NIW;
+    constexpr int NIW = Geo<D>::NIW;
     const int wave = threadIdx.x >> 6;
     const uint16_t* base = is_v ? vptr : kptr;
     uint32_t rng = range, toff = (uint32_t)kbase * row_bytes;
@@ -150,8 +177,8 @@ struct TileLoader {
     }
 #pragma unroll
     for (int i = 0; i < NIW; ++i) {
-      LDS_AS void* dst = (LDS_AS void*)(tile + (wave * NIW + i) * RPI * D);
-      buffer_load_lds16(base, rng, dst, voff[i] + toff, 0);
+      LDS_AS void* dst = (LDS_AS void*)(tile + (wave * NIW + i) * 512);
+      buffer_load_lds16(base, rng, dst, (is_v ? voff[i] : koff[i]) + toff, 0);
     }
   }
 };
@@ -178,13 +205,12 @@ __device__ __forceinline__ void wait_vm() {
 // Per-lane LDS offsets (in halves) of the MFMA operands inside a tile.
 template <int D>
 struct LaneOffs {
-  // The swizzle only permutes the low 3 bits of a chunk index, so chunk c + 8
-  // sits exactly 8 chunks (64 halves) after chunk c: four K and two V base
-  // offsets serve every slice, the rest being immediate offsets.
+  // Dims 64.. sit in the second half-tile, a fixed HT halves on: four K and
+  // two V base offsets serve every slice, the rest being immediate offsets.
   int k[4];   // K slice rows n, dims 16*st + 8*h .. +7 for st < 4
   int v[2];   // transposed V read for output blocks 0 and 1 (see attn_step)
-  __device__ __forceinline__ int kofs(int st) const { return k[st & 3] + (st >> 2) * 64; }
-  __device__ __forceinline__ int vofs(int nb) const { return v[nb & 1] + (nb >> 1) * 64; }
+  __device__ __forceinline__ int kofs(int st) const { return k[st & 3] + (st >> 2) * Geo<D>::HT; }
+  __device__ __forceinline__ int vofs(int nb) const { return v[nb & 1] + (nb >> 1) * Geo<D>::HT; }
 };
 
 template <int D>
@@ -193,13 +219,13 @@ __device__ __forceinline__ LaneOffs<D> lane_offsets() {
   const int lane = fresh_lane_id();
   const int n = lane & 31, h = lane >> 5;
 #pragma unroll
-  for (int st = 0; st < 4; ++st) o.k[st] = n * D + (((2 * st + h) ^ swz(n)) * 8);
+  for (int st = 0; st < 4; ++st) o.k[st] = n * RS + (((2 * st + h) ^ kswz(n)) * 8);
   const int blk = lane >> 4, s = lane & 15, r = s >> 2, q = s & 3;
   const int vrow = 4 * (blk >> 1) + r;   // row inside each 8-row group
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int chunk = nb * 4 + (blk & 1) * 2 + (q >> 1);
-    o.v[nb] = vrow * D + ((chunk ^ swz(vrow)) * 8) + (q & 1) * 4;
+    o.v[nb] = vrow * RS + ((chunk ^ vswz(vrow)) * 8) + (q & 1) * 4;
   }
   return o;
 }
@@ -261,7 +287,7 @@ __device__ __forceinline__ void attn_step(const uint16_t* __restrict__ kt, const
   f32x16 s[2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb) {
-    s[kb] = qk_slice<D>(kt + kb * 32 * D, lo, qf, f32x16{});
+    s[kb] = qk_slice<D>(kt + kb * 32 * RS, lo, qf, f32x16{});
   }
   // MODE_BSEL: the row's selection bits of the step's blocks, from block b0 (a
   // step spans at most four blocks, all in one word); MODE_POOLED: the bits of
@@ -369,9 +395,9 @@ __device__ __forceinline__ void attn_step(const uint16_t* __restrict__ kt, const
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const int off = lo.vofs(nb) + (kb * 32 + 16 * c) * D;
+        const int off = lo.vofs(nb) + (kb * 32 + 16 * c) * RS;
         const v4i16 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt + off));
-        const v4i16 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt + off + 8 * D));
+        const v4i16 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt + off + 8 * RS));
         o[nb] = pv_mfma(a0, a1, P[kb][c], o[nb]);
       }
     }
@@ -382,7 +408,7 @@ template <int D>
 __device__ __forceinline__ void qk_tile(const uint16_t* __restrict__ kt, const LaneOffs<D>& lo,
                                         const bf16x8 (&qf)[D / 16], f32x16 (&s)[2]) {
   s[0] = qk_slice<D>(kt, lo, qf, f32x16{});
-  s[1] = qk_slice<D>(kt + 32 * D, lo, qf, f32x16{});
+  s[1] = qk_slice<D>(kt + 32 * RS, lo, qf, f32x16{});
 }
 
 // The same scores with the K operands read straight from global memory (kg =
@@ -463,13 +489,13 @@ __device__ __forceinline__ float pipe_step(const uint16_t* __restrict__ kt_next,
   const float nmu = (m == -__builtin_inff()) ? 0.f : -m;
 
   auto kread = [&](int k) {
-    return *reinterpret_cast<const bf16x8*>(kt_next + (k / HS) * 32 * D + lo.kofs(k % HS));
+    return *reinterpret_cast<const bf16x8*>(kt_next + (k / HS) * 32 * RS + lo.kofs(k % HS));
   };
   auto vread = [&](int k, v4i16 (&dst)[2]) {
     const int f = k / NB, nb = k % NB;
-    const int off = lo.vofs(nb) + ((f >> 1) * 32 + 16 * (f & 1)) * D;
+    const int off = lo.vofs(nb) + ((f >> 1) * 32 + 16 * (f & 1)) * RS;
     dst[0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt_prev + off));
-    dst[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt_prev + off + 8 * D));
+    dst[1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt_prev + off + 8 * RS));
   };
   bf16x8 kf[KA];
 #pragma unroll
@@ -512,9 +538,9 @@ __device__ __forceinline__ void pv_only(const uint16_t* __restrict__ vt, const L
 #pragma unroll
   for (int k = 0; k < NS; ++k) {
     const int f = k / NB, nb = k % NB;
-    const int off = lo.vofs(nb) + ((f >> 1) * 32 + 16 * (f & 1)) * D;
+    const int off = lo.vofs(nb) + ((f >> 1) * 32 + 16 * (f & 1)) * RS;
     const v4i16 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt + off));
-    const v4i16 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt + off + 8 * D));
+    const v4i16 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS v4i16*)(vt + off + 8 * RS));
     o[nb] = pv_mfma(v0, v1, P[f >> 1][f & 1], o[nb]);
   }
 }
@@ -980,7 +1006,7 @@ struct PooledFetch {
         h = u32x4{pack_bf16x2(f[i][0].x, f[i][0].y), pack_bf16x2(f[i][0].z, f[i][0].w),
                   pack_bf16x2(f[i][1].x, f[i][1].y), pack_bf16x2(f[i][1].z, f[i][1].w)};
       }
-      *reinterpret_cast<u32x4*>(tile + row * D + ((lc ^ swz(row)) * 8)) = h;
+      *reinterpret_cast<u32x4*>(tile + tile_pos<D, F16>(row, lc)) = h;
     }
   }
 };

@@ -146,7 +146,18 @@ constexpr float SEL_ERR = 1.0e-4f;
 constexpr float SEL_ABS = 1.0e-30f;
 constexpr float SEL_MAG = 1.0e30f;
 
-__device__ __forceinline__ int sel_swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// Staged candidates in LDS: D/64 parts of [CH rows][64 dims] (rows of 128 bytes;
+// dims 64p .. 64p+63 in part p), the 16-byte chunk c of row r at chunk position
+// c ^ sel_swz(r). An MFMA operand read takes one chunk of 16 consecutive rows per
+// 256-byte group of lanes; with two rows per 256-byte bank line of the 64-bank LDS,
+// the swizzle gives the 8 even and the 8 odd rows distinct bank groups.
+__device__ __forceinline__ int sel_swz(int row) { return (row >> 1) & 7; }
+
+// halves offset of chunk c of candidate row r in the staged hi (or lo) array
+template <int D>
+__device__ __forceinline__ int sel_pos(int r, int c) {
+  return (c >> 3) * (SelGeo<D>::CH * 64) + r * 64 + (((c & 7) ^ sel_swz(r)) * 8);
+}
 
 // Workgroup barrier after this wave's LDS writes have completed, leaving its
 // global loads in flight (the query loads of the voter tile keep arriving while
@@ -230,7 +241,7 @@ __device__ __forceinline__ double dval(unsigned long long k) {
 template <int D>
 struct SelShared {
   struct {
-    uint16_t khi[SelGeo<D>::CH * D];   // bf16 hi parts, row-major [candidate][d], 16-byte chunks swizzled
+    uint16_t khi[SelGeo<D>::CH * D];   // bf16 hi parts (layout: sel_pos)
     uint16_t klo[SelGeo<D>::CH * D];   // bf16 lo parts, same layout
   } k;
   unsigned long long mxkey[SEL_VT];        // exact max (as dkey) of voters with ambiguous pairs
@@ -477,7 +488,7 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
               ss = __builtin_fmaf(a, a, ss);
               ss = __builtin_fmaf(bb, bb, ss);
             }
-            const int off = row * D + (((part * (DPT / 8) + c) ^ sel_swz(row)) * 8);
+            const int off = sel_pos<D>(row, part * (DPT / 8) + c);
             *reinterpret_cast<u32x4*>(&S.k.khi[off]) = h;
             *reinterpret_cast<u32x4*>(&S.k.klo[off]) = l;
           }
@@ -518,7 +529,7 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
             const int arow = 32 * t + col;
 #pragma unroll
             for (int st = 0; st < NST; ++st) {
-              const int off = arow * D + (((2 * st + half) ^ sel_swz(arow)) * 8);
+              const int off = sel_pos<D>(arow, 2 * st + half);
               const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&S.k.khi[off]);
               const bf16x8 al = *reinterpret_cast<const bf16x8*>(&S.k.klo[off]);
               acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, qf[0][st], acc[0], 0, 0, 0);
