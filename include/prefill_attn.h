@@ -269,6 +269,36 @@ int fold_keep_mask(const int32_t* keep_idx, int64_t keep_ld, const int32_t* keep
                    void* stream);
 
 /*
+ * prefill_attn_gather -- attention over a sparse indexer's compacted selection
+ * without a mask: each row scores only the keys it keeps. ("ANE Prefill Research",
+ * What worked, item 2, for the selection lists; "What would re-open it", for
+ * gathering the kept keys instead of masking the history.)
+ *
+ *   Q         bf16 [C][n_q][d]       row i is at position q_start + i
+ *   K, V      bf16 [T][n_kv][d]      token-major history and chunk keys
+ *   keep_idx  int32 [C][keep_ld]     per row, kept blocks of `width` keys (block c = keys
+ *                                    c*width .. c*width+width-1); may be NULL when keep_ld == 0
+ *   keep_cnt  int32 [C]              entries used in each row (clamped to 0 .. keep_ld)
+ *   O         fp32 [C][n_q][d]       output
+ *
+ * The result is prefill_attn_dense over the mask fold_keep_mask builds from the
+ * same lists: row i (position p) attends to the keys t <= p of its listed blocks
+ * and to the `recent` keys ending at p, each once (duplicate and out-of-range
+ * entries are ignored); a row that keeps no key outputs zeros. Scores, weights
+ * and sums are fp32 (no fp16 rounding of the weights); K and V are read as given
+ * (no value staging), so no workspace is needed.
+ * Requires C >= 1, q_start >= 0, q_start + C <= T, n_q % n_kv == 0, width >= 1,
+ * recent >= 0, keep_ld >= 0, finite scale > 0.
+ * Errors: PA_EINVAL; PA_EUNSUPPORTED for d other than 64 and 128, width above 64, or
+ * a history whose per-row block bitmap and list (4 * (ceil(T/width/32) +
+ * min(keep_ld, ceil(T/width))) bytes) exceed the 160 KB of a CU's LDS; PA_EHIP.
+ */
+int prefill_attn_gather(const uint16_t* Q, int C, int q_start, int n_q, const uint16_t* K,
+                        const uint16_t* V, int T, int n_kv, int d, const int32_t* keep_idx,
+                        int64_t keep_ld, const int32_t* keep_cnt, int width, int recent, float scale,
+                        float* O, void* stream);
+
+/*
  * Chunked block-sparse prefill over a growing history: the same three steps
  * with a pooled index that is built incrementally and kept between chunks.
  * ("Porting FlashPrefill V2 to Apple silicon", Part I: the pooled index
@@ -323,7 +353,8 @@ int prefill_attn_blocksparse_ld(const uint16_t* Q, int C, int q_start, int n_q,
  * recorded on the launch stream. pa_timing_read synchronises those events and
  * returns the summed milliseconds and launch count for `kernel`, one of
  * "attn_dense", "attn_blocksparse", "mask_classify", "stage_values", "attn_combine", "pool",
- * "select", "fold". "stage_values" covers the two passes of the fp16 value staging.
+ * "select", "fold", "attn_gather". "stage_values" covers the two passes of the fp16 value
+ * staging.
  * "select" covers the selection kernel and, when the call splits
  * its voters over several workgroups, the merge kernel after it.
  * pa_timing_reset clears the totals. Returns PA_OK or PA_EINVAL/PA_EHIP.

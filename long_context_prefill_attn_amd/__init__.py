@@ -24,7 +24,8 @@ from ._lib import PrefillAttnError, check, lib  # noqa: F401
 
 __all__ = ["prefill_attn_dense", "prefill_attn_dense_bits", "prefill_attn_dense_causal", "prefill_attn_dense_workspace",
            "prefill_attn_blocksparse_workspace", "build_pooled_index",
-           "select_blocks", "prefill_attn_blocksparse", "fold_keep_mask", "PrefillAttnError", "timing",
+           "select_blocks", "prefill_attn_blocksparse", "fold_keep_mask", "prefill_attn_gather",
+           "PrefillAttnError", "timing",
            "bisect_alpha", "calibrate_alpha"]
 
 
@@ -148,6 +149,34 @@ def fold_keep_mask(keep_idx, keep_cnt, q_start: int, T: int, width: int, recent:
                                T, width, recent, mask.data_ptr(), mask.stride(0), _stream()),
           "fold_keep_mask")
     return mask
+
+
+def prefill_attn_gather(Q, K, V, keep_idx, keep_cnt, q_start: int, width: int, recent: int, scale: float,
+                        O=None):
+    """Attention over an indexer's compacted selection, scoring only the kept keys.
+
+    Q bf16 [C][n_q][d] (row i at position q_start + i); K, V bf16 [T][n_kv][d];
+    keep_idx int32 [C][K] (kept blocks of `width` keys per row), keep_cnt int32 [C]
+    -> O fp32 [C][n_q][d]; the same result as prefill_attn_dense over
+    fold_keep_mask(keep_idx, keep_cnt, q_start, T, width, recent)."""
+    _req(Q, "Q", torch.bfloat16, 3)
+    _req(K, "K", torch.bfloat16, 3)
+    _req(V, "V", torch.bfloat16, 3)
+    _req(keep_idx, "keep_idx", torch.int32, 2)
+    _req(keep_cnt, "keep_cnt", torch.int32, 1)
+    C, n_q, d = Q.shape
+    T, n_kv, _ = K.shape
+    Kl = keep_idx.shape[1]
+    if V.shape != K.shape or K.shape[2] != d or keep_idx.shape[0] != C or keep_cnt.shape[0] != C:
+        raise ValueError("inconsistent shapes")
+    if O is None:
+        O = torch.empty((C, n_q, d), dtype=torch.float32, device=Q.device)
+    _req(O, "O", torch.float32, 3)
+    check(lib().prefill_attn_gather(Q.data_ptr(), C, q_start, n_q, K.data_ptr(), V.data_ptr(), T, n_kv, d,
+                                    keep_idx.data_ptr() if Kl else None, Kl, keep_cnt.data_ptr(), width,
+                                    recent, float(scale), O.data_ptr(), _stream()),
+          "prefill_attn_gather")
+    return O
 
 
 def _pooled(P, name, n_kv, nb, d, device):

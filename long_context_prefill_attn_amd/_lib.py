@@ -25,6 +25,13 @@ EXPORTS = {
         ctypes.c_float, ctypes.c_void_p,                                # scale, O
         ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]),            # workspace, bytes, stream
     "prefill_attn_dense_workspace": (ctypes.c_size_t, [ctypes.c_int] * 5),
+    "prefill_attn_gather": (ctypes.c_int, [
+        ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,      # Q, C, q_start, n_q
+        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,   # K, V, T, n_kv
+        ctypes.c_int,                                                   # d
+        ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,               # keep_idx, keep_ld, keep_cnt
+        ctypes.c_int, ctypes.c_int, ctypes.c_float,                     # width, recent, scale
+        ctypes.c_void_p, ctypes.c_void_p]),                             # O, stream
     "prefill_attn_dense_noalloc": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_int, ctypes.c_int,                    # Q, C, n_q
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,   # K, V, T, n_kv

@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libprefill_attn.so")
-SOURCES = ["api.cpp", "attention.hip", "pool_select.hip", "mask_combine.hip"]
+SOURCES = ["api.cpp", "attention.hip", "pool_select.hip", "mask_combine.hip", "gather.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -44,7 +44,7 @@ struct TimedKernel {
 std::mutex g_timing_mu;
 bool g_timing_on = false;
 TimedKernel g_timed[] = {{"attn_dense"}, {"attn_blocksparse"}, {"mask_classify"}, {"stage_values"},
-                         {"attn_combine"}, {"pool"}, {"select"}, {"fold"}};
+                         {"attn_combine"}, {"pool"}, {"select"}, {"fold"}, {"attn_gather"}};
 std::vector<hipEvent_t> g_event_pool;
 
 hipEvent_t take_event() {
@@ -278,6 +278,27 @@ int fold_keep_mask(const int32_t* keep_idx, int64_t keep_ld, const int32_t* keep
   return hip_status(timed("fold", s, [&] {
     return pa::launch_fold_keep(keep_idx, keep_ld, keep_cnt, C, q_start, T, width, recent, mask,
                                 mask_ld, s);
+  }));
+}
+
+int prefill_attn_gather(const uint16_t* Q, int C, int q_start, int n_q, const uint16_t* K,
+                        const uint16_t* V, int T, int n_kv, int d, const int32_t* keep_idx,
+                        int64_t keep_ld, const int32_t* keep_cnt, int width, int recent, float scale,
+                        float* O, void* stream) {
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || !aligned16(keep_cnt) ||
+      (keep_ld > 0 && !aligned16(keep_idx)))
+    return PA_EINVAL;
+  if (C < 1 || q_start < 0 || (long long)q_start + C > T || n_q < 1 || n_kv < 1 || n_q % n_kv != 0 ||
+      width < 1 || recent < 0 || keep_ld < 0 || !good_scale(scale))
+    return PA_EINVAL;
+  if ((d != 64 && d != 128) || width > 64) return PA_EUNSUPPORTED;
+  if ((long long)C * n_kv > (1LL << 30)) return PA_EUNSUPPORTED;
+  const pa::GatherPlan pl = pa::plan_gather(T, keep_ld, width);
+  if (pl.waves < 1) return PA_EUNSUPPORTED;   // one row's bitmap and list exceed the LDS
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(timed("attn_gather", s, [&] {
+    return pa::launch_gather_attn(Q, C, q_start, n_q, K, V, T, n_kv, d, keep_idx, keep_ld, keep_cnt, width,
+                                  recent, scale, O, pl, s);
   }));
 }
 

@@ -123,6 +123,19 @@ hipError_t launch_attn_dense(const uint16_t* Q, int C, int n_q, const uint16_t* 
 hipError_t launch_attn_combine(int C, int n_q, int d, int splits, const float* part_o,
                                const float* part_ml, float* O, hipStream_t stream);
 
+// Gather attention over a folded sparse-indexer selection (gather.hip): LDS per
+// wave holds the row's listed-block bitmap (words_cap words) and its compacted
+// block list (list_cap entries); `waves` waves per workgroup fit in 160 KB.
+struct GatherPlan {
+  int words_cap, list_cap, waves;
+  size_t lds_bytes;
+};
+GatherPlan plan_gather(int T, int64_t keep_ld, int width);
+hipError_t launch_gather_attn(const uint16_t* Q, int C, int q_start, int n_q, const uint16_t* K,
+                              const uint16_t* V, int T, int n_kv, int d, const int32_t* keep_idx,
+                              int64_t keep_ld, const int32_t* keep_cnt, int width, int recent,
+                              float scale, float* O, const GatherPlan& plan, hipStream_t stream);
+
 hipError_t launch_attn_blocksparse(const uint16_t* Q, int C, int q_start, int n_q,
                                    const uint16_t* K, const uint16_t* V16, const float* vscales,
                                    int T, int n_kv, int d,

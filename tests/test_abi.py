@@ -193,6 +193,33 @@ def test_fold_rejects():
     assert f(mask=FAKE + 4) == _lib.PA_EINVAL   # misaligned
 
 
+def test_gather_rejects():
+    """The gather entry's host-side checks (no kernel is launched on any of these)."""
+    lib = _lib.lib()
+    f = lambda **kw: lib.prefill_attn_gather(kw.get("Q", FAKE), kw.get("C", 16), kw.get("q0", 100),
+                                             kw.get("nq", 4), kw.get("K", FAKE), kw.get("V", FAKE),
+                                             kw.get("T", 116), kw.get("nkv", 2), kw.get("d", 128),
+                                             kw.get("idx", FAKE), kw.get("kl", 8), kw.get("cnt", FAKE),
+                                             kw.get("width", 4), kw.get("recent", 3), kw.get("scale", 0.1),
+                                             kw.get("O", FAKE), None)
+    assert f(T=115) == _lib.PA_EINVAL                   # rows past the history
+    assert f(q0=-1) == _lib.PA_EINVAL
+    assert f(C=0) == _lib.PA_EINVAL
+    assert f(nq=3) == _lib.PA_EINVAL                    # heads not a multiple of the KV heads
+    assert f(width=0) == _lib.PA_EINVAL
+    assert f(recent=-1) == _lib.PA_EINVAL
+    assert f(kl=-1) == _lib.PA_EINVAL
+    assert f(cnt=None) == _lib.PA_EINVAL
+    assert f(idx=None) == _lib.PA_EINVAL                # lists declared but missing
+    assert f(scale=0.0) == _lib.PA_EINVAL
+    assert f(scale=float("nan")) == _lib.PA_EINVAL
+    assert f(O=FAKE + 4) == _lib.PA_EINVAL              # misaligned
+    assert f(d=96) == _lib.PA_EUNSUPPORTED
+    assert f(width=65) == _lib.PA_EUNSUPPORTED
+    # one row's block bitmap and list beyond the LDS of a CU
+    assert f(T=1 << 24, width=1, kl=1 << 20) == _lib.PA_EUNSUPPORTED
+
+
 def test_timing_api_host_side():
     lib = _lib.lib()
     ms, n = ctypes.c_double(), ctypes.c_int64()
