@@ -159,27 +159,36 @@ __global__ void __launch_bounds__(64 * GATHER_MAX_WAVES) gather_attn_kernel(
       const float cm = wave_max_f(sc);
       if (cm == -__builtin_inff()) continue;   // no key of this slice is the row's
       const float m_new = fmaxf(m, cm);
-      const float alpha = m == -__builtin_inff() ? 0.f : exp2f(m - m_new);
+      const float alpha = m == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m - m_new);
 #pragma unroll
       for (int e = 0; e < DPL; ++e) o[e] *= alpha;
       lsum *= alpha;
       m = m_new;
-      const float pw = ok ? exp2f(sc - m) : 0.f;
+      const float pw = ok ? __builtin_amdgcn_exp2f(sc - m) : 0.f;
       lsum += pw;
-      // P V: lanes over dims (lane l: dims l*DPL .. l*DPL + DPL-1)
-      uint64_t live = __ballot(ok);
-      while (live != 0) {
-        const int src = __builtin_ctzll(live);
-        live &= live - 1;
-        const float pk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pw), src));
-        const int kk = __builtin_amdgcn_readlane(key, src);
-        const uint16_t* vp = vg + (size_t)kk * krow + lane * DPL;
-        if (DPL == 2) {
-          const uint32_t r = *reinterpret_cast<const uint32_t*>(vp);
-          o[0] = __builtin_fmaf(pk, __uint_as_float(r << 16), o[0]);
-          o[DPL - 1] = __builtin_fmaf(pk, __uint_as_float(r & 0xFFFF0000u), o[DPL - 1]);
-        } else {
-          o[0] = __builtin_fmaf(pk, __uint_as_float((uint32_t)vp[0] << 16), o[0]);
+      // P V: lanes over dims (lane l: dims l*DPL .. l*DPL + DPL-1), the slice's
+      // keys eight at a time with their V loads issued together (a key that is
+      // not the row's has weight 0 and reads row 0)
+      const int kq = ok ? key : 0;
+#pragma unroll 1
+      for (int k0 = 0; k0 < 64; k0 += 8) {
+        uint32_t r[8];
+        float pk[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int kk = __builtin_amdgcn_readlane(kq, k0 + u);
+          pk[u] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, pw), k0 + u));
+          const uint16_t* vp = vg + (size_t)kk * krow + lane * DPL;
+          r[u] = DPL == 2 ? *reinterpret_cast<const uint32_t*>(vp) : (uint32_t)vp[0];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (DPL == 2) {
+            o[0] = __builtin_fmaf(pk[u], __uint_as_float(r[u] << 16), o[0]);
+            o[DPL - 1] = __builtin_fmaf(pk[u], __uint_as_float(r[u] & 0xFFFF0000u), o[DPL - 1]);
+          } else {
+            o[0] = __builtin_fmaf(pk[u], __uint_as_float(r[u] << 16), o[0]);
+          }
         }
       }
     }
