@@ -40,6 +40,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
 PEAK_HBM_GBS = 8000.0
+PEAK_FP32_TFLOPS = 157.3   # MI355X fp32 vector (256 CUs x 2.4 GHz x 256 FLOP per clock), published
 METRIC = "prefill attention TFLOP/s (dense-equiv) + tokens/s at 32K; % bf16 MFMA peak"
 
 
@@ -51,10 +52,12 @@ def parse():
     ap.add_argument("--workload", default="prefill32k",
                     choices=["prefill32k", "dense128k", "sparse128k", "fold2k5", "gqa4k"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--dense-entry", default="mask", choices=["mask", "causal", "bits"],
+    ap.add_argument("--dense-entry", default="mask", choices=["mask", "causal", "bits", "gather"],
                     help="dense part: prefill_attn_dense over a causal fp16 mask (default), "
                          "prefill_attn_dense_causal (no mask buffer) or prefill_attn_dense_bits "
-                         "(the same causal masks packed one bit per key)")
+                         "(the same causal masks packed one bit per key); for the folded-selection "
+                         "workload, mask (fold the lists, then dense) or gather (prefill_attn_gather "
+                         "over the lists)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget for the CPU oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 512 MiB device copy (reference for HBM byte counters)")
@@ -200,6 +203,10 @@ def main():
 
     def dense_call(Q, K, V, q0, C, ci, O, wsp, entry):
         T = q0 + C
+        if keeps and entry == "gather":
+            lp.prefill_attn_gather(Q[q0:T], K[:T], V[:T], keeps[ci][0], keeps[ci][1], q0, s.fold_width,
+                                   s.fold_recent, scale, O=O[q0:T])
+            return
         if keeps:
             lp.fold_keep_mask(keeps[ci][0], keeps[ci][1], q0, T, s.fold_width, s.fold_recent, mask=masks[ci])
         if entry == "causal":
@@ -209,7 +216,17 @@ def main():
         else:
             lp.prefill_attn_dense(Q[q0:T], K[:T], V[:T], masks[ci], scale, O=O[q0:T], workspace=wsp)
 
-    entry = args.dense_entry if not fold else "mask"
+    kept_pairs = []
+    if fold:   # (row, key) pairs the folded selection keeps, per chunk (for the gather roofline)
+        for ci, (q0, C) in enumerate(dchunks):
+            lp.fold_keep_mask(keeps[ci][0], keeps[ci][1], q0, q0 + C, s.fold_width, s.fold_recent,
+                              mask=masks[ci])
+            kept_pairs.append(int((masks[ci] == 0).sum().item()))
+    if (args.dense_entry == "gather") != fold and args.dense_entry != "mask":
+        print("--dense-entry gather is for the folded-selection workload (fold2k5); causal and bits "
+              "are for causal workloads", file=sys.stderr)
+        sys.exit(2)
+    entry = args.dense_entry
 
     def run_dense():
         if do_dense:
@@ -261,7 +278,7 @@ def main():
     sparse_ms = float(np.median([b.elapsed_time(c) for _, b, c in part_ev])) if do_sparse else 0.0
     kern = {}
     for name in ("attn_dense", "mask_classify", "stage_values", "attn_combine", "attn_blocksparse", "pool",
-                 "select", "fold"):
+                 "select", "fold", "attn_gather"):
         tot, n = lp.timing.read(name)
         if n:
             kern[name] = {"avg_ms": tot / n, "launches_per_step": n // args.steps, "ms_per_step": tot / args.steps}
@@ -322,7 +339,7 @@ def main():
                           "tokens_per_s": round(Nd / (dense_ms * 1e-3)),
                           "data": f"{wd.spec.name} (seeded {'planted' if wd.spec.structure == 'planted' else 'N(0,1)'}"
                                   f"), first {Nd} tokens, {len(dchunks)} chunks"}
-    if keeps:
+    if keeps and "fold" in kern:
         fold_bytes = sum(2 * C * (q0 + C) + 4 * keeps[i][0].numel() for i, (q0, C) in enumerate(dchunks))
         fold_ms = kern["fold"]["ms_per_step"]
         parts["fold"] = {"ms": round(fold_ms, 4), "GB_per_s": round(fold_bytes / (fold_ms * 1e-3) / 1e9, 1),
@@ -355,10 +372,17 @@ def main():
     # roofline of the dominant kernel: dense attention, algorithmic FLOPs per launch
     dom = "attn_dense" if do_dense else "attn_blocksparse"
     per_launch = flops_dense / len(dchunks) if do_dense else exact_flops / len(scalls)
+    bound, peak = "mfma", PEAK_BF16_TFLOPS
+    if entry == "gather":
+        # fp32 VALU products over the kept keys only: 4 d FLOP per (query head, row, kept key)
+        dom, bound, peak = "attn_gather", "alu", PEAK_FP32_TFLOPS
+        per_launch = 4.0 * d * Hq * sum(kept_pairs) / len(dchunks)
+        parts["dense"]["kept_pairs_per_head"] = int(sum(kept_pairs))
+        parts["dense"]["kept_work_tflops"] = round(4.0 * d * Hq * sum(kept_pairs) / (dense_ms * 1e-3) / 1e12, 3)
     achieved = per_launch / (kern[dom]["avg_ms"] * 1e-3) / 1e12
-    roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": measured_traffic(dom, args.workload),
+    roofline = {"kernel": dom, "bound": bound, "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": measured_traffic(dom, args.workload) if dom in KERNEL_SOURCES else None,
                 "algorithmic_flops_per_launch": per_launch}
 
     cpu = None
