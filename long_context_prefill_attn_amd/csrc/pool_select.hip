@@ -86,13 +86,14 @@ hipError_t launch_pool(const uint16_t* K, const uint16_t* V, int T, int n_kv, in
 }
 
 // ---------------------------------------------------------------------------
-// select_blocks: one workgroup of 8 waves per (KV head g, query block j), or
+// select_blocks: one workgroup of 4 waves per (KV head g, query block j), or
 // several sharing its voter tiles when the pairs are too few to fill the chip
 // (their votes are merged by select_merge_kernel; see launch_select). A voter
-// tile is 512 voters (64 per wave): the 128 rows x 4 query heads of a block at
-// B = 128 in one tile. Candidates are staged into LDS as bf16 hi/lo in chunks
-// of 256 (head dim 128) or 512 (64); when all of a block's candidates fit in
-// one chunk they are staged once and serve both passes of every voter tile.
+// tile is 256 voters (64 per wave): the 128 rows x 4 query heads of a block at
+// B = 128 in two tiles. Two workgroups share a CU (80 KB of LDS each), so one
+// stages and waits on its loads while the other scores. Candidates are staged into LDS as fp16 in chunks of 256
+// (head dim 128) or 512 (64); when all of a block's candidates fit in one chunk
+// they are staged once and serve both passes of every voter tile.
 //
 // Voters are the (row, query head) pairs of block j in this chunk; candidates
 // are the blocks b < j. The result must equal the fixed-order fp64 rule
@@ -100,20 +101,22 @@ hipError_t launch_pool(const uint16_t* K, const uint16_t* V, int T, int n_kv, in
 // for every voter, bit for bit. Evaluating every r_ib in fp64 costs 2 d flops
 // per pair on the fp64 vector units; instead the kernel
 //
-//  1. filters on the bf16 matrix cores: kbar = hi + lo with hi = bf16(kbar),
-//     lo = bf16(kbar - hi) (round-to-nearest-even; kbar - hi is exact), and
-//     r'_ib = q_i.hi_b + q_i.lo_b accumulated in fp32 by v_mfma_f32_32x32x16_bf16
-//     (q is bf16, so every product is exact). With A = sum_d |q_d||kbar_d|
-//     <= |q|_2 |kbar|_2 (Cauchy-Schwarz):
-//        |kbar - hi - lo| <= 2^-16 |kbar|            (two roundings of 2^-8)
-//        fp32 accumulation of 2d+1 terms in any order, each step rounding by
-//        at most 2^-23 (also covers truncating adders): <= gamma_257 (1+2^-7) A
+//  1. filters on the fp16 matrix cores: k' = fp16(kbar), q' = fp16(q) (round
+//     to nearest even, subnormals kept: both checked on the device), and
+//     r'_ib = q'_i.k'_b accumulated in fp32 by v_mfma_f32_32x32x16_f16 (fp16
+//     products are exact in fp32). A bf16 q in fp16's normal range converts
+//     exactly; below it, and for kbar, each element moves by at most
+//     2^-11 |x| + 2^-25. With A = sum_d |q_d||kbar_d| <= |q|_2 |kbar|_2
+//     (Cauchy-Schwarz):
+//        conversions: <= 2^-11 A + 2^-25 sqrt(d) (|q| + |kbar|) (1 + 2^-11)
+//        fp32 accumulation of d+1 terms in any order, each step rounding by
+//        at most 2^-23 (also covers truncating adders): <= gamma_129 (1+2^-11) A
 //        the fp64 reference itself: <= 128 * 2^-53 A
-//     so |r' - r64| <= 4.6e-5 A. The kernel takes E = 1e-4 max|q| max|kbar|
-//     over the wave's voters and the candidates (over twice the bound, which
-//     also absorbs the fp32 norms and comparisons) plus 1e-30 per unit for
-//     flushed denormals. Then |(r' - M') - (r - M)| <= 2E, so a pair whose
-//     filtered gap lies more than 2E (+ 2^-22 |theta|) from theta is decided;
+//     so |r' - r64| <= 5.04e-4 A + 3.4e-7 (|q| + |kbar|). The kernel takes
+//     E = 6e-4 max|q| max|kbar| + 1e-6 (max|q| + max|kbar| + 1) over the
+//     wave's voters and the candidates (the margin absorbs the fp32 norms and
+//     comparisons). Then |(r' - M') - (r - M)| <= 2E, so a pair whose filtered
+//     gap lies more than 2E (+ 2^-22 |theta|) from theta is decided;
 //  2. lists the other pairs as ambiguous, and every pair whose filtered score
 //     lies within 2E of its voter's filtered max (near-max pairs): the exact
 //     max M_i is attained at one of those;
@@ -122,7 +125,7 @@ hipError_t launch_pool(const uint16_t* K, const uint16_t* V, int T, int n_kv, in
 //     ambiguous pairs, in one round, one pair per thread as a sequential fp64
 //     fma chain over d; then each ambiguous pair is tested against theta.
 // If a list overflows, or magnitudes leave the range where the bound holds
-// (|q|, |kbar| or their product above 1e30), the voter tile is redone exactly
+// (|q| or |kbar| above 65504, where fp16 would overflow), the voter tile is redone exactly
 // in fp64 for all pairs. alpha = 0 (theta = -inf) keeps every visible block.
 // Votes are ORed into a per-block bit mask in LDS, compacted in ascending
 // order, and the diagonal block appended.
@@ -134,17 +137,20 @@ hipError_t launch_pool(const uint16_t* K, const uint16_t* V, int T, int n_kv, in
 // voters of each half-wave with DPP row operations.
 // ---------------------------------------------------------------------------
 constexpr int SEL_WAVES = 8;
+constexpr int SEL_NG = 1;                // groups of 32 voters per wave
+constexpr int SEL_VW = 32 * SEL_NG;      // voters per wave
 constexpr int SEL_THREADS = SEL_WAVES * 64;
-constexpr int SEL_VT = SEL_WAVES * 64;   // voters per tile: 64 per wave
+constexpr int SEL_VT = SEL_WAVES * SEL_VW;   // voters per tile
+constexpr int SEL_WPE = 8 / SEL_NG / 2;  // waves per SIMD: two workgroups per CU
 constexpr int SEL_MAX_NB = 8192;
-constexpr int SEL_AMB_CAP = 1024;        // ambiguous pairs per voter tile
-constexpr int SEL_JOB_CAP = 1024;        // exact max evaluations per voter tile
-constexpr int SEL_NEAR_W = 128;          // near-max pairs per wave and voter tile (at least one per voter)
-// candidates per LDS chunk: 128 KB of bf16 hi + lo rows
+constexpr int SEL_AMB_CAP = 512;         // ambiguous pairs per voter tile
+constexpr int SEL_JOB_CAP = 512;         // exact max evaluations per voter tile
+constexpr int SEL_NEAR_W = 2 * SEL_VW;   // near-max pairs per wave and voter tile (at least one per voter)
+// candidates per LDS chunk: 64 KB of fp16 rows
 template <int D> struct SelGeo { static constexpr int CH = 32768 / D; };
-constexpr float SEL_ERR = 1.0e-4f;
-constexpr float SEL_ABS = 1.0e-30f;
-constexpr float SEL_MAG = 1.0e30f;
+constexpr float SEL_ERR = 6.0e-4f;
+constexpr float SEL_ABS = 1.0e-6f;
+constexpr float SEL_MAG = 65504.f;   // largest finite fp16
 
 // Staged candidates in LDS: D/64 parts of [CH rows][64 dims] (rows of 128 bytes;
 // dims 64p .. 64p+63 in part p), the 16-byte chunk c of row r at chunk position
@@ -153,7 +159,7 @@ constexpr float SEL_MAG = 1.0e30f;
 // the swizzle gives the 8 even and the 8 odd rows distinct bank groups.
 __device__ __forceinline__ int sel_swz(int row) { return (row >> 1) & 7; }
 
-// halves offset of chunk c of candidate row r in the staged hi (or lo) array
+// halves offset of chunk c of candidate row r in the staged array
 template <int D>
 __device__ __forceinline__ int sel_pos(int r, int c) {
   return (c >> 3) * (SelGeo<D>::CH * 64) + r * 64 + (((c & 7) ^ sel_swz(r)) * 8);
@@ -241,8 +247,7 @@ __device__ __forceinline__ double dval(unsigned long long k) {
 template <int D>
 struct SelShared {
   struct {
-    uint16_t khi[SelGeo<D>::CH * D];   // bf16 hi parts (layout: sel_pos)
-    uint16_t klo[SelGeo<D>::CH * D];   // bf16 lo parts, same layout
+    uint16_t kh[SelGeo<D>::CH * D];   // fp16 candidates (layout: sel_pos)
   } k;
   unsigned long long mxkey[SEL_VT];        // exact max (as dkey) of voters with ambiguous pairs
   double ambval[SEL_AMB_CAP];              // exact scores of the ambiguous pairs
@@ -258,15 +263,15 @@ struct SelShared {
   uint32_t overflow;
 };
 
-// r = q.kbar in fp64, dims in increasing order, with each half of both rows
-// loaded before its 64 fmas (two rounds of loads in flight instead of sixteen)
+// r = q.kbar in fp64, dims in increasing order, with each quarter of both rows
+// loaded before its fmas (four rounds of loads in flight instead of sixteen)
 template <int D>
 __device__ __forceinline__ double dot_exact_prefetched(const uint16_t* __restrict__ q,
                                                        const float* __restrict__ kb) {
-  constexpr int H = D / 2;
+  constexpr int H = D / 4;
   double acc = 0.0;
 #pragma unroll 1
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < 4; ++h) {
     u32x4 qv[H / 8];
     float4 kv[H / 4];
 #pragma unroll
@@ -377,10 +382,11 @@ __device__ void finish_selection(uint32_t* flagw, uint32_t* wsum, int nb, int nc
 }
 
 template <int D>
-// 8 waves, two per SIMD (up to 256 registers), one workgroup per CU (the LDS
-// holds a 128 KB candidate chunk). Each wave scores 64 voters: two groups of 32,
-// so every candidate fragment read from LDS feeds two MFMA chains.
-__global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_eu(1, 2))) select_kernel(
+// 4 waves, one per SIMD, two workgroups per CU (two waves per SIMD: up to 256
+// registers; the LDS holds a 64 KB candidate chunk per workgroup). Each wave
+// scores 64 voters: two groups of 32, so every candidate fragment read from LDS
+// feeds two MFMA chains.
+__global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_eu(SEL_WPE, SEL_WPE))) select_kernel(
     const uint16_t* __restrict__ Q, int C, int q_start, int n_q, int n_kv,
     const float* __restrict__ Kp, int pool_ld, int nb, int block, double theta, float theta_f,
     float theta_slack,
@@ -388,8 +394,8 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
     int n_split, int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_cnt) {
   constexpr int NST = D / 16;                 // MFMA k-steps
   constexpr int CH = SelGeo<D>::CH;           // candidates per LDS chunk
-  constexpr int TPR = SEL_THREADS / CH;       // staging threads per candidate row
-  constexpr int DPT = D / TPR;                // staged dims per thread
+  constexpr int UPR = D / 16;                 // 16-dim staging units per candidate row
+  constexpr int SR = CH * UPR / SEL_THREADS;  // staging rounds per chunk
   __shared__ __attribute__((aligned(16))) SelShared<D> S;
 
   // heaviest query blocks first, KV heads interleaved; n_split workgroups share a
@@ -426,15 +432,16 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
       for (int i = fresh_tid(); i < SEL_VT; i += SEL_THREADS) { S.va[i] = 0; S.mxkey[i] = 0; }
       if (tid == 0) { S.amb_cnt = 0; S.job_cnt = 0; S.overflow = exact_only; }
 
-      // B operands: q of the wave's two groups of 32 voters (voter = lane % 32),
-      // held for the whole tile; voter index in the tile vl = 64 wave + 32 gi + col
+      // B operands: q of the wave's SEL_NG groups of 32 voters (voter = lane % 32),
+      // held for the whole tile; voter index in the tile vl = SEL_VW wave + 32 gi + col.
+      // Loaded as bf16, converted to fp16 in place once the candidates are staged
       // (the norms |q| are formed at the end of pass 0, where the error bound needs them)
-      bf16x8 qf[2][NST];
-      bool vok[2];
+      u32x4 qf[SEL_NG][NST];
+      bool vok[SEL_NG];
       auto load_q = [&]() {
 #pragma unroll
-        for (int gi = 0; gi < 2; ++gi) {
-          const int vl = wave * 64 + gi * 32 + col;
+        for (int gi = 0; gi < SEL_NG; ++gi) {
+          const int vl = wave * SEL_VW + gi * 32 + col;
           vok[gi] = vt0 + vl < nv;
           const uint16_t* qp = vok[gi] ? qptr(vt0 + vl) : Q;
 #pragma unroll
@@ -443,78 +450,95 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
             // select: no branch, so the loads queue without forcing waits
             u32x4 raw = *reinterpret_cast<const u32x4*>(qp + 16 * st + 8 * half);
             if (!vok[gi]) raw = u32x4{0u, 0u, 0u, 0u};
-            qf[gi][st] = __builtin_bit_cast(bf16x8, raw);
+            qf[gi][st] = raw;
           }
         }
+      };
+      auto q_to_f16 = [&]() {
+#pragma unroll
+        for (int gi = 0; gi < SEL_NG; ++gi)
+#pragma unroll
+          for (int st = 0; st < NST; ++st)
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+              qf[gi][st][w] = pack_f16x2(__uint_as_float(qf[gi][st][w] << 16),
+                                         __uint_as_float(qf[gi][st][w] & 0xFFFF0000u));
       };
 
       // per voter: running max over this lane's candidates (pass 0); then the
       // thresholds yes-above tY, ambiguous-from tA and near-max-from tN (pass 1)
-      float m1[2] = {-__builtin_inff(), -__builtin_inff()};
-      float tY[2] = {0.f, 0.f}, tA[2] = {0.f, 0.f}, tN[2] = {0.f, 0.f};
+      float m1[SEL_NG], tY[SEL_NG], tA[SEL_NG], tN[SEL_NG];
+#pragma unroll
+      for (int gi = 0; gi < SEL_NG; ++gi) {
+        m1[gi] = -__builtin_inff();
+        tY[gi] = tA[gi] = tN[gi] = 0.f;
+      }
       float mloc = 0.f;
       uint32_t nbase = 0;   // entries in this wave's part of the near list (wave-uniform)
       const bool first_tile = vt0 == sp * SEL_VT;   // this workgroup's first voter tile
-      // Stage candidates c0 .. min(c0 + CH, nc) - 1 as bf16 hi/lo: TPR threads per
-      // candidate row, in two rounds of loads (half of the thread's dims each).
-      // Rows past the last candidate are left as they are: the tiles mask them.
-      // WithQ: the voter tile's q loads are issued behind the first round, so the
-      // candidates' loads do not queue behind them.
+      // Stage candidates c0 .. min(c0 + CH, nc) - 1 as fp16, in SR rounds of one
+      // 16-dim unit per thread (unit u: candidate row u / UPR, dims 16 (u % UPR)
+      // onwards), the loads of the next round in flight while a round converts.
+      // Every round is issued (units past the last candidate read zeros through
+      // the buffer range and write nothing), so the waits are the same on every
+      // path. Rows past the last candidate are left as they are: the tiles mask them.
+      // WithQ: the voter tile's q loads are issued behind the last round's, so
+      // the conversions do not wait for them.
       auto stage = [&](int c0, bool norms, auto with_q) {
         constexpr bool WithQ = decltype(with_q)::value;
         const int t = fresh_tid();   // recomputed here, not held through the passes
-        const int row = t / TPR, part = t % TPR;
-        const int b = c0 + row;
-        const bool live = b < nc;
-        // loads through a buffer resource over the candidates: a row past the
-        // last one reads nothing, and the loads need no branch, so the q loads
-        // behind them are not waited for with them
         const uint32_t range = (uint32_t)(nc * D * 4);
-        const uint32_t voff = (uint32_t)((b * D + part * DPT) * 4);
-        float ss = 0.f;
-        auto convert = [&](const float4* fv, int hh) {
+        auto issue = [&](int r, float4 (&f)[4]) {
+          const int u = r * SEL_THREADS + t;
+          const uint32_t voff = (uint32_t)(((c0 + u / UPR) * D + (u % UPR) * 16) * 4);
 #pragma unroll
-          for (int cc = 0; cc < DPT / 16; ++cc) {
-            const int c = hh * (DPT / 16) + cc;
-            const float x[8] = {fv[2 * cc].x, fv[2 * cc].y, fv[2 * cc].z, fv[2 * cc].w,
-                                fv[2 * cc + 1].x, fv[2 * cc + 1].y, fv[2 * cc + 1].z, fv[2 * cc + 1].w};
-            u32x4 h, l;
+          for (int c = 0; c < 4; ++c) f[c] = __builtin_bit_cast(float4, buffer_load16(kg, range, voff + 16 * c));
+        };
+        auto convert = [&](int r, const float4 (&f)[4]) {
+          const int u = r * SEL_THREADS + t;
+          const int row = u / UPR, part = u % UPR;
+          const bool live = c0 + row < nc;
+          float ss = 0.f;
+          if (live) {
 #pragma unroll
-            for (int w = 0; w < 4; ++w) {
-              const float a = x[2 * w], bb = x[2 * w + 1];
-              const uint32_t hp = pack_bf16x2(a, bb);
-              h[w] = hp;
-              l[w] = pack_bf16x2(a - __uint_as_float(hp << 16), bb - __uint_as_float(hp & 0xFFFF0000u));
-              ss = __builtin_fmaf(a, a, ss);
-              ss = __builtin_fmaf(bb, bb, ss);
+            for (int c = 0; c < 2; ++c) {
+              const float x[8] = {f[2 * c].x, f[2 * c].y, f[2 * c].z, f[2 * c].w,
+                                  f[2 * c + 1].x, f[2 * c + 1].y, f[2 * c + 1].z, f[2 * c + 1].w};
+              u32x4 h;
+#pragma unroll
+              for (int w = 0; w < 4; ++w) {
+                h[w] = pack_f16x2(x[2 * w], x[2 * w + 1]);
+                ss = __builtin_fmaf(x[2 * w], x[2 * w], ss);
+                ss = __builtin_fmaf(x[2 * w + 1], x[2 * w + 1], ss);
+              }
+              *reinterpret_cast<u32x4*>(&S.k.kh[sel_pos<D>(row, part * 2 + c)]) = h;
             }
-            const int off = sel_pos<D>(row, part * (DPT / 8) + c);
-            *reinterpret_cast<u32x4*>(&S.k.khi[off]) = h;
-            *reinterpret_cast<u32x4*>(&S.k.klo[off]) = l;
+          }
+          if (norms) {   // the UPR units of a row sit in consecutive lanes
+#pragma unroll
+            for (int off = 1; off < UPR; off <<= 1) ss += __shfl_xor(ss, off);
+            if (live) mloc = fmaxf(mloc, __builtin_sqrtf(ss));
           }
         };
-        float4 f0[DPT / 8], f1[DPT / 8];
-#pragma unroll
-        for (int c = 0; c < DPT / 8; ++c)
-          f0[c] = __builtin_bit_cast(float4, buffer_load16(kg, range, voff + 16 * c));
-#pragma unroll
-        for (int c = 0; c < DPT / 8; ++c)
-          f1[c] = __builtin_bit_cast(float4, buffer_load16(kg, range, voff + 16 * (DPT / 8 + c)));
+        static_assert(SR == 2 || SR == 4, "staging is written for two or four rounds");
+        float4 fa[4], fb[4];
+        issue(0, fa);
+        issue(1, fb);
+        if constexpr (SR == 4) {
+          convert(0, fa);
+          issue(2, fa);
+          convert(1, fb);
+          issue(3, fb);
+        }
         if constexpr (WithQ) load_q();
-        if (live) {
-          convert(f0, 0);
-          convert(f1, 1);
-        }
-        if (norms) {
-#pragma unroll
-          for (int off = 1; off < TPR; off <<= 1) ss += __shfl_xor(ss, off);
-          if (live) mloc = fmaxf(mloc, __builtin_sqrtf(ss));
-        }
+        convert(SR - 2, fa);
+        convert(SR - 1, fb);
         staged = resident;
         lds_barrier();
       };
       if (!(resident && staged)) stage(0, first_tile, std::true_type{});
       else load_q();
+      q_to_f16();
       for (int pass = 0; pass < 2; ++pass) {
         for (int c0 = 0; c0 < nc; c0 += CH) {
           if ((pass > 0 || c0 > 0) && !(resident && staged)) {
@@ -525,27 +549,27 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
 #pragma unroll 1
           for (int t = 0; t < (nch + 31) / 32; ++t) {
             const int cb = c0 + 32 * t;
-            f32x16 acc[2] = {f32x16{}, f32x16{}};
+            f32x16 acc[SEL_NG];
+#pragma unroll
+            for (int gi = 0; gi < SEL_NG; ++gi) acc[gi] = f32x16{};
             const int arow = 32 * t + col;
 #pragma unroll
             for (int st = 0; st < NST; ++st) {
               const int off = sel_pos<D>(arow, 2 * st + half);
-              const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&S.k.khi[off]);
-              const bf16x8 al = *reinterpret_cast<const bf16x8*>(&S.k.klo[off]);
-              acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, qf[0][st], acc[0], 0, 0, 0);
-              acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, qf[1][st], acc[1], 0, 0, 0);
-              acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, qf[0][st], acc[0], 0, 0, 0);
-              acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, qf[1][st], acc[1], 0, 0, 0);
+              const f16x8 ak = *reinterpret_cast<const f16x8*>(&S.k.kh[off]);
+#pragma unroll
+              for (int gi = 0; gi < SEL_NG; ++gi)
+                acc[gi] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ak, __builtin_bit_cast(f16x8, qf[gi][st]), acc[gi], 0, 0, 0);
             }
             // element i of acc[gi]: candidate cb + 4 half + 8(i/4) + i%4 against voter
-            // 64 wave + 32 gi + col
+            // SEL_VW wave + 32 gi + col
             const int cbase = cb + 4 * half;
             // RG: the tile runs past the last candidate (the final tile only)
             auto tile = [&](auto rg) {
               constexpr bool RG = decltype(rg)::value;
               if (pass == 0) {   // running max
 #pragma unroll
-                for (int gi = 0; gi < 2; ++gi) {
+                for (int gi = 0; gi < SEL_NG; ++gi) {
                   float x[16];
 #pragma unroll
                   for (int i = 0; i < 16; ++i)
@@ -559,20 +583,24 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
               // half-wave gives the slice's vote word (the second half's candidates
               // sit 4 positions up)
               uint32_t ymask = 0;
-              float dmin[2] = {__builtin_inff(), __builtin_inff()};
-              float smax[2] = {-__builtin_inff(), -__builtin_inff()};
+              float dmin[SEL_NG], smax[SEL_NG];
+#pragma unroll
+              for (int gi = 0; gi < SEL_NG; ++gi) {
+                dmin[gi] = __builtin_inff();
+                smax[gi] = -__builtin_inff();
+              }
               // threshold centre and the trigger band, formed here (from tA and tY) rather
               // than held through the loops
-              float ctr[2], band[2];
+              float ctr[SEL_NG], band[SEL_NG];
 #pragma unroll
-              for (int gi = 0; gi < 2; ++gi) {
+              for (int gi = 0; gi < SEL_NG; ++gi) {
                 float ya = tY[gi], aa = tA[gi];
                 asm volatile("" : "+v"(ya), "+v"(aa));
                 ctr[gi] = 0.5f * ya + 0.5f * aa;   // inf for a missing voter: |a - inf| = inf
                 band[gi] = (ya - aa) + 0x1p-20f * __builtin_fabsf(ctr[gi]);
               }
 #pragma unroll
-              for (int gi = 0; gi < 2; ++gi)
+              for (int gi = 0; gi < SEL_NG; ++gi)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                   const float a =
@@ -582,8 +610,8 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
                   smax[gi] = __builtin_fmaxf(smax[gi], a);
                 }
 #pragma unroll
-              for (int gi = 0; gi < 2; ++gi) {
-                const int vl = wave * 64 + gi * 32 + col;
+              for (int gi = 0; gi < SEL_NG; ++gi) {
+                const int vl = wave * SEL_VW + gi * 32 + col;
                 // ambiguous pairs lie within w of the threshold; dmin <= band is a
                 // conservative trigger for them (band covers w and the roundings of
                 // tA, tY and ctr), re-tested exactly below
@@ -645,22 +673,22 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
           }
           bool bad = false;
 #pragma unroll
-          for (int gi = 0; gi < 2; ++gi) {
+          for (int gi = 0; gi < SEL_NG; ++gi) {
             float ss = 0.f;
 #pragma unroll
             for (int st = 0; st < NST; ++st) {
-              const u32x4 raw = __builtin_bit_cast(u32x4, qf[gi][st]);
+              const u32x4 raw = qf[gi][st];
 #pragma unroll
               for (int w = 0; w < 4; ++w) {
-                const float a = __uint_as_float(raw[w] << 16), b = __uint_as_float(raw[w] & 0xFFFF0000u);
-                ss = __builtin_fmaf(a, a, ss);
-                ss = __builtin_fmaf(b, b, ss);
+                const f32x2 ab = __builtin_convertvector(__builtin_bit_cast(f16x2, raw[w]), f32x2);
+                ss = __builtin_fmaf(ab[0], ab[0], ss);
+                ss = __builtin_fmaf(ab[1], ab[1], ss);
               }
             }
             const float qn = __builtin_sqrtf(ss + partner32(ss));
             const float M = fmaxf(m1[gi], partner32(m1[gi]));
             const float nm = qn * mnorm;
-            bad = bad || (vok[gi] && !(qn <= SEL_MAG && mnorm <= SEL_MAG && nm <= SEL_MAG));
+            bad = bad || (vok[gi] && !(qn <= SEL_MAG && mnorm <= SEL_MAG));
             const float e2 = 2.f * (SEL_ERR * nm + SEL_ABS * (qn + mnorm + 1.f));
             tN[gi] = M - e2;
             tY[gi] = M + (theta_f + (e2 + theta_slack));
@@ -758,8 +786,8 @@ hipError_t launch_select(const uint16_t* Q, int C, int q_start, int n_q, int n_k
   const int exact_only = (!inf_theta && !(std::fabs(theta) <= 1e30)) ? 1 : 0;
   const float theta_f = inf_theta ? -HUGE_VALF : (exact_only ? 0.f : (float)theta);
   const float theta_slack = inf_theta || exact_only ? 0.f : (float)std::ldexp(std::fabs(theta), -22);
-  // One select workgroup fits on a CU. When the (KV head, query block) pairs
-  // are fewer than the CUs, their voter tiles are spread over n_split
+  // Two select workgroups fit on a CU. When the (KV head, query block) pairs
+  // are fewer than that, their voter tiles are spread over n_split
   // workgroups, as far as the tiles go and as the partial flag rows fit at the
   // front of a selection row (n_split nw <= nb).
   const int vt_max = (std::min(block, C) * (n_q / n_kv) + SEL_VT - 1) / SEL_VT;
@@ -767,7 +795,7 @@ hipError_t launch_select(const uint16_t* Q, int C, int q_start, int n_q, int n_k
   const int nw_max = (nb - 1 + 31) / 32;
   int n_split = 1;
   if (theta_f != -HUGE_VALF) {
-    const int want = (device_cus() + pairs - 1) / pairs;
+    const int want = (2 * device_cus() + pairs - 1) / pairs;
     n_split = std::max(1, std::min(std::min(want, vt_max), nw_max > 0 ? nb / nw_max : 1));
   }
   dim3 grid(pairs * n_split);
