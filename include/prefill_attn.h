@@ -232,7 +232,9 @@ int select_blocks(const uint16_t* Q, int C, int q_start, int n_q, int n_kv, int 
  * Arithmetic as prefill_attn_dense (pooled keys enter as bf16, pooled values as
  * fp16 with the staged values' factor). `workspace` must hold at least
  * prefill_attn_blocksparse_workspace(T, n_kv, d) bytes (the staged fp16 copy of
- * V[0..T)); scratch, as for prefill_attn_dense. Every block size select_blocks
+ * V[0..T), and the pooled keys and values rounded once per call as they enter
+ * the matrix cores, with room for the smallest block size); scratch, as for
+ * prefill_attn_dense. Every block size select_blocks
  * takes is supported (tuned for 128; smaller blocks give steps of 64 keys that
  * rows of different query blocks take differently, run with a per-key test).
  * Errors: PA_EINVAL, PA_EUNSUPPORTED, PA_EWORKSPACE, PA_EHIP.

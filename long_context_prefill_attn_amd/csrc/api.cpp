@@ -355,9 +355,12 @@ int select_blocks(const uint16_t* Q, int C, int q_start, int n_q, int n_kv, int 
                           alpha, scale, 0, 0, 0, sel_idx, sel_cnt, stream);
 }
 
+// room for the pooled operands of the smallest block size (16)
+static int pool_rows_max(int T) { return (T + 15) / 16; }
+
 size_t prefill_attn_blocksparse_workspace(int T, int n_kv, int d) {
   if (T < 1 || n_kv < 1 || (d != 64 && d != 128)) return 0;
-  return pa::plan_stage(T, n_kv, d).bytes;
+  return pa::plan_stage(T, n_kv, d, pool_rows_max(T)).bytes;
 }
 
 int prefill_attn_blocksparse_ld(const uint16_t* Q, int C, int q_start, int n_q, const uint16_t* K,
@@ -374,19 +377,26 @@ int prefill_attn_blocksparse_ld(const uint16_t* Q, int C, int q_start, int n_q, 
   const int nb = (T + block - 1) / block;
   if (nb > 8192) return PA_EUNSUPPORTED;
   if (pool_ld < nb) return PA_EINVAL;
-  const pa::StagePlan sp = pa::plan_stage(T, n_kv, d);
+  const pa::StagePlan sp = pa::plan_stage(T, n_kv, d, pool_rows_max(T));
   if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0 ||
       workspace_bytes < sp.bytes)
     return PA_EWORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* stage = static_cast<uint8_t*>(workspace);
-  hipError_t e = timed("stage_values", s, [&] { return pa::launch_stage_values(V, T, n_kv, d, stage, s); });
+  // the staged values, then the pooled operands (scaled by the values' factor)
+  hipError_t e = timed("stage_values", s, [&] {
+    const hipError_t e1 = pa::launch_stage_values(V, T, n_kv, d, stage, s);
+    if (e1 != hipSuccess) return e1;
+    return pa::launch_stage_pooled(K_pool, V_pool, pool_ld, nb, n_kv, d, stage, sp, s);
+  });
   if (e != hipSuccess) return hip_status(e);
   const uint16_t* V16 = reinterpret_cast<const uint16_t*>(stage + sp.v16_off);
   const float* vscales = reinterpret_cast<const float*>(stage + sp.scales_off);
+  const uint16_t* Kp16 = reinterpret_cast<const uint16_t*>(stage + sp.kp16_off);
+  const uint16_t* Vp16 = reinterpret_cast<const uint16_t*>(stage + sp.vp16_off);
   return hip_status(timed("attn_blocksparse", s, [&] {
-    return pa::launch_attn_blocksparse(Q, C, q_start, n_q, K, V16, vscales, T, n_kv, d, K_pool, V_pool,
-                                       pool_ld, block, sel_idx, sel_cnt, scale, O, s);
+    return pa::launch_attn_blocksparse(Q, C, q_start, n_q, K, V16, vscales, T, n_kv, d, Kp16, Vp16, block,
+                                       sel_idx, sel_cnt, scale, O, s);
   }));
 }
 

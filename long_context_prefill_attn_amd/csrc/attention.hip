@@ -961,62 +961,18 @@ attn_dense_kernel(const uint16_t* __restrict__ Q, int C, int n_q, const uint16_t
 // workgroup's rows as in the dense kernel: plain (every row takes all 64 keys
 // exactly: the pipelined loop), skipped (no row takes any), or masked (a per-key
 // test against the row's own selection and position). Then the pooled rows, 64
-// per step: pooled keys/values are fp32 in memory and enter the MFMAs rounded
-// (keys to bf16, values to fp16 with the staged values' factor); the next
-// pooled tile's global loads are in flight while the current one is computed.
+// per step: the pooled keys and values arrive staged once per call (bf16 keys,
+// fp16 values with the staged values' factor, token-major like K and V) and go
+// into LDS as tiles, the next tile's loads in flight while one is computed.
 // With an odd number of query heads per KV head, the second half of the
 // workgroup repeats the first head and does not store.
 // ---------------------------------------------------------------------------
-template <int D>
-struct PooledFetch {
-  float4 f[Geo<D>::KCH][2];   // this thread's 16-byte destination chunks, as 8 fp32 each
-
-  // global loads of pooled rows pbase .. pbase+63 (rows >= jlimit read as zeros)
-  __device__ __forceinline__ void load(const float* __restrict__ src, int pbase, int jlimit) {
-    constexpr int CPR = Geo<D>::CPR;
-#pragma unroll
-    for (int i = 0; i < Geo<D>::KCH; ++i) {
-      const int c = threadIdx.x + NT * i;
-      const int row = c / CPR, lc = c % CPR;
-      const int bb = pbase + row;
-      const bool ok = bb < jlimit;   // row 0 exists whenever this is called (jlimit >= 1)
-      const float* rp = src + (size_t)(ok ? bb : 0) * D + lc * 8;
-      const float4 x0 = *reinterpret_cast<const float4*>(rp);
-      const float4 x1 = *reinterpret_cast<const float4*>(rp + 4);
-      const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
-      f[i][0] = ok ? x0 : z;
-      f[i][1] = ok ? x1 : z;
-    }
-  }
-
-  // the same chunks rounded (nearest even) into a swizzled LDS tile: to bf16 for
-  // pooled keys (F16 false), or times vs to fp16 for pooled values (F16 true)
-  template <bool F16>
-  __device__ __forceinline__ void store(uint16_t* tile, float vs = 1.f) const {
-    constexpr int CPR = Geo<D>::CPR;
-#pragma unroll
-    for (int i = 0; i < Geo<D>::KCH; ++i) {
-      const int c = threadIdx.x + NT * i;
-      const int row = c / CPR, lc = c % CPR;
-      u32x4 h;
-      if (F16) {
-        h = u32x4{pack_f16x2(f[i][0].x * vs, f[i][0].y * vs), pack_f16x2(f[i][0].z * vs, f[i][0].w * vs),
-                  pack_f16x2(f[i][1].x * vs, f[i][1].y * vs), pack_f16x2(f[i][1].z * vs, f[i][1].w * vs)};
-      } else {
-        h = u32x4{pack_bf16x2(f[i][0].x, f[i][0].y), pack_bf16x2(f[i][0].z, f[i][0].w),
-                  pack_bf16x2(f[i][1].x, f[i][1].y), pack_bf16x2(f[i][1].z, f[i][1].w)};
-      }
-      *reinterpret_cast<u32x4*>(tile + tile_pos<D, F16>(row, lc)) = h;
-    }
-  }
-};
-
 template <int D>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
 attn_blocksparse_kernel(const uint16_t* __restrict__ Q, int C, int q_start, int n_q,
                         const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
                         const float* __restrict__ vscales, int T, int n_kv,
-                        const float* __restrict__ Kp, const float* __restrict__ Vp, int pool_ld, int nb,
+                        const uint16_t* __restrict__ Kp16, const uint16_t* __restrict__ Vp16, int nb,
                         int blog2, int n_qblk, int n_wrb, const int32_t* __restrict__ sel_idx,
                         const int32_t* __restrict__ sel_cnt, float scale_log2, float* __restrict__ O) {
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
@@ -1131,31 +1087,30 @@ attn_blocksparse_kernel(const uint16_t* __restrict__ Q, int C, int q_start, int 
     attn_step<D, MODE_BSEL, true>(kt, vt, lo2, qf, o, m, l, cx);
   });
 
-  // 3) pooled rows of blocks 0 .. j_hi - 1, 64 per step, in two alternating LDS
-  // buffers (one barrier per step); each row keeps those of its unselected
-  // blocks below its own
-  const float* kpg = Kp + (size_t)g * pool_ld * D;
-  const float* vpg = Vp + (size_t)g * pool_ld * D;
+  // 3) pooled rows of blocks 0 .. j_hi - 1, 64 per step, in ring slots 0 and 1
+  // alternately (one barrier per step: tile p has landed for every wave and tile
+  // p-1's readers are done before tile p+1 is issued into its slot); each row
+  // keeps those of its unselected blocks below its own. Rows at or past j_hi read
+  // as zeros.
   const int n_pool = (j_hi + BN - 1) / BN;
-  const float vdn = vscales[0];   // pooled values enter scaled like the staged values
-  PooledFetch<D> fk, fv;
   if (n_pool > 0) {
-    fk.load(kpg, 0, j_hi);
-    fv.load(vpg, 0, j_hi);
-  }
-  for (int p = 0; p < n_pool; ++p) {
-    uint16_t* kt = lds + (p & 1) * Geo<D>::TILE;
-    uint16_t* vt = lds + (KRK + (p & 1)) * Geo<D>::TILE;
-    fk.template store<false>(kt);
-    fv.template store<true>(vt, vdn);
-    __syncthreads();
-    if (p + 1 < n_pool) {
-      fk.load(kpg, (p + 1) * BN, j_hi);
-      fv.load(vpg, (p + 1) * BN, j_hi);
+    constexpr int TL = Geo<D>::TILE;
+    TileLoader<D> tp;
+    tp.init(Kp16, Vp16, j_hi, n_kv, g);
+    __syncthreads();   // every wave is done with the rings
+    tp.issue(false, 0, lds);
+    tp.issue(true, 0, lds + KRK * TL);
+    for (int p = 0; p < n_pool; ++p) {
+      wait_vm<0>();
+      bare_barrier();
+      if (p + 1 < n_pool) {
+        tp.issue(false, (p + 1) * BN, lds + ((p + 1) & 1) * TL);
+        tp.issue(true, (p + 1) * BN, lds + (KRK + ((p + 1) & 1)) * TL);
+      }
+      cx.key0 = p * BN;
+      cx.kvalid = BN;
+      attn_step<D, MODE_POOLED, false>(lds + (p & 1) * TL, lds + (KRK + (p & 1)) * TL, lo2, qf, o, m, l, cx);
     }
-    cx.key0 = p * BN;
-    cx.kvalid = BN;
-    attn_step<D, MODE_POOLED, false>(kt, vt, lo2, qf, o, m, l, cx);
   }
 
   const float lt = l + partner32(l);
@@ -1259,8 +1214,8 @@ hipError_t launch_attn_dense(const uint16_t* Q, int C, int n_q, const uint16_t* 
 
 template <int D>
 static hipError_t blocksparse_impl(const uint16_t* Q, int C, int q_start, int n_q, const uint16_t* K,
-                                   const uint16_t* V, const float* vscales, int T, int n_kv, const float* Kp,
-                                   const float* Vp, int pool_ld, int block, const int32_t* sel_idx,
+                                   const uint16_t* V, const float* vscales, int T, int n_kv, const uint16_t* Kp16,
+                                   const uint16_t* Vp16, int block, const int32_t* sel_idx,
                                    const int32_t* sel_cnt, float scale, float* O, hipStream_t stream) {
   const int nb = (T + block - 1) / block;
   const int blog2 = __builtin_ctz((unsigned)block);
@@ -1275,7 +1230,7 @@ static hipError_t blocksparse_impl(const uint16_t* Q, int C, int q_start, int n_
   hipFuncSetAttribute((const void*)attn_blocksparse_kernel<D>,
                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   hipLaunchKernelGGL(attn_blocksparse_kernel<D>, dim3(n_wrb * (n_q / hpw)), dim3(NT), lds, stream, Q, C,
-                     q_start, n_q, K, V, vscales, T, n_kv, Kp, Vp, pool_ld, nb, blog2, n_qblk, n_wrb, sel_idx,
+                     q_start, n_q, K, V, vscales, T, n_kv, Kp16, Vp16, nb, blog2, n_qblk, n_wrb, sel_idx,
                      sel_cnt, scale * LOG2E, O);
   return hipGetLastError();
 }
@@ -1283,14 +1238,14 @@ static hipError_t blocksparse_impl(const uint16_t* Q, int C, int q_start, int n_
 hipError_t launch_attn_blocksparse(const uint16_t* Q, int C, int q_start, int n_q,
                                    const uint16_t* K, const uint16_t* V16, const float* vscales,
                                    int T, int n_kv, int d,
-                                   const float* K_pool, const float* V_pool, int pool_ld, int block,
+                                   const uint16_t* Kp16, const uint16_t* Vp16, int block,
                                    const int32_t* sel_idx, const int32_t* sel_cnt, float scale,
                                    float* O, hipStream_t stream) {
   if (d == 128)
-    return blocksparse_impl<128>(Q, C, q_start, n_q, K, V16, vscales, T, n_kv, K_pool, V_pool, pool_ld, block,
-                                 sel_idx, sel_cnt, scale, O, stream);
-  return blocksparse_impl<64>(Q, C, q_start, n_q, K, V16, vscales, T, n_kv, K_pool, V_pool, pool_ld, block,
-                              sel_idx, sel_cnt, scale, O, stream);
+    return blocksparse_impl<128>(Q, C, q_start, n_q, K, V16, vscales, T, n_kv, Kp16, Vp16, block, sel_idx,
+                                 sel_cnt, scale, O, stream);
+  return blocksparse_impl<64>(Q, C, q_start, n_q, K, V16, vscales, T, n_kv, Kp16, Vp16, block, sel_idx, sel_cnt,
+                              scale, O, stream);
 }
 
 }  // namespace pa

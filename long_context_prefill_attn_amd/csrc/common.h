@@ -95,10 +95,15 @@ hipError_t launch_fold_keep(const int32_t* keep_idx, int64_t keep_ld, const int3
 // scales = {2^-k, 2^k} for the kernels that use the staged copy.
 constexpr int STAGE_PARTS = 512;   // workgroups of the range pass
 struct StagePlan {
-  size_t v16_off, part_off, scales_off, bytes;   // byte offsets inside the stage region
+  size_t v16_off, part_off, scales_off;   // byte offsets inside the stage region
+  size_t kp16_off, vp16_off;              // pooled operands (pool_rows > 0)
+  size_t bytes;
 };
-StagePlan plan_stage(int T, int n_kv, int d);
+// pool_rows: rows of pooled operands to make room for (0: none)
+StagePlan plan_stage(int T, int n_kv, int d, int pool_rows = 0);
 hipError_t launch_stage_values(const uint16_t* V, int T, int n_kv, int d, void* stage, hipStream_t stream);
+hipError_t launch_stage_pooled(const float* K_pool, const float* V_pool, int pool_ld, int nb, int n_kv, int d,
+                               void* stage, const StagePlan& plan, hipStream_t stream);
 
 struct DensePlan {
   int hg_log2;   // log2 of the query heads packed into one workgroup
@@ -139,7 +144,7 @@ hipError_t launch_gather_attn(const uint16_t* Q, int C, int q_start, int n_q, co
 hipError_t launch_attn_blocksparse(const uint16_t* Q, int C, int q_start, int n_q,
                                    const uint16_t* K, const uint16_t* V16, const float* vscales,
                                    int T, int n_kv, int d,
-                                   const float* K_pool, const float* V_pool, int pool_ld, int block,
+                                   const uint16_t* Kp16, const uint16_t* Vp16, int block,
                                    const int32_t* sel_idx, const int32_t* sel_cnt,
                                    float scale, float* O, hipStream_t stream);
 

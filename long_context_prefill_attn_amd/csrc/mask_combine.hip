@@ -1,5 +1,6 @@
 // Mask-tile classification and split-key combination for dense prefill attention.
 #include "common.h"
+#include <algorithm>
 
 namespace pa {
 
@@ -321,15 +322,59 @@ __global__ void __launch_bounds__(STAGE_THREADS) stage_convert_kernel(const u32x
   }
 }
 
+// Pooled operands of the block-sparse kernel, once per call: rows 0 .. nb-1 of
+// K_pool and V_pool ([n_kv][pool_ld][d] fp32) rounded to nearest even, keys to
+// bf16 and values times the staged values' factor to fp16, written token-major
+// ([nb][n_kv][d]) like K and V, so that the attention kernel loads 64 pooled rows
+// at a time straight into LDS as it does key and value tiles.
+__global__ void __launch_bounds__(STAGE_THREADS) stage_pooled_kernel(const float* __restrict__ Kp,
+                                                                      const float* __restrict__ Vp, int pool_ld,
+                                                                      int nb, int n_kv, int d,
+                                                                      const float* __restrict__ scales,
+                                                                      u32x4* __restrict__ Kp16,
+                                                                      u32x4* __restrict__ Vp16) {
+  const float dn = scales[0];
+  const int cpr = d / 8;   // 8-dim chunks per row
+  const size_t n8 = (size_t)nb * n_kv * cpr;
+  const size_t stride = (size_t)gridDim.x * STAGE_THREADS;
+  for (size_t c = (size_t)blockIdx.x * STAGE_THREADS + threadIdx.x; c < n8; c += stride) {
+    const size_t row = c / cpr;   // b * n_kv + g
+    const int cc = (int)(c % cpr);
+    const int b = (int)(row / n_kv), g = (int)(row % n_kv);
+    const size_t src = ((size_t)g * pool_ld + b) * d + (size_t)cc * 8;
+    const float4 k0 = *reinterpret_cast<const float4*>(Kp + src);
+    const float4 k1 = *reinterpret_cast<const float4*>(Kp + src + 4);
+    const float4 v0 = *reinterpret_cast<const float4*>(Vp + src);
+    const float4 v1 = *reinterpret_cast<const float4*>(Vp + src + 4);
+    Kp16[c] = u32x4{pack_bf16x2(k0.x, k0.y), pack_bf16x2(k0.z, k0.w), pack_bf16x2(k1.x, k1.y),
+                    pack_bf16x2(k1.z, k1.w)};
+    Vp16[c] = u32x4{pack_f16x2(v0.x * dn, v0.y * dn), pack_f16x2(v0.z * dn, v0.w * dn),
+                    pack_f16x2(v1.x * dn, v1.y * dn), pack_f16x2(v1.z * dn, v1.w * dn)};
+  }
+}
+
 static size_t align256_s(size_t x) { return (x + 255) & ~(size_t)255; }
 
-StagePlan plan_stage(int T, int n_kv, int d) {
+StagePlan plan_stage(int T, int n_kv, int d, int pool_rows) {
   StagePlan p{};
   p.v16_off = 0;
   p.part_off = align256_s((size_t)T * n_kv * d * 2);
   p.scales_off = p.part_off + align256_s(STAGE_PARTS * sizeof(uint32_t));
-  p.bytes = p.scales_off + 256;
+  p.kp16_off = p.scales_off + 256;
+  p.vp16_off = p.kp16_off + align256_s((size_t)pool_rows * n_kv * d * 2);
+  p.bytes = p.vp16_off + align256_s((size_t)pool_rows * n_kv * d * 2);
   return p;
+}
+
+hipError_t launch_stage_pooled(const float* K_pool, const float* V_pool, int pool_ld, int nb, int n_kv, int d,
+                               void* stage, const StagePlan& plan, hipStream_t stream) {
+  uint8_t* base = static_cast<uint8_t*>(stage);
+  const size_t n8 = (size_t)nb * n_kv * d / 8;
+  const int wgs = (int)std::min<size_t>((n8 + STAGE_THREADS - 1) / STAGE_THREADS, STAGE_CONVERT_WG);
+  hipLaunchKernelGGL(stage_pooled_kernel, dim3(std::max(wgs, 1)), dim3(STAGE_THREADS), 0, stream, K_pool, V_pool,
+                     pool_ld, nb, n_kv, d, reinterpret_cast<const float*>(base + plan.scales_off),
+                     reinterpret_cast<u32x4*>(base + plan.kp16_off), reinterpret_cast<u32x4*>(base + plan.vp16_off));
+  return hipGetLastError();
 }
 
 hipError_t launch_stage_values(const uint16_t* V, int T, int n_kv, int d, void* stage, hipStream_t stream) {
