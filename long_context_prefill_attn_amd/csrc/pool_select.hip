@@ -439,16 +439,19 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
       u32x4 qf[SEL_NG][NST];
       bool vok[SEL_NG];
       auto load_q = [&]() {
+        // lane-derived values formed afresh here, not held through the passes
+        const int t = fresh_tid();
+        const int wv = t >> 6, cl = t & 31, hf = (t >> 5) & 1;
 #pragma unroll
         for (int gi = 0; gi < SEL_NG; ++gi) {
-          const int vl = wave * SEL_VW + gi * 32 + col;
+          const int vl = wv * SEL_VW + gi * 32 + cl;
           vok[gi] = vt0 + vl < nv;
           const uint16_t* qp = vok[gi] ? qptr(vt0 + vl) : Q;
 #pragma unroll
           for (int st = 0; st < NST; ++st) {
             // loaded unconditionally (a missing voter reads row 0) and zeroed by a
             // select: no branch, so the loads queue without forcing waits
-            u32x4 raw = *reinterpret_cast<const u32x4*>(qp + 16 * st + 8 * half);
+            u32x4 raw = *reinterpret_cast<const u32x4*>(qp + 16 * st + 8 * hf);
             if (!vok[gi]) raw = u32x4{0u, 0u, 0u, 0u};
             qf[gi][st] = raw;
           }
@@ -553,10 +556,19 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
 #pragma unroll
             for (int gi = 0; gi < SEL_NG; ++gi) acc[gi] = f32x16{};
             const int arow = 32 * t + col;
+            // candidate fragments read KA steps ahead of their MFMA (a few in flight
+            // rather than all of them: registers)
+            constexpr int KA = 3;
+            auto kread = [&](int st) {
+              return *reinterpret_cast<const f16x8*>(&S.k.kh[sel_pos<D>(arow, 2 * st + half)]);
+            };
+            f16x8 kf[KA];
+#pragma unroll
+            for (int st = 0; st < KA; ++st) kf[st] = kread(st);
 #pragma unroll
             for (int st = 0; st < NST; ++st) {
-              const int off = sel_pos<D>(arow, 2 * st + half);
-              const f16x8 ak = *reinterpret_cast<const f16x8*>(&S.k.kh[off]);
+              const f16x8 ak = kf[st % KA];
+              if (st + KA < NST) kf[st % KA] = kread(st + KA);
 #pragma unroll
               for (int gi = 0; gi < SEL_NG; ++gi)
                 acc[gi] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ak, __builtin_bit_cast(f16x8, qf[gi][st]), acc[gi], 0, 0, 0);
@@ -602,12 +614,20 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
 #pragma unroll
               for (int gi = 0; gi < SEL_NG; ++gi)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                  const float a =
-                      (!RG || cbase + 8 * (i >> 2) + (i & 3) < nc) ? acc[gi][i] : -__builtin_inff();
-                  ymask |= (uint32_t)(a > tY[gi]) << (8 * (i >> 2) + (i & 3));
-                  dmin[gi] = fminf(dmin[gi], __builtin_fabsf(a - ctr[gi]));
-                  smax[gi] = __builtin_fmaxf(smax[gi], a);
+                for (int q4 = 0; q4 < 4; ++q4) {
+                  // the four bits of elements 4 q4 .. 4 q4 + 3 as a nibble (small
+                  // constants), then moved into place: no registers held for
+                  // per-bit constants
+                  uint32_t nib = 0;
+#pragma unroll
+                  for (int r = 0; r < 4; ++r) {
+                    const float a = (!RG || cbase + 8 * q4 + r < nc) ? acc[gi][4 * q4 + r] : -__builtin_inff();
+                    nib |= (uint32_t)(a > tY[gi]) << r;
+                    dmin[gi] = fminf(dmin[gi], __builtin_fabsf(a - ctr[gi]));
+                    smax[gi] = __builtin_fmaxf(smax[gi], a);
+                  }
+                  asm volatile("" : "+v"(nib));
+                  ymask |= nib << (8 * q4);
                 }
 #pragma unroll
               for (int gi = 0; gi < SEL_NG; ++gi) {
@@ -617,16 +637,27 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
                 // tA, tY and ctr), re-tested exactly below
                 const bool near_th = dmin[gi] <= band[gi];
                 if (__builtin_amdgcn_ballot_w64(near_th)) {
+                  // the lane's ambiguous elements as a mask (bit i: element i), built
+                  // from the top so that each step is a shift and an add; then listed
+                  // one per lane per round, lowest first (the scores are dead by then)
+                  uint32_t am = 0;
                   if (near_th) {
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
+                    for (int i = 15; i >= 0; --i) {
                       const int c = cbase + 8 * (i >> 2) + (i & 3);
-                      if ((!RG || c < nc) & (acc[gi][i] >= tA[gi]) & !(acc[gi][i] > tY[gi])) {
-                        const uint32_t k = atomicAdd(&S.amb_cnt, 1u);
-                        if (k < SEL_AMB_CAP) S.amb[k] = ((uint32_t)vl << 16) | (uint32_t)c;
-                        else S.overflow = 1u;
-                        S.va[vl] = 1;
-                      }
+                      const bool hit = (!RG || c < nc) & (acc[gi][i] >= tA[gi]) & !(acc[gi][i] > tY[gi]);
+                      am = 2u * am + (hit ? 1u : 0u);
+                    }
+                  }
+                  while (__builtin_amdgcn_ballot_w64(am != 0u)) {
+                    if (am != 0u) {
+                      const int i = __builtin_ctz(am);
+                      am &= am - 1u;
+                      const int c = cbase + 8 * (i >> 2) + (i & 3);
+                      const uint32_t k = atomicAdd(&S.amb_cnt, 1u);
+                      if (k < SEL_AMB_CAP) S.amb[k] = ((uint32_t)vl << 16) | (uint32_t)c;
+                      else S.overflow = 1u;
+                      S.va[vl] = 1;
                     }
                   }
                 }
@@ -635,20 +666,30 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
                 // (no atomics: the wave's count stays in a scalar register)
                 const bool near_max = smax[gi] >= tN[gi];
                 if (__builtin_amdgcn_ballot_w64(near_max)) {
+                  // as the mask of ambiguous elements above, then one per lane per round
+                  uint32_t nm = 0;
+                  if (near_max) {
 #pragma unroll
-                  for (int i = 0; i < 16; ++i) {
-                    const int c = cbase + 8 * (i >> 2) + (i & 3);
-                    const bool hit = (!RG || c < nc) & (acc[gi][i] >= tN[gi]);
-                    const uint64_t m = __builtin_amdgcn_ballot_w64(hit);
-                    if (m) {
-                      if (hit) {
-                        const uint32_t pos = nbase + __builtin_amdgcn_mbcnt_hi(
-                            (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-                        if (pos < (uint32_t)SEL_NEAR_W)
-                          S.nearl[wave * SEL_NEAR_W + pos] = ((uint32_t)vl << 16) | (uint32_t)c;
-                      }
-                      nbase += (uint32_t)__builtin_popcountll(m);
+                    for (int i = 15; i >= 0; --i) {
+                      const int c = cbase + 8 * (i >> 2) + (i & 3);
+                      const bool hit = (!RG || c < nc) & (acc[gi][i] >= tN[gi]);
+                      nm = 2u * nm + (hit ? 1u : 0u);
                     }
+                  }
+                  for (;;) {
+                    const bool has = nm != 0u;
+                    const uint64_t m = __builtin_amdgcn_ballot_w64(has);
+                    if (!m) break;
+                    if (has) {
+                      const int i = __builtin_ctz(nm);
+                      nm &= nm - 1u;
+                      const int c = cbase + 8 * (i >> 2) + (i & 3);
+                      const uint32_t pos = nbase + __builtin_amdgcn_mbcnt_hi(
+                          (uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                      if (pos < (uint32_t)SEL_NEAR_W)
+                        S.nearl[wave * SEL_NEAR_W + pos] = ((uint32_t)vl << 16) | (uint32_t)c;
+                    }
+                    nbase += (uint32_t)__builtin_popcountll(m);
                   }
                 }
               }
@@ -665,7 +706,7 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
             float m = mloc;
 #pragma unroll
             for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-            if (lane == 0) S.red[wave] = m;
+            if (lane == 0) S.red[fresh_tid() >> 6] = m;   // (the slot's address formed here)
             __syncthreads();
             mnorm = S.red[0];
 #pragma unroll
@@ -701,7 +742,7 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
         }
       }
       if (lane == 0) {
-        S.ncnt[wave] = nbase;
+        S.ncnt[fresh_tid() >> 6] = nbase;   // (the slot's address formed here)
         if (nbase > (uint32_t)SEL_NEAR_W) S.overflow = 1u;
       }
       __syncthreads();
