@@ -159,6 +159,29 @@ def test_select_huge_magnitudes(lp):
     assert rcnt.min() >= 1
 
 
+@pytest.mark.parametrize("case", ["subnormal_dims", "past_fp16_range"])
+def test_select_fp16_filter_ranges(lp, case):
+    """The filter scores in fp16: half of the dims of q and of the keys at 2^-17 of
+    the rest (fp16 subnormals, rounded by the conversion and kept by the matrix
+    cores), or magnitudes past fp16's largest value (decided in fp64 alone)."""
+    rng = np.random.default_rng(8 if case == "subnormal_dims" else 9)
+    C, q_start, n_q, n_kv, d, block = 384, 640, 4, 2, 128, 64
+    T = q_start + C
+    q = rng.standard_normal((C, n_q, d)).astype(np.float32) * 2.0
+    k = rng.standard_normal((T, n_kv, d)).astype(np.float32) * 2.0
+    if case == "subnormal_dims":
+        q[..., d // 2:] *= 2.0 ** -17
+        k[..., d // 2:] *= 2.0 ** -17
+    else:
+        q *= 3e4
+    q, k = bf16_bits(q), bf16_bits(k)
+    kp, _ = pooled_index_ref(f64(k), f64(k), block)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    say("select fp16 filter ranges", case)
+    rcnt = _select_pooled(lp, q, kp, q_start, block, 0.1, scale)
+    assert rcnt.min() >= 1
+
+
 def test_select_huge_theta(lp):
     """ln(alpha)/scale beyond fp32's comfortable range: decided in fp64 alone."""
     rng = np.random.default_rng(7)
