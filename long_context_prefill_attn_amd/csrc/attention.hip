@@ -1080,10 +1080,37 @@ attn_blocksparse_kernel(const uint16_t* __restrict__ Q, int C, int q_start, int 
   cx.blog2 = blog2;
   cx.pool_bias = (float)blog2;
 
-  // 2) masked steps: the diagonal blocks and partly selected steps
+  // 2) masked steps: the diagonal blocks and partly selected steps. With blocks
+  // of 64 keys or more a wave's 32 rows lie in one query block, and a step inside
+  // that block is causal by position alone for the wave: it is skipped when every
+  // key lies past the wave's rows, taken unmasked when every key lies at or
+  // before them, and masked by position otherwise (the same weights as the
+  // per-key test, with less work per key).
+  int own = -1, qlo = 0, qhi = 0;   // the wave's query block (-1: none or several), its positions
+  {
+    const bool mixed_blocks = __any(qvalid2 && jrow != __builtin_amdgcn_readfirstlane(jrow));
+    const uint64_t vb = __ballot(qvalid2);
+    if (blog2 >= 6 && vb != 0 && !mixed_blocks) {
+      // positions are consecutive over the lanes of a half-wave: the valid rows
+      // run from the lowest valid lane's position to the highest's
+      const int lo_lane = __builtin_ctzll(vb), hi_lane = 63 - __builtin_clzll(vb);
+      qlo = __shfl(qpos2, lo_lane);
+      qhi = __shfl(qpos2, hi_lane);
+      own = __shfl(jrow, lo_lane);
+    }
+  }
   special_steps<D>(tl, lds, frow, 0, n_steps, T, [&](int st, const uint16_t* kt, const uint16_t* vt) {
     cx.key0 = st * BN;
     cx.kvalid = min(BN, T - st * BN);
+    if (own >= 0 && (cx.key0 >> blog2) == own) {
+      if (cx.key0 > qhi) return;   // every key lies past every row of the wave
+      if (cx.key0 + BN - 1 <= qlo && cx.kvalid == BN) {
+        attn_step<D, MODE_PLAIN, false>(kt, vt, lo2, qf, o, m, l, cx);
+      } else {
+        attn_step<D, MODE_CAUSAL_K, true>(kt, vt, lo2, qf, o, m, l, cx);
+      }
+      return;
+    }
     attn_step<D, MODE_BSEL, true>(kt, vt, lo2, qf, o, m, l, cx);
   });
 
