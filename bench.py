@@ -56,8 +56,9 @@ def parse():
                     help="dense part: prefill_attn_dense over a causal fp16 mask (default), "
                          "prefill_attn_dense_causal (no mask buffer) or prefill_attn_dense_bits "
                          "(the same causal masks packed one bit per key); for the folded-selection "
-                         "workload, mask (fold the lists, then dense) or gather (prefill_attn_gather "
-                         "over the lists)")
+                         "workload, mask (fold the lists, then dense), bits (fold the lists into keep "
+                         "bits, then prefill_attn_dense_bits) or gather (prefill_attn_gather over the "
+                         "lists)")
     ap.add_argument("--cpu-seconds", type=float, default=20.0, help="budget for the CPU oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 512 MiB device copy (reference for HBM byte counters)")
@@ -175,6 +176,8 @@ def main():
         [torch.empty((C, q0 + C), dtype=torch.float16, device=dev) for q0, C in dchunks]
     if args.dense_entry == "bits" and not fold:   # packed on the host before the timed region
         mask_bits = [torch.from_numpy(pack_keep_bits(causal_mask(q0, C) == 0)).to(dev) for q0, C in dchunks]
+    if args.dense_entry == "bits" and fold:       # folded on the device inside each step
+        mask_bits = [torch.empty((C, (q0 + C + 31) // 32), dtype=torch.int32, device=dev) for q0, C in dchunks]
     keeps = [fold_lists(wd, q0, C, dev) for q0, C in dchunks] if fold else []
     O_dense = torch.empty((Nd, Hq, d), dtype=torch.float32, device=dev)
     wsd = torch.empty(max(max(lp.prefill_attn_dense_workspace(C, q0 + C, Hq, Hkv, d) for q0, C in dchunks), 256),
@@ -207,7 +210,9 @@ def main():
             lp.prefill_attn_gather(Q[q0:T], K[:T], V[:T], keeps[ci][0], keeps[ci][1], q0, s.fold_width,
                                    s.fold_recent, scale, O=O[q0:T])
             return
-        if keeps:
+        if keeps and entry == "bits":
+            lp.fold_keep_bits(keeps[ci][0], keeps[ci][1], q0, T, s.fold_width, s.fold_recent, bits=mask_bits[ci])
+        elif keeps:
             lp.fold_keep_mask(keeps[ci][0], keeps[ci][1], q0, T, s.fold_width, s.fold_recent, mask=masks[ci])
         if entry == "causal":
             lp.prefill_attn_dense_causal(Q[q0:T], K[:T], V[:T], q0, scale, O=O[q0:T], workspace=wsp)
@@ -222,9 +227,9 @@ def main():
             lp.fold_keep_mask(keeps[ci][0], keeps[ci][1], q0, q0 + C, s.fold_width, s.fold_recent,
                               mask=masks[ci])
             kept_pairs.append(int((masks[ci] == 0).sum().item()))
-    if (args.dense_entry == "gather") != fold and args.dense_entry != "mask":
-        print("--dense-entry gather is for the folded-selection workload (fold2k5); causal and bits "
-              "are for causal workloads", file=sys.stderr)
+    if (args.dense_entry == "gather" and not fold) or (args.dense_entry == "causal" and fold):
+        print("--dense-entry gather is for the folded-selection workload (fold2k5); causal is for "
+              "causal workloads", file=sys.stderr)
         sys.exit(2)
     entry = args.dense_entry
 
@@ -325,6 +330,8 @@ def main():
         calls = ([q0 + C for q0, C in dchunks] if do_dense else []) + \
                 ([q0 + C for q0, C in scalls] if do_sparse else [])
         hbm["stage_values"] = sum(3 * T * Hkv * d * 2 for T in calls)
+        if do_sparse:   # + the pooled operands of each block-sparse call: fp32 rows in, bf16/fp16 rows out
+            hbm["stage_values"] += sum(-(-(q0 + C) // B) * Hkv * d * (2 * 4 + 2 * 2) for q0, C in scalls)
     hbm_kernels = {k: {"bytes_per_step": b, "GB_per_s": round(b / (kern[k]["ms_per_step"] * 1e-3) / 1e9, 1),
                        "frac_of_hbm_peak": round(b / (kern[k]["ms_per_step"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)}
                    for k, b in hbm.items()}

@@ -271,6 +271,25 @@ int fold_keep_mask(const int32_t* keep_idx, int64_t keep_ld, const int32_t* keep
                    void* stream);
 
 /*
+ * fold_keep_bits -- the same fold as fold_keep_mask, written as the bit-packed
+ * keep mask that prefill_attn_dense_bits consumes (one bit per row and key
+ * instead of an fp16 entry). ("ANE Prefill Research", What worked, item 2.)
+ *
+ *   keep_idx, keep_cnt  as fold_keep_mask
+ *   bits      uint32 [C][bits_ld]  output; bit t % 32 of word t / 32 of row i is set
+ *                                  exactly where fold_keep_mask writes 0; bits of keys
+ *                                  >= T in the last word are clear; words past
+ *                                  ceil(T/32) are untouched
+ *
+ * Requires C >= 1, q_start >= 0, q_start + C <= T, bits_ld >= ceil(T/32),
+ * width >= 1, recent >= 0, keep_cnt and bits 16-byte aligned.
+ * Errors: PA_EINVAL, PA_EHIP.
+ */
+int fold_keep_bits(const int32_t* keep_idx, int64_t keep_ld, const int32_t* keep_cnt, int C,
+                   int q_start, int T, int width, int recent, uint32_t* bits, int64_t bits_ld,
+                   void* stream);
+
+/*
  * prefill_attn_gather -- attention over a sparse indexer's compacted selection
  * without a mask: each row scores only the keys it keeps. ("ANE Prefill Research",
  * What worked, item 2, for the selection lists; "What would re-open it", for

@@ -24,7 +24,8 @@ from ._lib import PrefillAttnError, check, lib  # noqa: F401
 
 __all__ = ["prefill_attn_dense", "prefill_attn_dense_bits", "prefill_attn_dense_causal", "prefill_attn_dense_workspace",
            "prefill_attn_blocksparse_workspace", "build_pooled_index",
-           "select_blocks", "prefill_attn_blocksparse", "fold_keep_mask", "prefill_attn_gather",
+           "select_blocks", "prefill_attn_blocksparse", "fold_keep_mask", "fold_keep_bits",
+           "prefill_attn_gather",
            "PrefillAttnError", "timing",
            "bisect_alpha", "calibrate_alpha"]
 
@@ -149,6 +150,26 @@ def fold_keep_mask(keep_idx, keep_cnt, q_start: int, T: int, width: int, recent:
                                T, width, recent, mask.data_ptr(), mask.stride(0), _stream()),
           "fold_keep_mask")
     return mask
+
+
+def fold_keep_bits(keep_idx, keep_cnt, q_start: int, T: int, width: int, recent: int, bits=None):
+    """Fold an indexer's compacted selection into a bit-packed keep mask int32 [C][ld >= ceil(T/32)]
+    (bit t % 32 of word t // 32 set for a kept key), as prefill_attn_dense_bits takes it."""
+    _req(keep_idx, "keep_idx", torch.int32, 2)
+    _req(keep_cnt, "keep_cnt", torch.int32, 1)
+    C, K = keep_idx.shape
+    if keep_cnt.shape[0] != C:
+        raise ValueError("keep_cnt must have one entry per row")
+    words = (T + 31) // 32
+    if bits is None:
+        bits = torch.empty((C, words), dtype=torch.int32, device=keep_idx.device)
+    _req(bits, "bits", torch.int32, 2)
+    if bits.shape[0] != C or bits.shape[1] < words:
+        raise ValueError(f"bits must be [{C}][>= {words}]")
+    check(lib().fold_keep_bits(keep_idx.data_ptr() if K else None, K, keep_cnt.data_ptr(), C, q_start,
+                               T, width, recent, bits.data_ptr(), bits.stride(0), _stream()),
+          "fold_keep_bits")
+    return bits
 
 
 def prefill_attn_gather(Q, K, V, keep_idx, keep_cnt, q_start: int, width: int, recent: int, scale: float,

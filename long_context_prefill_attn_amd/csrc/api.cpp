@@ -281,6 +281,19 @@ int fold_keep_mask(const int32_t* keep_idx, int64_t keep_ld, const int32_t* keep
   }));
 }
 
+int fold_keep_bits(const int32_t* keep_idx, int64_t keep_ld, const int32_t* keep_cnt, int C, int q_start,
+                   int T, int width, int recent, uint32_t* bits, int64_t bits_ld, void* stream) {
+  if (!aligned16(keep_cnt) || !aligned16(bits) || (keep_ld > 0 && !aligned16(keep_idx))) return PA_EINVAL;
+  if (C < 1 || q_start < 0 || (long long)q_start + C > T || width < 1 || recent < 0 || keep_ld < 0)
+    return PA_EINVAL;
+  if (bits_ld < ((long long)T + 31) / 32) return PA_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return hip_status(timed("fold", s, [&] {
+    return pa::launch_fold_keep_bits(keep_idx, keep_ld, keep_cnt, C, q_start, T, width, recent, bits, bits_ld,
+                                     s);
+  }));
+}
+
 int prefill_attn_gather(const uint16_t* Q, int C, int q_start, int n_q, const uint16_t* K,
                         const uint16_t* V, int T, int n_kv, int d, const int32_t* keep_idx,
                         int64_t keep_ld, const int32_t* keep_cnt, int width, int recent, float scale,

@@ -80,6 +80,9 @@ hipError_t launch_mask_classify(const uint16_t* mask, int64_t mask_ld, int C, in
                                 uint8_t* flags, hipStream_t stream);
 
 // Tile flags of a bit-packed mask: bit t % 32 of word t / 32 of a row set = key t kept.
+hipError_t launch_fold_keep_bits(const int32_t* keep_idx, int64_t keep_ld, const int32_t* keep_cnt, int C,
+                                 int q_start, int T, int width, int recent, uint32_t* bits, int64_t bits_ld,
+                                 hipStream_t stream);
 hipError_t launch_mask_classify_bits(const uint32_t* bits, int64_t bits_ld, int C, int T,
                                      uint8_t* flags, hipStream_t stream);
 

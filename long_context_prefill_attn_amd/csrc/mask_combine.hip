@@ -144,6 +144,75 @@ hipError_t launch_fold_keep(const int32_t* keep_idx, int64_t keep_ld, const int3
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// fold_keep_bits: the same fold as bits (bit t % 32 of word t / 32 of a row set
+// when key t is kept), for prefill_attn_dense_bits. One workgroup per query row;
+// the row is built in LDS in segments of FOLD_SEG_WORDS words (cleared, then the
+// kept ranges ORed in word by word, then copied out), so any T is taken.
+// Bits of keys at or past T in the last word stay clear; words past the row's
+// ceil(T/32) are untouched. grid = C, block = 256.
+// ---------------------------------------------------------------------------
+constexpr int FOLD_SEG_WORDS = 8192;   // 32 KB of LDS: 262,144 keys per segment
+
+// OR the keys [a, b] (segment-relative, a <= b) into the segment's words
+__device__ __forceinline__ void or_key_range(uint32_t* seg, int a, int b) {
+  for (int w = a >> 5; w <= (b >> 5); ++w) {
+    const int lo = max(a - 32 * w, 0), hi = min(b - 32 * w, 31);
+    const uint32_t upto = hi == 31 ? 0xFFFFFFFFu : ((1u << (hi + 1)) - 1u);
+    atomicOr(&seg[w], upto & ~((1u << lo) - 1u));
+  }
+}
+
+__global__ void __launch_bounds__(256) fold_keep_bits_kernel(const int32_t* __restrict__ keep_idx,
+                                                             int64_t keep_ld,
+                                                             const int32_t* __restrict__ keep_cnt,
+                                                             int q_start, int T, int width, int recent,
+                                                             uint32_t* __restrict__ bits, int64_t bits_ld) {
+  __shared__ uint32_t seg[FOLD_SEG_WORDS];
+  const int i = blockIdx.x;
+  const int tid = threadIdx.x;
+  uint32_t* row = bits + (size_t)i * bits_ld;
+  const int p = q_start + i;
+  const int last = min(p, T - 1);            // no key past the row's own position
+  const int64_t nblk = ((int64_t)T + width - 1) / width;
+  const int cnt = (int)min((int64_t)max(keep_cnt[i], 0), keep_ld);
+  const int32_t* ki = keep_idx + (size_t)i * keep_ld;
+  const int r_lo = max(0, p - recent + 1);   // the recent keys: r_lo .. last (none when recent == 0)
+  const int nwords = (T + 31) / 32;
+  for (int w0 = 0; w0 < nwords; w0 += FOLD_SEG_WORDS) {
+    const int nw = min(FOLD_SEG_WORDS, nwords - w0);
+    const int t_lo = 32 * w0, t_hi = min(T - 1, 32 * (w0 + nw) - 1);   // the segment's keys
+    for (int w = tid; w < nw; w += 256) seg[w] = 0u;
+    __syncthreads();
+    for (int e = tid; e < cnt; e += 256) {
+      const int c = ki[e];
+      if (c < 0 || c >= nblk) continue;
+      const int64_t k0 = (int64_t)c * width;
+      const int a = (int)max(k0, (int64_t)t_lo);
+      const int b = (int)min(min(k0 + width - 1, (int64_t)last), (int64_t)t_hi);
+      if (a <= b) or_key_range(seg, a - t_lo, b - t_lo);
+    }
+    if (recent > 0) {
+      // the recent range, one word per thread
+      const int a = max(r_lo, t_lo), b = min(last, t_hi);
+      if (a <= b)
+        for (int w = (a - t_lo) / 32 + tid; w <= (b - t_lo) / 32; w += 256)
+          or_key_range(seg, max(a - t_lo, 32 * w), min(b - t_lo, 32 * w + 31));
+    }
+    __syncthreads();
+    for (int w = tid; w < nw; w += 256) row[w0 + w] = seg[w];
+    __syncthreads();   // the segment is read out before it is cleared again
+  }
+}
+
+hipError_t launch_fold_keep_bits(const int32_t* keep_idx, int64_t keep_ld, const int32_t* keep_cnt, int C,
+                                 int q_start, int T, int width, int recent, uint32_t* bits, int64_t bits_ld,
+                                 hipStream_t stream) {
+  hipLaunchKernelGGL(fold_keep_bits_kernel, dim3(C), dim3(256), 0, stream, keep_idx, keep_ld, keep_cnt, q_start,
+                     T, width, recent, bits, bits_ld);
+  return hipGetLastError();
+}
+
 // mask_classify for a bit-packed mask: one workgroup per tile of 64 rows x 64 keys
 // (64 rows x 2 words, one word per thread of the first 128); only the bits of
 // keys below T count.

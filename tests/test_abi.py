@@ -193,6 +193,21 @@ def test_fold_rejects():
     assert f(mask=FAKE + 4) == _lib.PA_EINVAL   # misaligned
 
 
+def test_fold_bits_rejects():
+    lib = _lib.lib()
+    f = lambda **kw: lib.fold_keep_bits(kw.get("idx", FAKE), kw.get("K", 8), kw.get("cnt", FAKE),
+                                        kw.get("C", 16), kw.get("q0", 100), kw.get("T", 116),
+                                        kw.get("width", 4), kw.get("recent", 3), kw.get("bits", FAKE),
+                                        kw.get("ld", 4), None)
+    assert f(T=115) == _lib.PA_EINVAL          # rows past the last key
+    assert f(width=0) == _lib.PA_EINVAL
+    assert f(recent=-1) == _lib.PA_EINVAL
+    assert f(ld=3) == _lib.PA_EINVAL           # fewer words than ceil(T / 32)
+    assert f(K=-1) == _lib.PA_EINVAL
+    assert f(cnt=None) == _lib.PA_EINVAL
+    assert f(bits=FAKE + 4) == _lib.PA_EINVAL   # misaligned
+
+
 def test_gather_rejects():
     """The gather entry's host-side checks (no kernel is launched on any of these)."""
     lib = _lib.lib()

@@ -720,6 +720,64 @@ def test_fold_keep_mask_malformed_lists(lp):
     assert np.array_equal(m.cpu().numpy().view(np.uint16), want.view(np.uint16))
 
 
+def _bits_of(mask16, words):
+    """The keep bits of an fp16 fold mask (0 = kept), packed as prefill_attn_dense_bits reads them."""
+    return pack_keep_bits(mask16 == 0, words=words)
+
+
+def test_fold_keep_bits_bit_exact(lp):
+    """The folded keep bits equal the packing of the oracle's fold mask on the
+    fold2k5 chunks (words past ceil(T/32) untouched), and attention over them is
+    bit-identical to attention over the device-folded fp16 mask."""
+    import torch
+    w = make_workload("fold2k5")
+    s = w.spec
+    for q_start, C in s.chunks:
+        T = q_start + C
+        words = (T + 31) // 32
+        idx, cnt = _keep_lists(w, q_start, C)
+        say("fold bits", q_start, C)
+        buf = torch.full((C, words + 4), 0x5A5A5A5A, dtype=torch.int32, device="cuda")
+        bits = lp.fold_keep_bits(torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda(), q_start, T,
+                                 s.fold_width, s.fold_recent, bits=buf)
+        torch.cuda.synchronize()
+        got = bits.cpu().numpy()
+        want = _bits_of(fold_mask_ref(idx, cnt, q_start, T, s.fold_width, s.fold_recent), words)
+        assert np.array_equal(got[:, :words], want), q_start
+        assert np.all(got[:, words:] == 0x5A5A5A5A)             # words past the row's keys untouched
+    q0, C = s.chunks[-1]
+    T = q0 + C
+    idx, cnt = _keep_lists(w, q0, C)
+    ti, tc = torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda()
+    q, k, v = dev_bf16(w.Q[q0:T]), dev_bf16(w.K[:T]), dev_bf16(w.V[:T])
+    a = lp.prefill_attn_dense(q, k, v, lp.fold_keep_mask(ti, tc, q0, T, s.fold_width, s.fold_recent), s.scale)
+    b = lp.prefill_attn_dense_bits(q, k, v, lp.fold_keep_bits(ti, tc, q0, T, s.fold_width, s.fold_recent),
+                                   s.scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(a.cpu().numpy().view(np.uint32), b.cpu().numpy().view(np.uint32))
+
+
+@pytest.mark.parametrize("C,q_start,T,width,recent,K,seed", [
+    (300, 500, 900, 8, 5, 40, 41),            # out-of-range, duplicate and negative entries, odd counts
+    (3, 299997, 300000, 64, 100, 50, 42),     # rows over two LDS segments of 262,144 keys
+    (40, 60, 100, 1, 0, 70, 43),              # width 1, no recent keys
+    (17, 1000, 1017, 100, 37, 12, 44),        # blocks wider than a word, a ragged last word
+])
+def test_fold_keep_bits_lists(lp, C, q_start, T, width, recent, K, seed):
+    import torch
+    rng = np.random.default_rng(seed)
+    idx = rng.integers(-5, T // width + 10, size=(C, K)).astype(np.int32)
+    idx[:, 5] = idx[:, 4]                                    # duplicates
+    cnt = rng.integers(-3, K + 20, size=C).astype(np.int32)
+    say("fold bits lists", C, q_start, T, width, recent, K)
+    bits = lp.fold_keep_bits(torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda(), q_start, T,
+                             width, recent)
+    torch.cuda.synchronize()
+    words = (T + 31) // 32
+    want = _bits_of(fold_mask_ref(idx, cnt, q_start, T, width, recent), words)
+    assert np.array_equal(bits.cpu().numpy(), want)
+
+
 # ---------------------------------------------------------------- causal entry, per-key mask
 def test_dense_causal_gqa4k(lp):
     """The causal entry (no mask buffer) on both gqa4k chunks."""
