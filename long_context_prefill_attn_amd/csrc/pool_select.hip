@@ -143,7 +143,7 @@ constexpr int SEL_THREADS = SEL_WAVES * 64;
 constexpr int SEL_VT = SEL_WAVES * SEL_VW;   // voters per tile
 constexpr int SEL_WPE = 8 / SEL_NG / 2;  // waves per SIMD: two workgroups per CU
 constexpr int SEL_MAX_NB = 8192;
-constexpr int SEL_AMB_CAP = 512;         // ambiguous pairs per voter tile
+constexpr int SEL_AMB_CAP = 1536;        // ambiguous pairs per voter tile (the fp16 band at 1K candidates)
 constexpr int SEL_JOB_CAP = 512;         // exact max evaluations per voter tile
 constexpr int SEL_NEAR_W = 2 * SEL_VW;   // near-max pairs per wave and voter tile (at least one per voter)
 // candidates per LDS chunk: 64 KB of fp16 rows
@@ -250,7 +250,6 @@ struct SelShared {
     uint16_t kh[SelGeo<D>::CH * D];   // fp16 candidates (layout: sel_pos)
   } k;
   unsigned long long mxkey[SEL_VT];        // exact max (as dkey) of voters with ambiguous pairs
-  double ambval[SEL_AMB_CAP];              // exact scores of the ambiguous pairs
   uint32_t amb[SEL_AMB_CAP];               // (voter << 16) | block
   uint32_t jobs[SEL_JOB_CAP];              // pairs whose exact score enters a max
   uint32_t nearl[SEL_WAVES * SEL_NEAR_W];  // near-max pairs, (voter << 16) | block, a part per wave
@@ -292,26 +291,26 @@ __device__ __forceinline__ double dot_exact_prefetched(const uint16_t* __restric
   return acc;
 }
 
-// Exact fp64 scores of the listed pairs in one round, one pair per thread: the
-// max jobs (jobs[0 .. njob), whose results raise their voters' exact max) and the
-// ambiguous pairs (amb[0 .. namb), whose results are kept); then, after a
-// barrier, each ambiguous pair votes if it clears theta against its voter's max.
+// Exact fp64 scores of the listed pairs, one pair per thread: first the max
+// jobs (jobs[0 .. njob), whose results raise their voters' exact max), then,
+// after a barrier, the ambiguous pairs (amb[0 .. namb)), each of which votes if
+// its exact score clears theta against its voter's exact max.
 template <int D>
 __device__ __forceinline__ void exact_pairs(SelShared<D>& S, int njob, int namb, const uint16_t* qg,
                                             int group, int n_q, int vt0, const float* kg, double theta) {
-  for (int e = fresh_tid(); e < njob + namb; e += SEL_THREADS) {
-    const uint32_t pr = e < njob ? S.jobs[e] : S.amb[e - njob];
-    const int vl = (int)(pr >> 16), b = (int)(pr & 0xFFFFu);
-    const int v = vt0 + vl;
-    const double r = dot_exact_prefetched<D>(qg + ((size_t)(v / group) * n_q + (v % group)) * D, kg + (size_t)b * D);
-    if (e < njob) atomicMax(&S.mxkey[vl], dkey(r));
-    else S.ambval[e - njob] = r;
+  auto score = [&](uint32_t pr) {
+    const int v = vt0 + (int)(pr >> 16), b = (int)(pr & 0xFFFFu);
+    return dot_exact_prefetched<D>(qg + ((size_t)(v / group) * n_q + (v % group)) * D, kg + (size_t)b * D);
+  };
+  for (int e = fresh_tid(); e < njob; e += SEL_THREADS) {
+    const uint32_t pr = S.jobs[e];
+    atomicMax(&S.mxkey[pr >> 16], dkey(score(pr)));
   }
   __syncthreads();
   for (int e = fresh_tid(); e < namb; e += SEL_THREADS) {
     const uint32_t pr = S.amb[e];
-    const int vl = (int)(pr >> 16), b = (int)(pr & 0xFFFFu);
-    if (S.ambval[e] - dval(S.mxkey[vl]) > theta) atomicOr(&S.flagw[b >> 5], 1u << (b & 31));
+    const int b = (int)(pr & 0xFFFFu);
+    if (score(pr) - dval(S.mxkey[pr >> 16]) > theta) atomicOr(&S.flagw[b >> 5], 1u << (b & 31));
   }
 }
 
