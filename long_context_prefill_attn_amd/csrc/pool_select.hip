@@ -145,6 +145,7 @@ constexpr int SEL_WPE = 8 / SEL_NG / 2;  // waves per SIMD: two workgroups per C
 constexpr int SEL_MAX_NB = 8192;
 constexpr int SEL_AMB_CAP = 1536;        // ambiguous pairs per voter tile (the fp16 band at 1K candidates)
 constexpr int SEL_JOB_CAP = 512;         // exact max evaluations per voter tile
+constexpr int SEL_P2G = 4;               // pass 2: slices of 32 candidates per list flush
 constexpr int SEL_NEAR_W = 2 * SEL_VW;   // near-max pairs per wave and voter tile (at least one per voter)
 // candidates per LDS chunk: 64 KB of fp16 rows
 template <int D> struct SelGeo { static constexpr int CH = 32768 / D; };
@@ -260,6 +261,9 @@ struct SelShared {
   float red[SEL_WAVES];
   uint32_t amb_cnt, job_cnt;
   uint32_t overflow;
+  // pass 2 only, last (the fields above keep their offsets)
+  uint32_t pcnt[2];                        // list counts, alternating by slice group
+  float2 thr[SEL_VT];                      // per voter (tA, tY) of pass 1
 };
 
 // r = q.kbar in fp64, dims in increasing order, with each quarter of both rows
@@ -429,7 +433,7 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
     for (int vt0 = sp * SEL_VT; vt0 < nv; vt0 += n_split * SEL_VT) {
       __syncthreads();  // previous tile's readers of the shared state are done
       for (int i = fresh_tid(); i < SEL_VT; i += SEL_THREADS) { S.va[i] = 0; S.mxkey[i] = 0; }
-      if (tid == 0) { S.amb_cnt = 0; S.job_cnt = 0; S.overflow = exact_only; }
+      if (tid == 0) { S.amb_cnt = 0; S.job_cnt = 0; S.pcnt[0] = 0; S.pcnt[1] = 0; S.overflow = exact_only; }
 
       // B operands: q of the wave's SEL_NG groups of 32 voters (voter = lane % 32),
       // held for the whole tile; voter index in the tile vl = SEL_VW wave + 32 gi + col.
@@ -538,6 +542,30 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
         staged = resident;
         lds_barrier();
       };
+      // filtered scores of the staged chunk's slice t (its candidates 32 t ..
+      // 32 t + 31) against the wave's voters
+      auto slice_scores = [&](int t, f32x16 (&acc)[SEL_NG]) {
+#pragma unroll
+        for (int gi = 0; gi < SEL_NG; ++gi) acc[gi] = f32x16{};
+        const int arow = 32 * t + col;
+        // candidate fragments read KA steps ahead of their MFMA (a few in flight
+        // rather than all of them: registers)
+        constexpr int KA = 3;
+        auto kread = [&](int st) {
+          return *reinterpret_cast<const f16x8*>(&S.k.kh[sel_pos<D>(arow, 2 * st + half)]);
+        };
+        f16x8 kf[KA];
+#pragma unroll
+        for (int st = 0; st < KA; ++st) kf[st] = kread(st);
+#pragma unroll
+        for (int st = 0; st < NST; ++st) {
+          const f16x8 ak = kf[st % KA];
+          if (st + KA < NST) kf[st % KA] = kread(st + KA);
+#pragma unroll
+          for (int gi = 0; gi < SEL_NG; ++gi)
+            acc[gi] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ak, __builtin_bit_cast(f16x8, qf[gi][st]), acc[gi], 0, 0, 0);
+        }
+      };
       if (!(resident && staged)) stage(0, first_tile, std::true_type{});
       else load_q();
       q_to_f16();
@@ -552,26 +580,7 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
           for (int t = 0; t < (nch + 31) / 32; ++t) {
             const int cb = c0 + 32 * t;
             f32x16 acc[SEL_NG];
-#pragma unroll
-            for (int gi = 0; gi < SEL_NG; ++gi) acc[gi] = f32x16{};
-            const int arow = 32 * t + col;
-            // candidate fragments read KA steps ahead of their MFMA (a few in flight
-            // rather than all of them: registers)
-            constexpr int KA = 3;
-            auto kread = [&](int st) {
-              return *reinterpret_cast<const f16x8*>(&S.k.kh[sel_pos<D>(arow, 2 * st + half)]);
-            };
-            f16x8 kf[KA];
-#pragma unroll
-            for (int st = 0; st < KA; ++st) kf[st] = kread(st);
-#pragma unroll
-            for (int st = 0; st < NST; ++st) {
-              const f16x8 ak = kf[st % KA];
-              if (st + KA < NST) kf[st % KA] = kread(st + KA);
-#pragma unroll
-              for (int gi = 0; gi < SEL_NG; ++gi)
-                acc[gi] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ak, __builtin_bit_cast(f16x8, qf[gi][st]), acc[gi], 0, 0, 0);
-            }
+            slice_scores(t, acc);
             // element i of acc[gi]: candidate cb + 4 half + 8(i/4) + i%4 against voter
             // SEL_VW wave + 32 gi + col
             const int cbase = cb + 4 * half;
@@ -655,7 +664,6 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
                       const int c = cbase + 8 * (i >> 2) + (i & 3);
                       const uint32_t k = atomicAdd(&S.amb_cnt, 1u);
                       if (k < SEL_AMB_CAP) S.amb[k] = ((uint32_t)vl << 16) | (uint32_t)c;
-                      else S.overflow = 1u;
                       S.va[vl] = 1;
                     }
                   }
@@ -740,12 +748,20 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
           if (S.overflow) break;  // uniform: redo this voter tile exactly
         }
       }
+      // the voters' pass-1 thresholds, kept for pass 2
+      if (((fresh_tid() >> 5) & 1) == 0) {
+#pragma unroll
+        for (int gi = 0; gi < SEL_NG; ++gi)
+          S.thr[(fresh_tid() >> 6) * SEL_VW + gi * 32 + (fresh_tid() & 31)] = make_float2(tA[gi], tY[gi]);
+      }
       if (lane == 0) {
         S.ncnt[fresh_tid() >> 6] = nbase;   // (the slot's address formed here)
         if (nbase > (uint32_t)SEL_NEAR_W) S.overflow = 1u;
       }
       __syncthreads();
-      const bool go = !S.overflow && S.amb_cnt > 0;
+      const uint32_t namb = S.amb_cnt;   // counted past the list's capacity
+      const bool go = !S.overflow && namb > 0;
+      const bool redo = namb > (uint32_t)SEL_AMB_CAP;   // the list overflowed: pass 2
       __syncthreads();  // every thread has read the flags before they change again
       if (go) {
         // pairs whose exact score may be the max of a voter with ambiguous pairs:
@@ -760,9 +776,84 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
           else S.overflow = 1u;
         }
         __syncthreads();
-        if (!S.overflow) exact_pairs<D>(S, (int)S.job_cnt, (int)S.amb_cnt, qg, group, n_q, vt0, kg, theta);
+        if (!S.overflow)
+          exact_pairs<D>(S, (int)S.job_cnt, redo ? 0 : (int)namb, qg, group, n_q, vt0, kg, theta);
       }
       __syncthreads();
+      if (redo && !S.overflow) {
+        // Pass 2, after an overflow of the ambiguous list: the same filtered scores
+        // against the same thresholds give the same ambiguous pairs again; they are
+        // listed and decided against the exact maxima found above, SEL_P2G slices
+        // at a time. A group whose list overflows again decides every pair of its
+        // candidates for the voters with ambiguous pairs (the rest of those voters'
+        // pairs agree with the filter's decision).
+        // (the voters' q and thresholds are loaded afresh for each group, so that
+        // nothing of theirs is held through the exact evaluations)
+        int grp = 0;
+        for (int c0 = 0; c0 < nc; c0 += CH) {
+          if (!resident) {
+            __syncthreads();  // readers of the previous chunk are done
+            stage(c0, false, std::false_type{});
+          }
+          const int nsl = (min(CH, nc - c0) + 31) / 32;
+#pragma unroll 1
+          for (int t0 = 0; t0 < nsl; t0 += SEL_P2G, ++grp) {
+            const int t1 = min(t0 + SEL_P2G, nsl);
+            load_q();
+            q_to_f16();
+            float tA2[SEL_NG], tY2[SEL_NG];
+#pragma unroll
+            for (int gi = 0; gi < SEL_NG; ++gi) {
+              const int vl = (fresh_tid() >> 6) * SEL_VW + gi * 32 + (fresh_tid() & 31);
+              const float2 th = S.thr[vl];
+              tA2[gi] = S.va[vl] ? th.x : __builtin_inff();   // other voters list nothing
+              tY2[gi] = th.y;
+            }
+#pragma unroll 1
+            for (int t = t0; t < t1; ++t) {
+              f32x16 acc[SEL_NG];
+              slice_scores(t, acc);
+              const int cbase = c0 + 32 * t + 4 * half;
+#pragma unroll
+              for (int gi = 0; gi < SEL_NG; ++gi) {
+                const int vl = wave * SEL_VW + gi * 32 + col;
+                uint32_t am = 0;
+#pragma unroll
+                for (int i = 15; i >= 0; --i) {
+                  const int c = cbase + 8 * (i >> 2) + (i & 3);
+                  const bool hit = (c < nc) & (acc[gi][i] >= tA2[gi]) & !(acc[gi][i] > tY2[gi]);
+                  am = 2u * am + (hit ? 1u : 0u);
+                }
+                while (__builtin_amdgcn_ballot_w64(am != 0u)) {
+                  if (am != 0u) {
+                    const int i = __builtin_ctz(am);
+                    am &= am - 1u;
+                    const int c = cbase + 8 * (i >> 2) + (i & 3);
+                    const uint32_t k = atomicAdd(&S.pcnt[grp & 1], 1u);
+                    if (k < SEL_AMB_CAP) S.amb[k] = ((uint32_t)vl << 16) | (uint32_t)c;
+                  }
+                }
+              }
+            }
+            __syncthreads();  // the group's list is complete
+            const uint32_t n = S.pcnt[grp & 1];
+            // the other count was last read before this barrier: cleared for the next group
+            if (tid == 0) S.pcnt[(grp + 1) & 1] = 0;
+            if (n <= (uint32_t)SEL_AMB_CAP) {
+              exact_pairs<D>(S, 0, (int)n, qg, group, n_q, vt0, kg, theta);
+            } else {
+              const int cg0 = c0 + 32 * t0, w = min(c0 + 32 * t1, nc) - cg0;
+              for (int e = fresh_tid(); e < SEL_VT * w; e += SEL_THREADS) {
+                const int vl = e / w, c = cg0 + e % w;
+                if (!S.va[vl]) continue;
+                if (dot_exact_prefetched<D>(qptr(vt0 + vl), kg + (size_t)c * D) - dval(S.mxkey[vl]) > theta)
+                  atomicOr(&S.flagw[c >> 5], 1u << (c & 31));
+              }
+            }
+            __syncthreads();  // the list is read before the next group writes it
+          }
+        }
+      }
       if (S.overflow) {
         // exact fp64 for every pair of this voter tile; one wave per voter
         const int nvt = min(SEL_VT, nv - vt0);

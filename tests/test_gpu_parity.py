@@ -145,6 +145,40 @@ def test_select_identical_pooled_keys(lp, n_q):
     assert np.all(rcnt == 1)
 
 
+@pytest.mark.parametrize("d,nc,dense_group", [(128, 1100, False), (128, 1100, True), (64, 700, False)])
+def test_select_ambiguous_relisted(lp, d, nc, dense_group):
+    """More ambiguous pairs in a voter tile than its list holds, each voter with a
+    single near-max candidate: the pairs are formed again a few candidate slices at
+    a time and decided exactly against the exact maxima; a group with more pairs
+    than the list holds is decided pair by pair. nc candidates span several LDS
+    chunks (re-staged) and end in a ragged slice."""
+    block, n_q, C = 16, 16, 16
+    q_start = nc * block
+    scale = float(np.float32(1 / math.sqrt(d)))
+    alpha = 0.5
+    theta = math.log(alpha) / scale
+    q = np.zeros((C, n_q, d), dtype=np.float32)
+    q[:, :, 0] = 1.0
+    kp = np.zeros((1, nc + 1, d), dtype=np.float32)
+    kp[0, :, 0] = np.float32(theta - 12.0)              # clearly dropped
+    kp[0, 0, 0] = 1.0                                   # the row max M = 1
+    kept = list(range(3, nc, 64))
+    kp[0, kept, 0] = 0.5                                # clearly kept
+    amb = set(range(7, nc, 32))                         # about four per 128 candidates
+    if dense_group:
+        amb |= set(range(514, 640, 4))                  # 36 in candidates 512..639
+    edge = np.float32(1.0 + theta)
+    for i, c in enumerate(sorted(amb)):
+        v, s = edge, i % 21 - 10                        # |s| fp32 ulps away from the edge
+        for _ in range(abs(s)):
+            v = np.nextafter(v, np.float32(np.inf if s > 0 else -np.inf))
+        kp[0, c, 0] = v
+    say("select ambiguous relisted", d, nc, dense_group)
+    rcnt = _select_pooled(lp, bf16_bits(q), kp, q_start, block, alpha, scale)
+    base = 2 + len(kept)                                # the max, the clearly kept, the diagonal
+    assert base < rcnt[0, 0] < base + len(amb)          # both sides of the edge occur
+
+
 def test_select_huge_magnitudes(lp):
     """|q| |kbar| beyond the range of the filter's bound: decided in fp64 alone."""
     rng = np.random.default_rng(6)
