@@ -544,7 +544,7 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
       };
       // filtered scores of the staged chunk's slice t (its candidates 32 t ..
       // 32 t + 31) against the wave's voters
-      auto slice_scores = [&](int t, f32x16 (&acc)[SEL_NG]) {
+      auto slice_scores = [&](int t, f32x16 (&acc)[SEL_NG], int col, int half) {
 #pragma unroll
         for (int gi = 0; gi < SEL_NG; ++gi) acc[gi] = f32x16{};
         const int arow = 32 * t + col;
@@ -580,7 +580,7 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
           for (int t = 0; t < (nch + 31) / 32; ++t) {
             const int cb = c0 + 32 * t;
             f32x16 acc[SEL_NG];
-            slice_scores(t, acc);
+            slice_scores(t, acc, col, half);
             // element i of acc[gi]: candidate cb + 4 half + 8(i/4) + i%4 against voter
             // SEL_VW wave + 32 gi + col
             const int cbase = cb + 4 * half;
@@ -811,12 +811,16 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
             }
 #pragma unroll 1
             for (int t = t0; t < t1; ++t) {
+              // lane values formed afresh (nothing lane-derived is held through the
+              // exact evaluations between groups)
+              const int ft = fresh_tid();
+              const int fcol = ft & 31, fhalf = (ft >> 5) & 1;
               f32x16 acc[SEL_NG];
-              slice_scores(t, acc);
-              const int cbase = c0 + 32 * t + 4 * half;
+              slice_scores(t, acc, fcol, fhalf);
+              const int cbase = c0 + 32 * t + 4 * fhalf;
 #pragma unroll
               for (int gi = 0; gi < SEL_NG; ++gi) {
-                const int vl = wave * SEL_VW + gi * 32 + col;
+                const int vl = (ft >> 6) * SEL_VW + gi * 32 + fcol;
                 uint32_t am = 0;
 #pragma unroll
                 for (int i = 15; i >= 0; --i) {
@@ -856,15 +860,16 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
       }
       if (S.overflow) {
         // exact fp64 for every pair of this voter tile; one wave per voter
+        // (lane values formed here, so that no lane address is held from the start)
         const int nvt = min(SEL_VT, nv - vt0);
-        for (int u = wave; u < nvt; u += SEL_WAVES) {
+        for (int u = fresh_tid() >> 6; u < nvt; u += SEL_WAVES) {
           const uint16_t* qp = qptr(vt0 + u);
           double m = -__builtin_inf();
 #pragma unroll 1
-          for (int b = lane; b < nc; b += 64) m = fmax(m, dot_exact<D>(qp, kg + (size_t)b * D));
+          for (int b = fresh_tid() & 63; b < nc; b += 64) m = fmax(m, dot_exact<D>(qp, kg + (size_t)b * D));
           m = wave_max(m);
 #pragma unroll 1
-          for (int b = lane; b < nc; b += 64)
+          for (int b = fresh_tid() & 63; b < nc; b += 64)
             if (dot_exact<D>(qp, kg + (size_t)b * D) - m > theta) atomicOr(&S.flagw[b >> 5], 1u << (b & 31));
         }
       }
