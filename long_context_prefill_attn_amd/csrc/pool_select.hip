@@ -295,10 +295,11 @@ __device__ __forceinline__ double dot_exact_prefetched(const uint16_t* __restric
   return acc;
 }
 
-// Exact fp64 scores of the listed pairs, one pair per thread: first the max
-// jobs (jobs[0 .. njob), whose results raise their voters' exact max), then,
-// after a barrier, the ambiguous pairs (amb[0 .. namb)), each of which votes if
-// its exact score clears theta against its voter's exact max.
+// Exact fp64 scores of the listed pairs, one pair per thread: the max jobs
+// (jobs[0 .. njob), whose results raise their voters' exact max) and the
+// ambiguous pairs (amb[0 .. namb)), each of which votes if its exact score
+// clears theta against its voter's exact max once every job has landed (in one
+// round when the two lists fit the workgroup's threads, else jobs first).
 template <int D>
 __device__ __forceinline__ void exact_pairs(SelShared<D>& S, int njob, int namb, const uint16_t* qg,
                                             int group, int n_q, int vt0, const float* kg, double theta) {
@@ -306,6 +307,19 @@ __device__ __forceinline__ void exact_pairs(SelShared<D>& S, int njob, int namb,
     const int v = vt0 + (int)(pr >> 16), b = (int)(pr & 0xFFFFu);
     return dot_exact_prefetched<D>(qg + ((size_t)(v / group) * n_q + (v % group)) * D, kg + (size_t)b * D);
   };
+  if (njob + namb <= SEL_THREADS) {
+    // one pair per thread: every score in one round, the ambiguous ones held in
+    // a register across the barrier that completes the maxima
+    const int e = fresh_tid();
+    const bool has = e < njob + namb;
+    const uint32_t pr = has ? (e < njob ? S.jobs[e] : S.amb[e - njob]) : 0u;
+    const double r = has ? score(pr) : 0.0;
+    if (has && e < njob) atomicMax(&S.mxkey[pr >> 16], dkey(r));
+    __syncthreads();
+    const int b = (int)(pr & 0xFFFFu);
+    if (has && e >= njob && r - dval(S.mxkey[pr >> 16]) > theta) atomicOr(&S.flagw[b >> 5], 1u << (b & 31));
+    return;
+  }
   for (int e = fresh_tid(); e < njob; e += SEL_THREADS) {
     const uint32_t pr = S.jobs[e];
     atomicMax(&S.mxkey[pr >> 16], dkey(score(pr)));
