@@ -442,6 +442,37 @@ __device__ __forceinline__ float row_max(const f32x16 (&s)[2]) {
   return __builtin_fmaxf(mx, partner32(mx));
 }
 
+// Keep bits of a step for masked pipelined steps. Element i of a lane's S^T
+// slice kb holds key 32 kb + 8 (i / 4) + 4 h + i % 4 of the step, so once the
+// slice's keep word (bit t: key 32 kb + t) is shifted down by 4 h, element i's
+// bit is bit 8 (i / 4) + i % 4.
+// keep_or_zero: p if element i's keep bit is set, else +0: the bit sign-extended
+// to a 32-bit mask and ANDed with p's bits (two VALU instructions, no condition
+// registers)
+__device__ __forceinline__ float keep_or_zero(float p, uint32_t ws, int i) {
+  const uint32_t msk = (uint32_t)__builtin_amdgcn_sbfe((int)ws, (uint32_t)(8 * (i >> 2) + (i & 3)), 1u);
+  return __uint_as_float(__float_as_uint(p) & msk);
+}
+
+// The two keep words of a step shifted for this lane (see keep_or_zero).
+__device__ __forceinline__ void shift_keep(const uint32_t (&w)[2], uint32_t (&ws)[2]) {
+  const int h = fresh_lane_id() >> 5;
+  ws[0] = w[0] >> (4 * h);
+  ws[1] = w[1] >> (4 * h);
+}
+
+// Scores of dropped keys set to -inf in place (a bit-field insert per element:
+// the keep bit sign-extended selects the score's bits or those of -inf).
+__device__ __forceinline__ void drop_masked(f32x16 (&s)[2], const uint32_t (&ws)[2]) {
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t msk = (uint32_t)__builtin_amdgcn_sbfe((int)ws[kb], (uint32_t)(8 * (i >> 2) + (i & 3)), 1u);
+      s[kb][i] = __uint_as_float((__float_as_uint(s[kb][i]) & msk) | (0xFF800000u & ~msk));
+    }
+}
+
 // P = 2^(S*scale_log2 - m) packed to fp16 in PV-operand order; l += sum of the packed values
 __device__ __forceinline__ void exp_pack(const f32x16 (&s)[2], float m, float scale_log2, u32x4 (&P)[2][2],
                                          float& l) {
@@ -452,8 +483,9 @@ __device__ __forceinline__ void exp_pack(const f32x16 (&s)[2], float m, float sc
     for (int c = 0; c < 2; ++c) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * c + 2 * w], scale_log2, nmu));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][8 * c + 2 * w + 1], scale_log2, nmu));
+        const int e = 8 * c + 2 * w;
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e], scale_log2, nmu));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][e + 1], scale_log2, nmu));
         P[kb][c][w] = pack_f16x2(p0, p1);
         l = row_sum_add(P[kb][c][w], l);
       }
@@ -476,17 +508,20 @@ constexpr float PSUM_LIMIT = 4096.0f;
 //   PV slot k uses weight fragment f = k / (D/32) (keys 16f .. +15) and output
 //   block nb = k % (D/32), so fragment f is dead after its D/32 MFMAs.
 // Returns the row's sum of step i's packed weights.
-template <int D, bool PV>
+template <int D, bool PV, bool MASKED = false>
 __device__ __forceinline__ float pipe_step(const uint16_t* __restrict__ kt_next, const uint16_t* __restrict__ vt_prev,
                                            const LaneOffs<D>& lo, const bf16x8 (&qf)[D / 16],
                                            const f32x16 (&sc)[2], f32x16 (&sn)[2], const u32x4 (&pp)[2][2],
-                                           u32x4 (&pc)[2][2], f32x16 (&o)[D / 32], float m, float scale_log2) {
+                                           u32x4 (&pc)[2][2], f32x16 (&o)[D / 32], float m, float scale_log2,
+                                           const uint32_t (&mw)[2] = {0u, 0u}) {
   constexpr int NS = D / 8;             // QK^T MFMAs = PV MFMAs per step
   constexpr int HS = NS / 2;            // QK^T MFMAs per S^T accumulator
   constexpr int NB = D / 32;            // output blocks
   constexpr int KA = 3;                 // K fragments in flight
   constexpr int VA = 2;                 // V fragment pairs in flight
   const float nmu = (m == -__builtin_inff()) ? 0.f : -m;
+  uint32_t ws[2] = {0u, 0u};   // MASKED: step i's keep words, shifted for this lane
+  if (MASKED) shift_keep(mw, ws);
 
   auto kread = [&](int k) {
     return *reinterpret_cast<const bf16x8*>(kt_next + (k / HS) * 32 * RS + lo.kofs(k % HS));
@@ -519,9 +554,13 @@ __device__ __forceinline__ float pipe_step(const uint16_t* __restrict__ kt_next,
     }
 #pragma unroll
     for (int pi = k * 16 / NS; pi < (k + 1) * 16 / NS; ++pi) {
-      const int kb = pi >> 3, c = (pi >> 2) & 1, w = pi & 3;
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][8 * c + 2 * w], scale_log2, nmu));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][8 * c + 2 * w + 1], scale_log2, nmu));
+      const int kb = pi >> 3, c = (pi >> 2) & 1, w = pi & 3, e = 8 * c + 2 * w;
+      float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][e], scale_log2, nmu));
+      float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][e + 1], scale_log2, nmu));
+      if (MASKED) {
+        p0 = keep_or_zero(p0, ws[kb], e);
+        p1 = keep_or_zero(p1, ws[kb], e + 1);
+      }
       pc[kb][c][w] = pack_f16x2(p0, p1);
       psum = row_sum_add(pc[kb][c][w], psum);
     }
@@ -560,12 +599,33 @@ __device__ __forceinline__ void pv_only(const uint16_t* __restrict__ vt, const L
 // depend on the order. Loads past the last step re-read the first tile.
 // Src: int first(); int next(int st); int kbase(int st); a state < 0 ends the walk.
 // ---------------------------------------------------------------------------
-template <int D, class Src>
+// Keep bits for the pipelined loop: NoMask (every key of a step kept), or
+// BitsMask, the bit-packed keep row of the lane's query (bit t of word w: key
+// 32 w + t; no row: every key dropped).
+struct NoMask {
+  static constexpr bool kOn = false;
+  __device__ __forceinline__ void load(int, uint32_t (&w)[2]) const { w[0] = w[1] = 0u; }
+};
+struct BitsMask {
+  static constexpr bool kOn = true;
+  const uint32_t* __restrict__ row;
+  __device__ __forceinline__ void load(int st, uint32_t (&w)[2]) const {
+    w[0] = w[1] = 0u;
+    if (row != nullptr && st >= 0) {
+      w[0] = row[2 * st];
+      w[1] = row[2 * st + 1];
+    }
+  }
+};
+
+template <int D, class Src, class Msk = NoMask>
 __device__ __forceinline__ void plain_steps(const TileLoader<D>& tl, uint16_t* lds, Src& src,
                                             const LaneOffs<D>& lo, const bf16x8 (&qf)[D / 16],
-                                            f32x16 (&o)[D / 32], float& m, float& l, float scale_log2) {
+                                            f32x16 (&o)[D / 32], float& m, float& l, float scale_log2,
+                                            const Msk& msk = Msk{}) {
   static_assert(KRK == 4 && KRV == 4, "ring slots are step % 4");
   constexpr int TL = Geo<D>::TILE, NIW = Geo<D>::NIW;
+  constexpr bool MASKED = Msk::kOn;
   uint16_t* kring = lds;
   uint16_t* vring = lds + KRK * TL;
   const int s0 = src.first();
@@ -576,6 +636,14 @@ __device__ __forceinline__ void plain_steps(const TileLoader<D>& tl, uint16_t* l
   int t1 = src.next(s0);                 // step i+1
   int t2 = t1 >= 0 ? src.next(t1) : -1;  // step i+2
   int t3 = -1, t4 = -1;
+  // MASKED: keep words of the pair's two steps (mcur) and of the next pair's
+  // (mnxt, loaded at the top of the pair ahead of its tile loads, so that no
+  // wait for them holds up a tile)
+  uint32_t mcur[2][2], mnxt[2][2];
+  if (MASKED) {
+    msk.load(t0, mcur[0]);
+    msk.load(t1, mcur[1]);
+  }
   tl.issue(false, kfb, kring);              // K[0]
   tl.issue(false, kb(t1), kring + TL);      // K[1]
   tl.issue(true, kfb, vring);               // V[0]
@@ -591,6 +659,10 @@ __device__ __forceinline__ void plain_steps(const TileLoader<D>& tl, uint16_t* l
     bare_barrier();
     t3 = t2 >= 0 ? src.next(t2) : -1;
     t4 = t3 >= 0 ? src.next(t3) : -1;
+    if (MASKED) {
+      msk.load(t2, mnxt[0]);
+      msk.load(t3, mnxt[1]);
+    }
     tl.issue(false, kb(t3), kring + ((kc + 3) & 3) * TL);
     tl.issue(false, kb(t4), kring + kc * TL);
     tl.issue(true, kb(t1), vring + ((kc + 1) & 3) * TL);
@@ -601,15 +673,24 @@ __device__ __forceinline__ void plain_steps(const TileLoader<D>& tl, uint16_t* l
                   u32x4 (&pc)[2][2], auto pc_is_a, int ti, int tn) -> bool {
     constexpr bool HAS_PV = decltype(pvc)::value;
     const int kc = kcc;
-    float psum = pipe_step<D, HAS_PV>(kring + ((kc + 1) & 3) * TL, vring + ((kc + 3) & 3) * TL, lo, qf, sc,
-                                      sn, pp, pc, o, m, scale_log2);
-    if (__builtin_expect(__any(psum > PSUM_LIMIT), 0)) {
+    const uint32_t (&mw)[2] = mcur[decltype(pc_is_a)::value ? 0 : 1];   // MASKED: step i's keep words
+    // MASKED: a row with no max yet (every key so far dropped) that keeps a key
+    // here takes the rescale path, so that its max is the tile's max from then on
+    const bool first_kept = MASKED && m == -__builtin_inff() && (mw[0] | mw[1]) != 0u;
+    float psum = pipe_step<D, HAS_PV, MASKED>(kring + ((kc + 1) & 3) * TL, vring + ((kc + 3) & 3) * TL, lo, qf,
+                                              sc, sn, pp, pc, o, m, scale_log2, mw);
+    if (__builtin_expect(__any(psum > PSUM_LIMIT || first_kept), 0)) {
       // a row's weights outgrew the bound: raise m to the tile's max, rescale
       // what has been accumulated, and form the tile's weights again from
       // scores recomputed out of K[i] (read from global memory: its ring slot
       // may already be refilled, and sc's registers are reused inside pipe_step)
       f32x16 sr[2];
       qk_tile_global<D>(tl.kptr + (size_t)kb(ti) * tl.row_elems, tl.row_elems, qf, sr);
+      if (MASKED) {
+        uint32_t ws[2];
+        shift_keep(mw, ws);
+        drop_masked(sr, ws);
+      }
       const float m_new = __builtin_fmaxf(m, row_max(sr) * scale_log2);
       const float alpha = (m == -__builtin_inff()) ? 1.f : exp2f(m - m_new);
 #pragma unroll
@@ -631,6 +712,10 @@ __device__ __forceinline__ void plain_steps(const TileLoader<D>& tl, uint16_t* l
     t0 = t2;
     t1 = t3;
     t2 = t4;
+    if (MASKED) {
+      mcur[0][0] = mnxt[0][0]; mcur[0][1] = mnxt[0][1];
+      mcur[1][0] = mnxt[1][0]; mcur[1][1] = mnxt[1][1];
+    }
     return true;
   };
   using PV0 = std::integral_constant<bool, false>;
@@ -645,6 +730,11 @@ __device__ __forceinline__ void plain_steps(const TileLoader<D>& tl, uint16_t* l
   u32x4 pa[2][2], pb[2][2];
   qk_tile<D>(kring, lo, qf, sa);
   {
+    if (MASKED) {   // (the first step's weights are formed from these scores: -inf gives 0)
+      uint32_t ws[2];
+      shift_keep(mcur[0], ws);
+      drop_masked(sa, ws);
+    }
     const float m_new = __builtin_fmaxf(m, row_max(sa) * scale_log2);
     const float alpha = (m == -__builtin_inff()) ? 1.f : exp2f(m - m_new);
 #pragma unroll
@@ -693,7 +783,8 @@ __device__ __forceinline__ void plain_steps(const TileLoader<D>& tl, uint16_t* l
 }
 
 // Plain-step sources (see plain_steps).
-// Dense: steps [a, b) whose flag tile is ZERO and whose 64 keys all lie below T.
+// Dense: steps [a, b) whose flag tile is ZERO (any: ZERO or MIXED, for the
+// pipelined loop over bit-packed keep masks) and whose 64 keys all lie below T.
 // The walk keeps a 64-step window of plain bits in scalar registers, filled by one
 // wave-wide ballot over the LDS flag row; finding the next step is scalar bit
 // arithmetic, so an iteration never waits on an LDS read for it (the walk only
@@ -702,10 +793,12 @@ struct DenseSrc {
   int a, b, T;
   const uint32_t* frow;
   int wbase;        // first step of the window
-  uint64_t wmask;   // bit k: step wbase + k is plain
+  uint64_t wmask;   // bit k: step wbase + k is taken
+  bool any = false;
   __device__ void fill(int base) {
     const int sl = base + fresh_lane_id();
-    const bool p = sl < b && step_flag(frow, sl) == TILE_ZERO && (sl + 1) * BN <= T;
+    const int f = sl < b ? step_flag(frow, sl) : TILE_DROPPED;
+    const bool p = (f == TILE_ZERO || (any && f == TILE_MIXED)) && (sl + 1) * BN <= T;
     wbase = base;
     wmask = __ballot(p);
   }
@@ -728,17 +821,19 @@ struct DenseSrc {
 // flag row (every wave forms the same mask, so the barriers inside stay
 // uniform), their K and V tiles double buffered in the first two ring slots
 // (the next such step's tiles load while this one computes). run(st, kt, vt)
-// computes step st from the K and V tiles kt, vt.
+// computes step st from the K and V tiles kt, vt. mixed_piped: the MIXED steps
+// whose keys all lie below T were taken by the masked pipelined pass.
 template <int D, class Run>
 __device__ __forceinline__ void special_steps(const TileLoader<D>& tl, uint16_t* lds, const uint32_t* frow,
-                                              int a, int b, int T, Run&& run) {
+                                              int a, int b, int T, Run&& run, bool mixed_piped = false) {
   constexpr int TL = Geo<D>::TILE, NIW = Geo<D>::NIW;
   const int lane = fresh_lane_id();
   auto next_special = [&](int st) -> int {
     for (int base = st; base < b; base += 64) {
       const int sl = base + lane;
       const int fl = sl < b ? step_flag(frow, sl) : TILE_DROPPED;
-      const uint64_t hit = __ballot(!(fl == TILE_DROPPED || (fl == TILE_ZERO && (sl + 1) * BN <= T)));
+      const bool piped = (fl == TILE_ZERO || (mixed_piped && fl == TILE_MIXED)) && (sl + 1) * BN <= T;
+      const uint64_t hit = __ballot(!(fl == TILE_DROPPED || piped));
       if (hit != 0) return base + __builtin_ctzll(hit);
     }
     return b;
@@ -806,7 +901,7 @@ __device__ __forceinline__ int remap_xcd(int bid, int nblk) {
 // Workgroup = (KV head g, head slice hs, query tile qt, key split). Its 8 waves
 // cover query heads g*group + hs*Hg .. +Hg-1 and rows qt*R .. qt*R+R-1, R = 256/Hg.
 // ---------------------------------------------------------------------------
-template <int D, bool SPLIT>
+template <int D, bool SPLIT, bool BITS>
 __global__ void __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2)))
 attn_dense_kernel(const uint16_t* __restrict__ Q, int C, int n_q, const uint16_t* __restrict__ K,
                   const uint16_t* __restrict__ V, const float* __restrict__ vscales, int T, int n_kv,
@@ -889,9 +984,17 @@ attn_dense_kernel(const uint16_t* __restrict__ Q, int C, int n_q, const uint16_t
   TileLoader<D> tl;
   tl.init(K, V, T, n_kv, g);
 
-  // 1) plain steps: tiles flagged ZERO whose 64 keys all lie below T
-  DenseSrc dsrc{a, b, T, frow, -64, 0};
-  plain_steps<D>(tl, lds, dsrc, lo, qf, o, m, l, scale_log2);
+  if constexpr (BITS) {
+    // 1) bit-packed keep masks: every step whose 64 keys lie below T and are not
+    // all dropped, pipelined, each key's weight kept or zeroed by its bit
+    DenseSrc dsrc{a, b, T, frow, -64, 0, true};
+    const BitsMask bm{qvalid ? reinterpret_cast<const uint32_t*>(mask) + (size_t)qrow * mask_ld : nullptr};
+    plain_steps<D>(tl, lds, dsrc, lo, qf, o, m, l, scale_log2, bm);
+  } else {
+    // 1) plain steps: tiles flagged ZERO whose 64 keys all lie below T
+    DenseSrc dsrc{a, b, T, frow, -64, 0};
+    plain_steps<D>(tl, lds, dsrc, lo, qf, o, m, l, scale_log2);
+  }
 
   // lane-derived values for what follows, formed afresh (see fresh_lane_id)
   const int lane2 = fresh_lane_id();
@@ -915,22 +1018,28 @@ attn_dense_kernel(const uint16_t* __restrict__ Q, int C, int n_q, const uint16_t
   cx.mask_vec = mask_mode == MASK_F16_VEC;
   cx.selrow = nullptr; cx.jrow = -1; cx.blog2 = 0; cx.pool_bias = 0.f;
 
-  // 2) the remaining steps: mask tiles (MIXED) and a ragged last step
+  // 2) the remaining steps: mask tiles (MIXED; with keep bits only a ragged
+  // one) and a ragged last step
   special_steps<D>(tl, lds, frow, a, b, T, [&](int st, const uint16_t* kt, const uint16_t* vt) {
     const int f = step_flag(frow, st);
     cx.key0 = st * BN;
     cx.kvalid = min(BN, T - st * BN);
-    if (f == TILE_MIXED && causal_q0 >= 0)
-      attn_step<D, MODE_CAUSAL_K, true>(kt, vt, lo2, qf, o, m, l, cx);
-    else if (f == TILE_MIXED && mask_mode == MASK_BITS)
-      attn_step<D, MODE_GBITS, true>(kt, vt, lo2, qf, o, m, l, cx);
-    else if (f == TILE_MIXED && cx.kvalid == BN)   // a full step: 8-byte mask loads where aligned
-      attn_step<D, MODE_GMASK, false>(kt, vt, lo2, qf, o, m, l, cx);
-    else if (f == TILE_MIXED)
-      attn_step<D, MODE_GMASK, true>(kt, vt, lo2, qf, o, m, l, cx);
-    else
-      attn_step<D, MODE_PLAIN, true>(kt, vt, lo2, qf, o, m, l, cx);
-  });
+    if constexpr (BITS) {
+      if (f == TILE_MIXED)
+        attn_step<D, MODE_GBITS, true>(kt, vt, lo2, qf, o, m, l, cx);
+      else
+        attn_step<D, MODE_PLAIN, true>(kt, vt, lo2, qf, o, m, l, cx);
+    } else {
+      if (f == TILE_MIXED && causal_q0 >= 0)
+        attn_step<D, MODE_CAUSAL_K, true>(kt, vt, lo2, qf, o, m, l, cx);
+      else if (f == TILE_MIXED && cx.kvalid == BN)   // a full step: 8-byte mask loads where aligned
+        attn_step<D, MODE_GMASK, false>(kt, vt, lo2, qf, o, m, l, cx);
+      else if (f == TILE_MIXED)
+        attn_step<D, MODE_GMASK, true>(kt, vt, lo2, qf, o, m, l, cx);
+      else
+        attn_step<D, MODE_PLAIN, true>(kt, vt, lo2, qf, o, m, l, cx);
+    }
+  }, BITS);
 
   const float lt = l + partner32(l);
   if (!qvalid2) return;
@@ -1211,19 +1320,17 @@ static hipError_t dense_impl(const uint16_t* Q, int C, int n_q, const uint16_t* 
   const size_t lds = Geo<D>::LDS_BYTES + (size_t)((p.n_ktile + 63) / 64) * 16;   // rings + 2-bit flag row
   const bool vec = (mask_ld % 4 == 0) && (reinterpret_cast<uintptr_t>(mask) % 8 == 0);
   const int mask_mode = mask_bits ? MASK_BITS : vec ? MASK_F16_VEC : MASK_F16;
-  if (p.splits > 1) {
-    hipFuncSetAttribute((const void*)attn_dense_kernel<D, true>,
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL((attn_dense_kernel<D, true>), dim3(grid), dim3(NT), lds, stream, Q, C, n_q, K, V,
-                       vscales, T, n_kv, mask, mask_ld, sl2, O, flags, p.n_qt, p.n_ktile, p.splits, part_o,
-                       part_ml, mask_mode, p.hg_log2, causal_q0);
-  } else {
-    hipFuncSetAttribute((const void*)attn_dense_kernel<D, false>,
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL((attn_dense_kernel<D, false>), dim3(grid), dim3(NT), lds, stream, Q, C, n_q, K,
-                       V, vscales, T, n_kv, mask, mask_ld, sl2, O, flags, p.n_qt, p.n_ktile, 1, part_o,
-                       part_ml, mask_mode, p.hg_log2, causal_q0);
-  }
+  if (mask_bits && causal_q0 >= 0) return hipErrorInvalidValue;   // keep bits come without a causal rule
+  auto launch = [&](auto kern, int splits) {
+    hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(NT), lds, stream, Q, C, n_q, K, V, vscales, T, n_kv, mask,
+                       mask_ld, sl2, O, flags, p.n_qt, p.n_ktile, splits, part_o, part_ml, mask_mode, p.hg_log2,
+                       causal_q0);
+  };
+  if (p.splits > 1 && mask_bits) launch(attn_dense_kernel<D, true, true>, p.splits);
+  else if (p.splits > 1) launch(attn_dense_kernel<D, true, false>, p.splits);
+  else if (mask_bits) launch(attn_dense_kernel<D, false, true>, 1);
+  else launch(attn_dense_kernel<D, false, false>, 1);
   return hipGetLastError();
 }
 

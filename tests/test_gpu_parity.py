@@ -761,8 +761,9 @@ def _bits_of(mask16, words):
 
 def test_fold_keep_bits_bit_exact(lp):
     """The folded keep bits equal the packing of the oracle's fold mask on the
-    fold2k5 chunks (words past ceil(T/32) untouched), and attention over them is
-    bit-identical to attention over the device-folded fp16 mask."""
+    fold2k5 chunks (words past ceil(T/32) untouched), and attention over them (the
+    pipelined keep-bit loop) and over the device-folded fp16 mask are both within
+    tolerance of the oracle's attention under the fold mask."""
     import torch
     w = make_workload("fold2k5")
     s = w.spec
@@ -788,7 +789,11 @@ def test_fold_keep_bits_bit_exact(lp):
     b = lp.prefill_attn_dense_bits(q, k, v, lp.fold_keep_bits(ti, tc, q0, T, s.fold_width, s.fold_recent),
                                    s.scale)
     torch.cuda.synchronize()
-    assert np.array_equal(a.cpu().numpy().view(np.uint32), b.cpu().numpy().view(np.uint32))
+    rows = np.arange(0, C, 7)                                   # every 7th row, all heads
+    want = dense_ref(f64(w.Q[q0:T]), f64(w.K[:T]), f64(w.V[:T]),
+                     fold_mask_ref(idx, cnt, q0, T, s.fold_width, s.fold_recent), s.scale, rows=rows)
+    assert_close(b.cpu().numpy()[rows], want, "fold bits attention")
+    assert_close(a.cpu().numpy()[rows], want, "fold fp16-mask attention")
 
 
 @pytest.mark.parametrize("C,q_start,T,width,recent,K,seed", [
@@ -979,9 +984,9 @@ def test_dense_bits(lp, C, T, n_q, n_kv, d, kind, words):
     assert_close(got, want, f"bits {kind}")
     if kind == "random":
         assert np.all(got[0] == 0.0)
-    # the same keep pattern as an fp16 mask gives the same bits of output
+    # the same keep pattern as an fp16 mask (per-step masked loop) is within tolerance too
     same = gpu_dense(lp, q, k, v, np.where(keep, np.float16(0), np.float16(-30000)).astype(np.float16), scale)
-    assert np.array_equal(got.view(np.uint32), same.view(np.uint32))
+    assert_close(same, want, f"fp16 {kind}")
 
 
 # ---------------------------------------------------------------- block sizes other than 128
