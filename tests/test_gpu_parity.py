@@ -989,6 +989,36 @@ def test_dense_bits(lp, C, T, n_q, n_kv, d, kind, words):
     assert_close(same, want, f"fp16 {kind}")
 
 
+@pytest.mark.parametrize("kind", ["late_low", "sparse_long", "split_long"])
+def test_dense_bits_pipelined(lp, kind):
+    """The pipelined keep-bit loop over long histories: every key of the first half
+    dropped and the rest kept at random with scores near -200 in exp2 units (a row
+    has no max until its first kept key, whose weights would underflow against a
+    zero max); 10% of 16K keys kept (every step MIXED, ragged end); and a few rows
+    whose key range is split over workgroups."""
+    rng = np.random.default_rng({"late_low": 61, "sparse_long": 62, "split_long": 63}[kind])
+    d, n_q, n_kv = 128, 4, 2
+    C, T = {"late_low": (96, 8192), "sparse_long": (64, 16383), "split_long": (8, 20000)}[kind]
+    scale = float(np.float32(1 / math.sqrt(d)))
+    if kind == "late_low":
+        q = np.zeros((C, n_q, d), np.float32)
+        q[:, :, 0] = -1568.0                                  # s scale log2(e) ~ -200 for k0 ~ 1
+        k = np.zeros((T, n_kv, d), np.float32)
+        k[:, :, 0] = 1.0 + 0.01 * rng.standard_normal((T, n_kv))
+        q, k = bf16_bits(q), bf16_bits(k)
+        keep = np.zeros((C, T), bool)
+        keep[:, T // 2:] = rng.random((C, T - T // 2)) < 0.3
+    else:
+        q, k = rand_bits(rng, C, n_q, d), rand_bits(rng, T, n_kv, d)
+        keep = rng.random((C, T)) < 0.1
+    v = rand_bits(rng, T, n_kv, d)
+    bits = pack_keep_bits(keep)
+    say("dense bits pipelined", kind, C, T)
+    got = gpu_dense_bits(lp, q, k, v, bits, scale)
+    want = dense_ref(f64(q), f64(k), f64(v), bits_mask_ref(bits, T), scale)
+    assert_close(got, want, f"bits pipelined {kind}")
+
+
 # ---------------------------------------------------------------- block sizes other than 128
 @pytest.mark.parametrize("B,N,q_start,n_q,n_kv,d,alpha", [
     (16, 700, 300, 4, 2, 128, 0.2),      # four blocks per 64-key step, eight query blocks per workgroup
