@@ -66,6 +66,10 @@ def parse():
                     help="skip the dense comparators on the block-sparse part's tensors")
     ap.add_argument("--parts", default="dense,blocksparse",
                     help="subset of the step to run (for profiler runs); the default runs the whole step")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the step as HIP graph replays (one graph per part, captured after the "
+                         "eager timed steps, which still give the per-kernel times): the launch cost of "
+                         "the small prompts' many short kernels leaves the step")
     return ap.parse_args()
 
 
@@ -288,6 +292,45 @@ def main():
         if n:
             kern[name] = {"avg_ms": tot / n, "launches_per_step": n // args.steps, "ms_per_step": tot / args.steps}
 
+    # graph replays: each part's launches captured once into a HIP graph (the
+    # library allocates, synchronizes and clears nothing on its stream, so its
+    # calls capture as they run), then K steps timed as replays
+    eager = None
+    if args.graph:
+        graphs = {}
+        for name, fn, on in (("dense", run_dense, do_dense), ("blocksparse", run_sparse, do_sparse)):
+            if not on:
+                continue
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                fn()
+            torch.cuda.current_stream().wait_stream(side)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
+            graphs[name] = g
+        for g in graphs.values():
+            g.replay()
+        torch.cuda.synchronize()
+        gev = []
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            e0, e1, e2 = ev(), ev(), ev()
+            e0.record()
+            if "dense" in graphs:
+                graphs["dense"].replay()
+            e1.record()
+            if "blocksparse" in graphs:
+                graphs["blocksparse"].replay()
+            e2.record()
+            gev.append((e0, e1, e2))
+        torch.cuda.synchronize()
+        eager = {"ms_per_step": round(ms_step, 4), "dense_ms": round(dense_ms, 4), "sparse_ms": round(sparse_ms, 4)}
+        ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+        dense_ms = float(np.median([a.elapsed_time(b) for a, b, _ in gev])) if do_dense else 0.0
+        sparse_ms = float(np.median([b.elapsed_time(c) for _, b, c in gev])) if do_sparse else 0.0
+
     # dense comparators on the block-sparse part's own tensors, timed after the
     # step loop (3 runs each, median): the same chunking as the block-sparse
     # calls' prompt in 4,096-row chunks, and (32K only) one call over the whole prompt
@@ -412,11 +455,13 @@ def main():
                                                    if fold else ""), do_dense),
                        ("block-sparse prefill" + (" in chunks (incremental pooled index)" if len(scalls) > 1 else ""),
                         do_sparse)) if on),
-                   "parallelism": "none (1 GPU)"},
+                   "parallelism": "none (1 GPU)",
+                   "launch": "HIP graph replays (kernel times from the eager steps before them)" if args.graph
+                             else "eager"},
         "tokens_per_s": round(Nd / (dense_ms * 1e-3)) if do_dense else round(Ns / (sparse_ms * 1e-3)),
         "pct_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "parts": parts, "kernels": kern, "roofline": roofline,
-        "hbm_kernels": hbm_kernels, "cpu_baseline": cpu,
+        "hbm_kernels": hbm_kernels, "cpu_baseline": cpu, "eager": eager,
         "device": {"name": props.name, "cus": props.multi_processor_count},
     }
     print(json.dumps(line), flush=True)
