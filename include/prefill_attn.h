@@ -384,6 +384,24 @@ int pa_timing_enable(int on);
 int pa_timing_reset(void);
 int pa_timing_read(const char* kernel, double* total_ms, int64_t* launches);
 
+/* Selection path counters (diagnostics; "Porting FlashPrefill V2 to Apple
+ * silicon", A cheap map of where the attention lives: the selection must be
+ * exact, so which of its exact paths a run took is worth knowing). Every voter
+ * tile of a select_blocks / select_blocks_ld call on the current device adds to
+ *   counts[0]  voter tiles scored,
+ *   counts[1]  tiles whose ambiguous pairs were decided in fp64 (listed once),
+ *   counts[2]  tiles whose ambiguous list overflowed and were relisted group by
+ *              group (pass 2),
+ *   counts[3]  tiles decided in fp64 pair by pair (magnitudes past the
+ *              filter's range, |theta| past fp32's, or a near-max / max-job list
+ *              that overflowed).
+ * pa_select_path_counts waits for the device, copies the four totals since the
+ * last reset into counts (host memory, 4 entries) and, if reset != 0, clears
+ * them. The totals are shared by every caller on the device (calls running
+ * concurrently add into the same counters). Returns PA_OK, PA_EINVAL (counts
+ * null) or PA_EHIP. */
+int pa_select_path_counts(int64_t* counts, int reset);
+
 #ifdef __cplusplus
 }
 #endif

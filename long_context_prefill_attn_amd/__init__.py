@@ -348,6 +348,16 @@ def calibrate_alpha(Q, K_pool, q_start: int, block: int, scale: float, target_sk
     return bisect_alpha(skip_of, target_skip, 0.0, 1.0, iters)
 
 
+def select_path_counts(reset: bool = False) -> dict:
+    """Voter tiles scored by the selection on the current device since the last
+    reset, and how many took each exact path (see pa_select_path_counts):
+    {"tiles", "listed", "relisted", "pairwise"}. Waits for the device."""
+    import ctypes
+    out = (ctypes.c_int64 * 4)()
+    check(lib().pa_select_path_counts(ctypes.addressof(out), 1 if reset else 0), "pa_select_path_counts")
+    return dict(zip(("tiles", "listed", "relisted", "pairwise"), (int(v) for v in out)))
+
+
 class timing:
     """Per-kernel HIP-event timing inside the library (see pa_timing_* in the header)."""
 

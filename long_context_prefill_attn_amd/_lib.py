@@ -17,6 +17,7 @@ PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EHIP, PA_EWORKSPACE, PA_ESCRATCH = 0, -1, 
 EXPORTS = {
     # name: (restype, argtypes)
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "pa_select_path_counts": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int]),
     "prefill_attn_dense": (ctypes.c_int, [
         ctypes.c_void_p, ctypes.c_int, ctypes.c_int,                    # Q, C, n_q
         ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,   # K, V, T, n_kv

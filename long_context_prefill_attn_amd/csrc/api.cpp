@@ -445,6 +445,11 @@ int pa_timing_reset(void) {
   return PA_OK;
 }
 
+int pa_select_path_counts(int64_t* counts, int reset) {
+  if (counts == nullptr) return PA_EINVAL;
+  return hip_status(pa::select_path_counts(counts, reset != 0));
+}
+
 int pa_timing_read(const char* kernel, double* total_ms, int64_t* launches) {
   if (kernel == nullptr || total_ms == nullptr || launches == nullptr) return PA_EINVAL;
   std::lock_guard<std::mutex> lk(g_timing_mu);

@@ -71,6 +71,8 @@ int device_cus();
 hipError_t launch_pool(const uint16_t* K, const uint16_t* V, int T, int n_kv, int d, int block,
                        int b_first, float* K_pool, float* V_pool, int pool_ld, hipStream_t stream);
 
+// The selection path counters since the last reset (waits for the device).
+hipError_t select_path_counts(int64_t* out, bool reset);
 hipError_t launch_select(const uint16_t* Q, int C, int q_start, int n_q, int n_kv, int d,
                          const float* K_pool, int pool_ld, int T, int block, double theta,
                          int sink_blocks, int window_blocks, int dense_tail_blocks,

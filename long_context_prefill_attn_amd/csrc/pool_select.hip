@@ -245,6 +245,11 @@ __device__ __forceinline__ double dval(unsigned long long k) {
   return __longlong_as_double((k >> 63) ? (k & ~(1ull << 63)) : ~k);
 }
 
+// Selection path counters of this device (pa_select_path_counts): voter tiles
+// scored; tiles whose ambiguous pairs were listed once and decided in fp64;
+// tiles relisted group by group (pass 2); tiles decided in fp64 pair by pair.
+__device__ unsigned long long g_sel_paths[4];
+
 template <int D>
 struct SelShared {
   struct {
@@ -887,6 +892,11 @@ __global__ void __launch_bounds__(SEL_THREADS) __attribute__((amdgpu_waves_per_e
             if (dot_exact<D>(qp, kg + (size_t)b * D) - m > theta) atomicOr(&S.flagw[b >> 5], 1u << (b & 31));
         }
       }
+      if (tid == 0) {   // the tile's path (S.overflow is final here: set before the last barrier)
+        atomicAdd(&g_sel_paths[0], 1ull);
+        const int path = S.overflow ? 3 : (redo ? 2 : (go ? 1 : -1));
+        if (path > 0) atomicAdd(&g_sel_paths[path], 1ull);
+      }
     }
   }
   __syncthreads();
@@ -921,6 +931,19 @@ __global__ void __launch_bounds__(SEL_THREADS) select_merge_kernel(
   __syncthreads();   // every partial word is read before the row is rewritten
   finish_selection(flagw, wsum, nb, nc, jj, j, n_qblk, sink_blocks, window_blocks, dense_tail_blocks,
                    out, sel_cnt + (size_t)g * n_qblk + jj);
+}
+
+hipError_t select_path_counts(int64_t* out, bool reset) {
+  unsigned long long h[4] = {0, 0, 0, 0};
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpyFromSymbol(h, HIP_SYMBOL(g_sel_paths), sizeof(h), 0, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return e;
+  for (int i = 0; i < 4; ++i) out[i] = (int64_t)h[i];
+  if (reset) {
+    const unsigned long long z[4] = {0, 0, 0, 0};
+    e = hipMemcpyToSymbol(HIP_SYMBOL(g_sel_paths), z, sizeof(z), 0, hipMemcpyHostToDevice);
+  }
+  return e;
 }
 
 hipError_t launch_select(const uint16_t* Q, int C, int q_start, int n_q, int n_kv, int d,

@@ -257,3 +257,7 @@ def test_bisect_alpha_host_logic():
         assert abs(a - want) < 1e-9 and s >= target, (target, a, s)
     assert lp.bisect_alpha(skip_of, 0.99) == (1.0, 0.97)    # unreachable: hi and its share
     assert lp.bisect_alpha(skip_of, 0.0) == (0.0, 0.0)      # reached at lo
+
+
+def test_select_path_counts_rejects_null():
+    assert _lib.lib().pa_select_path_counts(None, 0) == _lib.PA_EINVAL

@@ -89,12 +89,18 @@ def test_select_bit_exact(lp, C, q_start, n_q, n_kv, d, block, alpha):
     assert np.array_equal(idx.cpu().numpy(), ridx)
 
 
-def _select_pooled(lp, q, kp, q_start, block, alpha, scale):
-    """Selection on a given pooled-key array, GPU vs oracle, bit-exact."""
+def _select_pooled(lp, q, kp, q_start, block, alpha, scale, path=None):
+    """Selection on a given pooled-key array, GPU vs oracle, bit-exact; `path`:
+    the exact path ("listed", "relisted", "pairwise") some voter tile must take."""
     import torch
-    idx, cnt = lp.select_blocks(dev_bf16(q), torch.from_numpy(np.ascontiguousarray(kp)).cuda(),
-                                q_start, block, alpha, scale)
-    torch.cuda.synchronize()
+    Kp = torch.from_numpy(np.ascontiguousarray(kp)).cuda()
+    Qd = dev_bf16(q)
+    lp.select_path_counts(reset=True)
+    idx, cnt = lp.select_blocks(Qd, Kp, q_start, block, alpha, scale)
+    paths = lp.select_path_counts(reset=True)
+    say("selection paths", paths)
+    if path is not None:
+        assert paths[path] >= 1, paths
     ridx, rcnt = select_ref(f64(q), kp, q_start, block, alpha, scale)
     assert np.array_equal(cnt.cpu().numpy(), rcnt)
     assert np.array_equal(idx.cpu().numpy(), ridx)
@@ -125,7 +131,8 @@ def test_select_threshold_edge(lp, n_q):
     kp[0, 21:31, 0] = 0.5                               # clearly kept
     kp[0, 31:40, 0] = -100.0                            # clearly dropped
     say("select threshold edge", n_q)
-    rcnt = _select_pooled(lp, bf16_bits(q), kp, q_start, block, alpha, scale)
+    rcnt = _select_pooled(lp, bf16_bits(q), kp, q_start, block, alpha, scale,
+                          path="relisted" if n_q == 16 else "listed")
     assert 10 < rcnt[0, 0] - 1 < 30                     # both sides of the edge occur
 
 
@@ -141,7 +148,7 @@ def test_select_identical_pooled_keys(lp, n_q):
     kp = np.broadcast_to(row, (n_kv, nb, d)).copy()
     scale = float(np.float32(1 / math.sqrt(d)))
     say("select identical keys", n_q)
-    rcnt = _select_pooled(lp, q, kp, q_start, block, 1.0, scale)
+    rcnt = _select_pooled(lp, q, kp, q_start, block, 1.0, scale, path="pairwise")
     assert np.all(rcnt == 1)
 
 
@@ -174,7 +181,7 @@ def test_select_ambiguous_relisted(lp, d, nc, dense_group):
             v = np.nextafter(v, np.float32(np.inf if s > 0 else -np.inf))
         kp[0, c, 0] = v
     say("select ambiguous relisted", d, nc, dense_group)
-    rcnt = _select_pooled(lp, bf16_bits(q), kp, q_start, block, alpha, scale)
+    rcnt = _select_pooled(lp, bf16_bits(q), kp, q_start, block, alpha, scale, path="relisted")
     base = 2 + len(kept)                                # the max, the clearly kept, the diagonal
     assert base < rcnt[0, 0] < base + len(amb)          # both sides of the edge occur
 
@@ -189,7 +196,7 @@ def test_select_huge_magnitudes(lp):
     kp, _ = pooled_index_ref(f64(k), f64(k), block)
     scale = float(np.float32(1 / math.sqrt(d)))
     say("select huge magnitudes")
-    rcnt = _select_pooled(lp, q, kp, q_start, block, 0.1, scale)
+    rcnt = _select_pooled(lp, q, kp, q_start, block, 0.1, scale, path="pairwise")
     assert rcnt.min() >= 1
 
 
@@ -486,7 +493,13 @@ def test_blocksparse_32k(lp):
     s = w.spec
     B = s.block
     say("blocksparse 32K: GPU")
+    lp.select_path_counts(reset=True)
     kp, vp, idx, cnt, got = _blocksparse_gpu(lp, w.Q, w.K, w.V, 0, B, s.alpha, s.scale)
+    paths = lp.select_path_counts(reset=True)
+    say("selection paths", paths)
+    # every (KV head, query block) past the first scores its 512 voters as two tiles,
+    # and the pairs inside the filter's band are decided in fp64 from the list
+    assert paths["tiles"] == s.n_kv * (s.N // B - 1) * 2 and paths["listed"] >= 1, paths
     Q64, K64, V64 = f64(w.Q), f64(w.K), f64(w.V)
     rkp, rvp = pooled_index_ref(K64, V64, B)
     assert np.array_equal(kp.view(np.uint32), rkp.view(np.uint32))
@@ -619,7 +632,14 @@ def test_blocksparse_128k_chunked(lp):
     B = s.block
     say("blocksparse 128K chunked: GPU")
     nb = s.N // B
+    lp.select_path_counts(reset=True)
     kp, vp, sels, got = _chunked_sparse_gpu(lp, w.Q, w.K, w.V, s.chunks, B, s.alpha, s.scale, cap=nb)
+    paths = lp.select_path_counts(reset=True)
+    say("selection paths", paths)
+    # at about 1,000 candidates some voter tiles hold more pairs inside the fp16
+    # filter's band than the list does: the relisting path runs (chunk 31's arrays
+    # are compared whole below)
+    assert paths["listed"] >= 1 and paths["relisted"] >= 1, paths
     say("blocksparse 128K chunked: oracle")
     K64, V64 = f64(w.K), f64(w.V)
     rkp, rvp = pooled_index_ref(K64, V64, B)
