@@ -543,6 +543,10 @@ __device__ __forceinline__ float pipe_step(const uint16_t* __restrict__ kt_next,
   float psum = 0.f;
 #pragma unroll
   for (int k = 0; k < NS; ++k) {
+    // the operand reads and the two MFMAs at raised wave priority, the weights
+    // of step i at the normal one: of the SIMD's two waves, the one about to
+    // feed the matrix core issues first, the other's VALU work fills in behind
+    __builtin_amdgcn_s_setprio(1);
     const bf16x8 a = kf[k % KA];
     if (k + KA < NS) kf[k % KA] = kread(k + KA);
     if (PV && k + VA < NS) vread(k + VA, vf[(k + VA) % (VA + 1)]);
@@ -552,6 +556,7 @@ __device__ __forceinline__ float pipe_step(const uint16_t* __restrict__ kt_next,
       const v4i16 (&v)[2] = vf[k % (VA + 1)];
       o[k % NB] = pv_mfma(v[0], v[1], pp[f >> 1][f & 1], o[k % NB]);
     }
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int pi = k * 16 / NS; pi < (k + 1) * 16 / NS; ++pi) {
       const int kb = pi >> 3, c = (pi >> 2) & 1, w = pi & 3, e = 8 * c + 2 * w;
