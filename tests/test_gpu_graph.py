@@ -128,3 +128,35 @@ def test_graph_blocksparse_chunks(lp):
     g = capture(step)
     other = torch.randn(1 << 20, device="cuda")
     replay_checks(g, outs, want, lambda: other.mul_(1.0001).sum())
+
+
+def test_graph_gqa_chunks(lp):
+    """gqa4k: the 4,096-row chunk and the 237-row tail (split key range and the
+    combine) through the fp16-mask entry and the causal entry, in one graph."""
+    from workloads import causal_mask
+    w = make_workload("gqa4k")
+    s = w.spec
+    Q, K, V = dev_bf16(w.Q), dev_bf16(w.K), dev_bf16(w.V)
+    O1 = torch.empty((w.N, s.n_q, s.d), dtype=torch.float32, device="cuda")
+    O2 = torch.empty_like(O1)
+    calls = []
+    for q0, C in s.chunks:
+        T = q0 + C
+        ws = torch.empty(lp.prefill_attn_dense_workspace(C, T, s.n_q, s.n_kv, s.d), dtype=torch.uint8, device="cuda")
+        calls.append((q0, C, torch.from_numpy(causal_mask(q0, C)).cuda(), ws))
+
+    def step():
+        for q0, C, mask, ws in calls:
+            T = q0 + C
+            lp.prefill_attn_dense(Q[q0:T], K[:T], V[:T], mask, s.scale, O=O1[q0:T], workspace=ws)
+            lp.prefill_attn_dense_causal(Q[q0:T], K[:T], V[:T], q0, s.scale, O=O2[q0:T], workspace=ws)
+
+    say("graph gqa chunks")
+    for o in (O1, O2):
+        o.fill_(float("nan"))
+    step()
+    torch.cuda.synchronize()
+    want = [O1.clone().view(torch.int32), O2.clone().view(torch.int32)]
+    g = capture(step)
+    other = torch.randn(1 << 20, device="cuda")
+    replay_checks(g, [O1, O2], want, lambda: other.mul_(1.0001).sum())
