@@ -569,7 +569,8 @@ __device__ __forceinline__ float pipe_step(const uint16_t* __restrict__ kt_next,
       pc[kb][c][w] = pack_f16x2(p0, p1);
       psum = row_sum_add(pc[kb][c][w], psum);
     }
-    __builtin_amdgcn_sched_barrier(0);
+    // (weights' VALU work may move across slots; memory and MFMA order stay fenced)
+    __builtin_amdgcn_sched_barrier(0x2);
   }
   return psum;
 }
